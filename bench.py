@@ -1,0 +1,228 @@
+"""Benchmark: one-launch MoE decode step on the K3-scale one-GPU share (MI355X).
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--batches 1,2,4,8] [--no-cpu-baseline]
+
+Prints ONE JSON line. `value` is decode tokens/s at batch 1 (the headline configuration:
+92 layers, hidden 7168, MLA with a 4096-long latent cache, 48 local experts top-1 plus a
+shared expert, LM-head slice 7168 x 40960); the other batch sizes of the metric are reported
+under "batches". Inputs are synthetic and seeded and already resident in HBM when the timed
+region starts. "roofline" divides the step's algorithmic bytes (the weights the step must
+read given its routing, the cache read and written, and the logits) by the megakernel's
+average duration, measured with HIP events on the launch stream, against 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "c3"
+
+
+# ------------------------------------------------------------------------------------------
+# algorithmic bytes of one step (what the step must move, given its routing)
+# ------------------------------------------------------------------------------------------
+def algorithmic_bytes(cfg: synth.ModelConfig, B: int, T: int, kv_len: int, route: np.ndarray) -> dict:
+    """route: [n_layers][B*T][top_k] selected experts. Returns a byte breakdown."""
+    H, V, M = cfg.hidden, cfg.vocab, B * T
+    per_layer_fixed = {}
+    for t in synth.tensor_list(cfg):
+        if t.layer < 0 or t.kind.startswith("exp_"):
+            continue
+        nb = synth.numel(t.shape) * (4 if t.dist == "sigmoid" else 2)
+        per_layer_fixed[t.layer] = per_layer_fixed.get(t.layer, 0) + nb
+    expert_bytes = 3 * cfg.ffn * H * 2
+    weights = sum(per_layer_fixed.values())
+    experts = 0
+    for l in range(cfg.n_layers):
+        experts += len(np.unique(route[l])) * expert_bytes
+    head = V * H * 2 + H * 2  # LM head + final norm
+    embed = M * H * 2
+    lat = cfg.latent_dim
+    n_attn = len(cfg.attention_layers())
+    if cfg.attn_kind == synth.ATTN_GQA:
+        entry = 2 * cfg.n_kv_heads * cfg.head_dim * 2
+    else:
+        entry = lat * 2
+    cache_read = n_attn * B * kv_len * entry
+    cache_write = n_attn * M * entry
+    state = 0
+    if cfg.attn_kind == synth.ATTN_HYBRID:
+        state = 2 * len(cfg.kda_layers()) * B * cfg.n_heads * cfg.kda_dk * cfg.kda_dv * 4
+    logits = M * V * 4
+    total = weights + experts + head + embed + cache_read + cache_write + state + logits
+    return {"total": total, "weights": weights, "experts": experts, "lm_head": head, "embed": embed,
+            "cache_read": cache_read, "cache_write": cache_write, "state": state, "logits": logits}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("mk_kernel.hip", "mk_api.cpp", "mk_internal.h"):
+        with open(os.path.join(ROOT, "decode_megakernel_cu_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(B: int):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on this kernel."""
+    path = os.path.join(ROOT, "profiles", "megakernel_k3_pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("kernel_hash") != kernel_source_hash():
+        return None
+    return d.get("per_launch_bytes", {}).get(str(B))
+
+
+# ------------------------------------------------------------------------------------------
+# CPU baseline: the oracle on the host's cores, on a bounded sample of the same step
+# ------------------------------------------------------------------------------------------
+def cpu_baseline(sample_layers: int = 8, budget_s: float = 12.0) -> dict:
+    from dataclasses import replace
+
+    import oracle
+
+    w = synth.WORKLOADS[WORKLOAD]
+    cfg = replace(w.model, n_layers=sample_layers, expert_pool_layers=0)
+    spec = synth.Spec(seed=0)
+    toks = synth.tokens(spec.seed, 0, cfg.vocab, w.batch, w.new_tokens)
+    caches0 = synth.host_caches(cfg, spec, w.batch, w.kv_len)
+    # first run records the tensors the step reads, which are then served from memory so the
+    # timed runs measure the oracle's arithmetic rather than the input generator
+    rec = oracle.Provider(cfg, spec)
+    oracle.decode_step(cfg, rec, toks, w.kv_len, {k: v.copy() for k, v in caches0.items()})
+    mem = {}
+    for t in synth.tensor_list(cfg):
+        if any(name == t.name for name, _ in rec.fetched):
+            mem[t.name] = synth.host_tensor(spec, t)
+    prov = oracle.Provider(cfg, spec, overrides=mem)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        c = {k: v.copy() for k, v in caches0.items()}
+        t0 = time.perf_counter()
+        oracle.decode_step(cfg, prov, toks, w.kv_len, c)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 5:
+            break
+    t = float(np.median(times))
+    # extrapolate the per-layer part to 92 layers; the embedding and LM head are paid once
+    head = oracle.Provider(replace(cfg, n_layers=0), spec, overrides=mem)
+    c = {k: v.copy() for k, v in caches0.items()}
+    t0 = time.perf_counter()
+    oracle.decode_step(replace(cfg, n_layers=0), head, toks, w.kv_len, c)
+    t_head = time.perf_counter() - t0
+    per_layer = max(t - t_head, 0.0) / sample_layers
+    step = t_head + per_layer * w.model.n_layers
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(w.batch * w.new_tokens / step, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample_layers} of {w.model.n_layers} layers of the batch-1 step (+ embedding and LM head), "
+                      f"median of {len(times)} runs, weights served from host memory; per-layer time scaled to "
+                      f"{w.model.n_layers} layers (step {step:.2f} s)"}
+
+
+# ------------------------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batches", default="1,2,4,8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the decode step; --gpus {args.gpus} is not supported "
+              f"(this build runs on exactly one GPU, with no collectives)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from synth.device_inputs import DeviceModel
+
+    w = synth.WORKLOADS[WORKLOAD]
+    cfg = w.model
+    spec = synth.Spec(seed=args.seed)
+    t0 = time.time()
+    dm = DeviceModel(cfg, spec, device=0)
+    batches = [int(b) for b in args.batches.split(",")]
+    dm.fill_caches(max(batches), w.kv_len)
+    print(f"# model loaded in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    results = {}
+    for B in batches:
+        toks = synth.tokens(spec.seed, 1, cfg.vocab, B, w.new_tokens)
+        d_tok = torch.from_numpy(toks.astype(np.int32)).cuda()
+        logits = torch.empty((B, w.new_tokens, cfg.vocab), dtype=torch.float32, device="cuda")
+        _, route = dm.step(toks, w.kv_len, route=True, logits=logits, d_tokens=d_tok)
+        torch.cuda.synchronize()
+        dm.poll()
+        route = route.cpu().numpy()
+        for _ in range(args.warmup):
+            dm.step(toks, w.kv_len, route=False, logits=logits, d_tokens=d_tok)
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        for i in range(args.steps):
+            starts[i].record(stream)
+            dm.step(toks, w.kv_len, route=False, logits=logits, d_tokens=d_tok)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        dm.poll()
+        kms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+        by = algorithmic_bytes(cfg, B, w.new_tokens, w.kv_len, route)
+        results[B] = {"ms_per_step": wall * 1e3 / args.steps, "kernel_ms_avg": float(kms.mean()),
+                      "kernel_ms_p10": float(np.percentile(kms, 10)), "kernel_ms_p90": float(np.percentile(kms, 90)),
+                      "tokens_per_s": B * w.new_tokens * args.steps / wall, "bytes": by["total"],
+                      "gbs": by["total"] / (kms.mean() * 1e-3) / 1e9}
+        print(f"# B={B}: {results[B]['kernel_ms_avg']:.3f} ms/launch, {results[B]['tokens_per_s']:.1f} tok/s, "
+              f"{results[B]['gbs']:.0f} GB/s ({by['total'] / 1e9:.2f} GB/step)", file=sys.stderr, flush=True)
+    dm.close()
+
+    head = results[batches[0]]
+    achieved = head["gbs"]
+    out = {
+        "metric": "decode tokens/s at batch 1/2/4/8 + achieved HBM GB/s as % of peak",
+        "value": round(head["tokens_per_s"], 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,0.02) weights, N(0,1) latent cache, uniform tokens)",
+        "config": {"workload": "k3-share decode step: 92 layers, hidden 7168, MLA 16 heads (q_lora 1536, kv_lora 512, "
+                               "rope 64), latent cache 4096, 48 experts top-1 ffn 2048 + shared 512, vocab slice "
+                               "40960", "batch": batches[0], "new_tokens": w.new_tokens, "kv_len": w.kv_len,
+                   "launches_per_step": 1},
+        "batches": {str(B): {"tokens_per_s": round(r["tokens_per_s"], 2), "kernel_ms": round(r["kernel_ms_avg"], 4),
+                             "gb_per_step": round(r["bytes"] / 1e9, 3), "hbm_gbs": round(r["gbs"], 1),
+                             "hbm_frac": round(r["gbs"] / HBM_PEAK_GBS, 4)} for B, r in results.items()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(batches[0])},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,465 @@
+// mk_api.cpp -- host side of the C ABI in include/mk.h: validation, arena and workspace layouts,
+// weight loading (with the one repack the kernel wants), the single launch per decode step, and
+// device status polling.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "mk_internal.h"
+
+namespace mk {
+size_t kernel_lds_bytes();
+hipError_t launch_decode(const Params& p, int nblocks, hipStream_t stream);
+hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd, int kvl, hipStream_t stream);
+hipError_t occupancy(int* blocks_per_cu);
+}  // namespace mk
+
+using namespace mk;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr uint64_t kAlign = 256;
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Slot {
+  uint64_t off = 0, bytes = 0;
+  int repack = 0;  // 1: W_uk transposed per head
+};
+
+using Key = std::tuple<int, int, int>;  // kind, layer (or slot), expert
+
+int layer_kind(const mk_config& c, int l) {
+  if (c.attn_kind == MK_ATTN_GQA) return kGqa;
+  if (c.attn_kind == MK_ATTN_MLA) return kMla;
+  return (l % c.hybrid_period == c.hybrid_period - 1) ? kMla : kKda;
+}
+
+struct Layout {
+  std::map<Key, Slot> tensors;
+  std::vector<LayerDev> layers;  // offsets (as pointers relative to 0) until rebased
+  uint64_t arena = 0;
+  WsLayout ws{};
+  uint64_t kv = 0, state = 0;
+  int n_mla = 0, n_kda = 0, n_gqa = 0;
+  int nsplit_max = 0;
+};
+
+int check_config(const mk_config* c) {
+  if (!c) return fail(MK_E_INVAL, "config is NULL");
+  if (c->n_layers < 1 || c->hidden < 8 || c->vocab < 1) return fail(MK_E_INVAL, "n_layers, hidden and vocab must be positive");
+  if (c->hidden % 8) return fail(MK_E_UNSUPPORTED, "hidden must be a multiple of 8");
+  if (c->attn_kind < 0 || c->attn_kind > 2) return fail(MK_E_INVAL, "attn_kind %d unknown", c->attn_kind);
+  if (c->max_batch < 1 || c->max_batch > MK_MAX_BATCH) return fail(MK_E_INVAL, "max_batch must be in 1..%d", MK_MAX_BATCH);
+  if (c->max_new_tokens < 1 || c->max_new_tokens > MK_MAX_NEW_TOKENS)
+    return fail(MK_E_INVAL, "max_new_tokens must be in 1..%d", MK_MAX_NEW_TOKENS);
+  if (c->kv_capacity < c->max_new_tokens) return fail(MK_E_INVAL, "kv_capacity below max_new_tokens");
+  if (c->n_experts < 1 || c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 8)
+    return fail(MK_E_INVAL, "need 1 <= top_k <= min(n_experts, 8)");
+  if (c->ffn < 8 || c->ffn % 8 || c->shared_ffn < 0 || c->shared_ffn % 8)
+    return fail(MK_E_UNSUPPORTED, "ffn and shared_ffn must be multiples of 8");
+  if (c->expert_pool_layers < 0) return fail(MK_E_INVAL, "expert_pool_layers must be >= 0");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(MK_E_INVAL, "rms_eps / rope_theta out of range");
+  if (c->n_heads < 1) return fail(MK_E_INVAL, "n_heads must be positive");
+  if (c->attn_kind == MK_ATTN_GQA) {
+    if (c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return fail(MK_E_INVAL, "n_heads must be a multiple of n_kv_heads");
+    if (c->head_dim < 8 || c->head_dim % 8 || c->head_dim > 2 * kMaxRopePairs)
+      return fail(MK_E_UNSUPPORTED, "head_dim must be a multiple of 8 and at most %d", 2 * kMaxRopePairs);
+    const int qg = c->n_heads / c->n_kv_heads;
+    if ((2 * kChunk + c->max_new_tokens * qg) * c->head_dim + c->max_new_tokens * qg * kChunk > kLdsFloats)
+      return fail(MK_E_UNSUPPORTED, "GQA group too large for the attention tile");
+  } else {
+    if (c->kv_lora < 8 || c->kv_lora % 8 || c->q_lora < 8 || c->q_lora % 8 || c->nope_dim < 8 || c->nope_dim % 8 ||
+        c->v_dim < 8 || c->v_dim % 8 || c->rope_dim < 2 || c->rope_dim % 2 || c->rope_dim > 2 * kMaxRopePairs)
+      return fail(MK_E_UNSUPPORTED, "MLA dims must be multiples of 8 (rope_dim even, <= %d)", 2 * kMaxRopePairs);
+    const int lat = c->kv_lora + c->rope_dim;
+    if ((kChunk + c->n_heads) * lat + c->n_heads * kChunk > kLdsFloats)
+      return fail(MK_E_UNSUPPORTED, "MLA latent too wide for the attention tile");
+    if (c->attn_kind == MK_ATTN_HYBRID) {
+      if (c->hybrid_period < 1) return fail(MK_E_INVAL, "hybrid_period must be positive");
+      if (c->kda_dk % 64 || c->kda_dk < 64 || c->kda_dk > 128 || c->kda_dv < 8 || c->kda_dv % 8)
+        return fail(MK_E_UNSUPPORTED, "kda_dk must be 64 or 128 and kda_dv a multiple of 8");
+    }
+  }
+  return MK_OK;
+}
+
+Layout make_layout(const mk_config& c) {
+  Layout Lt;
+  const uint64_t H = c.hidden, V = c.vocab, E = c.n_experts, F = c.ffn, SF = c.shared_ffn;
+  uint64_t off = align_up(sizeof(LayerDev) * (uint64_t)c.n_layers);
+  auto put = [&](int kind, int layer, int expert, uint64_t bytes, int repack = 0) {
+    Slot s;
+    s.off = off;
+    s.bytes = bytes;
+    s.repack = repack;
+    Lt.tensors[Key(kind, layer, expert)] = s;
+    off = align_up(off + bytes);
+    return s.off;
+  };
+  put(MK_W_EMBED, -1, -1, V * H * 2);
+  put(MK_W_FINAL_NORM, -1, -1, H * 2);
+  put(MK_W_LM_HEAD, -1, -1, V * H * 2);
+  Lt.layers.resize(c.n_layers);
+  auto rel = [](uint64_t o) { return reinterpret_cast<const uint16_t*>(o); };
+  for (int l = 0; l < c.n_layers; ++l) {
+    LayerDev& d = Lt.layers[l];
+    std::memset(&d, 0, sizeof d);
+    d.kind = layer_kind(c, l);
+    d.slot = c.expert_pool_layers ? l % c.expert_pool_layers : l;
+    d.attn_norm = rel(put(MK_W_ATTN_NORM, l, -1, H * 2));
+    if (d.kind == kGqa) {
+      d.ord = Lt.n_gqa++;
+      const uint64_t dq = (uint64_t)c.n_heads * c.head_dim, dkv = (uint64_t)c.n_kv_heads * c.head_dim;
+      d.wq = rel(put(MK_W_WQ, l, -1, dq * H * 2));
+      d.wk = rel(put(MK_W_WK, l, -1, dkv * H * 2));
+      d.wv = rel(put(MK_W_WV, l, -1, dkv * H * 2));
+      d.wo = rel(put(MK_W_WO, l, -1, H * dq * 2));
+    } else if (d.kind == kMla) {
+      d.ord = Lt.n_mla++;
+      const uint64_t nh = c.n_heads, ql = c.q_lora, kvl = c.kv_lora, rd = c.rope_dim, nd = c.nope_dim, vd = c.v_dim;
+      d.w_dq = rel(put(MK_W_W_DQ, l, -1, ql * H * 2));
+      d.q_norm = rel(put(MK_W_Q_NORM, l, -1, ql * 2));
+      d.w_uq = rel(put(MK_W_W_UQ, l, -1, nh * (nd + rd) * ql * 2));
+      d.w_dkv = rel(put(MK_W_W_DKV, l, -1, (kvl + rd) * H * 2));
+      d.kv_norm = rel(put(MK_W_KV_NORM, l, -1, kvl * 2));
+      d.w_ukT = rel(put(MK_W_W_UK, l, -1, nh * nd * kvl * 2, 1));
+      d.w_uv = rel(put(MK_W_W_UV, l, -1, nh * vd * kvl * 2));
+      d.wo = rel(put(MK_W_WO, l, -1, H * nh * vd * 2));
+    } else {
+      d.ord = Lt.n_kda++;
+      const uint64_t nh = c.n_heads, dk = c.kda_dk, dv = c.kda_dv;
+      d.kwq = rel(put(MK_W_KDA_WQ, l, -1, nh * dk * H * 2));
+      d.kwk = rel(put(MK_W_KDA_WK, l, -1, nh * dk * H * 2));
+      d.kwv = rel(put(MK_W_KDA_WV, l, -1, nh * dv * H * 2));
+      d.alpha = reinterpret_cast<const float*>(put(MK_W_KDA_ALPHA, l, -1, nh * dk * 4));
+      d.beta = reinterpret_cast<const float*>(put(MK_W_KDA_BETA, l, -1, nh * 4));
+      d.wo = rel(put(MK_W_WO, l, -1, H * nh * dv * 2));
+    }
+    d.moe_norm = rel(put(MK_W_MOE_NORM, l, -1, H * 2));
+    d.router = rel(put(MK_W_ROUTER, l, -1, E * H * 2));
+    if (SF) {
+      d.sh_gate = rel(put(MK_W_SH_GATE, l, -1, SF * H * 2));
+      d.sh_up = rel(put(MK_W_SH_UP, l, -1, SF * H * 2));
+      d.sh_down = rel(put(MK_W_SH_DOWN, l, -1, H * SF * 2));
+    }
+  }
+  // expert pool: per slot three contiguous blocks [E][F][H], [E][F][H], [E][H][F]
+  const int nslot = c.expert_pool_layers ? c.expert_pool_layers : c.n_layers;
+  std::vector<uint64_t> gbase(nslot), ubase(nslot), dbase(nslot);
+  for (int s = 0; s < nslot; ++s) {
+    gbase[s] = off;
+    for (int e = 0; e < c.n_experts; ++e) put(MK_W_EXP_GATE, s, e, F * H * 2);
+    ubase[s] = off;
+    for (int e = 0; e < c.n_experts; ++e) put(MK_W_EXP_UP, s, e, F * H * 2);
+    dbase[s] = off;
+    for (int e = 0; e < c.n_experts; ++e) put(MK_W_EXP_DOWN, s, e, H * F * 2);
+  }
+  for (int l = 0; l < c.n_layers; ++l) {
+    LayerDev& d = Lt.layers[l];
+    d.exp_gate = rel(gbase[d.slot]);
+    d.exp_up = rel(ubase[d.slot]);
+    d.exp_down = rel(dbase[d.slot]);
+  }
+  Lt.arena = off;
+
+  // caches
+  const uint64_t Bm = c.max_batch, cap = c.kv_capacity;
+  if (c.attn_kind == MK_ATTN_GQA)
+    Lt.kv = 2ull * c.n_layers * Bm * c.n_kv_heads * cap * c.head_dim * 2;
+  else
+    Lt.kv = (uint64_t)Lt.n_mla * Bm * cap * (c.kv_lora + c.rope_dim) * 2;
+  Lt.state = (uint64_t)Lt.n_kda * Bm * c.n_heads * c.kda_dk * c.kda_dv * 4;
+
+  // workspace
+  const uint64_t M = (uint64_t)std::min(MK_MAX_M, c.max_batch * c.max_new_tokens);
+  const uint64_t nh = c.n_heads;
+  uint64_t w1 = 0, w2 = 0, w3 = 0, dmax = 0, w4 = 0, wo2 = 0;
+  if (c.attn_kind == MK_ATTN_GQA) {
+    w1 = nh * c.head_dim;
+    w2 = w3 = (uint64_t)c.n_kv_heads * c.head_dim;
+    dmax = c.head_dim;
+  } else {
+    w1 = std::max<uint64_t>(c.q_lora, nh * c.kda_dk);
+    w2 = std::max<uint64_t>(c.kv_lora + c.rope_dim, nh * c.kda_dk);
+    w3 = std::max<uint64_t>(nh * (c.nope_dim + c.rope_dim), nh * c.kda_dv);
+    w4 = nh * c.kv_lora;
+    wo2 = nh * c.v_dim;
+    dmax = std::max<uint64_t>(c.kv_lora, c.kda_dv);
+  }
+  Lt.nsplit_max = (c.kv_capacity + kChunk - 1) / kChunk;
+  uint64_t part = M * nh * Lt.nsplit_max * (dmax + 2);
+  if (c.attn_kind != MK_ATTN_GQA) {
+    // the W_uk repack stages a host tensor here
+    const uint64_t uk = nh * c.nope_dim * c.kv_lora * 2 / 4 + 64;
+    part = std::max(part, uk);
+  }
+  WsLayout& w = Lt.ws;
+  uint64_t o = 0;
+  auto take = [&](uint64_t bytes) {
+    uint64_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  w.flags = take(kMaxBlocks * 4);
+  w.status = take(64 * 4);
+  w.rope = take((uint64_t)MK_MAX_NEW_TOKENS * kMaxRopePairs * 2 * 4);
+  w.x = take(M * H * 4);
+  w.a1 = take(M * w1 * 4);
+  w.a2 = take(M * w2 * 4);
+  w.a3 = take(M * w3 * 4);
+  w.a4 = take(M * std::max<uint64_t>(w4, 1) * 4);
+  w.att = take(M * nh * dmax * 4);
+  w.o2 = take(M * std::max<uint64_t>(wo2, 1) * 4);
+  w.part = take(part * 4);
+  w.part_floats = part;
+  w.rlog = take(M * E * 4);
+  w.sact = take(M * std::max<uint64_t>(SF, 1) * 4);
+  w.eact = take(M * c.top_k * F * 4);
+  w.scratch = w.part;
+  w.total = o;
+  return Lt;
+}
+
+}  // namespace
+
+struct mk_ctx {
+  mk_config cfg;
+  Layout lt;
+  int device;
+  uint8_t* arena;
+  uint8_t* ws;
+  int nblocks;
+  uint64_t launches;
+  uint64_t watchdog_ticks;
+  bool poisoned;
+  std::vector<uint8_t> loaded;  // per tensor slot, in map order
+  std::map<Key, size_t> index;
+  size_t n_loaded;
+};
+
+extern "C" {
+
+const char* mk_last_error(void) { return g_err.c_str(); }
+
+int mk_query_sizes(const mk_config* cfg, mk_sizes* out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(MK_E_INVAL, "sizes output is NULL");
+  Layout lt = make_layout(*cfg);
+  out->arena_bytes = lt.arena;
+  out->workspace_bytes = lt.ws.total;
+  out->kv_bytes = lt.kv;
+  out->kda_state_bytes = lt.state;
+  g_err.clear();
+  return MK_OK;
+}
+
+int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_bytes, void* d_workspace,
+              uint64_t workspace_bytes, mk_ctx** out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(MK_E_INVAL, "context output is NULL");
+  *out = nullptr;
+  Layout lt = make_layout(*cfg);
+  if (device != MK_DEVICE_NONE) {
+    if (!d_arena || !d_workspace) return fail(MK_E_INVAL, "arena and workspace must be device pointers");
+    if ((reinterpret_cast<uintptr_t>(d_arena) | reinterpret_cast<uintptr_t>(d_workspace)) & (kAlign - 1))
+      return fail(MK_E_INVAL, "arena and workspace must be 256-byte aligned");
+  }
+  if (arena_bytes < lt.arena) return fail(MK_E_NOMEM, "arena has %llu bytes, needs %llu", (unsigned long long)arena_bytes, (unsigned long long)lt.arena);
+  if (workspace_bytes < lt.ws.total)
+    return fail(MK_E_NOMEM, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes, (unsigned long long)lt.ws.total);
+  mk_ctx* c = new mk_ctx();
+  c->cfg = *cfg;
+  c->lt = lt;
+  c->device = device;
+  c->arena = static_cast<uint8_t*>(d_arena);
+  c->ws = static_cast<uint8_t*>(d_workspace);
+  c->launches = 0;
+  c->poisoned = false;
+  c->n_loaded = 0;
+  size_t i = 0;
+  for (auto& kv : c->lt.tensors) c->index[kv.first] = i++;
+  c->loaded.assign(i, 0);
+  c->nblocks = 0;
+  if (device != MK_DEVICE_NONE) {
+    hipError_t e = hipSetDevice(device);
+    int cus = 0, rate_khz = 0, per_cu = 0;
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, device);
+    if (e == hipSuccess) e = occupancy(&per_cu);
+    if (e != hipSuccess) {
+      delete c;
+      return fail(MK_E_HIP, "device query failed: %s", hipGetErrorString(e));
+    }
+    if (per_cu < 1) {
+      delete c;
+      return fail(MK_E_UNSUPPORTED, "the megakernel does not fit on a CU (LDS %zu bytes)", kernel_lds_bytes());
+    }
+    c->nblocks = std::min(cus, kMaxBlocks);
+    double ms = 2000.0;
+    if (const char* env = std::getenv("MK_WATCHDOG_MS")) ms = std::max(1.0, std::atof(env));
+    c->watchdog_ticks = (uint64_t)(ms * (rate_khz > 0 ? rate_khz : 100000));
+    // write the layer table (pointers rebased onto the arena) and clear the workspace
+    std::vector<LayerDev> tab = c->lt.layers;
+    const uintptr_t base = reinterpret_cast<uintptr_t>(c->arena);
+    for (auto& d : tab) {
+      const uint16_t** ps[] = {&d.attn_norm, &d.moe_norm, &d.router, &d.sh_gate, &d.sh_up, &d.sh_down, &d.wo,
+                               &d.wq, &d.wk, &d.wv, &d.w_dq, &d.q_norm, &d.w_uq, &d.w_dkv, &d.kv_norm, &d.w_ukT,
+                               &d.w_uv, &d.kwq, &d.kwk, &d.kwv, &d.exp_gate, &d.exp_up, &d.exp_down};
+      for (auto p : ps)
+        if (*p) *p = reinterpret_cast<const uint16_t*>(base + reinterpret_cast<uintptr_t>(*p));
+      if (d.alpha) d.alpha = reinterpret_cast<const float*>(base + reinterpret_cast<uintptr_t>(d.alpha));
+      if (d.beta) d.beta = reinterpret_cast<const float*>(base + reinterpret_cast<uintptr_t>(d.beta));
+    }
+    e = hipMemcpy(c->arena, tab.data(), sizeof(LayerDev) * tab.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(c->ws, 0, c->lt.ws.total);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      delete c;
+      return fail(MK_E_HIP, "context set-up failed: %s", hipGetErrorString(e));
+    }
+  }
+  *out = c;
+  g_err.clear();
+  return MK_OK;
+}
+
+int mk_load_weights(mk_ctx* c, const mk_tensor_desc* d, int n, void* stream) {
+  if (!c) return fail(MK_E_INVAL, "context is NULL");
+  if (n < 0 || (n > 0 && !d)) return fail(MK_E_INVAL, "bad descriptor list");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < n; ++i) {
+    const mk_tensor_desc& t = d[i];
+    const bool global = t.kind == MK_W_EMBED || t.kind == MK_W_FINAL_NORM || t.kind == MK_W_LM_HEAD;
+    const bool expert = t.kind == MK_W_EXP_GATE || t.kind == MK_W_EXP_UP || t.kind == MK_W_EXP_DOWN;
+    Key k(t.kind, global ? -1 : t.layer, expert ? t.expert : -1);
+    auto it = c->lt.tensors.find(k);
+    if (t.kind < 0 || t.kind >= MK_W_N_KINDS || it == c->lt.tensors.end())
+      return fail(MK_E_INVAL, "tensor %d: no tensor of kind %d, layer %d, expert %d in this model", i, t.kind, t.layer, t.expert);
+    if (t.bytes != it->second.bytes)
+      return fail(MK_E_INVAL, "tensor %d (kind %d layer %d): %llu bytes given, %llu expected", i, t.kind, t.layer,
+                  (unsigned long long)t.bytes, (unsigned long long)it->second.bytes);
+    if (!t.src) return fail(MK_E_INVAL, "tensor %d: NULL source", i);
+    if (c->device != MK_DEVICE_NONE) {
+      uint8_t* dst = c->arena + it->second.off;
+      hipError_t e;
+      if (it->second.repack == 1) {
+        const void* src = t.src;
+        if (!t.src_on_device) {
+          e = hipMemcpyAsync(c->ws + c->lt.ws.scratch, t.src, t.bytes, hipMemcpyHostToDevice, st);
+          if (e != hipSuccess) return fail(MK_E_HIP, "copy of tensor %d failed: %s", i, hipGetErrorString(e));
+          src = c->ws + c->lt.ws.scratch;
+        }
+        e = launch_transpose_uk(static_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(dst), c->cfg.n_heads,
+                                c->cfg.nope_dim, c->cfg.kv_lora, st);
+      } else {
+        e = hipMemcpyAsync(dst, t.src, t.bytes, t.src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, st);
+      }
+      if (e != hipSuccess) return fail(MK_E_HIP, "load of tensor %d failed: %s", i, hipGetErrorString(e));
+    }
+    size_t idx = c->index[k];
+    if (!c->loaded[idx]) {
+      c->loaded[idx] = 1;
+      c->n_loaded++;
+    }
+  }
+  g_err.clear();
+  return MK_OK;
+}
+
+int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens, void* d_kv, float* d_kda_state,
+                   float* d_logits, int32_t* d_route, void* stream) {
+  if (!c) return fail(MK_E_INVAL, "context is NULL");
+  const mk_config& g = c->cfg;
+  if (B < 1 || B > g.max_batch) return fail(MK_E_INVAL, "batch %d outside 1..%d", B, g.max_batch);
+  if (T < 1 || T > g.max_new_tokens) return fail(MK_E_INVAL, "n_new_tokens %d outside 1..%d", T, g.max_new_tokens);
+  if (B * T > MK_MAX_M) return fail(MK_E_UNSUPPORTED, "batch * n_new_tokens = %d exceeds %d", B * T, MK_MAX_M);
+  if (kv_len < 0) return fail(MK_E_INVAL, "kv_len %d is negative", kv_len);
+  if ((long long)kv_len + T > g.kv_capacity)
+    return fail(MK_E_KV_OVERFLOW, "kv_len %d + %d new tokens exceeds capacity %d", kv_len, T, g.kv_capacity);
+  if (!d_tokens || !d_logits || !d_kv) return fail(MK_E_INVAL, "tokens, kv and logits must be non-NULL");
+  if (g.attn_kind == MK_ATTN_HYBRID && !d_kda_state) return fail(MK_E_INVAL, "hybrid model needs the delta-rule state");
+  const int M = B * T;
+  // shape limits of the LDS tiles for this step
+  const int np = M * g.top_k;
+  if ((long long)np * g.ffn + (long long)M * g.shared_ffn > kLdsFloats)
+    return fail(MK_E_UNSUPPORTED, "expert activations of this step do not fit LDS");
+  if (c->n_loaded != c->loaded.size())
+    return fail(MK_E_STATE, "%zu of %zu weight tensors loaded", c->n_loaded, c->loaded.size());
+  if (c->poisoned) return fail(MK_E_STATE, "context poisoned by an earlier device error");
+  if (c->device == MK_DEVICE_NONE) return fail(MK_E_STATE, "host-only context cannot launch");
+
+  const WsLayout& w = c->lt.ws;
+  Params p{};
+  p.L = g.n_layers; p.H = g.hidden; p.V = g.vocab; p.nh = g.n_heads; p.nkv = g.n_kv_heads; p.hd = g.head_dim;
+  p.ql = g.q_lora; p.kvl = g.attn_kind == MK_ATTN_GQA ? 0 : g.kv_lora; p.rd = g.rope_dim; p.nd = g.nope_dim;
+  p.vd = g.v_dim; p.dk = g.kda_dk; p.dv = g.kda_dv; p.E = g.n_experts; p.topk = g.top_k; p.F = g.ffn;
+  p.SF = g.shared_ffn; p.norm_topk = g.norm_topk; p.cap = g.kv_capacity; p.Bmax = g.max_batch;
+  p.eps = g.rms_eps; p.rope_theta = g.rope_theta;
+  p.B = B; p.T = T; p.M = M; p.kv_len = kv_len;
+  p.nsplit = (kv_len + T + kChunk - 1) / kChunk;
+  p.epoch = (uint32_t)(c->launches * 65536ull);
+  p.tokens = d_tokens; p.logits = d_logits; p.route = d_route;
+  p.layers = reinterpret_cast<const LayerDev*>(c->arena);
+  auto wt = [&](int kind) { return reinterpret_cast<const uint16_t*>(c->arena + c->lt.tensors.at(Key(kind, -1, -1)).off); };
+  p.embed = wt(MK_W_EMBED); p.final_norm = wt(MK_W_FINAL_NORM); p.lm_head = wt(MK_W_LM_HEAD);
+  p.kv = static_cast<uint16_t*>(d_kv);
+  p.kda_state = d_kda_state;
+  uint8_t* ws = c->ws;
+  p.flags = reinterpret_cast<uint32_t*>(ws + w.flags);
+  p.status = reinterpret_cast<uint32_t*>(ws + w.status);
+  auto f = [&](uint64_t o) { return reinterpret_cast<float*>(ws + o); };
+  p.rope = f(w.rope); p.x = f(w.x); p.a1 = f(w.a1); p.a2 = f(w.a2); p.a3 = f(w.a3); p.a4 = f(w.a4);
+  p.att = f(w.att); p.o2 = f(w.o2); p.part = f(w.part); p.rlog = f(w.rlog); p.sact = f(w.sact); p.eact = f(w.eact);
+  p.watchdog_ticks = c->watchdog_ticks;
+  const int nh = g.n_heads;
+  const uint64_t dmax = g.attn_kind == MK_ATTN_GQA ? g.head_dim : std::max(g.kv_lora, g.kda_dv);
+  if ((uint64_t)M * nh * p.nsplit * (dmax + 2) > w.part_floats)
+    return fail(MK_E_UNSUPPORTED, "attention partials exceed the workspace");
+  hipError_t e = hipSetDevice(c->device);
+  if (e == hipSuccess) e = launch_decode(p, c->nblocks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MK_E_HIP, "launch failed: %s", hipGetErrorString(e));
+  c->launches++;
+  g_err.clear();
+  return MK_OK;
+}
+
+int mk_poll(mk_ctx* c) {
+  if (!c) return fail(MK_E_INVAL, "context is NULL");
+  if (c->device == MK_DEVICE_NONE) return c->poisoned ? fail(MK_E_DEVICE, "context poisoned") : MK_OK;
+  uint32_t st[4] = {0, 0, 0, 0};
+  hipError_t e = hipMemcpy(st, c->ws + c->lt.ws.status, sizeof st, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MK_E_HIP, "status read failed: %s", hipGetErrorString(e));
+  if (st[0] != 0 || c->poisoned) {
+    c->poisoned = true;
+    if (st[3]) return fail(MK_E_DEVICE, "token %u of the step is outside the vocabulary", st[3] - 1);
+    return fail(MK_E_DEVICE, "device watchdog fired at grid barrier %u", st[2]);
+  }
+  g_err.clear();
+  return MK_OK;
+}
+
+void mk_destroy(mk_ctx* c) { delete c; }
+
+}  // extern "C"

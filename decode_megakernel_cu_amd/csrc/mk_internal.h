@@ -1,0 +1,61 @@
+// mk_internal.h -- layouts shared by the host front end (mk_api.cpp) and the megakernel
+// (mk_kernel.hip). Not part of the public ABI.
+#pragma once
+#include <stdint.h>
+
+#include "../../include/mk.h"
+
+namespace mk {
+
+constexpr int kThreads = 512;            // threads per workgroup (8 wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxBlocks = 1024;         // barrier flag slots
+constexpr int kLdsFloats = 36 * 1024;    // 144 KiB of LDS per workgroup
+constexpr int kChunk = 16;               // cache positions per split-KV task
+constexpr int kMaxRopePairs = 64;
+constexpr int kMaxQueue = MK_MAX_M * 8;  // token-expert pairs per step (top_k <= 8)
+
+enum LayerKind : int32_t { kGqa = 0, kMla = 1, kKda = 2 };
+
+// Device-side pointers of one layer, stored in a table at the start of the arena.
+struct LayerDev {
+  int32_t kind, ord, slot, pad;
+  const uint16_t *attn_norm, *moe_norm, *router, *sh_gate, *sh_up, *sh_down, *wo;
+  const uint16_t *wq, *wk, *wv;                                     // GQA
+  const uint16_t *w_dq, *q_norm, *w_uq, *w_dkv, *kv_norm, *w_ukT, *w_uv;  // MLA (w_ukT: [h][kv_lora][nope])
+  const uint16_t *kwq, *kwk, *kwv;                                  // KDA
+  const float *alpha, *beta;
+  const uint16_t *exp_gate, *exp_up, *exp_down;                     // pool slot base, [E][F][H] / [E][H][F]
+};
+
+// Workspace carve-up (byte offsets from the workspace base).
+struct WsLayout {
+  uint64_t flags, status, rope, x, a1, a2, a3, a4, att, o2, part, rlog, sact, eact, scratch, total;
+  uint64_t part_floats;  // capacity of the partials buffer in floats
+};
+
+// Everything the kernel needs, passed by value.
+struct Params {
+  // model
+  int32_t L, H, V, nh, nkv, hd, ql, kvl, rd, nd, vd, dk, dv, E, topk, F, SF, norm_topk, cap, Bmax;
+  float eps, rope_theta;
+  // step
+  int32_t B, T, M, kv_len, nsplit;
+  uint32_t epoch;
+  const int32_t* tokens;
+  float* logits;
+  int32_t* route;
+  // weights
+  const LayerDev* layers;
+  const uint16_t *embed, *final_norm, *lm_head;
+  // caches
+  uint16_t* kv;  // GQA: K block then V block; MLA: latent
+  float* kda_state;
+  // workspace
+  uint32_t* flags;
+  uint32_t* status;  // [0] error code, [1] abort flag, [2] detail
+  float *rope, *x, *a1, *a2, *a3, *a4, *att, *o2, *part, *rlog, *sact, *eact;
+  uint64_t watchdog_ticks;  // s_memrealtime ticks (100 MHz) a barrier may wait
+};
+
+}  // namespace mk

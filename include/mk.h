@@ -1,0 +1,150 @@
+/*
+ * mk.h -- C ABI of the one-launch MoE decode megakernel for AMD MI355X (gfx950).
+ *
+ * One call to mk_decode_step runs a whole decode step of a deep MoE transformer
+ * -- every layer's RMSNorm, attention (GQA, multi-head latent attention over a
+ * compressed cache, or the gated delta rule of the hybrid model), router top-k,
+ * SwiGLU routed and shared experts, residuals, and the final norm plus LM head --
+ * as a single persistent kernel launch. This is the method of
+ * "700 TPS on Kimi K3: A Case for TPU Megakernels" (tpu-megakernels README:
+ * the decode step fused into one kernel, FAQ "why build a custom megakernel";
+ * weights of layer n+1 fetched while layer n computes, in the news digests'
+ * sections on where the speedup comes from), built for one MI355X.
+ *
+ * Ownership: the caller owns every device buffer (weight arena, workspace, KV
+ * cache, recurrent state, tokens, logits). The library allocates no device
+ * memory; it owns only the host context.
+ * Errors: every function returns MK_OK (0) or a negative mk_status; argument
+ * errors are detected on the host before anything is launched, and
+ * mk_last_error() then describes the failure (thread-local string).
+ * Threading: a context may be used by one host thread and one stream at a time
+ * (its workspace holds the grid-barrier flags of the running step).
+ */
+#ifndef MK_H
+#define MK_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_MAX_M 16          /* batch * new tokens per step */
+#define MK_MAX_BATCH 8
+#define MK_MAX_NEW_TOKENS 8
+#define MK_DEVICE_NONE (-1)  /* host-only context: validates and lays out, never launches */
+
+typedef enum {
+  MK_OK = 0,
+  MK_E_INVAL = -1,        /* bad argument: batch, T, kv_len, token pointer, config field, tensor id */
+  MK_E_STATE = -2,        /* weights not loaded, host-only context, or context poisoned by a device error */
+  MK_E_KV_OVERFLOW = -3,  /* kv_len + n_new_tokens > kv_capacity */
+  MK_E_NOMEM = -4,        /* a caller buffer is smaller than mk_query_sizes requires */
+  MK_E_HIP = -5,          /* a HIP runtime call failed (message in mk_last_error) */
+  MK_E_DEVICE = -6,       /* the device reported an error (watchdog timeout or bad token id); see mk_poll */
+  MK_E_UNSUPPORTED = -7   /* valid but not supported by this build (e.g. shape limits) */
+} mk_status;
+
+typedef enum { MK_ATTN_GQA = 0, MK_ATTN_MLA = 1, MK_ATTN_HYBRID = 2 } mk_attn_kind;
+
+/* Model and capacity description. Matrices are bf16, stored [out][in] (row = output feature).
+ * attn_kind GQA: n_heads query heads and n_kv_heads key/value heads of head_dim, RoPE over the
+ *   whole head. MLA: n_heads heads, q_lora / kv_lora latent ranks, rope_dim + nope_dim query-key
+ *   width per head, v_dim value width. HYBRID: layer l is MLA when l % hybrid_period ==
+ *   hybrid_period - 1, otherwise a gated delta-rule layer with n_heads heads of kda_dk x kda_dv.
+ * Every layer has a MoE block: n_experts routed SwiGLU experts of width ffn, top_k chosen by a
+ * softmax router (weights are the chosen probabilities; renormalised over the chosen set when
+ * norm_topk != 0), plus a shared SwiGLU expert of width shared_ffn (0 = none).
+ * expert_pool_layers > 0: layer l uses the expert weights of pool slot l % expert_pool_layers. */
+typedef struct {
+  int32_t n_layers, hidden, vocab, attn_kind;
+  int32_t n_heads, n_kv_heads, head_dim;
+  int32_t q_lora, kv_lora, rope_dim, nope_dim, v_dim;
+  int32_t kda_dk, kda_dv, hybrid_period;
+  int32_t n_experts, top_k, ffn, shared_ffn, norm_topk;
+  int32_t expert_pool_layers;
+  int32_t max_batch, max_new_tokens, kv_capacity;
+  float rms_eps, rope_theta;
+} mk_config;
+
+typedef struct {
+  uint64_t arena_bytes;      /* weights (device, caller-allocated, 256-byte aligned) */
+  uint64_t workspace_bytes;  /* activations, attention partials, barrier flags, status (device) */
+  uint64_t kv_bytes;         /* KV cache (device), layout below */
+  uint64_t kda_state_bytes;  /* recurrent state of delta-rule layers (device, fp32), 0 if none */
+} mk_sizes;
+
+/* Weight kinds. Shapes (row-major) for mk_load_weights:
+ *   EMBED [vocab][hidden]  FINAL_NORM [hidden]  LM_HEAD [vocab][hidden]
+ *   per layer: ATTN_NORM, MOE_NORM [hidden]; ROUTER [n_experts][hidden];
+ *     SH_GATE, SH_UP [shared_ffn][hidden]; SH_DOWN [hidden][shared_ffn]
+ *     GQA: WQ [n_heads*head_dim][hidden], WK, WV [n_kv_heads*head_dim][hidden], WO [hidden][n_heads*head_dim]
+ *     MLA: W_DQ [q_lora][hidden], Q_NORM [q_lora], W_UQ [n_heads*(nope_dim+rope_dim)][q_lora]
+ *          (per head: nope part first, then rope part), W_DKV [kv_lora+rope_dim][hidden]
+ *          (latent first, then the shared rope key), KV_NORM [kv_lora], W_UK [n_heads][nope_dim][kv_lora],
+ *          W_UV [n_heads][v_dim][kv_lora], WO [hidden][n_heads*v_dim]
+ *     KDA: KDA_WQ, KDA_WK [n_heads*kda_dk][hidden], KDA_WV [n_heads*kda_dv][hidden],
+ *          KDA_ALPHA [n_heads][kda_dk] fp32, KDA_BETA [n_heads] fp32, WO [hidden][n_heads*kda_dv]
+ *   per pool slot and expert: EXP_GATE, EXP_UP [ffn][hidden]; EXP_DOWN [hidden][ffn]
+ * Everything is bf16 except KDA_ALPHA/KDA_BETA. */
+typedef enum {
+  MK_W_EMBED = 0, MK_W_FINAL_NORM, MK_W_LM_HEAD,
+  MK_W_ATTN_NORM, MK_W_WQ, MK_W_WK, MK_W_WV, MK_W_WO,
+  MK_W_W_DQ, MK_W_Q_NORM, MK_W_W_UQ, MK_W_W_DKV, MK_W_KV_NORM, MK_W_W_UK, MK_W_W_UV,
+  MK_W_KDA_WQ, MK_W_KDA_WK, MK_W_KDA_WV, MK_W_KDA_ALPHA, MK_W_KDA_BETA,
+  MK_W_MOE_NORM, MK_W_ROUTER, MK_W_SH_GATE, MK_W_SH_UP, MK_W_SH_DOWN,
+  MK_W_EXP_GATE, MK_W_EXP_UP, MK_W_EXP_DOWN,
+  MK_W_N_KINDS
+} mk_weight_kind;
+
+typedef struct {
+  int32_t kind;           /* mk_weight_kind */
+  int32_t layer;          /* layer index; pool slot for EXP_*; ignored for global tensors */
+  int32_t expert;         /* expert index for EXP_*, otherwise ignored */
+  int32_t src_on_device;  /* 1: src is device memory, 0: host memory */
+  const void* src;        /* tensor data in the layout above */
+  uint64_t bytes;         /* must equal the tensor's size */
+} mk_tensor_desc;
+
+typedef struct mk_ctx mk_ctx;
+
+/* Sizes of the caller-owned buffers for cfg. Returns MK_E_INVAL / MK_E_UNSUPPORTED for bad configs.
+ * KV cache layout (bf16):
+ *   GQA:    K block then V block, each [n_layers][max_batch][n_kv_heads][kv_capacity][head_dim]
+ *   MLA:    [n_mla_layers][max_batch][kv_capacity][kv_lora + rope_dim]   (normed latent, then
+ *           the RoPE'd shared key); MLA layers numbered by their ordinal among MLA layers
+ * Delta-rule state (fp32): [n_kda_layers][max_batch][n_heads][kda_dk][kda_dv]. */
+int mk_query_sizes(const mk_config* cfg, mk_sizes* out);
+
+/* Create a context on HIP device `device` (or MK_DEVICE_NONE) over caller buffers of at least the
+ * queried sizes. The workspace is cleared here (once); the arena is filled by mk_load_weights. */
+int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_bytes, void* d_workspace,
+              uint64_t workspace_bytes, mk_ctx** out);
+
+/* Copy (and, where the kernel wants another layout, repack) n tensors into the arena, in stream
+ * order on hip_stream. Every tensor of the model must have been loaded once before the first step. */
+int mk_load_weights(mk_ctx* ctx, const mk_tensor_desc* descs, int n, void* hip_stream);
+
+/* One decode step, a single kernel launch, asynchronous on hip_stream.
+ * d_tokens [batch][n_new_tokens] int32 (device); new tokens take positions kv_len .. kv_len+T-1 of
+ * each sequence, attend causally to positions 0 .. their own, and their cache entries are written
+ * (rounded to bf16) at those positions; d_kv holds entries 0 .. kv_len-1 on entry. kv_len is
+ * owned by the caller (the step never advances it), so rejected speculative tokens roll back for
+ * free. d_kda_state (hybrid only, else NULL) is updated in place. d_logits [batch][n_new_tokens][vocab]
+ * fp32 (device). d_route (optional, may be NULL): [n_layers][batch*n_new_tokens][top_k] int32, the
+ * selected experts in descending probability. Device-side errors surface through mk_poll. */
+int mk_decode_step(mk_ctx* ctx, int batch, int n_new_tokens, int kv_len, const int32_t* d_tokens, void* d_kv,
+                   float* d_kda_state, float* d_logits, int32_t* d_route, void* hip_stream);
+
+/* After the caller synchronised the step's stream: MK_OK, or MK_E_DEVICE if the kernel reported a
+ * watchdog timeout or an out-of-range token (the context is then poisoned). */
+int mk_poll(mk_ctx* ctx);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* mk_last_error(void);
+
+void mk_destroy(mk_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

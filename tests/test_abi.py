@@ -1,0 +1,174 @@
+"""The C ABI on the host: exports, size queries, and every argument error (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def mk():
+    import decode_megakernel_cu_amd as mk
+
+    return mk
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mk.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(mk_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(mk):
+    names = declared_functions()
+    assert names == sorted(mk.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", mk.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(l.split()[-1] for l in out.stdout.splitlines() if " T " in l)
+    for n in names:
+        assert n in exported, n
+        assert hasattr(mk.lib, n)
+
+
+def test_library_is_gfx950():
+    import decode_megakernel_cu_amd as mk
+
+    out = subprocess.run(["strings", mk.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "gfx950" in out
+
+
+def test_struct_sizes_match_header(mk):
+    # mk_config: 24 int32 + 2 float; mk_tensor_desc: 4 int32 + pointer + uint64
+    assert ctypes.sizeof(mk.MkConfig) == 26 * 4
+    assert ctypes.sizeof(mk.MkTensorDesc) == 32
+    assert ctypes.sizeof(mk.MkSizes) == 32
+
+
+def sizes(mk, cfg):
+    return mk.mk_query_sizes(mk.config(cfg))
+
+
+def test_query_sizes_match_documented_layouts(mk):
+    s = sizes(mk, synth.K3)
+    c = synth.K3
+    assert s.kv_bytes == c.n_layers * c.max_batch * c.kv_capacity * c.latent_dim * 2
+    assert s.kda_state_bytes == 0
+    # every weight tensor is in the arena once (plus the layer table and 256-byte padding)
+    total = sum(synth.numel(t.shape) * (4 if t.dist == "sigmoid" else 2) for t in synth.tensor_list(c))
+    assert total <= s.arena_bytes <= total + 256 * (len(synth.tensor_list(c)) + 1) + c.n_layers * 256
+    assert s.arena_bytes < 288e9  # fits one MI355X
+    h = sizes(mk, synth.K3_HYBRID)
+    nk = len(synth.K3_HYBRID.kda_layers())
+    assert h.kda_state_bytes == nk * 8 * 16 * 128 * 128 * 4
+    assert h.kv_bytes == 23 * 8 * c.kv_capacity * c.latent_dim * 2
+    t = sizes(mk, synth.TINY)
+    tc = synth.TINY
+    assert t.kv_bytes == 2 * tc.n_layers * tc.max_batch * tc.n_kv_heads * tc.kv_capacity * tc.head_dim * 2
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("n_layers", 0, -1), ("attn_kind", 7, -1), ("top_k", 9, -1), ("max_batch", 9, -1),
+    ("max_new_tokens", 0, -1), ("hidden", 100, -7), ("n_kv_heads", 3, -1), ("head_dim", 256, -7),
+])
+def test_bad_configs(mk, field, value, code):
+    cfg = replace(synth.TINY, **{field: value})
+    with pytest.raises(mk.MkError) as e:
+        sizes(mk, cfg)
+    assert e.value.code == code
+    assert mk.mk_last_error()
+
+
+@pytest.fixture
+def host_ctx(mk):
+    cfg = synth.TINY
+    s = sizes(mk, cfg)
+    ctx = mk.mk_create(mk.config(cfg), mk.MK_DEVICE_NONE, 0, s.arena_bytes, 0, s.workspace_bytes)
+    yield cfg, ctx
+    mk.mk_destroy(ctx)
+
+
+def load_all(mk, cfg, ctx):
+    descs = []
+    for t in synth.tensor_list(cfg):
+        nbytes = synth.numel(t.shape) * (4 if t.dist == "sigmoid" else 2)
+        descs.append(mk.tensor_desc(t.kind, t.layer, t.expert, 1, nbytes, False))
+    mk.mk_load_weights(ctx, descs)
+
+
+def test_create_rejects_small_buffers(mk):
+    cfg = synth.TINY
+    s = sizes(mk, cfg)
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_create(mk.config(cfg), mk.MK_DEVICE_NONE, 0, s.arena_bytes - 1, 0, s.workspace_bytes)
+    assert e.value.code == mk.MK_E_NOMEM
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_create(mk.config(cfg), mk.MK_DEVICE_NONE, 0, s.arena_bytes, 0, s.workspace_bytes - 1)
+    assert e.value.code == mk.MK_E_NOMEM
+
+
+def test_load_weights_validates_descriptors(mk, host_ctx):
+    cfg, ctx = host_ctx
+    H = cfg.hidden
+    bad = [
+        mk.tensor_desc("wq", 0, -1, 1, 3, False),  # wrong size
+        mk.tensor_desc("wq", cfg.n_layers, -1, 1, H * H * 2, False),  # no such layer
+        mk.tensor_desc("w_dq", 0, -1, 1, 1536 * H * 2, False),  # not in a GQA model
+        mk.tensor_desc("exp_gate", 0, cfg.n_experts, 1, cfg.ffn * H * 2, False),  # no such expert
+        mk.tensor_desc("wq", 0, -1, 0, H * H * 2, False),  # NULL source
+    ]
+    for d in bad:
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_load_weights(ctx, [d])
+        assert e.value.code == mk.MK_E_INVAL
+
+
+def test_decode_step_argument_errors(mk, host_ctx):
+    cfg, ctx = host_ctx
+    ok = dict(batch=1, n_new_tokens=1, kv_len=10, tokens=1, kv=1, kda_state=0, logits=1)
+
+    def step(**kw):
+        a = dict(ok)
+        a.update(kw)
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_decode_step(ctx, **a)
+        return e.value.code
+
+    assert step(batch=0) == mk.MK_E_INVAL
+    assert step(batch=cfg.max_batch + 1) == mk.MK_E_INVAL
+    assert step(n_new_tokens=0) == mk.MK_E_INVAL
+    assert step(n_new_tokens=9) == mk.MK_E_INVAL
+    assert step(batch=4, n_new_tokens=5) == mk.MK_E_UNSUPPORTED  # 20 rows > 16
+    assert step(kv_len=-1) == mk.MK_E_INVAL
+    assert step(kv_len=cfg.kv_capacity) == mk.MK_E_KV_OVERFLOW
+    assert step(kv_len=cfg.kv_capacity - 2, n_new_tokens=3) == mk.MK_E_KV_OVERFLOW
+    assert step(tokens=0) == mk.MK_E_INVAL
+    assert step(logits=0) == mk.MK_E_INVAL
+    # arguments valid, weights missing
+    assert step() == mk.MK_E_STATE
+    assert "weight tensors loaded" in mk.mk_last_error()
+    load_all(mk, cfg, ctx)
+    # all loaded; a host-only context never launches
+    assert step() == mk.MK_E_STATE
+    assert "host-only" in mk.mk_last_error()
+
+
+def test_hybrid_needs_state(mk):
+    cfg = replace(synth.K3_HYBRID, n_layers=4, expert_pool_layers=0)
+    s = sizes(mk, cfg)
+    ctx = mk.mk_create(mk.config(cfg), mk.MK_DEVICE_NONE, 0, s.arena_bytes, 0, s.workspace_bytes)
+    try:
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_decode_step(ctx, 1, 1, 10, 1, 1, 0, 1)
+        assert e.value.code == mk.MK_E_INVAL
+    finally:
+        mk.mk_destroy(ctx)
+
+
+def test_null_context(mk):
+    for fn, args in ((mk.lib.mk_poll, (None,)), (mk.lib.mk_load_weights, (None, None, 0, None))):
+        assert fn(*args) == mk.MK_E_INVAL

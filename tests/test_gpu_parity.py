@@ -1,0 +1,202 @@
+"""GPU parity: the HIP megakernel (through the C ABI) against the fp64 oracle.
+
+Bar (per workload): per (b, t) row max|logit_gpu - logit_oracle| <= 2e-2 * max|logit_oracle|,
+identical argmax, identical expert selection in every layer, appended cache entries within
+one bf16 rounding of the oracle's, untouched cache entries bitwise unchanged, and the
+delta-rule state within fp32 accumulation error.
+"""
+import gc
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+_models = {}
+
+
+def device_model(cfg, spec):
+    """One resident model at a time (the K3-scale arenas take ~200 GB each)."""
+    from synth.device_inputs import DeviceModel
+
+    key = (cfg, spec.seed, tuple(sorted(spec.sigma_by_kind.items())))
+    if key not in _models:
+        for k in list(_models):
+            _models.pop(k).close()
+        gc.collect()
+        torch.cuda.empty_cache()
+        _models[key] = DeviceModel(cfg, spec, device=0)
+    return _models[key]
+
+
+def teardown_module(_):
+    for k in list(_models):
+        _models.pop(k).close()
+
+
+def run_pair(cfg, spec, B, T, kv_len, step=0):
+    import oracle
+
+    print(f"[case] {cfg.name} L={cfg.n_layers} B={B} T={T} kv_len={kv_len} seed={spec.seed}", flush=True)
+    toks = synth.tokens(spec.seed, step, cfg.vocab, B, T)
+    dm = device_model(cfg, spec)
+    dm.fill_caches(B, kv_len)
+    logits, route = dm.step(toks, kv_len)
+    torch.cuda.synchronize()
+    dm.poll()
+    caches = synth.host_caches(cfg, spec, B, kv_len, cache_batch=cfg.max_batch)
+    init = {k: v.copy() for k, v in caches.items()}
+    ref = oracle.decode_step(cfg, oracle.Provider(cfg, spec), toks, kv_len, caches, cache_batch=cfg.max_batch,
+                             trace=True)
+    return dm, logits.cpu().numpy(), route.cpu().numpy(), ref, caches, init
+
+
+def check_logits(got, ref):
+    exp = ref["logits"]
+    got = got.astype(np.float64)
+    scale = np.abs(exp).max(axis=-1)
+    err = np.abs(got - exp).max(axis=-1) / scale
+    assert np.all(err <= TOL), f"per-row relative logit error {err.max():.3e} > {TOL}"
+    ga, ea = got.argmax(-1), exp.astype(np.float32).argmax(-1)
+    if not np.array_equal(ga, ea):
+        srt = np.sort(exp, axis=-1)
+        margin = (srt[..., -1] - srt[..., -2]) / scale
+        pytest.fail(f"argmax differs: gpu {ga.ravel()} oracle {ea.ravel()}, oracle top-2 margin {margin.ravel()}")
+    return err.max()
+
+
+def check_route(route, ref):
+    sel = ref["sel"]
+    if not np.array_equal(route, sel):
+        bad = np.argwhere((route != sel).any(-1))
+        l, m = bad[0]
+        p = np.sort(ref["probs"][l, m])[::-1]
+        pytest.fail(f"expert selection differs at layer {l} row {m}: gpu {route[l, m]} oracle {sel[l, m]}, "
+                    f"oracle probability margin {p[ref['sel'].shape[-1] - 1] - p[ref['sel'].shape[-1]]:.3e} "
+                    f"({len(bad)} rows differ)")
+
+
+def bf(u):
+    return synth.bf16_to_f32(u).astype(np.float64)
+
+
+def check_rounded(a_bits, b_bits, what):
+    """a, b: bf16 patterns of the same quantity computed in fp32 (GPU) and fp64 (oracle) and
+    rounded once to bf16. They may differ by one bf16 step of the larger magnitude, plus the
+    fp32 error the GPU accumulates through earlier layers (1e-4 of the entry vector's largest
+    magnitude; it matters only for entries close to zero). The last axis is the entry vector."""
+    a, b = bf(a_bits), bf(b_bits)
+    step = 2.0 ** (np.floor(np.log2(np.maximum(np.maximum(np.abs(a), np.abs(b)), 1e-30))) - 7)
+    scale = np.abs(b).max(axis=-1, keepdims=True)
+    bad = np.abs(a - b) > step * 1.0001 + 1e-4 * scale
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        rows = ", ".join(f"{tuple(i)}: gpu {a[tuple(i)]:.6g} oracle {b[tuple(i)]:.6g}" for i in idx)
+        pytest.fail(f"{what}: {bad.sum()} of {bad.size} new entries differ by more than one bf16 step: {rows}")
+
+
+def check_cache(cfg, dm, caches, init, B, T, kv_len):
+    new = slice(kv_len, kv_len + T)
+    if cfg.attn_kind == synth.ATTN_GQA:
+        gk, gv = dm.gqa_cache()
+        pairs = [(gk, caches["k"], init["k"]), (gv, caches["v"], init["v"])]
+        for g, o, i0 in pairs:
+            # untouched entries bitwise equal, new entries within one bf16 rounding
+            assert np.array_equal(g[:, :B, :, :kv_len], i0[:, :B, :, :kv_len])
+            check_rounded(g[:, :B, :, new], o[:, :B, :, new], "GQA cache")
+    else:
+        g = dm.latent_cache()
+        o, i0 = caches["latent"], init["latent"]
+        assert np.array_equal(g[:, :B, :kv_len], i0[:, :B, :kv_len])
+        check_rounded(g[:, :B, new], o[:, :B, new], "latent cache")
+        if "kda_state" in caches:
+            s = dm.kda_state()[:, :B]
+            r = caches["kda_state"][:, :B]
+            err = np.abs(s - r).max() / np.abs(r).max()
+            assert err < 1e-4, f"delta-rule state error {err:.3e}"
+
+
+def parity(cfg, spec, B, T, kv_len):
+    dm, got, route, ref, caches, init = run_pair(cfg, spec, B, T, kv_len)
+    err = check_logits(got, ref)
+    check_route(route, ref)
+    check_cache(cfg, dm, caches, init, B, T, kv_len)
+    print(f"[ok] {cfg.name} B={B} T={T}: max rel logit err {err:.2e}", flush=True)
+
+
+# --------------------------------------------------------------------------------------------
+# small models: several tiles, ragged tails, every seed
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_batch1(seed):
+    w = synth.WORKLOADS["c1"]
+    parity(w.model, synth.Spec(seed=seed), w.batch, w.new_tokens, w.kv_len)
+
+
+@pytest.mark.parametrize("B,T,kv_len", [(2, 3, 37), (4, 4, 0), (8, 2, 129), (1, 8, 5)])
+def test_tiny_shapes(B, T, kv_len):
+    parity(synth.TINY, synth.Spec(seed=5), B, T, kv_len)
+
+
+def test_tiny_peaked_attention():
+    # larger query/key weights make attention sharply peaked, so attention errors reach the logits
+    spec = synth.Spec(seed=6, sigma_by_kind={"wq": 0.25, "wk": 0.25, "wv": 0.1, "wo": 0.1})
+    parity(synth.TINY, spec, 2, 3, 64)
+
+
+def test_mid_batch1():
+    w = synth.WORKLOADS["c2"]
+    parity(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
+
+
+def test_mid_batch4():
+    w = synth.WORKLOADS["c2b4"]
+    parity(w.model, synth.Spec(seed=1), w.batch, w.new_tokens, w.kv_len)
+
+
+K3_SMALL = replace(synth.K3, name="k3-2layer", n_layers=2, expert_pool_layers=0)
+HYB_SMALL = replace(synth.K3_HYBRID, name="hybrid-4layer", n_layers=4, expert_pool_layers=0)
+
+
+@pytest.mark.parametrize("B,T,kv_len", [(1, 1, 4096), (3, 2, 1000), (1, 7, 4096), (8, 1, 33)])
+def test_k3_two_layers(B, T, kv_len):
+    parity(K3_SMALL, synth.Spec(seed=2), B, T, kv_len)
+
+
+def test_k3_two_layers_peaked_mla():
+    spec = synth.Spec(seed=3, sigma_by_kind={"w_uq": 0.1, "w_uk": 0.1, "w_dkv": 0.05, "w_uv": 0.1, "wo": 0.05})
+    parity(K3_SMALL, spec, 2, 3, 300)
+
+
+@pytest.mark.parametrize("B,T", [(8, 1), (2, 3)])
+def test_hybrid_four_layers(B, T):
+    parity(HYB_SMALL, synth.Spec(seed=4), B, T, 517)
+
+
+# --------------------------------------------------------------------------------------------
+# full sizes, the launch configuration the benchmark times
+# --------------------------------------------------------------------------------------------
+def test_k3_full_batch1():
+    w = synth.WORKLOADS["c3"]
+    parity(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
+
+
+def test_k3_full_verify_t7():
+    w = synth.WORKLOADS["c4"]
+    parity(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
+
+
+def test_k3_full_batch8():
+    w = synth.WORKLOADS["c3b8"]
+    parity(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
+
+
+def test_hybrid_full_batch8():
+    w = synth.WORKLOADS["c5"]
+    parity(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
