@@ -134,6 +134,68 @@ def cpu_baseline(sample_layers: int = 8, budget_s: float = 12.0) -> dict:
 
 
 # ------------------------------------------------------------------------------------------
+# per-phase timing from the device trace (mk_set_trace / mk_read_trace)
+# ------------------------------------------------------------------------------------------
+PHASES = {
+    "gqa": ["qkv", "attention", "merge", "w_o"],
+    "mla": ["q_a+kv_a", "q_b", "absorb", "attention", "merge", "w_uv", "w_o"],
+    "kda": ["qkv", "delta_rule", "w_o"],
+}
+MOE_PHASES = ["router+shared_up", "experts_up", "experts_down"]
+
+
+def phase_names(cfg) -> list[str]:
+    names = ["embed"]
+    for l in range(cfg.n_layers):
+        kind = cfg.layer_kind(l)
+        names += [f"{kind}:{p}" for p in PHASES[kind]] + [f"moe:{p}" for p in MOE_PHASES]
+    return names + ["lm_head"]
+
+
+def trace_summary(cfg, tr: np.ndarray, tick_ns: float = 10.0) -> dict:
+    """tr [n_barriers + 1][blocks][arrive, depart]. The phase before barrier j runs from the last
+    departure of barrier j-1 to the last arrival at barrier j; the barrier itself from the last
+    arrival to the last departure."""
+    names = phase_names(cfg)
+    arr = tr[:, :, 0].astype(np.int64)
+    dep = tr[:, :, 1].astype(np.int64)
+    stg = tr[:, :, 2].astype(np.int64)
+    cmp_ = tr[:, :, 3].astype(np.int64)
+    t0 = arr[0].min()
+    out = {}
+    prev_dep = t0
+    for j, name in enumerate(names):
+        a_max = arr[j].max()
+        d_max = dep[j].max()
+        work = (a_max - prev_dep) * tick_ns / 1e3
+        sync = (d_max - a_max) * tick_ns / 1e3
+        s = out.setdefault(name, {"count": 0, "work_us": 0.0, "sync_us": 0.0, "stage_us": 0.0, "dot_us": 0.0,
+                                  "tail_us": 0.0})
+        s["count"] += 1
+        s["work_us"] += work
+        s["sync_us"] += sync
+        # GEMV sub-phases of this phase (stamped in the record of the barrier before it)
+        if j >= 1 and j < len(names) - 1 and (stg[j - 1] > 0).all():
+            s["stage_us"] += float(np.median(stg[j - 1] - dep[j - 1])) * tick_ns / 1e3
+            s["dot_us"] += float(np.median(cmp_[j - 1] - stg[j - 1])) * tick_ns / 1e3
+            s["tail_us"] += float(np.median(arr[j] - cmp_[j - 1])) * tick_ns / 1e3
+        prev_dep = d_max
+    total = (dep[-1].max() - t0) * tick_ns / 1e3
+    return {"total_us": total, "phases": out}
+
+
+def print_trace(summary: dict) -> None:
+    print(f"# traced step: {summary['total_us']:.1f} us", file=sys.stderr)
+    print(f"# {'phase':28s} {'n':>4s} {'work us':>10s} {'sync us':>10s} {'work/n':>8s} {'sync/n':>8s} "
+          f"{'stage/n':>8s} {'dot/n':>8s} {'tail/n':>8s}", file=sys.stderr)
+    for name, s in sorted(summary["phases"].items(), key=lambda kv: -(kv[1]["work_us"] + kv[1]["sync_us"])):
+        n = s["count"]
+        print(f"# {name:28s} {n:4d} {s['work_us']:10.1f} {s['sync_us']:10.1f} {s['work_us'] / n:8.2f} "
+              f"{s['sync_us'] / n:8.2f} {s['stage_us'] / n:8.2f} {s['dot_us'] / n:8.2f} {s['tail_us'] / n:8.2f}",
+              file=sys.stderr)
+
+
+# ------------------------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +204,7 @@ def main():
     ap.add_argument("--batches", default="1,2,4,8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--trace", action="store_true", help="print per-phase device timings of one step per batch")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the decode step; --gpus {args.gpus} is not supported "
@@ -192,6 +255,15 @@ def main():
                       "gbs": by["total"] / (kms.mean() * 1e-3) / 1e9}
         print(f"# B={B}: {results[B]['kernel_ms_avg']:.3f} ms/launch, {results[B]['tokens_per_s']:.1f} tok/s, "
               f"{results[B]['gbs']:.0f} GB/s ({by['total'] / 1e9:.2f} GB/step)", file=sys.stderr, flush=True)
+        if args.trace:
+            dm.mk.mk_set_trace(dm.ctx, True)
+            dm.step(toks, w.kv_len, route=False, logits=logits, d_tokens=d_tok)
+            torch.cuda.synchronize()
+            summary = trace_summary(cfg, dm.mk.mk_read_trace(dm.ctx))
+            dm.mk.mk_set_trace(dm.ctx, False)
+            print(f"# trace B={B}", file=sys.stderr)
+            print_trace(summary)
+            results[B]["trace"] = summary
     dm.close()
 
     head = results[batches[0]]

@@ -22,8 +22,8 @@ KINDS = ["embed", "final_norm", "lm_head", "attn_norm", "wq", "wk", "wv", "wo", 
          "router", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"]
 KIND_ID = {k: i for i, k in enumerate(KINDS)}
 
-EXPORTS = ["mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_poll", "mk_last_error",
-           "mk_destroy"]
+EXPORTS = ["mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_poll", "mk_set_trace",
+           "mk_read_trace", "mk_last_error", "mk_destroy"]
 
 
 class MkConfig(ctypes.Structure):
@@ -64,7 +64,10 @@ def _load():
     L.mk_last_error.argtypes = []
     L.mk_destroy.argtypes = [vp]
     L.mk_destroy.restype = None
-    for f in ("mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_poll"):
+    L.mk_set_trace.argtypes = [vp, i32]
+    L.mk_read_trace.argtypes = [vp, vp, u64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    for f in ("mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_poll", "mk_set_trace",
+              "mk_read_trace"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -123,3 +126,18 @@ def mk_destroy(ctx) -> None:
 
 def tensor_desc(kind: str, layer: int, expert: int, src: int, nbytes: int, on_device: bool) -> MkTensorDesc:
     return MkTensorDesc(KIND_ID[kind], layer, expert, int(on_device), src, nbytes)
+
+
+def mk_set_trace(ctx, enable: bool) -> None:
+    _check(lib.mk_set_trace(ctx, int(enable)))
+
+
+def mk_read_trace(ctx):
+    """Trace of the last step as a numpy array [n_barriers + 1][n_blocks][4] of wall-clock ticks."""
+    import numpy as np
+
+    nb, nk = ctypes.c_int(), ctypes.c_int()
+    _check(lib.mk_read_trace(ctx, None, 0, ctypes.byref(nb), ctypes.byref(nk)))
+    out = np.zeros((nb.value + 1, nk.value, 4), dtype=np.uint64)
+    _check(lib.mk_read_trace(ctx, out.ctypes.data, out.size, ctypes.byref(nb), ctypes.byref(nk)))
+    return out

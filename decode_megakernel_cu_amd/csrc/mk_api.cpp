@@ -20,6 +20,7 @@ size_t kernel_lds_bytes();
 hipError_t launch_decode(const Params& p, int nblocks, hipStream_t stream);
 hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd, int kvl, hipStream_t stream);
 hipError_t occupancy(int* blocks_per_cu);
+int max_grid();
 }  // namespace mk
 
 using namespace mk;
@@ -222,6 +223,8 @@ Layout make_layout(const mk_config& c) {
   };
   w.flags = take(kMaxBlocks * 4);
   w.status = take(64 * 4);
+  w.trace_slots = (uint64_t)(2 + 10 * c.n_layers) * kMaxBlocks;
+  w.trace = take(w.trace_slots * 32);
   w.rope = take((uint64_t)MK_MAX_NEW_TOKENS * kMaxRopePairs * 2 * 4);
   w.x = take(M * H * 4);
   w.a1 = take(M * w1 * 4);
@@ -252,6 +255,8 @@ struct mk_ctx {
   uint64_t launches;
   uint64_t watchdog_ticks;
   bool poisoned;
+  bool trace;
+  int last_barriers;
   std::vector<uint8_t> loaded;  // per tensor slot, in map order
   std::map<Key, size_t> index;
   size_t n_loaded;
@@ -297,6 +302,8 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
   c->ws = static_cast<uint8_t*>(d_workspace);
   c->launches = 0;
   c->poisoned = false;
+  c->trace = false;
+  c->last_barriers = 0;
   c->n_loaded = 0;
   size_t i = 0;
   for (auto& kv : c->lt.tensors) c->index[kv.first] = i++;
@@ -316,7 +323,7 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
       delete c;
       return fail(MK_E_UNSUPPORTED, "the megakernel does not fit on a CU (LDS %zu bytes)", kernel_lds_bytes());
     }
-    c->nblocks = std::min(cus, kMaxBlocks);
+    c->nblocks = std::min(cus, max_grid());
     double ms = 2000.0;
     if (const char* env = std::getenv("MK_WATCHDOG_MS")) ms = std::max(1.0, std::atof(env));
     c->watchdog_ticks = (uint64_t)(ms * (rate_khz > 0 ? rate_khz : 100000));
@@ -433,6 +440,7 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   p.rope = f(w.rope); p.x = f(w.x); p.a1 = f(w.a1); p.a2 = f(w.a2); p.a3 = f(w.a3); p.a4 = f(w.a4);
   p.att = f(w.att); p.o2 = f(w.o2); p.part = f(w.part); p.rlog = f(w.rlog); p.sact = f(w.sact); p.eact = f(w.eact);
   p.watchdog_ticks = c->watchdog_ticks;
+  p.trace = c->trace ? reinterpret_cast<uint64_t*>(ws + w.trace) : nullptr;
   const int nh = g.n_heads;
   const uint64_t dmax = g.attn_kind == MK_ATTN_GQA ? g.head_dim : std::max(g.kv_lora, g.kda_dv);
   if ((uint64_t)M * nh * p.nsplit * (dmax + 2) > w.part_floats)
@@ -441,6 +449,34 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   if (e == hipSuccess) e = launch_decode(p, c->nblocks, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MK_E_HIP, "launch failed: %s", hipGetErrorString(e));
   c->launches++;
+  int nb = 1;
+  for (int l = 0; l < g.n_layers; ++l) {
+    const int k = layer_kind(g, l);
+    nb += k == kGqa ? 7 : k == kMla ? 10 : 6;
+  }
+  c->last_barriers = nb;
+  g_err.clear();
+  return MK_OK;
+}
+
+int mk_set_trace(mk_ctx* c, int enable) {
+  if (!c) return fail(MK_E_INVAL, "context is NULL");
+  c->trace = enable != 0;
+  g_err.clear();
+  return MK_OK;
+}
+
+int mk_read_trace(mk_ctx* c, uint64_t* out, uint64_t capacity, int* n_barriers, int* n_blocks) {
+  if (!c || !n_barriers || !n_blocks) return fail(MK_E_INVAL, "NULL argument");
+  if (c->device == MK_DEVICE_NONE) return fail(MK_E_STATE, "host-only context has no trace");
+  if (!c->trace || c->last_barriers == 0) return fail(MK_E_STATE, "no traced step since tracing was enabled");
+  const uint64_t n = (uint64_t)(c->last_barriers + 1) * c->nblocks * 4;
+  *n_barriers = c->last_barriers;
+  *n_blocks = c->nblocks;
+  if (!out) return MK_OK;
+  if (capacity < n) return fail(MK_E_NOMEM, "trace needs %llu slots", (unsigned long long)n);
+  hipError_t e = hipMemcpy(out, c->ws + c->lt.ws.trace, n * 8, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MK_E_HIP, "trace read failed: %s", hipGetErrorString(e));
   g_err.clear();
   return MK_OK;
 }

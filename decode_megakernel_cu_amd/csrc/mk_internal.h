@@ -30,8 +30,9 @@ struct LayerDev {
 
 // Workspace carve-up (byte offsets from the workspace base).
 struct WsLayout {
-  uint64_t flags, status, rope, x, a1, a2, a3, a4, att, o2, part, rlog, sact, eact, scratch, total;
+  uint64_t flags, status, trace, rope, x, a1, a2, a3, a4, att, o2, part, rlog, sact, eact, scratch, total;
   uint64_t part_floats;  // capacity of the partials buffer in floats
+  uint64_t trace_slots;  // barriers x blocks the trace region holds
 };
 
 // Everything the kernel needs, passed by value.
@@ -55,7 +56,8 @@ struct Params {
   uint32_t* flags;
   uint32_t* status;  // [0] error code, [1] abort flag, [2] detail
   float *rope, *x, *a1, *a2, *a3, *a4, *att, *o2, *part, *rlog, *sact, *eact;
-  uint64_t watchdog_ticks;  // s_memrealtime ticks (100 MHz) a barrier may wait
+  uint64_t watchdog_ticks;  // wall-clock ticks a barrier may wait
+  uint64_t* trace;          // optional [barrier][block][arrive, depart] wall-clock stamps
 };
 
 }  // namespace mk

@@ -139,6 +139,20 @@ int mk_decode_step(mk_ctx* ctx, int batch, int n_new_tokens, int kv_len, const i
  * watchdog timeout or an out-of-range token (the context is then poisoned). */
 int mk_poll(mk_ctx* ctx);
 
+/* Profiling: while enabled, every step records, for each grid barrier and workgroup, four stamps
+ * of the device wall clock (wall_clock64, 100 MHz on MI355X): arrival at the barrier, departure,
+ * and, for the GEMV phase that follows it, the time its input was staged and the time its dot
+ * products were done (0 for other phases). One extra record per workgroup holds the time it
+ * finished the step. */
+int mk_set_trace(mk_ctx* ctx, int enable);
+
+/* Copy the last traced step: out[((barrier * n_blocks) + block) * 4 + {0: arrive, 1: depart,
+ * 2: staged, 3: computed}] for
+ * barrier < *n_barriers + 1 (the last record is the end of the step). Call with out == NULL to get
+ * the counts; capacity is the number of uint64_t slots in out. Synchronous (after the step's stream
+ * has finished). */
+int mk_read_trace(mk_ctx* ctx, uint64_t* out, uint64_t capacity, int* n_barriers, int* n_blocks);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* mk_last_error(void);
 
