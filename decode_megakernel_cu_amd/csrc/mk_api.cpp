@@ -40,6 +40,7 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr uint64_t kAlign = 256;
+constexpr int kThreadsHost = kThreads;
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Slot {
@@ -76,6 +77,7 @@ int check_config(const mk_config* c) {
   if (c->kv_capacity < c->max_new_tokens) return fail(MK_E_INVAL, "kv_capacity below max_new_tokens");
   if (c->n_experts < 1 || c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 8)
     return fail(MK_E_INVAL, "need 1 <= top_k <= min(n_experts, 8)");
+  if (c->n_experts > kMaxExperts) return fail(MK_E_UNSUPPORTED, "at most %d experts", kMaxExperts);
   if (c->ffn < 8 || c->ffn % 8 || c->shared_ffn < 0 || c->shared_ffn % 8)
     return fail(MK_E_UNSUPPORTED, "ffn and shared_ffn must be multiples of 8");
   if (c->expert_pool_layers < 0) return fail(MK_E_INVAL, "expert_pool_layers must be >= 0");
@@ -92,9 +94,11 @@ int check_config(const mk_config* c) {
     if (c->kv_lora < 8 || c->kv_lora % 8 || c->q_lora < 8 || c->q_lora % 8 || c->nope_dim < 8 || c->nope_dim % 8 ||
         c->v_dim < 8 || c->v_dim % 8 || c->rope_dim < 2 || c->rope_dim % 2 || c->rope_dim > 2 * kMaxRopePairs)
       return fail(MK_E_UNSUPPORTED, "MLA dims must be multiples of 8 (rope_dim even, <= %d)", 2 * kMaxRopePairs);
-    const int lat = c->kv_lora + c->rope_dim;
-    if ((kChunk + c->n_heads) * lat + c->n_heads * kChunk > kLdsFloats)
-      return fail(MK_E_UNSUPPORTED, "MLA latent too wide for the attention tile");
+    const int lat = c->kv_lora + c->rope_dim, nh = c->n_heads;
+    if (c->rope_dim % 8 || nh % 4) return fail(MK_E_UNSUPPORTED, "MLA needs rope_dim % 8 == 0 and n_heads % 4 == 0");
+    if (kSub * (lat + 4) + nh * lat + c->max_new_tokens * lat + nh * kSub + nh * 4 + 8 + c->kv_lora > kLdsFloats ||
+        nh * lat / 4 > 5 * kThreadsHost || kSub * lat / 8 > 5 * kThreadsHost || (nh / 4) * (c->kv_lora / 4) > 2 * kThreadsHost)
+      return fail(MK_E_UNSUPPORTED, "MLA heads / latent too wide for the attention tile");
     if (c->attn_kind == MK_ATTN_HYBRID) {
       if (c->hybrid_period < 1) return fail(MK_E_INVAL, "hybrid_period must be positive");
       if (c->kda_dk % 64 || c->kda_dk < 64 || c->kda_dk > 128 || c->kda_dv < 8 || c->kda_dv % 8)
@@ -102,6 +106,32 @@ int check_config(const mk_config* c) {
     }
   }
   return MK_OK;
+}
+
+// Whether every GEMV phase of a step with M token rows fits the LDS carve-up of the kernel: the
+// task accumulators of a workgroup's share (3 x MM floats per task) at the end of the buffer, the
+// staged input (at least 8 columns of each staged row, the whole window of per-head phases) before.
+bool step_fits(const mk_config& c, int M, int nb) {
+  if (nb < 1) return true;
+  const long long MM = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+  auto cap_of = [&](long long ntasks) { return (long long)kLdsFloats - (ntasks + nb - 1) / nb * 3 * MM; };
+  auto ok = [&](long long ntasks, long long rows) { return cap_of(ntasks) >= rows * 8; };
+  auto ok_off = [&](long long ntasks, long long rph, long long seg) {
+    const long long nloc = (ntasks + nb - 1) / nb, window = ((nloc + rph - 1) / rph + 1) * seg;
+    return cap_of(ntasks) >= window * M;
+  };
+  const long long E = c.n_experts, F = c.ffn, SF = c.shared_ffn, H = c.hidden, nh = c.n_heads;
+  const long long np = (long long)M * c.top_k;
+  bool good = ok(c.vocab, M) && ok(H, M) && ok(E + SF, M) && ok(std::min(E, np) * F, M) && ok(H, np + M);
+  if (c.attn_kind == MK_ATTN_GQA) {
+    good = good && ok(nh * c.head_dim + 2LL * c.n_kv_heads * c.head_dim, M);
+  } else {
+    const long long lat = c.kv_lora + c.rope_dim, qd = c.nope_dim + c.rope_dim;
+    good = good && ok(c.q_lora + lat, M) && ok(nh * qd, M) && ok_off(nh * c.kv_lora, c.kv_lora, c.nope_dim) &&
+           ok_off(nh * c.v_dim, c.v_dim, c.kv_lora);
+    if (c.attn_kind == MK_ATTN_HYBRID) good = good && ok(2 * nh * c.kda_dk + nh * c.kda_dv, M);
+  }
+  return good;
 }
 
 Layout make_layout(const mk_config& c) {
@@ -208,7 +238,7 @@ Layout make_layout(const mk_config& c) {
     dmax = std::max<uint64_t>(c.kv_lora, c.kda_dv);
   }
   Lt.nsplit_max = (c.kv_capacity + kChunk - 1) / kChunk;
-  uint64_t part = M * nh * Lt.nsplit_max * (dmax + 2);
+  uint64_t part = M * nh * Lt.nsplit_max * (dmax + kPartPad);
   if (c.attn_kind != MK_ATTN_GQA) {
     // the W_uk repack stages a host tensor here
     const uint64_t uk = nh * c.nope_dim * c.kv_lora * 2 / 4 + 64;
@@ -292,6 +322,7 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
       return fail(MK_E_INVAL, "arena and workspace must be 256-byte aligned");
   }
   if (arena_bytes < lt.arena) return fail(MK_E_NOMEM, "arena has %llu bytes, needs %llu", (unsigned long long)arena_bytes, (unsigned long long)lt.arena);
+  if (lt.ws.total >= (1ull << 31)) return fail(MK_E_UNSUPPORTED, "workspace above 2 GiB");
   if (workspace_bytes < lt.ws.total)
     return fail(MK_E_NOMEM, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes, (unsigned long long)lt.ws.total);
   mk_ctx* c = new mk_ctx();
@@ -408,10 +439,8 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   if (!d_tokens || !d_logits || !d_kv) return fail(MK_E_INVAL, "tokens, kv and logits must be non-NULL");
   if (g.attn_kind == MK_ATTN_HYBRID && !d_kda_state) return fail(MK_E_INVAL, "hybrid model needs the delta-rule state");
   const int M = B * T;
-  // shape limits of the LDS tiles for this step
-  const int np = M * g.top_k;
-  if ((long long)np * g.ffn + (long long)M * g.shared_ffn > kLdsFloats)
-    return fail(MK_E_UNSUPPORTED, "expert activations of this step do not fit LDS");
+  if (!step_fits(g, M, c->nblocks))
+    return fail(MK_E_UNSUPPORTED, "a phase of this step does not fit the workgroup's LDS");
   if (c->n_loaded != c->loaded.size())
     return fail(MK_E_STATE, "%zu of %zu weight tensors loaded", c->n_loaded, c->loaded.size());
   if (c->poisoned) return fail(MK_E_STATE, "context poisoned by an earlier device error");
@@ -425,7 +454,12 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   p.SF = g.shared_ffn; p.norm_topk = g.norm_topk; p.cap = g.kv_capacity; p.Bmax = g.max_batch;
   p.eps = g.rms_eps; p.rope_theta = g.rope_theta;
   p.B = B; p.T = T; p.M = M; p.kv_len = kv_len;
-  p.nsplit = (kv_len + T + kChunk - 1) / kChunk;
+  // split-KV: GQA uses fixed chunks; MLA sizes them so that the tasks of the step fill the grid
+  const int npos = kv_len + T;
+  p.chunk = kChunk;
+  if (g.attn_kind != MK_ATTN_GQA && c->nblocks > 0)
+    p.chunk = std::max(kChunk, (int)(((long long)B * npos + c->nblocks - 1) / c->nblocks));
+  p.nsplit = (npos + p.chunk - 1) / p.chunk;
   p.epoch = (uint32_t)(c->launches * 65536ull);
   p.tokens = d_tokens; p.logits = d_logits; p.route = d_route;
   p.layers = reinterpret_cast<const LayerDev*>(c->arena);
@@ -439,11 +473,13 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   auto f = [&](uint64_t o) { return reinterpret_cast<float*>(ws + o); };
   p.rope = f(w.rope); p.x = f(w.x); p.a1 = f(w.a1); p.a2 = f(w.a2); p.a3 = f(w.a3); p.a4 = f(w.a4);
   p.att = f(w.att); p.o2 = f(w.o2); p.part = f(w.part); p.rlog = f(w.rlog); p.sact = f(w.sact); p.eact = f(w.eact);
+  p.wsb = reinterpret_cast<const char*>(ws);
+  p.ws_bytes = (uint32_t)w.total;
   p.watchdog_ticks = c->watchdog_ticks;
   p.trace = c->trace ? reinterpret_cast<uint64_t*>(ws + w.trace) : nullptr;
   const int nh = g.n_heads;
   const uint64_t dmax = g.attn_kind == MK_ATTN_GQA ? g.head_dim : std::max(g.kv_lora, g.kda_dv);
-  if ((uint64_t)M * nh * p.nsplit * (dmax + 2) > w.part_floats)
+  if ((uint64_t)M * nh * p.nsplit * (dmax + kPartPad) > w.part_floats)
     return fail(MK_E_UNSUPPORTED, "attention partials exceed the workspace");
   hipError_t e = hipSetDevice(c->device);
   if (e == hipSuccess) e = launch_decode(p, c->nblocks, static_cast<hipStream_t>(stream));

@@ -11,7 +11,10 @@ constexpr int kThreads = 512;            // threads per workgroup (8 wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBlocks = 1024;         // barrier flag slots
 constexpr int kLdsFloats = 36 * 1024;    // 144 KiB of LDS per workgroup
-constexpr int kChunk = 16;               // cache positions per split-KV task
+constexpr int kChunk = 16;               // minimum cache positions per split-KV task
+constexpr int kSub = 32;                 // cache positions an MLA task stages at once
+constexpr int kPartPad = 4;              // a partial is [max, sum, pad, pad, values...]: values 16-byte aligned
+constexpr int kMaxExperts = 256;
 constexpr int kMaxRopePairs = 64;
 constexpr int kMaxQueue = MK_MAX_M * 8;  // token-expert pairs per step (top_k <= 8)
 
@@ -41,7 +44,7 @@ struct Params {
   int32_t L, H, V, nh, nkv, hd, ql, kvl, rd, nd, vd, dk, dv, E, topk, F, SF, norm_topk, cap, Bmax;
   float eps, rope_theta;
   // step
-  int32_t B, T, M, kv_len, nsplit;
+  int32_t B, T, M, kv_len, nsplit, chunk;  // chunk: cache positions per split
   uint32_t epoch;
   const int32_t* tokens;
   float* logits;
@@ -56,6 +59,8 @@ struct Params {
   uint32_t* flags;
   uint32_t* status;  // [0] error code, [1] abort flag, [2] detail
   float *rope, *x, *a1, *a2, *a3, *a4, *att, *o2, *part, *rlog, *sact, *eact;
+  const char* wsb;    // workspace base: activations are addressed by byte offsets from here
+  uint32_t ws_bytes;  // workspace size (< 2^31)
   uint64_t watchdog_ticks;  // wall-clock ticks a barrier may wait
   uint64_t* trace;          // optional [barrier][block][arrive, depart] wall-clock stamps
 };

@@ -17,8 +17,12 @@
 // Weights, the KV cache entries a workgroup owns, and the recurrent state are read and written
 // with ordinary cached accesses: within one step no other workgroup touches them.
 //
+// Latency. Under full weight streaming every dependent round trip to memory costs about a
+// microsecond, so activations are moved with 16-byte agent-scope buffer loads issued in batches
+// (up to eight per lane in flight before the first is consumed), never one load per loop trip.
+//
 // Prefetch. The weights of a phase do not depend on activations, so every wave except the
-// polling one issues the loads of its first task of the next phase before it arrives at the
+// polling one issues the loads of its first rows of the next phase before it arrives at the
 // barrier ("layer n+1 loads while layer n computes", the news digests' account of the design);
 // the barrier wait and the input staging then overlap the HBM latency.
 //
@@ -40,6 +44,7 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 template <class T>
 __device__ __forceinline__ GLOBAL T* gp(T* p) {
@@ -50,11 +55,10 @@ __device__ __forceinline__ const GLOBAL T* gp(const T* p) {
   return (const GLOBAL T*)p;
 }
 
-constexpr int kInFloats = 24576;   // staged input slab
-constexpr int kAccFloats = 12288;  // per-task accumulators
 constexpr int kPollWave = kWaves - 1;
-constexpr int kMaxGrid = 256;      // workgroups the barrier polls (4 flags per lane)
-static_assert(kInFloats + kAccFloats <= kLdsFloats, "LDS carve-up");
+constexpr int kMaxGrid = 256;  // workgroups the barrier polls (4 flags per lane)
+constexpr int kQSlots = 5;     // MLA: 16-byte query loads per lane in one batch
+constexpr int kCSlots = 5;     // MLA: 16-byte cache loads per lane in one batch
 static_assert(sizeof(Params) % 4 == 0, "Params copied as words");
 
 // ----------------------------------------------------------------------------------------------
@@ -85,10 +89,6 @@ __device__ __forceinline__ uint4 ldw(const uint16_t* p) {
 __device__ __forceinline__ float ldc(const float* p) {
   return __hip_atomic_load((GLOBAL float*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float2 ldc2(const float* p) {  // p 8-byte aligned
-  const uint64_t u = __hip_atomic_load((GLOBAL uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
-}
 __device__ __forceinline__ void stc(float* p, float v) {
   __hip_atomic_store((GLOBAL float*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -98,6 +98,31 @@ __device__ __forceinline__ uint32_t ldc_u32(const uint32_t* p) {
 __device__ __forceinline__ void stc_u32(uint32_t* p, uint32_t v) {
   __hip_atomic_store((GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// 16-byte coherent accesses through a buffer resource over the workspace. The cache policy is
+// sc1, the same bits an agent-scope relaxed atomic access carries; offsets are in bytes.
+constexpr int kCoherent = 16;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Workspace view: activations addressed by byte offsets from the workspace base.
+struct Ws {
+  Rsrc r;
+  const char* base;
+  __device__ __forceinline__ uint32_t off(const float* p) const { return (uint32_t)((const char*)p - base); }
+  __device__ __forceinline__ f32x4 ld4(const float* p) const {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off(p), 0, kCoherent);
+    return f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+  }
+  __device__ __forceinline__ float ld1(const float* p) const {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off(p), 0, kCoherent));
+  }
+  __device__ __forceinline__ void st4(float* p, f32x4 v) const {
+    const u32x4 u{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, off(p), 0, kCoherent);
+  }
+};
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // execution barrier of the workgroup that does not wait for outstanding global loads
@@ -116,10 +141,47 @@ __device__ __forceinline__ float wave_max(float v, int width) {
   return v;
 }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+
+// Uniform values read from LDS land in vector registers; these move them into scalar ones.
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The thread index, opaque to the optimiser at each use: values derived from it are then computed
+// where they are needed instead of being hoisted to the kernel's entry and kept live (spilled to
+// scratch) across every phase of the step.
+__device__ __forceinline__ int tid_x() {
+  int t = (int)__builtin_amdgcn_workitem_id_x();
+  asm volatile("" : "+v"(t));
+  return t;
+}
+__device__ __forceinline__ int lane_id() { return tid_x() & 63; }
+__device__ __forceinline__ int wave_id() { return rfl(tid_x() >> 6); }
+__device__ __forceinline__ float rflf(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
+template <class T>
+__device__ __forceinline__ T* rflp(T* ptr) {
+  const uint64_t u = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = (uint32_t)rfl((int)(uint32_t)u), hi = (uint32_t)rfl((int)(uint32_t)(u >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// Copy n 16-byte units of coherent workspace data into LDS, all threads: unit i is read from
+// src(i) and written to dst(i). NS loads per lane are in flight before the first is consumed.
+template <int NS, class Src, class Dst>
+__device__ __forceinline__ void copy_units(const Ws& ws, int n, Src src, Dst dst) {
+  for (int b = 0; b < n; b += NS * kThreads) {
+    f32x4 v[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+      if (b + u * kThreads < n) v[u] = ws.ld4(src(min(b + u * kThreads + tid_x(), n - 1)));
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int i = b + u * kThreads + tid_x();
+      if (b + u * kThreads < n && i < n) *reinterpret_cast<f32x4*>(dst(i)) = v[u];
+    }
+  }
+}
 
 // ----------------------------------------------------------------------------------------------
 // grid barrier
@@ -175,56 +237,27 @@ __device__ __forceinline__ bool grid_sync(const Params& p, uint32_t& gen, int* s
 }
 
 // ----------------------------------------------------------------------------------------------
-// block-wide helpers
-// ----------------------------------------------------------------------------------------------
-// inv[m] = 1/sqrt(mean(src[m][:K]^2) + eps) for m < M (coherent loads), written to LDS
-__device__ __forceinline__ void block_inv_rms(const float* src, int ld, int M, int K, float eps, float* inv, float* red) {
-  for (int m = 0; m < M; ++m) {
-    float ss = 0.f;
-    for (int k = 2 * threadIdx.x; k < K; k += 2 * kThreads) {
-      const float2 v = ldc2(src + (size_t)m * ld + k);
-      ss += v.x * v.x + v.y * v.y;
-    }
-    ss = wave_sum(ss, 64);
-    if (lane_id() == 0) red[m * kWaves + wave_id()] = ss;
-  }
-  __syncthreads();
-  if (threadIdx.x < M) {
-    float t = 0.f;
-    for (int w = 0; w < kWaves; ++w) t += red[threadIdx.x * kWaves + w];
-    inv[threadIdx.x] = 1.0f / sqrtf(t / (float)K + eps);
-  }
-  __syncthreads();
-}
-
-// ----------------------------------------------------------------------------------------------
 // GEMV executor (one copy in the kernel, driven by a per-phase descriptor)
 //
-// A phase is a set of tasks; a task is one or two weight rows of length K (two for SwiGLU gate/up
-// pairs) dotted with the staged input rows of a list of tokens. The task space is split into
-// contiguous ranges per workgroup; within a workgroup lane groups of LPR lanes take tasks. Each
-// lane group streams its rows through two register buffers -- row r+2 is loaded while row r+1 is
-// computed -- so a row of loads is always in flight; the first two rows of a phase are loaded
-// before the barrier that precedes it. The staged input (rows of width Wst) is processed in slabs
-// that fit LDS; partial dot products are reduced across the lane group and accumulated in LDS,
-// and the epilogue writes each task's outputs.
+// A phase is a set of tasks (output rows); a task owns one or more weight rows (two for SwiGLU
+// gate/up pairs, one per routed expert plus the shared expert for the down projection), each
+// dotted with some of the staged input rows. The task space is split into contiguous ranges per
+// workgroup; within a workgroup lane groups of LPR lanes take tasks. Each lane group streams its
+// rows through two register buffers -- element e+2 is requested while element e+1 is computed --
+// so a block of loads is always in flight; the first two elements of a phase are requested
+// before the barrier that precedes it. The staged input is processed in column slabs that fit
+// LDS; partial dot products are reduced across the lane group and accumulated in LDS, and the
+// epilogue writes each task's outputs.
 // ----------------------------------------------------------------------------------------------
-struct TaskRows {
-  const uint16_t* w0;
-  const uint16_t* w1;  // nullptr for single-row tasks
-  int xoff;            // offset of the task's input inside a staged row (offset phases)
-  int ntok;            // tokens to compute (<= MM)
-  const int* tok;      // token slots (indices of staged rows); nullptr = 0..ntok-1
-};
-
 enum GemvKind : int {
   G_STACK = 0,  // up to three stacked matrices, store
   G_RESID,      // one matrix, residual add into the output
   G_OFF,        // per-head rows: row t reads the staged input at (t / rph) * seg, store
   G_RS,         // router rows (store logits) then shared-expert gate/up pairs (store SwiGLU)
   G_EXP,        // routed-expert gate/up pairs of the unique experts (store SwiGLU per pair)
+  G_DOWN,       // routed and shared down projections, router-weighted, residual add
 };
-enum StageKind : int { S_NORM = 0, S_PLAIN, S_NOPE };
+enum StageKind : int { S_NORM = 0, S_PLAIN, S_NOPE, S_DOWN };
 
 struct Route {
   int nu;                     // unique experts
@@ -233,6 +266,23 @@ struct Route {
   int ptok[kMaxQueue];        // token of each pair
   float pw[kMaxQueue];        // router weight of each pair
 };
+
+// one weight row of a task
+struct RowRef {
+  const uint16_t* w;  // nullptr: the task has no such row
+  int len;            // weights in the row
+  int xoff;           // column of the row's input inside a staged row
+  int ntok;           // staged rows it is dotted with
+  int tbase;          // first of them when tok is nullptr (they are then consecutive)
+  const int* tok;     // staged rows, or nullptr
+};
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+__device__ __forceinline__ int pow2ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
 
 struct Gemv {
   int kind, stage;
@@ -243,40 +293,65 @@ struct Gemv {
   const uint16_t* gain;
   int nh, nd, qd;  // S_NOPE
   float eps;
+  const float* src2;  // S_DOWN: src = expert activations [np][F], src2 = shared activations [M][SF]
+  int np;
   // rows and outputs
-  const uint16_t *W0, *W1, *W2;
+  const uint16_t *W0, *W1, *W2, *Wg, *Wu;
+  const uint16_t* safe;  // a valid weight address for lanes without a row
   int n0, n1;
   float *out0, *out1, *out2;
   int ldo0, ldo1, ldo2;
-  int rph, seg;  // G_OFF
-  int E, SF, F;  // G_RS / G_EXP
-  const uint16_t *Wg, *Wu;
+  int rph, seg;    // G_OFF
+  int E, SF, F, H;  // G_RS / G_EXP / G_DOWN
   float *rlog, *sact, *eact;
   const Route* rt;
 
-  __device__ __forceinline__ TaskRows rows(int t) const {
+  __device__ __forceinline__ RowRef row(int t, int which) const {
+    RowRef r{nullptr, K, 0, M, 0, nullptr};
     switch (kind) {
       case G_STACK:
-        if (t < n0) return TaskRows{W0 + (size_t)t * K, nullptr, 0, M, nullptr};
-        if (t < n0 + n1) return TaskRows{W1 + (size_t)(t - n0) * K, nullptr, 0, M, nullptr};
-        return TaskRows{W2 + (size_t)(t - n0 - n1) * K, nullptr, 0, M, nullptr};
+        if (t < n0) r.w = W0 + (size_t)t * K;
+        else if (t < n0 + n1) r.w = W1 + (size_t)(t - n0) * K;
+        else r.w = W2 + (size_t)(t - n0 - n1) * K;
+        break;
       case G_RESID:
-        return TaskRows{W0 + (size_t)t * K, nullptr, 0, M, nullptr};
+        r.w = W0 + (size_t)t * K;
+        break;
       case G_OFF:
-        return TaskRows{W0 + (size_t)t * seg, nullptr, (t / rph) * seg, M, nullptr};
+        r.w = W0 + (size_t)t * seg;
+        r.len = seg;
+        r.xoff = (t / rph) * seg;
+        break;
       case G_RS:
-        if (t < E) return TaskRows{W0 + (size_t)t * K, nullptr, 0, M, nullptr};
-        return TaskRows{Wg + (size_t)(t - E) * K, Wu + (size_t)(t - E) * K, 0, M, nullptr};
-      default: {  // G_EXP
+        if (t < E) r.w = which ? nullptr : W0 + (size_t)t * K;
+        else r.w = (which ? Wu : Wg) + (size_t)(t - E) * K;
+        break;
+      case G_EXP: {
         const int u = t / F, j = t - u * F;
-        const size_t off = ((size_t)rt->uexp[u] * F + j) * K;
+        r.w = (which ? Wu : Wg) + ((size_t)rt->uexp[u] * F + j) * K;
         const int s0 = rt->ustart[u];
-        return TaskRows{Wg + off, Wu + off, 0, rt->ustart[u + 1] - s0, rt->ptok + s0};
+        r.ntok = rt->ustart[u + 1] - s0;
+        r.tok = rt->ptok + s0;
+        break;
       }
+      default:  // G_DOWN: row `which` of the unique experts, then the shared expert's row
+        if (which < rt->nu) {
+          r.w = Wg + ((size_t)rt->uexp[which] * H + t) * F;
+          r.len = F;
+          const int s0 = rt->ustart[which];
+          r.ntok = rt->ustart[which + 1] - s0;
+          r.tbase = s0;
+        } else {
+          r.w = Wu + (size_t)t * SF;
+          r.len = SF;
+          r.tbase = np;
+        }
     }
+    return r;
   }
 
-  __device__ __forceinline__ void epilogue(int t, const float* a0, const float* a1, int ntok) const {
+  // a0/a1: the task's accumulators (LDS), res: its residual inputs (LDS)
+  __device__ __forceinline__ void epilogue(int t, const float* a0, const float* a1, const float* res) const {
     switch (kind) {
       case G_STACK: {
         float* o = out0;
@@ -290,86 +365,167 @@ struct Gemv {
           ld_o = ldo1;
           t -= n0;
         }
-        for (int k = 0; k < ntok; ++k) stc(o + (size_t)k * ld_o + t, a0[k]);
+        for (int k = 0; k < M; ++k) stc(o + (size_t)k * ld_o + t, a0[k]);
         break;
       }
       case G_RESID:
-        for (int k = 0; k < ntok; ++k) {
-          float* o = out0 + (size_t)k * ldo0 + t;
-          stc(o, ldc(o) + a0[k]);
-        }
+      case G_DOWN:
+        for (int k = 0; k < M; ++k) stc(out0 + (size_t)k * ldo0 + t, res[k] + a0[k]);
         break;
       case G_OFF:
-        for (int k = 0; k < ntok; ++k) stc(out0 + (size_t)k * ldo0 + t, a0[k]);
+        for (int k = 0; k < M; ++k) stc(out0 + (size_t)k * ldo0 + t, a0[k]);
         break;
       case G_RS:
         if (t < E) {
-          for (int k = 0; k < ntok; ++k) stc(rlog + (size_t)k * E + t, a0[k]);
+          for (int k = 0; k < M; ++k) stc(rlog + (size_t)k * E + t, a0[k]);
         } else {
-          for (int k = 0; k < ntok; ++k) stc(sact + (size_t)k * SF + (t - E), silu(a0[k]) * a1[k]);
+          for (int k = 0; k < M; ++k) stc(sact + (size_t)k * SF + (t - E), silu(a0[k]) * a1[k]);
         }
         break;
       default: {  // G_EXP
         const int u = t / F, j = t - u * F;
-        const int s0 = rt->ustart[u];
-        for (int k = 0; k < ntok; ++k) stc(eact + (size_t)(s0 + k) * F + j, silu(a0[k]) * a1[k]);
+        const int s0 = rt->ustart[u], n = rt->ustart[u + 1] - s0;
+        for (int k = 0; k < n; ++k) stc(eact + (size_t)(s0 + k) * F + j, silu(a0[k]) * a1[k]);
       }
     }
   }
 
-  // stage rows [k0, k0+ks) of the input into LDS (all threads). inv/red: LDS scratch.
-  __device__ __forceinline__ void stage_in(float* dst, int k0, int ks, float* inv, float* red) const {
-    if (stage == S_NORM) {
-      if (k0 == 0 && ks == K) {  // one pass: raw rows and their sums of squares
-        for (int m = 0; m < M; ++m) {
-          float ss = 0.f;
-          for (int k = 2 * threadIdx.x; k < K; k += 2 * kThreads) {
-            const float2 v = ldc2(src + (size_t)m * ld + k);
-            dst[m * ks + k] = v.x;
-            dst[m * ks + k + 1] = v.y;
-            ss += v.x * v.x + v.y * v.y;
-          }
-          ss = wave_sum(ss, 64);
-          if (lane_id() == 0) red[m * kWaves + wave_id()] = ss;
+  // inv[m] = 1/sqrt(mean(src[m][:K]^2) + eps): one batched pass over every row
+  template <int MM>
+  __device__ __forceinline__ void row_inv(const Ws& ws, float* inv, float* red) const {
+    const int rq = K >> 2, n = M * rq, tid = tid_x();
+    float ss[MM];
+#pragma unroll
+    for (int k = 0; k < MM; ++k) ss[k] = 0.f;
+    for (int b = 0; b < n; b += 8 * kThreads) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b + u * kThreads < n) {
+          const int i = min(b + u * kThreads + tid, n - 1), m = i / rq;
+          v[u] = ws.ld4(src + (size_t)m * ld + 4 * (i - m * rq));
         }
-        __syncthreads();
-        if (threadIdx.x < M) {
-          float t = 0.f;
-          for (int w = 0; w < kWaves; ++w) t += red[threadIdx.x * kWaves + w];
-          inv[threadIdx.x] = 1.0f / sqrtf(t / (float)K + eps);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = b + u * kThreads + tid;
+        if (b + u * kThreads < n && i < n) {
+          const int m = i / rq;
+          const float s = dot4(v[u], v[u]);
+#pragma unroll
+          for (int k = 0; k < MM; ++k) ss[k] += (k == m) ? s : 0.f;
         }
-        __syncthreads();
-        const int n = M * ks;
-        for (int e = threadIdx.x; e < n; e += kThreads) {
-          const int m = e / ks, k = e - m * ks;
-          dst[e] *= inv[m] * bf2f(gp(gain)[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < MM; ++k) {
+      const float s = wave_sum(ss[k], 64);
+      if (lane_id() == 0 && k < M) red[k * kWaves + wave_id()] = s;
+    }
+    __syncthreads();
+    if (tid < M) {
+      float t = 0.f;
+      for (int w = 0; w < kWaves; ++w) t += red[tid * kWaves + w];
+      inv[tid] = 1.0f / sqrtf(t / (float)K + eps);
+    }
+    __syncthreads();
+  }
+
+  // Stage input columns [k0, k0+ks) into dst (LDS) as rows of ks floats, all threads. S_NORM
+  // rows are scaled by their RMS over all K columns (computed on the first slab) and the gain.
+  template <int MM>
+  __device__ __forceinline__ void stage_in(const Ws& ws, float* dst, int k0, int ks, bool one_slab, float* inv,
+                                           float* red) const {
+    const int tid = tid_x(), rq = ks >> 2;
+    if (stage == S_DOWN) {  // expert activation rows, then shared activation rows
+      const int ue = max(0, min(F - k0, ks)) >> 2, us = max(0, min(SF - k0, ks)) >> 2, ne = np * ue;
+      copy_units<8>(
+          ws, ne + M * us,
+          [&](int i) {
+            if (i < ne) {
+              const int s = i / ue;
+              return src + (size_t)s * F + k0 + 4 * (i - s * ue);
+            }
+            const int j = i - ne, m = j / us;
+            return src2 + (size_t)m * SF + k0 + 4 * (j - m * us);
+          },
+          [&](int i) {
+            if (i < ne) {
+              const int s = i / ue;
+              return dst + s * ks + 4 * (i - s * ue);
+            }
+            const int j = i - ne, m = j / us;
+            return dst + (np + m) * ks + 4 * (j - m * us);
+          });
+      return;
+    }
+    if (stage == S_NOPE) {  // the nope parts of the heads, concatenated, from rows [nh][qd]
+      copy_units<8>(
+          ws, M * rq,
+          [&](int i) {
+            const int m = i / rq, k = k0 + 4 * (i - m * rq), h = k / nd;
+            return src + (size_t)m * nh * qd + h * qd + (k - h * nd);
+          },
+          [&](int i) { return dst + 4 * i; });
+      return;
+    }
+    if (stage == S_NORM && !one_slab && k0 == 0) row_inv<MM>(ws, inv, red);
+    const int no = ks >> 3;
+    const bool greg = stage == S_NORM && no <= 4 * kThreads;
+    uint4 gv[4];  // the slab's gain, requested ahead of the input
+    if (greg) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (u * kThreads < no) gv[u] = ldw(gain + k0 + 8 * min(u * kThreads + tid, no - 1));
+    }
+    copy_units<8>(
+        ws, M * rq,
+        [&](int i) {
+          const int m = i / rq;
+          return src + (size_t)m * ld + k0 + 4 * (i - m * rq);
+        },
+        [&](int i) { return dst + 4 * i; });
+    if (stage != S_NORM) return;
+    __syncthreads();
+    if (one_slab) {  // sums of squares from the staged rows
+      for (int m = 0; m < M; ++m) {
+        float ss = 0.f;
+        for (int k = 4 * tid; k < ks; k += 4 * kThreads) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(dst + m * ks + k);
+          ss += dot4(v, v);
         }
-        return;
+        ss = wave_sum(ss, 64);
+        if (lane_id() == 0) red[m * kWaves + wave_id()] = ss;
       }
-      if (k0 == 0) block_inv_rms(src, ld, M, K, eps, inv, red);
-      const int n = M * ks;
-      for (int e = 2 * threadIdx.x; e < n; e += 2 * kThreads) {
-        const int m = e / ks, k = e - m * ks;  // ks even, so a pair never straddles rows
-        const float2 v = ldc2(src + (size_t)m * ld + k0 + k);
-        dst[e] = v.x * inv[m] * bf2f(gp(gain)[k0 + k]);
-        dst[e + 1] = v.y * inv[m] * bf2f(gp(gain)[k0 + k + 1]);
+      __syncthreads();
+      if (tid < M) {
+        float t = 0.f;
+        for (int w = 0; w < kWaves; ++w) t += red[tid * kWaves + w];
+        inv[tid] = 1.0f / sqrtf(t / (float)K + eps);
       }
-    } else if (stage == S_PLAIN) {
-      const int n = M * ks;
-      for (int e = 2 * threadIdx.x; e < n; e += 2 * kThreads) {
-        const int m = e / ks, k = e - m * ks;
-        const float2 v = ldc2(src + (size_t)m * ld + k0 + k);
-        dst[e] = v.x;
-        dst[e + 1] = v.y;
+      __syncthreads();
+    }
+    auto scale8 = [&](int o, const uint4& gw) {
+      float gf[8];
+      unpack8(gw, gf);
+      for (int m = 0; m < M; ++m) {
+        const float s = inv[m];
+        f32x4* d = reinterpret_cast<f32x4*>(dst + m * ks + 8 * o);
+        f32x4 a = d[0], b = d[1];
+        a.x *= s * gf[0]; a.y *= s * gf[1]; a.z *= s * gf[2]; a.w *= s * gf[3];
+        b.x *= s * gf[4]; b.y *= s * gf[5]; b.z *= s * gf[6]; b.w *= s * gf[7];
+        d[0] = a;
+        d[1] = b;
       }
-    } else {  // S_NOPE: the nope parts of every head, contiguous [M][nh*nd] from [M][nh*qd]
-      const int n = M * ks;
-      for (int e = 2 * threadIdx.x; e < n; e += 2 * kThreads) {
-        const int m = e / ks, k = k0 + e - m * ks, h = k / nd, i = k - h * nd;  // nd even
-        const float2 v = ldc2(src + (size_t)m * nh * qd + h * qd + i);
-        dst[e] = v.x;
-        dst[e + 1] = v.y;
+    };
+    if (greg) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int o = u * kThreads + tid;
+        if (o < no) scale8(o, gv[u]);
       }
+    } else {
+      for (int o = tid; o < no; o += kThreads) scale8(o, ldw(gain + k0 + 8 * o));
     }
   }
 };
@@ -381,12 +537,12 @@ struct RowBuf {
 };
 
 // Issue the loads of this lane's chunks of one block of a weight row: chunks c = c0 + sub + u*LPR
-// (u < kNC, c < nch), at chunk offset c_begin from w. Every load is issued (out-of-range chunks
-// read `safe`, a valid address, and are ignored): branches around individual loads make the
-// compiler wait for each load before issuing the next.
-__device__ __forceinline__ void load_block(const uint16_t* w, int c_begin, int c0, int nch, int sub, int LPR,
-                                           const uint16_t* safe, RowBuf& b) {
-  const uint16_t* base = w + (size_t)(c_begin + c0 + sub) * 8;
+// (u < kNC, c < nch) of w. Every load is issued (out-of-range chunks read `safe`, a valid
+// address, and are ignored): branches around individual loads make the compiler wait for each
+// load before issuing the next.
+__device__ __forceinline__ void load_block(const uint16_t* w, int c0, int nch, int sub, int LPR, const uint16_t* safe,
+                                           RowBuf& b) {
+  const uint16_t* base = w + (size_t)(c0 + sub) * 8;
 #pragma unroll
   for (int u = 0; u < kNC; ++u) {
     const bool ok = c0 + sub + u * LPR < nch;
@@ -394,14 +550,14 @@ __device__ __forceinline__ void load_block(const uint16_t* w, int c_begin, int c
   }
 }
 
-// d[q] = this lane's partial dot product of the block with staged input row tok[q]
+// d[q] = this lane's partial dot product of the block with the staged input row of q
 template <int MM>
-__device__ __forceinline__ void dot_block(const RowBuf& b, const float* xin, int ldx, int xoff, const int* tok,
-                                          int ntok, int c0, int nch, int sub, int LPR, float (&d)[MM]) {
+__device__ __forceinline__ void dot_block(const RowBuf& b, const float* xin, int ldx, int xoff, const RowRef& r, int c0,
+                                          int nch, int sub, int LPR, float (&d)[MM]) {
   int tk[MM];
 #pragma unroll
   for (int q = 0; q < MM; ++q) {
-    tk[q] = tok ? tok[q < ntok ? q : 0] : q;
+    tk[q] = r.tok ? r.tok[q < r.ntok ? q : 0] : r.tbase + q;
     d[q] = 0.f;
   }
 #pragma unroll
@@ -412,7 +568,7 @@ __device__ __forceinline__ void dot_block(const RowBuf& b, const float* xin, int
       unpack8(b.v[u], f);
 #pragma unroll
       for (int q = 0; q < MM; ++q) {
-        if (q < ntok) {
+        if (q < r.ntok) {
           const float* xp = xin + (size_t)tk[q] * ldx + xoff + c * 8;
           const float4 xa = *reinterpret_cast<const float4*>(xp);
           const float4 xb = *reinterpret_cast<const float4*>(xp + 4);
@@ -424,25 +580,25 @@ __device__ __forceinline__ void dot_block(const RowBuf& b, const float* xin, int
   }
 }
 
-__device__ __forceinline__ int pow2ceil(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
-
 // Static distribution of a phase's tasks (identical whenever it is computed for the same phase).
 // Each lane group streams elements e = (task it, row which, block blk) in that order.
 struct Plan {
   int t0, nloc, wbase, Wst, KS, LPR, G, sub, grp, iters, nblk, nel;
   bool one_slab;
+  float* acc;  // [nloc][2][MM] task accumulators, at the end of the LDS buffer
+  float* res;  // [nloc][MM] residual inputs
 };
 
-__device__ __forceinline__ Plan make_plan(const Gemv& g) {
+template <int MM>
+__device__ __forceinline__ Plan make_plan(const Gemv& g, float* smem) {
   Plan q;
   const int nt = g.ntasks;
   q.t0 = (int)(((long long)nt * blockIdx.x) / gridDim.x);
   const int t1 = (int)(((long long)nt * (blockIdx.x + 1)) / gridDim.x);
   q.nloc = t1 - q.t0;
+  const int in_cap = (kLdsFloats - q.nloc * 3 * MM) & ~7;
+  q.acc = smem + in_cap;
+  q.res = q.acc + q.nloc * 2 * MM;
   q.wbase = 0;
   q.Wst = g.Wst;
   const bool offs = g.kind == G_OFF;
@@ -452,72 +608,76 @@ __device__ __forceinline__ Plan make_plan(const Gemv& g) {
   }
   q.KS = q.Wst;
   if (!offs) {
-    int cap = (kInFloats / g.M) & ~511;
-    if (cap < 512) cap = 512;
+    const int rows = g.stage == S_DOWN ? g.np + g.M : g.M;
+    int cap = (in_cap / rows) & ~7;
+    if (cap < 8) cap = 8;
     if (q.KS > cap) q.KS = cap;
   }
-  const int nch_full = (offs ? g.seg : q.KS) >> 3;
-  q.LPR = nch_full >= 64 ? 64 : pow2ceil(nch_full);
+  const int nch = (offs ? g.seg : q.KS) >> 3;
+  // lanes per row: enough that kNC chunks per lane cover the row, few enough that every wave has
+  // a task when the workgroup has few
+  const int lo = min(64, pow2ceil(cdiv(nch, kNC))), hi = min(64, pow2ceil(nch));
+  const int per_wave = max(1, cdiv(q.nloc, kWaves));
+  int bal = 64;
+  while (bal > 1 && bal * per_wave > 64) bal >>= 1;
+  q.LPR = min(max(bal, lo), max(hi, lo));
   q.G = 64 / q.LPR;
   q.sub = lane_id() % q.LPR;
   q.grp = lane_id() / q.LPR;
-  const int per_iter = kWaves * q.G;
-  q.iters = (q.nloc + per_iter - 1) / per_iter;
-  q.nblk = (nch_full + kNC * q.LPR - 1) / (kNC * q.LPR);
+  q.iters = cdiv(q.nloc, kWaves * q.G);
+  q.nblk = cdiv(nch, kNC * q.LPR);
   q.nel = q.iters * g.pairs * q.nblk;
   q.one_slab = q.KS >= q.Wst;
   return q;
 }
 
 // Issue the loads of stream element e into b (a wave-uniform decision: elements past the end of
-// the stream are skipped as a whole; lanes without a task read a valid dummy row).
-__device__ __forceinline__ void load_element(const Gemv& g, const Plan& q, int e, int c_begin, int nch, RowBuf& b) {
+// the stream are skipped as a whole; lanes without a row read a valid dummy address).
+__device__ __forceinline__ void load_element(const Gemv& g, const Plan& q, int e, int k0, int ks, RowBuf& b) {
   if (e >= q.nel) return;
-  const int per_task = g.pairs * q.nblk;
-  const int it = e / per_task, rem = e - it * per_task, which = rem / q.nblk, blk = rem - which * q.nblk;
+  const int per = g.pairs * q.nblk;
+  const int it = e / per, rem = e - it * per, which = rem / q.nblk, blk = rem - which * q.nblk;
   const int i = (it * kWaves + wave_id()) * q.G + q.grp;
-  // a row that exists in every model: the first matrix of the phase (the router for G_RS; the
-  // shared expert may be absent), or the expert pool of the layer for G_EXP
-  const uint16_t* safe = g.kind == G_EXP ? g.Wg : g.W0;
-  const uint16_t* w = safe;
+  const uint16_t* w = g.safe;
   int nc = 0;
   if (i < q.nloc) {
-    const TaskRows tr = g.rows(q.t0 + i);
-    const uint16_t* wr = which ? tr.w1 : tr.w0;
-    if (wr) {
-      w = wr;
-      nc = nch;
+    const RowRef r = g.row(q.t0 + i, which);
+    if (r.w) {
+      w = r.w + k0;
+      nc = max(0, min(r.len - k0, ks)) >> 3;
     }
   }
-  load_block(w, c_begin, blk * kNC * q.LPR, nc, q.sub, q.LPR, safe, b);
+  load_block(w, blk * kNC * q.LPR, nc, q.sub, q.LPR, g.safe, b);
 }
 
-// Load the first two elements of this lane group's stream before the barrier (not the polling
-// wave, whose poll would otherwise wait for them). Returns 2 when issued, else 0.
-__device__ __forceinline__ int gemv_preload(const Gemv& g, RowBuf& b0, RowBuf& b1) {
+// Request the first two elements of this lane group's stream before the barrier (not on the
+// polling wave, whose poll would otherwise wait for them). Returns 2 when issued, else 0.
+template <int MM>
+__device__ __forceinline__ int gemv_preload(const Gemv& g, float* smem, RowBuf& b0, RowBuf& b1) {
   if (wave_id() == kPollWave) return 0;
-  const Plan q = make_plan(g);
-  if (!q.one_slab) return 0;
-  const int nch = (g.kind == G_OFF ? g.seg : q.KS) >> 3;
-  load_element(g, q, 0, 0, nch, b0);
-  load_element(g, q, 1, 0, nch, b1);
+  const Plan q = make_plan<MM>(g, smem);
+  const int ks = min(q.KS, q.Wst);
+  load_element(g, q, 0, 0, ks, b0);
+  load_element(g, q, 1, 0, ks, b1);
   return 2;
 }
 
 template <int MM>
-__device__ __forceinline__ void reduce_task(const Plan& q, int i, bool first_slab, float (&a0)[MM], float (&a1)[MM],
-                                            float* acc) {
+__device__ __forceinline__ void reduce_task(const Gemv& g, const Plan& q, int i, bool first, float (&a0)[MM],
+                                            float (&a1)[MM]) {
+  const bool two = g.kind == G_RS || g.kind == G_EXP;
 #pragma unroll
-  for (int k = 0; k < MM; ++k) {
-    a0[k] = wave_sum(a0[k], q.LPR);
-    a1[k] = wave_sum(a1[k], q.LPR);
+  for (int k = 0; k < MM; ++k) a0[k] = wave_sum(a0[k], q.LPR);
+  if (two) {
+#pragma unroll
+    for (int k = 0; k < MM; ++k) a1[k] = wave_sum(a1[k], q.LPR);
   }
   if (i < q.nloc && q.sub == 0) {
-    float* ac = acc + (size_t)i * 2 * MM;
+    float* ac = q.acc + (size_t)i * 2 * MM;
 #pragma unroll
     for (int k = 0; k < MM; ++k) {
-      ac[k] = first_slab ? a0[k] : ac[k] + a0[k];
-      ac[MM + k] = first_slab ? a1[k] : ac[MM + k] + a1[k];
+      ac[k] = first ? a0[k] : ac[k] + a0[k];
+      if (two) ac[MM + k] = first ? a1[k] : ac[MM + k] + a1[k];
     }
   }
 #pragma unroll
@@ -526,230 +686,205 @@ __device__ __forceinline__ void reduce_task(const Plan& q, int i, bool first_sla
 
 // Consume stream element e from b, then reuse b for element e + 2.
 template <int MM>
-__device__ __forceinline__ void step_element(const Gemv& g, const Plan& q, int e, int c_begin, int nch,
-                                             const float* xin, int ldx, bool first_slab, RowBuf& b, float (&a0)[MM],
-                                             float (&a1)[MM], float* acc) {
-  const int per_task = g.pairs * q.nblk;
-  const int it = e / per_task, rem = e - it * per_task, which = rem / q.nblk, blk = rem - which * q.nblk;
+__device__ __forceinline__ void step_element(const Gemv& g, const Plan& q, int e, int k0, int ks, const float* xin,
+                                             bool first, RowBuf& b, float (&a0)[MM], float (&a1)[MM]) {
+  const int per = g.pairs * q.nblk;
+  const int it = e / per, rem = e - it * per, which = rem / q.nblk, blk = rem - which * q.nblk;
   const int i = (it * kWaves + wave_id()) * q.G + q.grp;
   if (i < q.nloc) {
-    const TaskRows tr = g.rows(q.t0 + i);
-    if (which == 0 || tr.w1) {
+    const RowRef r = g.row(q.t0 + i, which);
+    if (r.w) {
+      const int nc = max(0, min(r.len - k0, ks)) >> 3;
       float d[MM];
-      dot_block<MM>(b, xin, ldx, tr.xoff - q.wbase, tr.tok, tr.ntok, blk * kNC * q.LPR, nch, q.sub, q.LPR, d);
+      dot_block<MM>(b, xin, ks, r.xoff - q.wbase, r, blk * kNC * q.LPR, nc, q.sub, q.LPR, d);
+      if (g.kind == G_DOWN && which < g.rt->nu) {  // each pair into its token, with its router weight
 #pragma unroll
-      for (int k = 0; k < MM; ++k) {
-        a0[k] += which ? 0.f : d[k];
-        a1[k] += which ? d[k] : 0.f;
+        for (int k = 0; k < MM; ++k) {
+          if (k < r.ntok) {
+            const int s = r.tbase + k, m = g.rt->ptok[s];
+            const float v = g.rt->pw[s] * d[k];
+#pragma unroll
+            for (int mm = 0; mm < MM; ++mm) a0[mm] += (mm == m) ? v : 0.f;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < MM; ++k) {
+          a0[k] += which && g.kind != G_DOWN ? 0.f : d[k];
+          a1[k] += which && g.kind != G_DOWN ? d[k] : 0.f;
+        }
       }
     }
   }
-  load_element(g, q, e + 2, c_begin, nch, b);
-  if (rem == per_task - 1) reduce_task<MM>(q, i, first_slab, a0, a1, acc);
+  load_element(g, q, e + 2, k0, ks, b);
+  if (rem == per - 1) reduce_task<MM>(g, q, i, first, a0, a1);
 }
 
+// Returns true when the LDS input buffer ends the phase holding the whole normalised input.
 template <int MM>
-__device__ __forceinline__ void gemv_phase(const Gemv& g, float* smem, float* inv, float* red, RowBuf& b0,
-                                           RowBuf& b1, int npre, uint64_t* trace) {
+__device__ __forceinline__ bool gemv_phase(const Gemv& g, const Ws& ws, float* smem, float* inv, float* red,
+                                           RowBuf& b0, RowBuf& b1, int npre, bool keep_in, uint64_t* trace) {
   float* xin = smem;
-  float* acc = smem + kInFloats;
-  const Plan q = make_plan(g);
-  const bool offs = g.kind == G_OFF;
+  const Plan q = make_plan<MM>(g, smem);
+  const int tid = tid_x();
+  const bool keep = keep_in && q.one_slab;  // input already staged by the previous phase
+  const bool resid = g.kind == G_RESID || g.kind == G_DOWN;
   for (int k0 = 0; k0 < q.Wst; k0 += q.KS) {
     const int ks = min(q.KS, q.Wst - k0);
-    const int c_begin = offs ? 0 : (k0 >> 3);
-    const int nch = offs ? (g.seg >> 3) : (ks >> 3);
     if (!(k0 == 0 && npre == 2)) {
-      load_element(g, q, 0, c_begin, nch, b0);
-      load_element(g, q, 1, c_begin, nch, b1);
+      load_element(g, q, 0, k0, ks, b0);
+      load_element(g, q, 1, k0, ks, b1);
     }
     __syncthreads();
-    g.stage_in(xin, q.wbase + k0, ks, inv, red);
+    if (!keep) {
+      // the residual inputs of this workgroup's rows travel with the staging loads
+      const bool rl = resid && k0 == 0 && tid < q.nloc * g.M;
+      float rv = 0.f;
+      if (rl) {
+        const int i = tid / g.M, m = tid - i * g.M;
+        rv = ws.ld1(g.out0 + (size_t)m * g.ldo0 + q.t0 + i);
+      }
+      g.stage_in<MM>(ws, xin, q.wbase + k0, ks, q.one_slab, inv, red);
+      if (rl) {
+        const int i = tid / g.M, m = tid - i * g.M;
+        q.res[i * MM + m] = rv;
+      }
+      if (resid && k0 == 0) {
+        for (int e = tid + kThreads; e < q.nloc * g.M; e += kThreads) {
+          const int i = e / g.M, m = e - i * g.M;
+          q.res[i * MM + m] = ws.ld1(g.out0 + (size_t)m * g.ldo0 + q.t0 + i);
+        }
+      }
+    }
     __syncthreads();
-    if (trace && k0 == 0 && threadIdx.x == 0) gp(trace)[2] = wall_clock64();
+    if (trace && k0 == 0 && tid == 0) gp(trace)[2] = wall_clock64();
     float a0[MM], a1[MM];
 #pragma unroll
     for (int k = 0; k < MM; ++k) a0[k] = a1[k] = 0.f;
     for (int e = 0; e < q.nel; e += 2) {
-      step_element<MM>(g, q, e, c_begin, nch, xin, ks, k0 == 0, b0, a0, a1, acc);
-      if (e + 1 < q.nel) step_element<MM>(g, q, e + 1, c_begin, nch, xin, ks, k0 == 0, b1, a0, a1, acc);
+      step_element<MM>(g, q, e, k0, ks, xin, k0 == 0, b0, a0, a1);
+      if (e + 1 < q.nel) step_element<MM>(g, q, e + 1, k0, ks, xin, k0 == 0, b1, a0, a1);
     }
   }
-  if (trace && threadIdx.x == 0) gp(trace)[3] = wall_clock64();
+  if (trace && tid == 0) gp(trace)[3] = wall_clock64();
   // epilogue: each task by the lane that accumulated it
   for (int it = 0; it < q.iters; ++it) {
     const int i = (it * kWaves + wave_id()) * q.G + q.grp;
     if (i < q.nloc && q.sub == 0) {
-      const TaskRows tr = g.rows(q.t0 + i);
-      const float* ac = acc + (size_t)i * 2 * MM;
-      g.epilogue(q.t0 + i, ac, ac + MM, tr.ntok);
+      const float* ac = q.acc + (size_t)i * 2 * MM;
+      g.epilogue(q.t0 + i, ac, ac + MM, q.res + i * MM);
     }
   }
+  return q.one_slab && g.stage == S_NORM;
 }
 
 // ----------------------------------------------------------------------------------------------
-// routing (every workgroup): softmax over the experts of each token, top-k by logit with ties to
-// the lower index, then the unique experts in ascending order with their token lists
+// routing (every workgroup, one wave per token): softmax over the token's router logits, top-k
+// by logit with ties to the lower expert index, weights renormalised over the chosen experts when
+// the model asks; then the unique experts in ascending order, each with its (token, weight)
+// pairs in token order
 // ----------------------------------------------------------------------------------------------
-__device__ __forceinline__ void compute_route(const Params& p, int layer, Route* rt, int* sel_lds, float* w_lds, float* r_lds) {
-  const int M = p.M, E = p.E, K = p.topk;
-  for (int e = threadIdx.x; e < M * E; e += kThreads) r_lds[e] = ldc(p.rlog + e);
-  __syncthreads();
-  if (threadIdx.x < M) {
-    const int m = threadIdx.x;
-    const float* r = r_lds + (size_t)m * E;
-    float mx = -INFINITY;
-    for (int e = 0; e < E; ++e) mx = fmaxf(mx, r[e]);
+__device__ __forceinline__ void compute_route(const Params& p, const Ws& ws, int layer, Route* rt, int* sel,
+                                              float* wsel, int* cnt) {
+  const int M = p.M, E = p.E, K = p.topk, lane = lane_id(), tid = tid_x();
+  constexpr int R = kMaxExperts / 64;
+  for (int m = wave_id(); m < M; m += kWaves) {
+    float r[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int e = lane + 64 * k;
+      const float v = ws.ld1(p.rlog + (size_t)m * E + min(e, E - 1));
+      r[k] = e < E ? v : -INFINITY;
+    }
+    float mx = r[0];
+#pragma unroll
+    for (int k = 1; k < R; ++k) mx = fmaxf(mx, r[k]);
+    mx = wave_max(mx, 64);
     float sum = 0.f;
-    for (int e = 0; e < E; ++e) sum += __expf(r[e] - mx);
-    int chosen[8];
+#pragma unroll
+    for (int k = 0; k < R; ++k) sum += (lane + 64 * k < E) ? __expf(r[k] - mx) : 0.f;
+    sum = wave_sum(sum, 64);
+    unsigned taken = 0;
     float tot = 0.f;
     for (int j = 0; j < K; ++j) {
-      int best = -1;
       float bv = 0.f;
-      for (int e = 0; e < E; ++e) {
-        bool taken = false;
-        for (int q = 0; q < j; ++q) taken |= (chosen[q] == e);
-        if (taken) continue;
-        if (best < 0 || r[e] > bv) {
-          best = e;
-          bv = r[e];
+      int be = -1;
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int e = lane + 64 * k;
+        if (e < E && !((taken >> k) & 1u) && (be < 0 || r[k] > bv)) {
+          bv = r[k];
+          be = e;
         }
       }
-      chosen[j] = best;
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oe = __shfl_xor(be, o, 64);
+        if (oe >= 0 && (be < 0 || ov > bv || (ov == bv && oe < be))) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if ((be & 63) == lane) taken |= 1u << (be >> 6);
       const float pe = __expf(bv - mx) / sum;
-      w_lds[m * K + j] = pe;
-      sel_lds[m * K + j] = best;
       tot += pe;
+      if (lane == 0) {
+        sel[m * K + j] = be;
+        wsel[m * K + j] = pe;
+      }
     }
-    if (p.norm_topk)
-      for (int j = 0; j < K; ++j) w_lds[m * K + j] /= tot;
-    if (p.route != nullptr && blockIdx.x == 0)
-      for (int j = 0; j < K; ++j) gp(p.route)[((size_t)layer * M + m) * K + j] = chosen[j];
+    if (lane == 0) {
+      if (p.norm_topk)
+        for (int j = 0; j < K; ++j) wsel[m * K + j] /= tot;
+      if (p.route != nullptr && blockIdx.x == 0)
+        for (int j = 0; j < K; ++j) gp(p.route)[((size_t)layer * M + m) * K + j] = sel[m * K + j];
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  const int nq = M * K;
+  for (int e = tid; e < E; e += kThreads) {
+    int c = 0;
+    for (int q = 0; q < nq; ++q) c += sel[q] == e;
+    cnt[e] = c;
+  }
+  __syncthreads();
+  if (tid == 0) {
     int nu = 0, np = 0;
     for (int e = 0; e < E; ++e) {
-      const int start = np;
-      for (int m = 0; m < M; ++m)
-        for (int j = 0; j < K; ++j)
-          if (sel_lds[m * K + j] == e) {
-            rt->ptok[np] = m;
-            rt->pw[np] = w_lds[m * K + j];
-            ++np;
-          }
-      if (np > start) {
+      const int c = cnt[e];
+      if (c) {
         rt->uexp[nu] = e;
-        rt->ustart[nu] = start;
+        rt->ustart[nu] = np;
+        cnt[e] = np;
+        np += c;
         ++nu;
+      } else {
+        cnt[e] = -1;
       }
     }
     rt->ustart[nu] = np;
     rt->nu = nu;
   }
   __syncthreads();
-}
-
-// down projections of the routed experts plus the shared expert, weighted and added to x
-__device__ __forceinline__ void moe_down_phase(const Params& p, const LayerDev& ly, const Route* rt, float* smem) {
-  const int H = p.H, F = p.F, SF = p.SF, M = p.M;
-  const int np = rt->ustart[rt->nu];
-  float* eact = smem;                   // [np][F]
-  float* sact = smem + (size_t)np * F;  // [M][SF]
-  const int r0 = (int)(((long long)H * blockIdx.x) / gridDim.x);
-  const int r1 = (int)(((long long)H * (blockIdx.x + 1)) / gridDim.x);
-  const int lane = lane_id();
-  const int nchF = F >> 3;
-  // the first 256 chunks of the first row's weights in flight while the activations are staged
-  uint4 pre[4];
-  const int r_first = r0 + wave_id();
-  const bool has_pre = rt->nu > 0 && r_first < r1;
-  if (has_pre) {
-    const uint16_t* w = ly.exp_down + ((size_t)rt->uexp[0] * H + r_first) * F;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = lane + u * 64;
-      if (c < nchF) pre[u] = ldw(w + (size_t)c * 8);
+  for (int e = tid; e < E; e += kThreads) {
+    int k = cnt[e];
+    if (k >= 0) {
+      for (int q = 0; q < nq; ++q) {
+        if (sel[q] == e) {
+          rt->ptok[k] = q / K;
+          rt->pw[k] = wsel[q];
+          ++k;
+        }
+      }
     }
-  }
-  for (int e = 2 * threadIdx.x; e < np * F; e += 2 * kThreads) {
-    const float2 v = ldc2(p.eact + e);
-    eact[e] = v.x;
-    eact[e + 1] = v.y;
-  }
-  for (int e = 2 * threadIdx.x; e < M * SF; e += 2 * kThreads) {
-    const float2 v = ldc2(p.sact + e);
-    sact[e] = v.x;
-    sact[e + 1] = v.y;
   }
   __syncthreads();
-  for (int r = r_first; r < r1; r += kWaves) {
-    float acc[MK_MAX_M];
-#pragma unroll
-    for (int m = 0; m < MK_MAX_M; ++m) acc[m] = 0.f;
-    for (int u = 0; u < rt->nu; ++u) {
-      const uint16_t* w = ly.exp_down + ((size_t)rt->uexp[u] * H + r) * F;
-      const int s0 = rt->ustart[u], s1 = rt->ustart[u + 1];
-      for (int cb = 0; cb < nchF; cb += 256) {
-        const bool use_pre = has_pre && r == r_first && u == 0 && cb == 0;
-        uint4 wv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c = cb + lane + k * 64;
-          if (c < nchF) wv[k] = use_pre ? pre[k] : ldw(w + (size_t)c * 8);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c = cb + lane + k * 64;
-          if (c >= nchF) continue;
-          float f[8];
-          unpack8(wv[k], f);
-          for (int s = s0; s < s1; ++s) {
-            const float* xp = eact + (size_t)s * F + c * 8;
-            float d = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) d += f[j] * xp[j];
-            const int m = rt->ptok[s];
-            const float wgt = rt->pw[s];
-#pragma unroll
-            for (int mm = 0; mm < MK_MAX_M; ++mm)
-              if (mm == m) acc[mm] += wgt * d;
-          }
-        }
-      }
-    }
-    if (SF > 0) {
-      const uint16_t* w = ly.sh_down + (size_t)r * SF;
-      for (int c = lane; c < (SF >> 3); c += 64) {
-        float f[8];
-        unpack8(ldw(w + (size_t)c * 8), f);
-#pragma unroll
-        for (int m = 0; m < MK_MAX_M; ++m) {
-          if (m < M) {
-            const float* xp = sact + (size_t)m * SF + c * 8;
-            float d = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) d += f[j] * xp[j];
-            acc[m] += d;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < MK_MAX_M; ++m) {
-      if (m < M) {
-        const float v = wave_sum(acc[m], 64);
-        if (lane == 0) stc(p.x + (size_t)m * H + r, ldc(p.x + (size_t)m * H + r) + v);
-      }
-    }
-  }
 }
 
 // ----------------------------------------------------------------------------------------------
 // attention
 // ----------------------------------------------------------------------------------------------
-// RoPE table of the step, copied into LDS: table[(t * kMaxRopePairs + j) * 2 + {cos, sin}]
+// RoPE table of the step, in LDS: table[(t * kMaxRopePairs + j) * 2 + {cos, sin}]
 __device__ __forceinline__ void rope_pair(const float* table, int t, int j, float& x0, float& x1) {
   const float c = table[(t * kMaxRopePairs + j) * 2], s = table[(t * kMaxRopePairs + j) * 2 + 1];
   const float a = x0, b = x1;
@@ -759,90 +894,132 @@ __device__ __forceinline__ void rope_pair(const float* table, int t, int j, floa
 
 // GQA split-KV partials. Task (b, g, s): positions [s*C, s*C+C) of sequence b, kv head g, every
 // query head of the group and every new token. New positions in the chunk are appended here.
-__device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev& ly, float* smem, const float* rope) {
-  const int d = p.hd, nq = p.nh, nkv = p.nkv, T = p.T, cap = p.cap;
-  const int npos = p.kv_len + T;
+__device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev& ly, const Ws& ws, float* smem,
+                                               const float* rope) {
+  const int d = p.hd, nq = p.nh, nkv = p.nkv, T = p.T, cap = p.cap, d2 = d / 2, d4 = d / 4, d8 = d / 8;
+  const int npos = p.kv_len + T, C = p.chunk;
   const int nsplit = p.nsplit;
   const int qg = nq / nkv;
   const int ntask = p.B * nkv * nsplit;
-  float* Ks = smem;                 // [C][d]
-  float* Vs = Ks + kChunk * d;      // [C][d]
-  float* Qs = Vs + kChunk * d;      // [T*qg][d]
-  float* S = Qs + T * qg * d;       // [T*qg][C]
+  const int tid = tid_x();
+  float* Ks = smem;             // [C][d]
+  float* Vs = Ks + C * d;       // [C][d]
+  float* Qs = Vs + C * d;       // [T*qg][d]
+  float* S = Qs + T * qg * d;   // [T*qg][C]
   const size_t lstride = (size_t)p.Bmax * nkv * cap * d;
   uint16_t* Kc = p.kv + (size_t)ly.ord * lstride;
   uint16_t* Vc = p.kv + (size_t)p.L * lstride + (size_t)ly.ord * lstride;
   const float scale = 1.0f / sqrtf((float)d);
+  const int stride = d + kPartPad;
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int s = task % nsplit, g = (task / nsplit) % nkv, b = task / (nsplit * nkv);
-    const int p0 = s * kChunk, p1 = min(npos, p0 + kChunk), np = p1 - p0;
+    const int p0 = s * C, p1 = min(npos, p0 + C), np = p1 - p0;
+    const size_t row0 = ((size_t)b * nkv + g) * cap;  // cache row of position 0
     __syncthreads();
-    for (int e = threadIdx.x; e < np * (d / 2); e += kThreads) {
-      const int pl = e / (d / 2), j = e - pl * (d / 2), pos = p0 + pl;
-      const size_t ci = (((size_t)b * nkv + g) * cap + pos) * d;
-      float k0, k1, v0, v1;
-      if (pos < p.kv_len) {
-        k0 = bf2f(gp(Kc)[ci + j]);
-        k1 = bf2f(gp(Kc)[ci + j + d / 2]);
-        v0 = bf2f(gp(Vc)[ci + j]);
-        v1 = bf2f(gp(Vc)[ci + j + d / 2]);
-      } else {
-        const int t = pos - p.kv_len, m = b * T + t;
-        k0 = ldc(p.a2 + (size_t)m * nkv * d + g * d + j);
-        k1 = ldc(p.a2 + (size_t)m * nkv * d + g * d + j + d / 2);
-        rope_pair(rope, t, j, k0, k1);
-        const uint16_t kb0 = f2bf(k0), kb1 = f2bf(k1);
-        const uint16_t vb0 = f2bf(ldc(p.a3 + (size_t)m * nkv * d + g * d + j));
-        const uint16_t vb1 = f2bf(ldc(p.a3 + (size_t)m * nkv * d + g * d + j + d / 2));
-        gp(Kc)[ci + j] = kb0;
-        gp(Kc)[ci + j + d / 2] = kb1;
-        gp(Vc)[ci + j] = vb0;
-        gp(Vc)[ci + j + d / 2] = vb1;
-        k0 = bf2f(kb0); k1 = bf2f(kb1); v0 = bf2f(vb0); v1 = bf2f(vb1);
+    // cached rows (bf16, 8 per load), then the raw queries and new rows (coherent)
+    {
+      const int ncu = np * d8;
+      for (int b0 = 0; b0 < ncu; b0 += 2 * kThreads) {
+        uint4 kv4[2], vv4[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (b0 + u * kThreads < ncu) {
+            const int i = min(b0 + u * kThreads + tid, ncu - 1), pl = i / d8, c = i - pl * d8, pos = p0 + pl;
+            const size_t off = (row0 + (pos < p.kv_len ? pos : 0)) * d + 8 * c;
+            kv4[u] = ldw(Kc + off);
+            vv4[u] = ldw(Vc + off);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = b0 + u * kThreads + tid;
+          if (b0 + u * kThreads < ncu && i < ncu) {
+            const int pl = i / d8, c = i - pl * d8;
+            if (p0 + pl < p.kv_len) {
+              float f[8];
+              unpack8(kv4[u], f);
+              for (int j = 0; j < 8; ++j) Ks[pl * d + 8 * c + j] = f[j];
+              unpack8(vv4[u], f);
+              for (int j = 0; j < 8; ++j) Vs[pl * d + 8 * c + j] = f[j];
+            }
+          }
+        }
       }
-      Ks[pl * d + j] = k0;
-      Ks[pl * d + j + d / 2] = k1;
-      Vs[pl * d + j] = v0;
-      Vs[pl * d + j + d / 2] = v1;
     }
-    for (int e = threadIdx.x; e < T * qg * (d / 2); e += kThreads) {
-      const int r = e / (d / 2), j = e - r * (d / 2);
-      const int t = r / qg, hq = g * qg + (r - t * qg), m = b * T + t;
-      float q0 = ldc(p.a1 + (size_t)m * nq * d + hq * d + j), q1 = ldc(p.a1 + (size_t)m * nq * d + hq * d + j + d / 2);
+    copy_units<4>(
+        ws, T * qg * d4,
+        [&](int i) {
+          const int r = i / d4, t = r / qg, hq = g * qg + (r - t * qg);
+          return p.a1 + (size_t)(b * T + t) * nq * d + hq * d + 4 * (i - r * d4);
+        },
+        [&](int i) { return Qs + 4 * i; });
+    const int n0 = max(p0, p.kv_len), nnew = max(0, p1 - n0);
+    copy_units<2>(
+        ws, nnew * 2 * d4,
+        [&](int i) {
+          const int r = i / (2 * d4), c = i - r * 2 * d4, m = b * T + (n0 - p.kv_len) + r;
+          return (c < d4 ? p.a2 : p.a3) + (size_t)m * nkv * d + g * d + 4 * (c < d4 ? c : c - d4);
+        },
+        [&](int i) {
+          const int r = i / (2 * d4), c = i - r * 2 * d4, pl = n0 - p0 + r;
+          return (c < d4 ? Ks : Vs) + pl * d + 4 * (c < d4 ? c : c - d4);
+        });
+    __syncthreads();
+    // rotate the queries and the new keys; round new rows to bf16 and append them
+    for (int e = tid; e < T * qg * d2; e += kThreads) {
+      const int r = e / d2, j = e - r * d2, t = r / qg;
+      float q0 = Qs[r * d + j], q1 = Qs[r * d + j + d2];
       rope_pair(rope, t, j, q0, q1);
       Qs[r * d + j] = q0;
-      Qs[r * d + j + d / 2] = q1;
+      Qs[r * d + j + d2] = q1;
+    }
+    for (int e = tid; e < nnew * d2; e += kThreads) {
+      const int r = e / d2, j = e - r * d2, pl = n0 - p0 + r, t = n0 - p.kv_len + r;
+      float k0 = Ks[pl * d + j], k1 = Ks[pl * d + j + d2];
+      rope_pair(rope, t, j, k0, k1);
+      const uint16_t kb0 = f2bf(k0), kb1 = f2bf(k1);
+      const uint16_t vb0 = f2bf(Vs[pl * d + j]), vb1 = f2bf(Vs[pl * d + j + d2]);
+      const size_t ci = (row0 + n0 + r) * d;
+      gp(Kc)[ci + j] = kb0;
+      gp(Kc)[ci + j + d2] = kb1;
+      gp(Vc)[ci + j] = vb0;
+      gp(Vc)[ci + j + d2] = vb1;
+      Ks[pl * d + j] = bf2f(kb0);
+      Ks[pl * d + j + d2] = bf2f(kb1);
+      Vs[pl * d + j] = bf2f(vb0);
+      Vs[pl * d + j + d2] = bf2f(vb1);
     }
     __syncthreads();
     const int nr = T * qg;
-    for (int e = threadIdx.x; e < nr * kChunk; e += kThreads) {
-      const int r = e / kChunk, pl = e - r * kChunk, t = r / qg;
+    for (int e = tid; e < nr * C; e += kThreads) {
+      const int r = e / C, pl = e - r * C, t = r / qg;
       float sc = -INFINITY;
       if (pl < np && p0 + pl <= p.kv_len + t) {
         float acc = 0.f;
-        for (int j = 0; j < d; ++j) acc += Qs[r * d + j] * Ks[pl * d + j];
+        for (int j = 0; j < d; j += 4)
+          acc += dot4(*reinterpret_cast<const f32x4*>(Qs + r * d + j), *reinterpret_cast<const f32x4*>(Ks + pl * d + j));
         sc = acc * scale;
       }
-      S[r * kChunk + pl] = sc;
+      S[r * C + pl] = sc;
     }
     __syncthreads();
     for (int r = wave_id(); r < nr; r += kWaves) {
       const int t = r / qg, hq = g * qg + (r - t * qg), m = b * T + t;
       float mx = -INFINITY;
-      for (int pl = 0; pl < kChunk; ++pl) mx = fmaxf(mx, S[r * kChunk + pl]);
-      float* dst = p.part + ((size_t)(m * nq + hq) * nsplit + s) * (d + 2);
+      for (int pl = 0; pl < C; ++pl) mx = fmaxf(mx, S[r * C + pl]);
+      float* dst = p.part + ((size_t)(m * nq + hq) * nsplit + s) * stride;
       float l = 0.f;
       for (int j = lane_id(); j < d; j += 64) {
         float acc = 0.f;
         l = 0.f;
         if (mx != -INFINITY) {
           for (int pl = 0; pl < np; ++pl) {
-            const float w = (S[r * kChunk + pl] == -INFINITY) ? 0.f : __expf(S[r * kChunk + pl] - mx);
+            const float w = (S[r * C + pl] == -INFINITY) ? 0.f : __expf(S[r * C + pl] - mx);
             l += w;
             acc += w * Vs[pl * d + j];
           }
         }
-        stc(dst + 2 + j, acc);
+        stc(dst + kPartPad + j, acc);
       }
       if (lane_id() == 0) {
         stc(dst, mx);
@@ -852,186 +1029,319 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev& 
   }
 }
 
-// Merge split-KV partials: out[m][h*dim + j] = sum_s e^{mx_s - M} u_s[j] / sum_s e^{mx_s - M} l_s.
-// Workgroup task (m, h, 32-wide slice of dims): the split weights are computed once into LDS,
-// then 16 groups of 32 threads sum disjoint sets of splits and LDS reduces the groups.
-__device__ __forceinline__ void merge_phase(const Params& p, int heads, int dim, float* out, float* smem) {
-  const int nsplit = p.nsplit;
-  const int nj = (dim + 31) / 32;
-  const int ntask = p.M * heads * nj;
-  float* w = smem;            // [nsplit]
-  float* red = smem + 1024;   // [16][32]
-  float* misc = smem + 1600;  // [2 * kWaves]
-  const int tid = threadIdx.x, sg = tid >> 5, jj = tid & 31;
+// Merge split-KV partials: out[m][h*dim + j] = sum_s e^{mx_s - M} u_s[j] / sum_s e^{mx_s - M} l_s
+// over the splits s (M the largest mx_s). Task (m, h, 32 values): threads (split lane sl = tid/8,
+// quad q = tid%8) sum splits sl, sl + 64, ... of four values; the splits' statistics are read in
+// the same batch as the first values.
+__device__ __forceinline__ void merge_phase(const Params& p, const Ws& ws, int heads, int dim, float* out,
+                                            float* smem) {
+  constexpr int NS = 5;
+  const int nsplit = p.nsplit, stride = dim + kPartPad, nj = (dim + 31) >> 5, ntask = p.M * heads * nj;
+  const int tid = tid_x(), lane = lane_id(), wave = wave_id(), sl = tid >> 3, qd = tid & 7;
+  float* w = smem;                                                     // [nsplit] split weights
+  f32x4* red = reinterpret_cast<f32x4*>(smem + ((nsplit + 3) & ~3));  // [kWaves][8]
+  float* misc = reinterpret_cast<float*>(red + kWaves * 8);           // [2][kWaves]
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int mh = task / nj, j0 = (task - mh * nj) * 32;
-    const float* src = p.part + (size_t)mh * nsplit * (dim + 2);
-    float mx = -INFINITY;
-    for (int s = tid; s < nsplit; s += kThreads) mx = fmaxf(mx, ldc(src + (size_t)s * (dim + 2)));
+    const float* src = p.part + (size_t)mh * nsplit * stride;
+    const int jq = j0 + 4 * qd < dim ? j0 + 4 * qd : j0;
+    __syncthreads();
+    f32x4 v[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+      if (u * 64 < nsplit) v[u] = ws.ld4(src + (size_t)min(sl + 64 * u, nsplit - 1) * stride + kPartPad + jq);
+    const f32x4 hd = ws.ld4(src + (size_t)min(tid, nsplit - 1) * stride);
+    float mx = tid < nsplit ? hd.x : -INFINITY;
+    for (int s = tid + kThreads; s < nsplit; s += kThreads) mx = fmaxf(mx, ws.ld1(src + (size_t)s * stride));
     mx = wave_max(mx, 64);
+    if (lane == 0) misc[wave] = mx;
     __syncthreads();
-    if (lane_id() == 0) misc[wave_id()] = mx;
-    __syncthreads();
-    float mg = misc[0];
-    for (int i = 1; i < kWaves; ++i) mg = fmaxf(mg, misc[i]);
+    float M = misc[0];
+    for (int i = 1; i < kWaves; ++i) M = fmaxf(M, misc[i]);
     float lsum = 0.f;
-    for (int s = tid; s < nsplit; s += kThreads) {
-      const float2 ml = ldc2(src + (size_t)s * (dim + 2));
-      const float ws = (ml.x == -INFINITY) ? 0.f : __expf(ml.x - mg);
-      w[s] = ws;
-      lsum += ws * ml.y;
+    if (tid < nsplit) {
+      const float ws_ = hd.x == -INFINITY ? 0.f : __expf(hd.x - M);
+      w[tid] = ws_;
+      lsum += ws_ * hd.y;
+    }
+    for (int s = tid + kThreads; s < nsplit; s += kThreads) {
+      const f32x4 h2 = ws.ld4(src + (size_t)s * stride);
+      const float ws_ = h2.x == -INFINITY ? 0.f : __expf(h2.x - M);
+      w[s] = ws_;
+      lsum += ws_ * h2.y;
     }
     lsum = wave_sum(lsum, 64);
-    if (lane_id() == 0) misc[kWaves + wave_id()] = lsum;
+    if (lane == 0) misc[kWaves + wave] = lsum;
     __syncthreads();
     float L = 0.f;
     for (int i = 0; i < kWaves; ++i) L += misc[kWaves + i];
-    float acc = 0.f;
-    const int j = j0 + jj;
-    if (j < dim) {
-#pragma unroll 8
-      for (int s = sg; s < nsplit; s += 16) acc += w[s] * ldc(src + (size_t)s * (dim + 2) + 2 + j);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int s = sl + 64 * u;
+      if (u * 64 < nsplit && s < nsplit) acc += w[s] * v[u];
     }
-    red[sg * 32 + jj] = acc;
+    for (int sb = NS * 64; sb < nsplit; sb += 64) {
+      const int s = sb + sl;
+      if (s < nsplit) acc += w[s] * ws.ld4(src + (size_t)s * stride + kPartPad + jq);
+    }
+    for (int o = 8; o < 64; o <<= 1) {
+      acc.x += __shfl_xor(acc.x, o, 64);
+      acc.y += __shfl_xor(acc.y, o, 64);
+      acc.z += __shfl_xor(acc.z, o, 64);
+      acc.w += __shfl_xor(acc.w, o, 64);
+    }
+    if (lane < 8) red[wave * 8 + lane] = acc;
     __syncthreads();
-    if (tid < 32 && j0 + tid < dim) {
-      float t = 0.f;
-      for (int g = 0; g < 16; ++g) t += red[g * 32 + tid];
-      stc(out + (size_t)mh * dim + j0 + tid, t / L);
+    if (tid < 8 && j0 + 4 * tid < dim) {
+      f32x4 t = red[tid];
+      for (int i = 1; i < kWaves; ++i) t += red[i * 8 + tid];
+      const float il = 1.0f / L;
+      ws.st4(out + (size_t)mh * dim + j0 + 4 * tid, t * il);
     }
   }
 }
 
-// MLA split-KV partials over the latent cache. Task (b, s): every head and every new token of
-// sequence b against positions [s*C, s*C+C). Scores use the absorbed query (W_uk^T q_nope) on the
-// latent part and the RoPE'd query on the shared rope key. New entries are appended here.
-__device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev& ly, float* smem, float* misc, const float* rope) {
+// MLA split-KV partials over the latent cache. Task (b, s) covers positions [s*C, s*C + C) of
+// sequence b for every head and every new token. Scores use the absorbed query (W_uk^T q_nope)
+// against the latent part and the rotated query against the shared rope key, scaled by
+// 1/sqrt(nope + rope); positions are staged kSub at a time with a running max and sum per head.
+// New entries (normalised latent, rotated rope key, rounded to bf16) are appended to the cache by
+// the task whose range holds their position.
+__device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev& ly, const Ws& ws, float* smem,
+                                               const float* rope) {
+  static_assert(kSub == 32, "score lanes map one position each in a half wave");
   const int nh = p.nh, kvl = p.kvl, rd = p.rd, nd = p.nd, T = p.T, cap = p.cap;
-  const int lat = kvl + rd, qd = nd + rd;
-  const int npos = p.kv_len + T, nsplit = p.nsplit;
-  const int ntask = p.B * nsplit;
-  float* Cs = smem;               // [C][lat]
-  float* Qt = Cs + kChunk * lat;  // [nh][lat]  (absorbed query | rope query) for one token
-  float* S = Qt + nh * lat;       // [nh][C]
+  const int lat = kvl + rd, latp = lat + 4, qd = nd + rd, h2 = rd / 2, half = lat / 2;
+  const int npos = p.kv_len + T, C = p.chunk, nsplit = p.nsplit, ntask = p.B * nsplit;
+  const int tid = tid_x(), lane = lane_id(), wave = wave_id();
+  float* Cs = smem;              // [kSub][latp] cache rows
+  float* Qt = Cs + kSub * latp;  // [nh][lat] query of one token
+  float* Nw = Qt + nh * lat;     // [T][lat] new latent rows, rounded
+  float* S = Nw + T * lat;       // [nh][kSub] scores, then weights
+  float* st = S + nh * kSub;     // [nh][4] running max, running sum, rescale
+  float* nrm = st + nh * 4;      // [T] RMS scale of the new rows
+  float* gk = nrm + 8;           // [kvl] latent norm gain
   uint16_t* Lc = p.kv + (size_t)ly.ord * p.Bmax * cap * lat;
   const float scale = 1.0f / sqrtf((float)qd);
+  const int lq = lat >> 2, lc = lat >> 3, nq = nh * lq, kq = kvl >> 2, ntile = (nh >> 2) * kq;
+  const int stride = kvl + kPartPad;
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int s = task % nsplit, b = task / nsplit;
-    const int p0 = s * kChunk, p1 = min(npos, p0 + kChunk), np = p1 - p0;
+    const int p0 = s * C, p1 = min(npos, p0 + C);
+    uint16_t* Lb = Lc + (size_t)b * cap * lat;
+    const int n0 = max(p0, p.kv_len), nnew = max(0, p1 - n0), tA = n0 - p.kv_len;
     __syncthreads();
-    for (int pl = wave_id(); pl < np; pl += kWaves) {
-      const int pos = p0 + pl;
-      if (pos >= p.kv_len) {
-        const int m = b * T + (pos - p.kv_len);
+    if (nnew > 0) {
+      for (int j = tid; j < kvl; j += kThreads) gk[j] = bf2f(gp(ly.kv_norm)[j]);
+      copy_units<2>(
+          ws, nnew * lq,
+          [&](int i) {
+            const int r = i / lq;
+            return p.a2 + (size_t)(b * T + tA + r) * lat + 4 * (i - r * lq);
+          },
+          [&](int i) {
+            const int r = i / lq;
+            return Nw + (tA + r) * lat + 4 * (i - r * lq);
+          });
+      __syncthreads();
+      for (int r = wave; r < nnew; r += kWaves) {
         float ss = 0.f;
-        for (int j = lane_id(); j < kvl; j += 64) {
-          const float v = ldc(p.a2 + (size_t)m * lat + j);
+        for (int j = lane; j < kvl; j += 64) {
+          const float v = Nw[(tA + r) * lat + j];
           ss += v * v;
         }
         ss = wave_sum(ss, 64);
-        if (lane_id() == 0) misc[pl] = 1.0f / sqrtf(ss / (float)kvl + p.eps);
+        if (lane == 0) nrm[r] = 1.0f / sqrtf(ss / (float)kvl + p.eps);
+      }
+      __syncthreads();
+      const int per = kvl + h2;
+      for (int e = tid; e < nnew * per; e += kThreads) {
+        const int r = e / per, j = e - r * per, t = tA + r;
+        float* row = Nw + t * lat;
+        uint16_t* dst = Lb + (size_t)(p.kv_len + t) * lat;
+        if (j < kvl) {
+          const uint16_t v = f2bf(row[j] * nrm[r] * gk[j]);
+          row[j] = bf2f(v);
+          gp(dst)[j] = v;
+        } else {
+          const int jj = j - kvl;
+          float x0 = row[kvl + jj], x1 = row[kvl + jj + h2];
+          rope_pair(rope, t, jj, x0, x1);
+          const uint16_t v0 = f2bf(x0), v1 = f2bf(x1);
+          row[kvl + jj] = bf2f(v0);
+          row[kvl + jj + h2] = bf2f(v1);
+          gp(dst)[kvl + jj] = v0;
+          gp(dst)[kvl + jj + h2] = v1;
+        }
       }
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < np * lat; e += kThreads) {
-      const int pl = e / lat, j = e - pl * lat, pos = p0 + pl;
-      uint16_t* dst = Lc + ((size_t)b * cap + pos) * lat;
-      float v;
+    // cache row i of a stage: unit (row, 8 values) from the cache, or from the new rows
+    auto put_c = [&](int i, int c0, const uint4& v) {
+      const int r = i / lc, cc = i - r * lc, pos = c0 + r;
+      f32x4* dq = reinterpret_cast<f32x4*>(Cs + r * latp + 8 * cc);
       if (pos < p.kv_len) {
-        v = bf2f(gp(dst)[j]);
+        float f[8];
+        unpack8(v, f);
+        dq[0] = f32x4{f[0], f[1], f[2], f[3]};
+        dq[1] = f32x4{f[4], f[5], f[6], f[7]};
       } else {
-        const int t = pos - p.kv_len, m = b * T + t;
-        const float* src = p.a2 + (size_t)m * lat;
-        if (j < kvl) {
-          v = ldc(src + j) * misc[pl] * bf2f(gp(ly.kv_norm)[j]);
-        } else {
-          const int jj = j - kvl, h2 = rd / 2;
-          float x0, x1;
-          if (jj < h2) {
-            x0 = ldc(src + kvl + jj);
-            x1 = ldc(src + kvl + jj + h2);
-            rope_pair(rope, t, jj, x0, x1);
-            v = x0;
-          } else {
-            x0 = ldc(src + kvl + jj - h2);
-            x1 = ldc(src + kvl + jj);
-            rope_pair(rope, t, jj - h2, x0, x1);
-            v = x1;
-          }
-        }
-        const uint16_t vb = f2bf(v);
-        gp(dst)[j] = vb;
-        v = bf2f(vb);
+        const f32x4* sq = reinterpret_cast<const f32x4*>(Nw + (pos - p.kv_len) * lat + 8 * cc);
+        dq[0] = sq[0];
+        dq[1] = sq[1];
       }
-      Cs[pl * lat + j] = v;
-    }
+    };
+    auto c_addr = [&](int i, int c0) {
+      const int r = i / lc, pos = c0 + r;
+      return Lb + (size_t)(pos < p.kv_len ? pos : 0) * lat + 8 * (i - r * lc);
+    };
+    const bool whole = p1 - p0 <= kSub;  // the range is staged once, by the first token that reads it
+    bool staged = false;
     for (int t = 0; t < T; ++t) {
-      const int m = b * T + t;
+      const int m = b * T + t, qpos = p.kv_len + t, pe = min(p1, qpos + 1);
+      f32x4 u[2][4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[k][i] = f32x4{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
-      for (int e = threadIdx.x; e < nh * lat; e += kThreads) {
-        const int h = e / lat, j = e - h * lat;
-        float v;
-        if (j < kvl) {
-          v = ldc(p.a4 + ((size_t)m * nh + h) * kvl + j);
-        } else {
-          const int jj = j - kvl, h2 = rd / 2;
-          const float* qp = p.a3 + (size_t)m * nh * qd + h * qd + nd;
-          float x0, x1;
-          if (jj < h2) {
-            x0 = ldc(qp + jj);
-            x1 = ldc(qp + jj + h2);
-            rope_pair(rope, t, jj, x0, x1);
-            v = x0;
-          } else {
-            x0 = ldc(qp + jj - h2);
-            x1 = ldc(qp + jj);
-            rope_pair(rope, t, jj - h2, x0, x1);
-            v = x1;
-          }
-        }
-        Qt[e] = v;
+      if (tid < nh) {
+        st[tid * 4] = -INFINITY;
+        st[tid * 4 + 1] = 0.f;
+        st[tid * 4 + 2] = 1.f;
       }
-      __syncthreads();
-      for (int h = wave_id(); h < nh; h += kWaves) {
-        for (int pl = 0; pl < kChunk; ++pl) {
-          float acc = 0.f;
-          if (pl < np) {
-            for (int j = lane_id(); j < lat; j += 64) acc += Qt[h * lat + j] * Cs[pl * lat + j];
-          }
-          acc = wave_sum(acc, 64);
-          if (lane_id() == 0) S[h * kChunk + pl] = (pl < np && p0 + pl <= p.kv_len + t) ? acc * scale : -INFINITY;
-        }
-      }
-      __syncthreads();
-      for (int h = wave_id(); h < nh; h += kWaves) {
-        float mx = -INFINITY;
-        for (int pl = 0; pl < kChunk; ++pl) mx = fmaxf(mx, S[h * kChunk + pl]);
-        float* dst = p.part + ((size_t)(m * nh + h) * nsplit + s) * (kvl + 2);
-        float l = 0.f;
-        for (int j = lane_id(); j < kvl; j += 64) {
-          float acc = 0.f;
-          l = 0.f;
-          if (mx != -INFINITY) {
-            for (int pl = 0; pl < np; ++pl) {
-              const float sv = S[h * kChunk + pl];
-              const float w = (sv == -INFINITY) ? 0.f : __expf(sv - mx);
-              l += w;
-              acc += w * Cs[pl * lat + j];
+      if (pe > p0) {
+        // the token's query (absorbed latent part | raw rope part) and the first cache rows
+        {
+          const int ncu = (!whole || !staged) ? (whole ? p1 - p0 : min(kSub, pe - p0)) * lc : 0;
+          staged = true;
+          f32x4 qv[kQSlots];
+          uint4 cv[kCSlots];
+#pragma unroll
+          for (int k = 0; k < kQSlots; ++k) {
+            if (k * kThreads < nq) {
+              const int i = min(k * kThreads + tid, nq - 1), h = i / lq, j = 4 * (i - h * lq);
+              qv[k] = ws.ld4(j < kvl ? p.a4 + ((size_t)m * nh + h) * kvl + j
+                                     : p.a3 + ((size_t)m * nh + h) * qd + nd + (j - kvl));
             }
           }
-          stc(dst + 2 + j, acc);
+#pragma unroll
+          for (int k = 0; k < kCSlots; ++k)
+            if (k * kThreads < ncu) cv[k] = ldw(c_addr(min(k * kThreads + tid, ncu - 1), p0));
+#pragma unroll
+          for (int k = 0; k < kQSlots; ++k) {
+            const int i = k * kThreads + tid;
+            if (k * kThreads < nq && i < nq) *reinterpret_cast<f32x4*>(Qt + 4 * i) = qv[k];
+          }
+#pragma unroll
+          for (int k = 0; k < kCSlots; ++k) {
+            const int i = k * kThreads + tid;
+            if (k * kThreads < ncu && i < ncu) put_c(i, p0, cv[k]);
+          }
         }
-        if (lane_id() == 0) {
-          stc(dst, mx);
-          stc(dst + 1, l);
+        __syncthreads();
+        for (int e = tid; e < nh * h2; e += kThreads) {
+          const int h = e / h2, jj = e - h * h2;
+          float* qr = Qt + h * lat + kvl;
+          float x0 = qr[jj], x1 = qr[jj + h2];
+          rope_pair(rope, t, jj, x0, x1);
+          qr[jj] = x0;
+          qr[jj + h2] = x1;
+        }
+        for (int c0 = p0; c0 < pe; c0 += kSub) {
+          const int n = min(kSub, pe - c0);
+          if (c0 != p0) {
+            __syncthreads();
+            const int ncu = n * lc;
+            for (int bb = 0; bb < ncu; bb += kCSlots * kThreads) {
+              uint4 cv[kCSlots];
+#pragma unroll
+              for (int k = 0; k < kCSlots; ++k)
+                if (bb + k * kThreads < ncu) cv[k] = ldw(c_addr(min(bb + k * kThreads + tid, ncu - 1), c0));
+#pragma unroll
+              for (int k = 0; k < kCSlots; ++k) {
+                const int i = bb + k * kThreads + tid;
+                if (bb + k * kThreads < ncu && i < ncu) put_c(i, c0, cv[k]);
+              }
+            }
+          }
+          __syncthreads();
+          // scores: a wave per head pair, lane (position, half of the latent)
+          for (int it = tid; it < (nh >> 1) * 64; it += kThreads) {
+            const int hp = it >> 6, ln = it & 63, pl = ln & 31, jh = ln >> 5;
+            float s0 = 0.f, s1 = 0.f;
+            if (pl < n) {
+              const float* q0 = Qt + (2 * hp) * lat + jh * half;
+              const float* q1 = q0 + lat;
+              const float* cr = Cs + pl * latp + jh * half;
+              for (int j = 0; j < half; j += 4) {
+                const f32x4 c = *reinterpret_cast<const f32x4*>(cr + j);
+                s0 += dot4(*reinterpret_cast<const f32x4*>(q0 + j), c);
+                s1 += dot4(*reinterpret_cast<const f32x4*>(q1 + j), c);
+              }
+            }
+            s0 += __shfl_xor(s0, 32, 64);
+            s1 += __shfl_xor(s1, 32, 64);
+            if (jh == 0) {
+              S[(2 * hp) * kSub + pl] = pl < n ? s0 * scale : -INFINITY;
+              S[(2 * hp + 1) * kSub + pl] = pl < n ? s1 * scale : -INFINITY;
+            }
+          }
+          __syncthreads();
+          // running max and sum: half a wave per head
+          for (int hp = wave; hp < (nh >> 1); hp += kWaves) {
+            const int h = 2 * hp + (lane >> 5), pl = lane & 31;
+            const float sv = S[h * kSub + pl];
+            const float cm = wave_max(sv, 32);
+            const float mo = st[h * 4], lo = st[h * 4 + 1];
+            const float mn = fmaxf(mo, cm);
+            const float sc = mn == -INFINITY ? 1.f : __expf(mo - mn);
+            const float w = sv == -INFINITY ? 0.f : __expf(sv - mn);
+            const float ls = wave_sum(w, 32);
+            S[h * kSub + pl] = w;
+            if (pl == 0) {
+              st[h * 4] = mn;
+              st[h * 4 + 1] = lo * sc + ls;
+              st[h * 4 + 2] = sc;
+            }
+          }
+          __syncthreads();
+          // values: thread tile of 4 heads x 4 latent columns
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int tt = tid + k * kThreads;
+            if (tt < ntile) {
+              const int hg = tt / kq, jt = tt - hg * kq;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) u[k][i] *= st[(4 * hg + i) * 4 + 2];
+              for (int pl = 0; pl < n; ++pl) {
+                const f32x4 c = *reinterpret_cast<const f32x4*>(Cs + pl * latp + 4 * jt);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[k][i] += S[(4 * hg + i) * kSub + pl] * c;
+              }
+            }
+          }
         }
       }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int tt = tid + k * kThreads;
+        if (tt < ntile) {
+          const int hg = tt / kq, jt = tt - hg * kq;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ws.st4(p.part + ((size_t)(m * nh + 4 * hg + i) * nsplit + s) * stride + kPartPad + 4 * jt, u[k][i]);
+        }
+      }
+      if (tid < nh)
+        ws.st4(p.part + ((size_t)(m * nh + tid) * nsplit + s) * stride, f32x4{st[tid * 4], st[tid * 4 + 1], 0.f, 0.f});
     }
   }
 }
 
 // gated delta rule: task (b, h, cb) owns columns [8cb, 8cb+8) of S_bh, one wave per task
-__device__ __forceinline__ void kda_phase(const Params& p, const LayerDev& ly) {
+__device__ __forceinline__ void kda_phase(const Params& p, const LayerDev& ly, const Ws& ws) {
   const int nh = p.nh, dk = p.dk, dv = p.dv, T = p.T;
   const int ncb = dv / 8;
   const int ntask = p.B * nh * ncb;
@@ -1044,8 +1354,9 @@ __device__ __forceinline__ void kda_phase(const Params& p, const LayerDev& ly) {
     float* Sbh = St + ((size_t)b * nh + h) * dk * dv;
     float S[2][8];
     float al[2];
-    for (int r = 0; r < rpl; ++r) {
-      const int i = lane + r * 64;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = lane + (r < rpl ? r : 0) * 64;
       const f32x4 a = *(const GLOBAL f32x4*)(Sbh + (size_t)i * dv + cb * 8);
       const f32x4 c = *(const GLOBAL f32x4*)(Sbh + (size_t)i * dv + cb * 8 + 4);
       S[r][0] = a.x; S[r][1] = a.y; S[r][2] = a.z; S[r][3] = a.w;
@@ -1059,43 +1370,60 @@ __device__ __forceinline__ void kda_phase(const Params& p, const LayerDev& ly) {
       const float* qv = p.a1 + (size_t)m * nh * dk + h * dk;
       const float* vv = p.a3 + (size_t)m * nh * dv + h * dv + cb * 8;
       float kk[2], qq[2];
-      float nrm = 0.f;
-      for (int r = 0; r < rpl; ++r) {
-        kk[r] = ldc(kv + lane + r * 64);
-        qq[r] = ldc(qv + lane + r * 64);
-        nrm += kk[r] * kk[r];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = lane + (r < rpl ? r : 0) * 64;
+        kk[r] = ws.ld1(kv + i);
+        qq[r] = ws.ld1(qv + i);
       }
+      const f32x4 va = ws.ld4(vv), vb = ws.ld4(vv + 4);
+      const float vj[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+      float nrm = 0.f;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) nrm += r < rpl ? kk[r] * kk[r] : 0.f;
       nrm = wave_sum(nrm, 64);
       const float inv = 1.0f / sqrtf(nrm);
-      for (int r = 0; r < rpl; ++r) kk[r] *= inv;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) kk[r] *= inv;
       float kS[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float a = 0.f;
-        for (int r = 0; r < rpl; ++r) {
-          S[r][j] *= al[r];
-          a += kk[r] * S[r][j];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          if (r < rpl) {
+            S[r][j] *= al[r];
+            a += kk[r] * S[r][j];
+          }
         }
         kS[j] = wave_sum(a, 64);
       }
       float o[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float vj = ldc(vv + j);
         float a = 0.f;
-        for (int r = 0; r < rpl; ++r) {
-          S[r][j] = S[r][j] - beta * kk[r] * kS[j] + beta * kk[r] * vj;
-          a += S[r][j] * qq[r];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          if (r < rpl) {
+            S[r][j] = S[r][j] - beta * kk[r] * kS[j] + beta * kk[r] * vj[j];
+            a += S[r][j] * qq[r];
+          }
         }
         o[j] = wave_sum(a, 64);
       }
-      if (lane == 0)
-        for (int j = 0; j < 8; ++j) stc(p.att + (size_t)m * nh * dv + h * dv + cb * 8 + j, o[j]);
+      if (lane == 0) {
+        float* od = p.att + (size_t)m * nh * dv + h * dv + cb * 8;
+        ws.st4(od, f32x4{o[0], o[1], o[2], o[3]});
+        ws.st4(od + 4, f32x4{o[4], o[5], o[6], o[7]});
+      }
     }
-    for (int r = 0; r < rpl; ++r) {
-      const int i = lane + r * 64;
-      *(GLOBAL f32x4*)(Sbh + (size_t)i * dv + cb * 8) = f32x4{S[r][0], S[r][1], S[r][2], S[r][3]};
-      *(GLOBAL f32x4*)(Sbh + (size_t)i * dv + cb * 8 + 4) = f32x4{S[r][4], S[r][5], S[r][6], S[r][7]};
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (r < rpl) {
+        const int i = lane + r * 64;
+        *(GLOBAL f32x4*)(Sbh + (size_t)i * dv + cb * 8) = f32x4{S[r][0], S[r][1], S[r][2], S[r][3]};
+        *(GLOBAL f32x4*)(Sbh + (size_t)i * dv + cb * 8 + 4) = f32x4{S[r][4], S[r][5], S[r][6], S[r][7]};
+      }
     }
   }
 }
@@ -1113,15 +1441,15 @@ struct Smem {
   float buf[kLdsFloats];
   float inv[MK_MAX_M];
   float red[kWaves * MK_MAX_M];
-  float misc[256];
   float rope[MK_MAX_NEW_TOKENS * kMaxRopePairs * 2];
   float rw[kMaxQueue];
   int rsel[kMaxQueue];
+  int cnt[kMaxExperts];
   Route route;
   int abort;
 };
 
-enum PhaseType : int { PT_GEMV = 0, PT_ATTN_GQA, PT_ATTN_MLA, PT_MERGE, PT_KDA, PT_EXPERT, PT_DOWN };
+enum PhaseType : int { PT_GEMV = 0, PT_ATTN_GQA, PT_ATTN_MLA, PT_MERGE, PT_KDA, PT_EXPERT };
 
 __device__ __forceinline__ int attn_phases(int kind) { return kind == kGqa ? 4 : kind == kMla ? 7 : 3; }
 
@@ -1140,9 +1468,18 @@ __device__ __forceinline__ void plain_input(Gemv& g, const float* src, int ld, i
   g.K = K;
   g.Wst = K;
 }
+__device__ __forceinline__ void resid_out(Gemv& g, const Params& p, const uint16_t* w, int K) {
+  g.kind = G_RESID;
+  g.W0 = g.safe = w;
+  g.out0 = p.x;
+  g.ldo0 = p.H;
+  g.ntasks = p.H;
+  (void)K;
+}
 
-// Phase i of layer l (l == L: the final norm and LM head). Fills g for GEMV phases.
-__device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) {
+// Phase i of layer l (l == L: the final norm and LM head). Fills g for GEMV phases; the down
+// projection reads this workgroup's routing of the layer (rt).
+__device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, const Route* rt) {
   g.M = p.M;
   g.eps = p.eps;
   g.pairs = 1;
@@ -1150,7 +1487,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) 
   if (l == p.L) {
     norm_input(g, p.x, p.H, p.H, p.final_norm);
     g.kind = G_STACK;
-    g.W0 = p.lm_head;
+    g.W0 = g.safe = p.lm_head;
     g.n0 = p.V;
     g.out0 = p.logits;
     g.ldo0 = p.V;
@@ -1161,38 +1498,56 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) 
   const int kind = ly->kind;
   const int na = attn_phases(kind);
   if (i >= na) {
-    norm_input(g, p.x, p.H, p.H, ly->moe_norm);
     if (i == na) {
+      norm_input(g, p.x, p.H, p.H, ly->moe_norm);
       g.kind = G_RS;
       g.E = p.E;
       g.SF = p.SF;
-      g.W0 = ly->router;
+      g.W0 = g.safe = ly->router;
       g.Wg = ly->sh_gate;
       g.Wu = ly->sh_up;
       g.rlog = p.rlog;
       g.sact = p.sact;
       g.ntasks = p.E + p.SF;
-      g.pairs = 2;
+      g.pairs = p.SF > 0 ? 2 : 1;
       return PT_GEMV;
     }
     if (i == na + 1) {
+      norm_input(g, p.x, p.H, p.H, ly->moe_norm);
       g.kind = G_EXP;
       g.F = p.F;
-      g.Wg = ly->exp_gate;
+      g.Wg = g.safe = ly->exp_gate;
       g.Wu = ly->exp_up;
       g.eact = p.eact;
       g.pairs = 2;
       g.ntasks = 0;  // known after routing
       return PT_EXPERT;
     }
-    return PT_DOWN;
+    // routed down projections (pool rows [E][H][F]) and the shared down projection
+    g.kind = G_DOWN;
+    g.stage = S_DOWN;
+    g.src = p.eact;
+    g.src2 = p.sact;
+    g.rt = rt;
+    g.np = rt->ustart[rt->nu];
+    g.F = p.F;
+    g.SF = p.SF;
+    g.H = p.H;
+    g.K = g.Wst = p.F > p.SF ? p.F : p.SF;
+    g.Wg = g.safe = ly->exp_down;
+    g.Wu = ly->sh_down;
+    g.out0 = p.x;
+    g.ldo0 = p.H;
+    g.ntasks = p.H;
+    g.pairs = rt->nu + (p.SF > 0 ? 1 : 0);
+    return PT_GEMV;
   }
   if (kind == kGqa) {
     const int dq = p.nh * p.hd, dkv = p.nkv * p.hd;
     if (i == 0) {
       norm_input(g, p.x, p.H, p.H, ly->attn_norm);
       g.kind = G_STACK;
-      g.W0 = ly->wq; g.W1 = ly->wk; g.W2 = ly->wv;
+      g.W0 = g.safe = ly->wq; g.W1 = ly->wk; g.W2 = ly->wv;
       g.n0 = dq; g.n1 = dkv;
       g.out0 = p.a1; g.out1 = p.a2; g.out2 = p.a3;
       g.ldo0 = dq; g.ldo1 = dkv; g.ldo2 = dkv;
@@ -1202,11 +1557,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) 
     if (i == 1) return PT_ATTN_GQA;
     if (i == 2) return PT_MERGE;
     plain_input(g, p.att, dq, dq);
-    g.kind = G_RESID;
-    g.W0 = ly->wo;
-    g.out0 = p.x;
-    g.ldo0 = p.H;
-    g.ntasks = p.H;
+    resid_out(g, p, ly->wo, dq);
     return PT_GEMV;
   }
   if (kind == kMla) {
@@ -1215,7 +1566,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) 
       case 0:
         norm_input(g, p.x, p.H, p.H, ly->attn_norm);
         g.kind = G_STACK;
-        g.W0 = ly->w_dq; g.W1 = ly->w_dkv;
+        g.W0 = g.safe = ly->w_dq; g.W1 = ly->w_dkv;
         g.n0 = p.ql; g.n1 = lat;
         g.out0 = p.a1; g.out1 = p.a2;
         g.ldo0 = p.ql; g.ldo1 = lat;
@@ -1224,7 +1575,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) 
       case 1:
         norm_input(g, p.a1, p.ql, p.ql, ly->q_norm);
         g.kind = G_STACK;
-        g.W0 = ly->w_uq;
+        g.W0 = g.safe = ly->w_uq;
         g.n0 = p.nh * qd;
         g.out0 = p.a3;
         g.ldo0 = p.nh * qd;
@@ -1237,7 +1588,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) 
         g.K = p.nd;
         g.Wst = p.nh * p.nd;
         g.kind = G_OFF;
-        g.W0 = ly->w_ukT;
+        g.W0 = g.safe = ly->w_ukT;
         g.rph = p.kvl;
         g.seg = p.nd;
         g.out0 = p.a4;
@@ -1252,7 +1603,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) 
         plain_input(g, p.att, p.nh * p.kvl, p.kvl);
         g.Wst = p.nh * p.kvl;
         g.kind = G_OFF;
-        g.W0 = ly->w_uv;
+        g.W0 = g.safe = ly->w_uv;
         g.rph = p.vd;
         g.seg = p.kvl;
         g.out0 = p.o2;
@@ -1261,11 +1612,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) 
         return PT_GEMV;
       default:
         plain_input(g, p.o2, p.nh * p.vd, p.nh * p.vd);
-        g.kind = G_RESID;
-        g.W0 = ly->wo;
-        g.out0 = p.x;
-        g.ldo0 = p.H;
-        g.ntasks = p.H;
+        resid_out(g, p, ly->wo, p.nh * p.vd);
         return PT_GEMV;
     }
   }
@@ -1274,7 +1621,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) 
   if (i == 0) {
     norm_input(g, p.x, p.H, p.H, ly->attn_norm);
     g.kind = G_STACK;
-    g.W0 = ly->kwq; g.W1 = ly->kwk; g.W2 = ly->kwv;
+    g.W0 = g.safe = ly->kwq; g.W1 = ly->kwk; g.W2 = ly->kwv;
     g.n0 = dq; g.n1 = dq;
     g.out0 = p.a1; g.out1 = p.a2; g.out2 = p.a3;
     g.ldo0 = dq; g.ldo1 = dq; g.ldo2 = dvv;
@@ -1283,31 +1630,20 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g) 
   }
   if (i == 1) return PT_KDA;
   plain_input(g, p.att, dvv, dvv);
-  g.kind = G_RESID;
-  g.W0 = ly->wo;
-  g.out0 = p.x;
-  g.ldo0 = p.H;
-  g.ntasks = p.H;
+  resid_out(g, p, ly->wo, dvv);
   return PT_GEMV;
 }
 
-// Uniform values read from LDS land in vector registers; move the descriptor into scalar ones.
-__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ float rflf(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
-template <class T>
-__device__ __forceinline__ T* rflp(T* ptr) {
-  const uint64_t u = reinterpret_cast<uint64_t>(ptr);
-  const uint32_t lo = (uint32_t)rfl((int)(uint32_t)u), hi = (uint32_t)rfl((int)(uint32_t)(u >> 32));
-  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
-}
 __device__ __forceinline__ void scalarize(Gemv& g) {
   g.kind = rfl(g.kind); g.stage = rfl(g.stage); g.ntasks = rfl(g.ntasks); g.K = rfl(g.K); g.Wst = rfl(g.Wst);
   g.pairs = rfl(g.pairs); g.M = rfl(g.M); g.src = rflp(g.src); g.ld = rfl(g.ld); g.gain = rflp(g.gain);
   g.nh = rfl(g.nh); g.nd = rfl(g.nd); g.qd = rfl(g.qd); g.eps = rflf(g.eps);
-  g.W0 = rflp(g.W0); g.W1 = rflp(g.W1); g.W2 = rflp(g.W2); g.n0 = rfl(g.n0); g.n1 = rfl(g.n1);
+  g.src2 = rflp(g.src2); g.np = rfl(g.np);
+  g.W0 = rflp(g.W0); g.W1 = rflp(g.W1); g.W2 = rflp(g.W2); g.Wg = rflp(g.Wg); g.Wu = rflp(g.Wu);
+  g.safe = rflp(g.safe); g.n0 = rfl(g.n0); g.n1 = rfl(g.n1);
   g.out0 = rflp(g.out0); g.out1 = rflp(g.out1); g.out2 = rflp(g.out2);
   g.ldo0 = rfl(g.ldo0); g.ldo1 = rfl(g.ldo1); g.ldo2 = rfl(g.ldo2); g.rph = rfl(g.rph); g.seg = rfl(g.seg);
-  g.E = rfl(g.E); g.SF = rfl(g.SF); g.F = rfl(g.F); g.Wg = rflp(g.Wg); g.Wu = rflp(g.Wu);
+  g.E = rfl(g.E); g.SF = rfl(g.SF); g.F = rfl(g.F); g.H = rfl(g.H);
   g.rlog = rflp(g.rlog); g.sact = rflp(g.sact); g.eact = rflp(g.eact);
 }
 
@@ -1324,10 +1660,12 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(&pk);
     uint32_t* dst = reinterpret_cast<uint32_t*>(&sp);
-    for (int i = threadIdx.x; i < (int)(sizeof(Params) / 4); i += kThreads) dst[i] = src[i];
+    for (int i = tid_x(); i < (int)(sizeof(Params) / 4); i += kThreads) dst[i] = src[i];
     __syncthreads();
   }
   const Params& p = sp;
+  const char* wsb = rflp(p.wsb);
+  const Ws ws{make_rsrc(wsb, (uint32_t)rfl((int)p.ws_bytes)), wsb};
   uint32_t gen = 0;
   const int M = p.M, H = p.H;
   const int rpairs = ((p.kvl > 0) ? p.rd : p.hd) / 2;
@@ -1335,7 +1673,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   // ---- embedding rows and the RoPE table of this step's positions ----
   {
     const int n = M * H;
-    for (int e = blockIdx.x * kThreads + threadIdx.x; e < n; e += gridDim.x * kThreads) {
+    for (int e = blockIdx.x * kThreads + tid_x(); e < n; e += gridDim.x * kThreads) {
       const int m = e / H, i = e - m * H;
       int tok = gp(p.tokens)[m];
       if (tok < 0 || tok >= p.V) {
@@ -1348,7 +1686,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       stc(p.x + e, bf2f(gp(p.embed)[(size_t)tok * H + i]));
     }
     // every workgroup computes the table itself (no cross-workgroup dependency)
-    for (int e = threadIdx.x; e < p.T * rpairs; e += kThreads) {
+    for (int e = tid_x(); e < p.T * rpairs; e += kThreads) {
       const int t = e / rpairs, j = e - t * rpairs;
       const double inv_freq = pow((double)p.rope_theta, -2.0 * j / (2 * rpairs));
       const double a = (double)(p.kv_len + t) * inv_freq;
@@ -1358,41 +1696,44 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
     wait_vm();
   }
 
+  bool resident = false;  // the LDS input buffer holds this layer's normalised MoE input
   for (int l = 0; l <= p.L; ++l) {
     const int nph = (l == p.L) ? 1 : attn_phases(gp(p.layers + l)->kind) + 3;
     for (int i = 0; i < nph; ++i) {
       Gemv g{};
       RowBuf b0, b1;  // per phase: dead outside GEMV phases
-      const int type = rfl(describe(p, l, i, g));
+      const int type = rfl(describe(p, l, i, g, &sm.route));
       scalarize(g);
-      const int npre = (type == PT_GEMV) ? gemv_preload(g, b0, b1) : 0;
+      const int npre = (type == PT_GEMV) ? gemv_preload<MM>(g, sm.buf, b0, b1) : 0;
       MK_SYNC();
       // sub-phase stamps of this phase go to the record of the barrier that preceded it
       uint64_t* trec = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * 4 : nullptr;
       switch (type) {
         case PT_GEMV:
-          gemv_phase<MM>(g, sm.buf, sm.inv, sm.red, b0, b1, npre, trec);
+          resident = gemv_phase<MM>(g, ws, sm.buf, sm.inv, sm.red, b0, b1, npre, false, trec) && g.kind == G_RS;
           break;
         case PT_ATTN_GQA:
-          gqa_attn_phase(p, p.layers[l], sm.buf, sm.rope);
+          gqa_attn_phase(p, p.layers[l], ws, sm.buf, sm.rope);
+          resident = false;
           break;
         case PT_ATTN_MLA:
-          mla_attn_phase(p, p.layers[l], sm.buf, sm.misc, sm.rope);
+          mla_attn_phase(p, p.layers[l], ws, sm.buf, sm.rope);
+          resident = false;
           break;
         case PT_MERGE:
-          merge_phase(p, p.nh, p.kvl > 0 ? p.kvl : p.hd, p.att, sm.buf);
+          merge_phase(p, ws, p.nh, p.kvl > 0 ? p.kvl : p.hd, p.att, sm.buf);
+          resident = false;
           break;
         case PT_KDA:
-          kda_phase(p, p.layers[l]);
+          kda_phase(p, p.layers[l], ws);
+          resident = false;
           break;
-        case PT_EXPERT:
-          compute_route(p, l, &sm.route, sm.rsel, sm.rw, sm.buf);
+        default:  // PT_EXPERT
+          compute_route(p, ws, l, &sm.route, sm.rsel, sm.rw, sm.cnt);
           g.rt = &sm.route;
           g.ntasks = rfl(sm.route.nu * p.F);
-          gemv_phase<MM>(g, sm.buf, sm.inv, sm.red, b0, b1, 0, trec);
-          break;
-        default:
-          moe_down_phase(p, p.layers[l], &sm.route, sm.buf);
+          gemv_phase<MM>(g, ws, sm.buf, sm.inv, sm.red, b0, b1, 0, resident, trec);
+          resident = false;
           break;
       }
       wait_vm();
@@ -1400,7 +1741,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   }
   if (p.trace) {
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid_x() == 0) {
       uint64_t* tr = p.trace + ((size_t)gen * gridDim.x + blockIdx.x) * 4;
       gp(tr)[0] = gp(tr)[1] = gp(tr)[2] = gp(tr)[3] = wall_clock64();
     }
@@ -1410,7 +1751,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
 // W_uk [h][nope][kv_lora] -> W_ukT [h][kv_lora][nope]
 __global__ void transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd, int kvl) {
   const size_t n = (size_t)nh * nd * kvl;
-  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + tid_x(); e < n; e += (size_t)gridDim.x * blockDim.x) {
     const size_t h = e / ((size_t)nd * kvl), r = e - h * nd * kvl, i = r / kvl, j = r - i * kvl;
     gp(dst)[(h * kvl + j) * nd + i] = gp(src)[e];
   }
@@ -1420,7 +1761,7 @@ __global__ void transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd,
 
 namespace mk {
 
-size_t kernel_lds_bytes() { return sizeof(Smem); }
+size_t kernel_lds_bytes() { return sizeof(Smem) + sizeof(Params); }
 int max_grid() { return kMaxGrid; }
 
 hipError_t launch_decode(const Params& p, int nblocks, hipStream_t stream) {
