@@ -153,46 +153,74 @@ def phase_names(cfg) -> list[str]:
 
 
 def trace_summary(cfg, tr: np.ndarray, tick_ns: float = 10.0) -> dict:
-    """tr [n_barriers + 1][blocks][arrive, depart]. The phase before barrier j runs from the last
-    departure of barrier j-1 to the last arrival at barrier j; the barrier itself from the last
-    arrival to the last departure."""
+    """tr [n_barriers + 1][blocks][stamps] (stamp meanings in include/mk.h). The phase before barrier
+    j runs from the last departure of barrier j-1 to the last arrival at barrier j; the barrier
+    itself from the last arrival to the last departure. Segments inside a phase are medians over
+    workgroups of the differences between its stamps (a stamp of 0 means the phase has no such
+    mark)."""
     names = phase_names(cfg)
-    arr = tr[:, :, 0].astype(np.int64)
-    dep = tr[:, :, 1].astype(np.int64)
-    stg = tr[:, :, 2].astype(np.int64)
-    cmp_ = tr[:, :, 3].astype(np.int64)
+    t = tr.astype(np.int64)
+    arr, dep = t[:, :, 0], t[:, :, 1]
     t0 = arr[0].min()
     out = {}
     prev_dep = t0
+    us = tick_ns / 1e3
+
+    def seg(j, a, b):  # median over the workgroups that have both stamps of stamp b - stamp a in record j
+        ta = a if isinstance(a, np.ndarray) else t[j, :, a]
+        tb = b if isinstance(b, np.ndarray) else t[j, :, b]
+        ok = (ta > 0) & (tb > 0)
+        if not ok.any():
+            return 0.0
+        return float(np.median((tb - ta)[ok])) * us
+
     for j, name in enumerate(names):
         a_max = arr[j].max()
         d_max = dep[j].max()
-        work = (a_max - prev_dep) * tick_ns / 1e3
-        sync = (d_max - a_max) * tick_ns / 1e3
-        s = out.setdefault(name, {"count": 0, "work_us": 0.0, "sync_us": 0.0, "stage_us": 0.0, "dot_us": 0.0,
-                                  "tail_us": 0.0})
+        s = out.setdefault(name, {"count": 0, "work_us": 0.0, "sync_us": 0.0, "enter_us": 0.0, "route_us": 0.0, "issue_us": 0.0,
+                                  "stage_us": 0.0, "dot_us": 0.0, "epi_us": 0.0, "tail_us": 0.0, "drain_us": 0.0,
+                                  "next_us": 0.0, "desc_us": 0.0, "plan_us": 0.0})
         s["count"] += 1
-        s["work_us"] += work
-        s["sync_us"] += sync
-        # GEMV sub-phases of this phase (stamped in the record of the barrier before it)
-        if j >= 1 and j < len(names) - 1 and (stg[j - 1] > 0).all():
-            s["stage_us"] += float(np.median(stg[j - 1] - dep[j - 1])) * tick_ns / 1e3
-            s["dot_us"] += float(np.median(cmp_[j - 1] - stg[j - 1])) * tick_ns / 1e3
-            s["tail_us"] += float(np.median(arr[j] - cmp_[j - 1])) * tick_ns / 1e3
+        s["work_us"] += (a_max - prev_dep) * us
+        s["sync_us"] += (d_max - a_max) * us
+        if 1 <= j < len(names) - 1:
+            r = j - 1  # record of the barrier before this phase
+            nxt = arr[j]
+            s["enter_us"] += seg(r, 1, 7)
+            if (t[r, :, 6] > 0).any():
+                s["route_us"] += seg(r, 1, 6)
+                s["issue_us"] += seg(r, 6, 4)
+            elif not name.endswith("attention"):
+                s["issue_us"] += seg(r, 1, 4)
+            s["drain_us"] += seg(r, 5 if (t[r, :, 5] > 0).any() else 3, 8)  # stores of this phase
+            s["next_us"] += seg(r, 0, 9)    # preparation while waiting (from arrival)
+            s["desc_us"] += seg(r, 0, 10)
+            s["plan_us"] += seg(r, 10, 11)
+            if name.endswith("attention"):  # staged, scores, softmax (4, 5), values accumulated (3)
+                s["stage_us"] += seg(r, 1, 2)
+                s["dot_us"] += seg(r, 2, 3)
+                s["issue_us"] += seg(r, 2, 4)  # scores
+                s["epi_us"] += seg(r, 4, 5)    # softmax
+                s["tail_us"] += seg(r, t[r, :, 3], nxt)
+            elif (t[r, :, 4] > 0).any():
+                s["stage_us"] += seg(r, 4, 2)
+                s["dot_us"] += seg(r, 2, 3)
+                s["epi_us"] += seg(r, 3, 5)
+                s["tail_us"] += seg(r, t[r, :, 5], nxt)
         prev_dep = d_max
-    total = (dep[-1].max() - t0) * tick_ns / 1e3
+    total = (dep[-1].max() - t0) * us
     return {"total_us": total, "phases": out}
 
 
 def print_trace(summary: dict) -> None:
     print(f"# traced step: {summary['total_us']:.1f} us", file=sys.stderr)
-    print(f"# {'phase':28s} {'n':>4s} {'work us':>10s} {'sync us':>10s} {'work/n':>8s} {'sync/n':>8s} "
-          f"{'stage/n':>8s} {'dot/n':>8s} {'tail/n':>8s}", file=sys.stderr)
+    cols = ["enter", "route", "issue", "stage", "dot", "epi", "tail", "drain", "next", "desc", "plan"]
+    print(f"# {'phase':24s} {'n':>4s} {'work/n':>8s} {'sync/n':>8s} " + " ".join(f"{c:>7s}" for c in cols),
+          file=sys.stderr)
     for name, s in sorted(summary["phases"].items(), key=lambda kv: -(kv[1]["work_us"] + kv[1]["sync_us"])):
         n = s["count"]
-        print(f"# {name:28s} {n:4d} {s['work_us']:10.1f} {s['sync_us']:10.1f} {s['work_us'] / n:8.2f} "
-              f"{s['sync_us'] / n:8.2f} {s['stage_us'] / n:8.2f} {s['dot_us'] / n:8.2f} {s['tail_us'] / n:8.2f}",
-              file=sys.stderr)
+        print(f"# {name:24s} {n:4d} {s['work_us'] / n:8.2f} {s['sync_us'] / n:8.2f} " +
+              " ".join(f"{s[c + '_us'] / n:7.2f}" for c in cols), file=sys.stderr)
 
 
 # ------------------------------------------------------------------------------------------

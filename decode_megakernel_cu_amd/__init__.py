@@ -22,6 +22,8 @@ KINDS = ["embed", "final_norm", "lm_head", "attn_norm", "wq", "wk", "wv", "wo", 
          "router", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"]
 KIND_ID = {k: i for i, k in enumerate(KINDS)}
 
+TRACE_STAMPS = 16  # MK_TRACE_STAMPS
+
 EXPORTS = ["mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_poll", "mk_set_trace",
            "mk_read_trace", "mk_last_error", "mk_destroy"]
 
@@ -133,11 +135,12 @@ def mk_set_trace(ctx, enable: bool) -> None:
 
 
 def mk_read_trace(ctx):
-    """Trace of the last step as a numpy array [n_barriers + 1][n_blocks][4] of wall-clock ticks."""
+    """Trace of the last step as a numpy array [n_barriers + 1][n_blocks][TRACE_STAMPS] of wall-clock
+    ticks (stamp meanings in include/mk.h)."""
     import numpy as np
 
     nb, nk = ctypes.c_int(), ctypes.c_int()
     _check(lib.mk_read_trace(ctx, None, 0, ctypes.byref(nb), ctypes.byref(nk)))
-    out = np.zeros((nb.value + 1, nk.value, 4), dtype=np.uint64)
+    out = np.zeros((nb.value + 1, nk.value, TRACE_STAMPS), dtype=np.uint64)
     _check(lib.mk_read_trace(ctx, out.ctypes.data, out.size, ctypes.byref(nb), ctypes.byref(nk)))
     return out

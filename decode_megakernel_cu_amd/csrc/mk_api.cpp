@@ -96,8 +96,8 @@ int check_config(const mk_config* c) {
       return fail(MK_E_UNSUPPORTED, "MLA dims must be multiples of 8 (rope_dim even, <= %d)", 2 * kMaxRopePairs);
     const int lat = c->kv_lora + c->rope_dim, nh = c->n_heads;
     if (c->rope_dim % 8 || nh % 4) return fail(MK_E_UNSUPPORTED, "MLA needs rope_dim % 8 == 0 and n_heads % 4 == 0");
-    if (kSub * (lat + 4) + nh * lat + c->max_new_tokens * lat + nh * kSub + nh * 4 + 8 + c->kv_lora > kLdsFloats ||
-        nh * lat / 4 > 5 * kThreadsHost || kSub * lat / 8 > 5 * kThreadsHost || (nh / 4) * (c->kv_lora / 4) > 2 * kThreadsHost)
+    if (kSub * (lat + 8) / 2 + nh * lat + c->max_new_tokens * lat + nh * kSub + nh * 4 + 8 + c->kv_lora / 2 > kLdsFloats ||
+        (nh / 4) * (c->kv_lora / 4) > kThreadsHost)
       return fail(MK_E_UNSUPPORTED, "MLA heads / latent too wide for the attention tile");
     if (c->attn_kind == MK_ATTN_HYBRID) {
       if (c->hybrid_period < 1) return fail(MK_E_INVAL, "hybrid_period must be positive");
@@ -254,7 +254,7 @@ Layout make_layout(const mk_config& c) {
   w.flags = take(kMaxBlocks * 4);
   w.status = take(64 * 4);
   w.trace_slots = (uint64_t)(2 + 10 * c.n_layers) * kMaxBlocks;
-  w.trace = take(w.trace_slots * 32);
+  w.trace = take(w.trace_slots * kTraceStamps * 8);
   w.rope = take((uint64_t)MK_MAX_NEW_TOKENS * kMaxRopePairs * 2 * 4);
   w.x = take(M * H * 4);
   w.a1 = take(M * w1 * 4);
@@ -506,7 +506,7 @@ int mk_read_trace(mk_ctx* c, uint64_t* out, uint64_t capacity, int* n_barriers, 
   if (!c || !n_barriers || !n_blocks) return fail(MK_E_INVAL, "NULL argument");
   if (c->device == MK_DEVICE_NONE) return fail(MK_E_STATE, "host-only context has no trace");
   if (!c->trace || c->last_barriers == 0) return fail(MK_E_STATE, "no traced step since tracing was enabled");
-  const uint64_t n = (uint64_t)(c->last_barriers + 1) * c->nblocks * 4;
+  const uint64_t n = (uint64_t)(c->last_barriers + 1) * c->nblocks * kTraceStamps;
   *n_barriers = c->last_barriers;
   *n_blocks = c->nblocks;
   if (!out) return MK_OK;

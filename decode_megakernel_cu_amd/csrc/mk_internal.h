@@ -15,13 +15,14 @@ constexpr int kChunk = 16;               // minimum cache positions per split-KV
 constexpr int kSub = 32;                 // cache positions an MLA task stages at once
 constexpr int kPartPad = 4;              // a partial is [max, sum, pad, pad, values...]: values 16-byte aligned
 constexpr int kMaxExperts = 256;
+constexpr int kTraceStamps = MK_TRACE_STAMPS;
 constexpr int kMaxRopePairs = 64;
 constexpr int kMaxQueue = MK_MAX_M * 8;  // token-expert pairs per step (top_k <= 8)
 
 enum LayerKind : int32_t { kGqa = 0, kMla = 1, kKda = 2 };
 
 // Device-side pointers of one layer, stored in a table at the start of the arena.
-struct LayerDev {
+struct alignas(16) LayerDev {
   int32_t kind, ord, slot, pad;
   const uint16_t *attn_norm, *moe_norm, *router, *sh_gate, *sh_up, *sh_down, *wo;
   const uint16_t *wq, *wk, *wv;                                     // GQA
@@ -29,7 +30,9 @@ struct LayerDev {
   const uint16_t *kwq, *kwk, *kwv;                                  // KDA
   const float *alpha, *beta;
   const uint16_t *exp_gate, *exp_up, *exp_down;                     // pool slot base, [E][F][H] / [E][H][F]
+  const void* pad2;                                                 // size a multiple of 16 (copied in 16-byte units)
 };
+static_assert(sizeof(LayerDev) % 16 == 0, "layer table rows are copied in 16-byte units");
 
 // Workspace carve-up (byte offsets from the workspace base).
 struct WsLayout {
@@ -62,7 +65,7 @@ struct Params {
   const char* wsb;    // workspace base: activations are addressed by byte offsets from here
   uint32_t ws_bytes;  // workspace size (< 2^31)
   uint64_t watchdog_ticks;  // wall-clock ticks a barrier may wait
-  uint64_t* trace;          // optional [barrier][block][arrive, depart] wall-clock stamps
+  uint64_t* trace;          // optional [barrier][block][kTraceStamps] wall-clock stamps
 };
 
 }  // namespace mk

@@ -80,8 +80,10 @@ __device__ __forceinline__ void unpack8(const uint4& w, float (&f)[8]) {
   f[4] = lo_bf(w.z); f[5] = hi_bf(w.z); f[6] = lo_bf(w.w); f[7] = hi_bf(w.w);
 }
 
+// Weights and cache rows are read once per step: non-temporal loads keep them from evicting the
+// kernel's code and the activations from L2.
 __device__ __forceinline__ uint4 ldw(const uint16_t* p) {
-  const u32x4 v = *(const GLOBAL u32x4*)p;
+  const u32x4 v = __builtin_nontemporal_load((const GLOBAL u32x4*)p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -166,6 +168,31 @@ __device__ __forceinline__ T* rflp(T* ptr) {
   return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
 
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+// Direct memory-to-LDS copies (buffer_load ... lds): no registers hold the data, so nothing forces
+// a wait on earlier loads (prefetched weights) before the copies are issued. Rows r < R of U
+// 16-byte units are read at byte offsets off(r, c) of the buffer r_ and land at
+// dst + r * DS + 4c (floats); a wave instruction moves up to 64 units of one row (lane l writes
+// the block's base + 16 l). Nothing waits here: the caller waits for vmcnt and synchronises.
+template <int AUX, class Off>
+__device__ __forceinline__ void dma_rows(Rsrc r_, float* dst, int R, int U, int DS, Off off) {
+  const int bpr = (U + 63) >> 6, nb = R * bpr, lane = lane_id();
+  for (int b = wave_id(); b < nb; b += kWaves) {
+    const int r = b / bpr, c0 = (b - r * bpr) << 6, c = c0 + lane;
+    if (c < U) __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, (LdsPtr)(dst + r * DS + 4 * c0), 16, off(r, c), 0, 0, AUX);
+  }
+}
+// the same with 4-byte units (lane l writes the block's base + 4 l)
+template <int AUX, class Off>
+__device__ __forceinline__ void dma_rows4(Rsrc r_, float* dst, int R, int U, int DS, Off off) {
+  const int bpr = (U + 63) >> 6, nb = R * bpr, lane = lane_id();
+  for (int b = wave_id(); b < nb; b += kWaves) {
+    const int r = b / bpr, c0 = (b - r * bpr) << 6, c = c0 + lane;
+    if (c < U) __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, (LdsPtr)(dst + r * DS + c0), 4, off(r, c), 0, 0, AUX);
+  }
+}
+
 // Copy n 16-byte units of coherent workspace data into LDS, all threads: unit i is read from
 // src(i) and written to dst(i). NS loads per lane are in flight before the first is consumed.
 template <int NS, class Src, class Dst>
@@ -184,21 +211,27 @@ __device__ __forceinline__ void copy_units(const Ws& ws, int n, Src src, Dst dst
 }
 
 // ----------------------------------------------------------------------------------------------
-// grid barrier
-// Every wave has completed its stores (wait_vm) before calling. The polling wave publishes the
-// workgroup's flag and polls all flags with independent loads (four per lane).
+// grid barrier, in two halves so that a workgroup prepares its next phase while it waits
+// arrive: every wave has completed its stores (wait_vm) before calling; the polling wave publishes
+//   the workgroup's flag.
+// wait: the polling wave polls all flags with independent loads (four per lane) until every
+//   workgroup has arrived, or the abort flag or the watchdog ends the step.
 // ----------------------------------------------------------------------------------------------
-__device__ __forceinline__ bool grid_sync(const Params& p, uint32_t& gen, int* s_abort) {
+__device__ __forceinline__ void barrier_arrive(const Params& p, uint32_t& gen) {
   gen += 1;
-  const uint32_t target = p.epoch + gen;
   wg_barrier();
+  if (wave_id() == kPollWave && lane_id() == 0) {
+    uint64_t* tr = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
+    if (tr) gp(tr)[0] = wall_clock64();
+    stc_u32(p.flags + blockIdx.x, p.epoch + gen);
+  }
+}
+
+__device__ __forceinline__ bool barrier_wait(const Params& p, uint32_t gen, int* s_abort) {
+  const uint32_t target = p.epoch + gen;
   if (wave_id() == kPollWave) {
     const int lane = lane_id();
-    uint64_t* tr = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * 4 : nullptr;
-    if (lane == 0) {
-      if (tr) gp(tr)[0] = wall_clock64();
-      stc_u32(p.flags + blockIdx.x, target);
-    }
+    uint64_t* tr = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
     const uint64_t t0 = wall_clock64();
     int abort = 0;
     while (true) {
@@ -350,8 +383,8 @@ struct Gemv {
     return r;
   }
 
-  // a0/a1: the task's accumulators (LDS), res: its residual inputs (LDS)
-  __device__ __forceinline__ void epilogue(int t, const float* a0, const float* a1, const float* res) const {
+  // a0/a1: the task's accumulators (LDS), res: its residual inputs (LDS, token stride rs)
+  __device__ __forceinline__ void epilogue(int t, const float* a0, const float* a1, const float* res, int rs) const {
     switch (kind) {
       case G_STACK: {
         float* o = out0;
@@ -370,7 +403,7 @@ struct Gemv {
       }
       case G_RESID:
       case G_DOWN:
-        for (int k = 0; k < M; ++k) stc(out0 + (size_t)k * ldo0 + t, res[k] + a0[k]);
+        for (int k = 0; k < M; ++k) stc(out0 + (size_t)k * ldo0 + t, res[k * rs] + a0[k]);
         break;
       case G_OFF:
         for (int k = 0; k < M; ++k) stc(out0 + (size_t)k * ldo0 + t, a0[k]);
@@ -431,63 +464,39 @@ struct Gemv {
     __syncthreads();
   }
 
-  // Stage input columns [k0, k0+ks) into dst (LDS) as rows of ks floats, all threads. S_NORM
-  // rows are scaled by their RMS over all K columns (computed on the first slab) and the gain.
-  template <int MM>
-  __device__ __forceinline__ void stage_in(const Ws& ws, float* dst, int k0, int ks, bool one_slab, float* inv,
-                                           float* red) const {
-    const int tid = tid_x(), rq = ks >> 2;
+  // Issue the staging of input columns [k0, k0+ks) into dst (LDS) as rows of ks floats, and of
+  // the slab's norm gain (bf16) into gl. Direct memory-to-LDS copies; the caller waits.
+  __device__ __forceinline__ void stage_issue(const Ws& ws, float* dst, uint16_t* gl, int k0, int ks) const {
     if (stage == S_DOWN) {  // expert activation rows, then shared activation rows
-      const int ue = max(0, min(F - k0, ks)) >> 2, us = max(0, min(SF - k0, ks)) >> 2, ne = np * ue;
-      copy_units<8>(
-          ws, ne + M * us,
-          [&](int i) {
-            if (i < ne) {
-              const int s = i / ue;
-              return src + (size_t)s * F + k0 + 4 * (i - s * ue);
-            }
-            const int j = i - ne, m = j / us;
-            return src2 + (size_t)m * SF + k0 + 4 * (j - m * us);
-          },
-          [&](int i) {
-            if (i < ne) {
-              const int s = i / ue;
-              return dst + s * ks + 4 * (i - s * ue);
-            }
-            const int j = i - ne, m = j / us;
-            return dst + (np + m) * ks + 4 * (j - m * us);
-          });
+      const int ue = max(0, min(F - k0, ks)) >> 2, us = max(0, min(SF - k0, ks)) >> 2;
+      dma_rows<kCoherent>(ws.r, dst, np, ue, ks, [&](int r, int c) { return ws.off(src + (size_t)r * F + k0 + 4 * c); });
+      dma_rows<kCoherent>(ws.r, dst + np * ks, M, us, ks,
+               [&](int r, int c) { return ws.off(src2 + (size_t)r * SF + k0 + 4 * c); });
       return;
     }
-    if (stage == S_NOPE) {  // the nope parts of the heads, concatenated, from rows [nh][qd]
-      copy_units<8>(
-          ws, M * rq,
-          [&](int i) {
-            const int m = i / rq, k = k0 + 4 * (i - m * rq), h = k / nd;
-            return src + (size_t)m * nh * qd + h * qd + (k - h * nd);
-          },
-          [&](int i) { return dst + 4 * i; });
+    if (stage == S_NOPE) {  // the nope parts of the window's heads, from rows [nh][qd]
+      const int h0 = k0 / nd, nhw = ks / nd;
+      dma_rows<kCoherent>(ws.r, dst, M * nhw, nd >> 2, nd, [&](int r, int c) {
+        const int m = r / nhw;
+        return ws.off(src + (size_t)m * nh * qd + (h0 + r - m * nhw) * qd + 4 * c);
+      });
       return;
     }
-    if (stage == S_NORM && !one_slab && k0 == 0) row_inv<MM>(ws, inv, red);
-    const int no = ks >> 3;
-    const bool greg = stage == S_NORM && no <= 4 * kThreads;
-    uint4 gv[4];  // the slab's gain, requested ahead of the input
-    if (greg) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u * kThreads < no) gv[u] = ldw(gain + k0 + 8 * min(u * kThreads + tid, no - 1));
+    dma_rows<kCoherent>(ws.r, dst, M, ks >> 2, ks, [&](int r, int c) { return ws.off(src + (size_t)r * ld + k0 + 4 * c); });
+    if (stage == S_NORM) {  // the gain of the slab, 8 bf16 per unit
+      const Rsrc gr = make_rsrc(gain + k0, (uint32_t)ks * 2);
+      dma_rows<0>(gr, reinterpret_cast<float*>(gl), 1, ks >> 3, 0, [&](int, int c) { return (uint32_t)c * 16; });
     }
-    copy_units<8>(
-        ws, M * rq,
-        [&](int i) {
-          const int m = i / rq;
-          return src + (size_t)m * ld + k0 + 4 * (i - m * rq);
-        },
-        [&](int i) { return dst + 4 * i; });
+  }
+
+  // After the staged data has landed (waited and synchronised): S_NORM rows are scaled by their RMS
+  // over all K columns (from the staged rows when there is one slab, else from row_inv) and the gain.
+  template <int MM>
+  __device__ __forceinline__ void stage_finish(float* dst, const uint16_t* gl, int ks, bool one_slab, float* inv,
+                                               float* red) const {
     if (stage != S_NORM) return;
-    __syncthreads();
-    if (one_slab) {  // sums of squares from the staged rows
+    const int tid = tid_x();
+    if (one_slab) {
       for (int m = 0; m < M; ++m) {
         float ss = 0.f;
         for (int k = 4 * tid; k < ks; k += 4 * kThreads) {
@@ -505,9 +514,9 @@ struct Gemv {
       }
       __syncthreads();
     }
-    auto scale8 = [&](int o, const uint4& gw) {
+    for (int o = tid; o < (ks >> 3); o += kThreads) {
       float gf[8];
-      unpack8(gw, gf);
+      unpack8(*reinterpret_cast<const uint4*>(gl + 8 * o), gf);
       for (int m = 0; m < M; ++m) {
         const float s = inv[m];
         f32x4* d = reinterpret_cast<f32x4*>(dst + m * ks + 8 * o);
@@ -517,15 +526,6 @@ struct Gemv {
         d[0] = a;
         d[1] = b;
       }
-    };
-    if (greg) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int o = u * kThreads + tid;
-        if (o < no) scale8(o, gv[u]);
-      }
-    } else {
-      for (int o = tid; o < no; o += kThreads) scale8(o, ldw(gain + k0 + 8 * o));
     }
   }
 };
@@ -580,21 +580,26 @@ __device__ __forceinline__ void dot_block(const RowBuf& b, const float* xin, int
   }
 }
 
-// Static distribution of a phase's tasks (identical whenever it is computed for the same phase).
-// Each lane group streams elements e = (task it, row which, block blk) in that order.
+// Static distribution of a phase's tasks, computed once per phase (before its barrier). Each lane
+// group streams elements (slab, task it, row which, block blk) in that order, the element count of
+// a slab padded to even so that the two register buffers alternate the same way in every slab.
+constexpr int kGemvWaves = kWaves;
+
 struct Plan {
-  int t0, nloc, wbase, Wst, KS, LPR, G, sub, grp, iters, nblk, nel;
+  int t0, nloc, wbase, Wst, KS, nslab, lg, LPR, G, sub, grp, iters, nblk, per, nel, nelp, ntot;
   bool one_slab;
   float* acc;  // [nloc][2][MM] task accumulators, at the end of the LDS buffer
-  float* res;  // [nloc][MM] residual inputs
+  float* res;  // [M][nloc] residual inputs
 };
+
+__device__ __forceinline__ int log2ceil(int x) { return x <= 1 ? 0 : 32 - __clz(x - 1); }
 
 template <int MM>
 __device__ __forceinline__ Plan make_plan(const Gemv& g, float* smem) {
   Plan q;
-  const int nt = g.ntasks;
-  q.t0 = (int)(((long long)nt * blockIdx.x) / gridDim.x);
-  const int t1 = (int)(((long long)nt * (blockIdx.x + 1)) / gridDim.x);
+  const unsigned nt = (unsigned)g.ntasks, gb = blockIdx.x, gn = gridDim.x;  // nt * gn < 2^32
+  q.t0 = (int)(nt * gb / gn);
+  const int t1 = (int)(nt * (gb + 1) / gn);
   q.nloc = t1 - q.t0;
   const int in_cap = (kLdsFloats - q.nloc * 3 * MM) & ~7;
   q.acc = smem + in_cap;
@@ -609,57 +614,76 @@ __device__ __forceinline__ Plan make_plan(const Gemv& g, float* smem) {
   q.KS = q.Wst;
   if (!offs) {
     const int rows = g.stage == S_DOWN ? g.np + g.M : g.M;
-    int cap = (in_cap / rows) & ~7;
+    // staged rows, then (S_NORM) the slab's gain in bf16: rows * KS + KS / 2 floats
+    int cap = ((2 * in_cap) / (2 * rows + (g.stage == S_NORM ? 1 : 0))) & ~7;
     if (cap < 8) cap = 8;
     if (q.KS > cap) q.KS = cap;
   }
+  q.nslab = q.KS > 0 ? (q.Wst + q.KS - 1) / q.KS : 0;
   const int nch = (offs ? g.seg : q.KS) >> 3;
-  // lanes per row: enough that kNC chunks per lane cover the row, few enough that every wave has
-  // a task when the workgroup has few
-  const int lo = min(64, pow2ceil(cdiv(nch, kNC))), hi = min(64, pow2ceil(nch));
-  const int per_wave = max(1, cdiv(q.nloc, kWaves));
-  int bal = 64;
-  while (bal > 1 && bal * per_wave > 64) bal >>= 1;
-  q.LPR = min(max(bal, lo), max(hi, lo));
-  q.G = 64 / q.LPR;
-  q.sub = lane_id() % q.LPR;
-  q.grp = lane_id() / q.LPR;
-  q.iters = cdiv(q.nloc, kWaves * q.G);
-  q.nblk = cdiv(nch, kNC * q.LPR);
-  q.nel = q.iters * g.pairs * q.nblk;
+  // lanes per row (a power of two): enough that kNC chunks per lane cover the row, few enough that
+  // every wave has a task when the workgroup has few
+  const int lo = min(6, log2ceil(cdiv(nch, kNC))), hi = max(lo, min(6, log2ceil(nch)));
+  const int bal = max(0, 6 - log2ceil(max(1, cdiv(q.nloc, kGemvWaves))));
+  q.lg = min(max(bal, lo), hi);
+  q.LPR = 1 << q.lg;
+  q.G = 64 >> q.lg;
+  const int lane = lane_id();
+  q.sub = lane & (q.LPR - 1);
+  q.grp = lane >> q.lg;
+  q.iters = cdiv(q.nloc, kGemvWaves * q.G);
+  q.nblk = (nch + (kNC << q.lg) - 1) >> (3 + q.lg);
+  q.per = g.pairs * q.nblk;
+  q.nel = q.iters * q.per;
+  q.nelp = q.nel + (q.nel & 1);
+  q.ntot = q.nslab * q.nelp;
   q.one_slab = q.KS >= q.Wst;
   return q;
 }
 
-// Issue the loads of stream element e into b (a wave-uniform decision: elements past the end of
-// the stream are skipped as a whole; lanes without a row read a valid dummy address).
-__device__ __forceinline__ void load_element(const Gemv& g, const Plan& q, int e, int k0, int ks, RowBuf& b) {
-  if (e >= q.nel) return;
-  const int per = g.pairs * q.nblk;
-  const int it = e / per, rem = e - it * per, which = rem / q.nblk, blk = rem - which * q.nblk;
-  const int i = (it * kWaves + wave_id()) * q.G + q.grp;
+// Position in a lane group's element stream (wave-uniform): slab, element of the slab, and the
+// element's task iteration, row and block.
+struct Cursor {
+  int slab, ei, it, which, blk;
+};
+__device__ __forceinline__ void advance(Cursor& c, const Plan& q, int pairs) {
+  if (++c.ei == q.nelp) {
+    c.ei = c.it = c.which = c.blk = 0;
+    ++c.slab;
+  } else if (++c.blk == q.nblk) {
+    c.blk = 0;
+    if (++c.which == pairs) {
+      c.which = 0;
+      ++c.it;
+    }
+  }
+}
+
+__device__ __forceinline__ int task_of(const Plan& q, int it) { return (it * kGemvWaves + wave_id()) * q.G + q.grp; }
+
+// Issue the loads of the element at c into b (lanes without a row read a valid dummy address).
+__device__ __forceinline__ void load_element(const Gemv& g, const Plan& q, const Cursor& c, RowBuf& b) {
+  const int k0 = c.slab * q.KS, ks = min(q.KS, q.Wst - k0);
+  const int i = task_of(q, c.it);
   const uint16_t* w = g.safe;
   int nc = 0;
-  if (i < q.nloc) {
-    const RowRef r = g.row(q.t0 + i, which);
+  if (c.ei < q.nel && i < q.nloc) {
+    const RowRef r = g.row(q.t0 + i, c.which);
     if (r.w) {
       w = r.w + k0;
       nc = max(0, min(r.len - k0, ks)) >> 3;
     }
   }
-  load_block(w, blk * kNC * q.LPR, nc, q.sub, q.LPR, g.safe, b);
+  load_block(w, c.blk * kNC * q.LPR, nc, q.sub, q.LPR, g.safe, b);
 }
 
-// Request the first two elements of this lane group's stream before the barrier (not on the
-// polling wave, whose poll would otherwise wait for them). Returns 2 when issued, else 0.
-template <int MM>
-__device__ __forceinline__ int gemv_preload(const Gemv& g, float* smem, RowBuf& b0, RowBuf& b1) {
-  if (wave_id() == kPollWave) return 0;
-  const Plan q = make_plan<MM>(g, smem);
-  const int ks = min(q.KS, q.Wst);
-  load_element(g, q, 0, 0, ks, b0);
-  load_element(g, q, 1, 0, ks, b1);
-  return 2;
+// Request the first two elements of this lane group's stream (before the phase's barrier; on the
+// polling wave the poll then waits for them, which the barrier's own latency mostly covers).
+__device__ __forceinline__ void gemv_preload(const Gemv& g, const Plan& q, RowBuf& b0, RowBuf& b1) {
+  Cursor c{0, 0, 0, 0, 0};
+  if (q.ntot > 0) load_element(g, q, c, b0);
+  advance(c, q, g.pairs);
+  if (q.ntot > 1) load_element(g, q, c, b1);
 }
 
 template <int MM>
@@ -684,19 +708,21 @@ __device__ __forceinline__ void reduce_task(const Gemv& g, const Plan& q, int i,
   for (int k = 0; k < MM; ++k) a0[k] = a1[k] = 0.f;
 }
 
-// Consume stream element e from b, then reuse b for element e + 2.
+// Consume stream element eg (at cursor cc, of the slab [k0, k0+ks)) from b, then reuse b for
+// element eg + 2 (at cursor pc, possibly of the next slab).
 template <int MM>
-__device__ __forceinline__ void step_element(const Gemv& g, const Plan& q, int e, int k0, int ks, const float* xin,
-                                             bool first, RowBuf& b, float (&a0)[MM], float (&a1)[MM]) {
-  const int per = g.pairs * q.nblk;
-  const int it = e / per, rem = e - it * per, which = rem / q.nblk, blk = rem - which * q.nblk;
-  const int i = (it * kWaves + wave_id()) * q.G + q.grp;
-  if (i < q.nloc) {
+__device__ __forceinline__ void step_element(const Gemv& g, const Plan& q, int eg, Cursor& cc, Cursor& pc, int k0,
+                                             int ks, const float* xin, RowBuf& b, float (&a0)[MM],
+                                             float (&a1)[MM]) {
+  const int which = cc.which;
+  const int i = task_of(q, cc.it);
+  const bool real = cc.ei < q.nel;
+  if (real && i < q.nloc) {
     const RowRef r = g.row(q.t0 + i, which);
     if (r.w) {
       const int nc = max(0, min(r.len - k0, ks)) >> 3;
       float d[MM];
-      dot_block<MM>(b, xin, ks, r.xoff - q.wbase, r, blk * kNC * q.LPR, nc, q.sub, q.LPR, d);
+      dot_block<MM>(b, xin, ks, r.xoff - q.wbase, r, cc.blk * kNC * q.LPR, nc, q.sub, q.LPR, d);
       if (g.kind == G_DOWN && which < g.rt->nu) {  // each pair into its token, with its router weight
 #pragma unroll
         for (int k = 0; k < MM; ++k) {
@@ -716,65 +742,67 @@ __device__ __forceinline__ void step_element(const Gemv& g, const Plan& q, int e
       }
     }
   }
-  load_element(g, q, e + 2, k0, ks, b);
-  if (rem == per - 1) reduce_task<MM>(g, q, i, first, a0, a1);
+  if (eg + 2 < q.ntot) load_element(g, q, pc, b);
+  const bool task_end = real && which == g.pairs - 1 && cc.blk == q.nblk - 1;
+  const bool first = cc.slab == 0;
+  advance(cc, q, g.pairs);
+  advance(pc, q, g.pairs);
+  if (task_end) reduce_task<MM>(g, q, i, first, a0, a1);
 }
 
 // Returns true when the LDS input buffer ends the phase holding the whole normalised input.
+// The first two elements of the stream were requested by gemv_preload.
 template <int MM>
-__device__ __forceinline__ bool gemv_phase(const Gemv& g, const Ws& ws, float* smem, float* inv, float* red,
-                                           RowBuf& b0, RowBuf& b1, int npre, bool keep_in, uint64_t* trace) {
+__device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const Ws& ws, float* smem, float* inv,
+                                           float* red, RowBuf& b0, RowBuf& b1, bool keep_in, uint64_t* trace) {
   float* xin = smem;
-  const Plan q = make_plan<MM>(g, smem);
   const int tid = tid_x();
+  const bool compute = true;
   const bool keep = keep_in && q.one_slab;  // input already staged by the previous phase
   const bool resid = g.kind == G_RESID || g.kind == G_DOWN;
-  for (int k0 = 0; k0 < q.Wst; k0 += q.KS) {
-    const int ks = min(q.KS, q.Wst - k0);
-    if (!(k0 == 0 && npre == 2)) {
-      load_element(g, q, 0, k0, ks, b0);
-      load_element(g, q, 1, k0, ks, b1);
-    }
+  Cursor cc{0, 0, 0, 0, 0}, pc{0, 0, 0, 0, 0};
+  advance(pc, q, g.pairs);
+  advance(pc, q, g.pairs);
+  if (trace && tid == 0) gp(trace)[4] = wall_clock64();
+  for (int sl = 0; sl < q.nslab; ++sl) {
+    const int k0 = sl * q.KS, ks = min(q.KS, q.Wst - k0);
     __syncthreads();
+    uint16_t* gl = reinterpret_cast<uint16_t*>(xin + (g.stage == S_DOWN ? g.np + g.M : g.M) * ks);
     if (!keep) {
-      // the residual inputs of this workgroup's rows travel with the staging loads
-      const bool rl = resid && k0 == 0 && tid < q.nloc * g.M;
-      float rv = 0.f;
-      if (rl) {
-        const int i = tid / g.M, m = tid - i * g.M;
-        rv = ws.ld1(g.out0 + (size_t)m * g.ldo0 + q.t0 + i);
-      }
-      g.stage_in<MM>(ws, xin, q.wbase + k0, ks, q.one_slab, inv, red);
-      if (rl) {
-        const int i = tid / g.M, m = tid - i * g.M;
-        q.res[i * MM + m] = rv;
-      }
-      if (resid && k0 == 0) {
-        for (int e = tid + kThreads; e < q.nloc * g.M; e += kThreads) {
-          const int i = e / g.M, m = e - i * g.M;
-          q.res[i * MM + m] = ws.ld1(g.out0 + (size_t)m * g.ldo0 + q.t0 + i);
-        }
-      }
+      if (g.stage == S_NORM && !q.one_slab && sl == 0) g.row_inv<MM>(ws, inv, red);
+      g.stage_issue(ws, xin, gl, q.wbase + k0, ks);
+      if (resid && sl == 0)  // this workgroup's residual inputs, [token][task]
+        dma_rows4<kCoherent>(ws.r, q.res, g.M, q.nloc, q.nloc,
+                  [&](int m, int c) { return ws.off(g.out0 + (size_t)m * g.ldo0 + q.t0 + c); });
+      wait_vm();
+      __syncthreads();
+      g.stage_finish<MM>(xin, gl, ks, q.one_slab, inv, red);
     }
     __syncthreads();
-    if (trace && k0 == 0 && tid == 0) gp(trace)[2] = wall_clock64();
-    float a0[MM], a1[MM];
+    if (trace && sl == 0 && tid == 0) gp(trace)[2] = wall_clock64();
+    if (compute) {
+      float a0[MM], a1[MM];
 #pragma unroll
-    for (int k = 0; k < MM; ++k) a0[k] = a1[k] = 0.f;
-    for (int e = 0; e < q.nel; e += 2) {
-      step_element<MM>(g, q, e, k0, ks, xin, k0 == 0, b0, a0, a1);
-      if (e + 1 < q.nel) step_element<MM>(g, q, e + 1, k0, ks, xin, k0 == 0, b1, a0, a1);
+      for (int k = 0; k < MM; ++k) a0[k] = a1[k] = 0.f;
+      const int eg0 = sl * q.nelp;
+      for (int e = 0; e < q.nelp; e += 2) {
+        step_element<MM>(g, q, eg0 + e, cc, pc, k0, ks, xin, b0, a0, a1);
+        step_element<MM>(g, q, eg0 + e + 1, cc, pc, k0, ks, xin, b1, a0, a1);
+      }
     }
   }
   if (trace && tid == 0) gp(trace)[3] = wall_clock64();
   // epilogue: each task by the lane that accumulated it
-  for (int it = 0; it < q.iters; ++it) {
-    const int i = (it * kWaves + wave_id()) * q.G + q.grp;
-    if (i < q.nloc && q.sub == 0) {
-      const float* ac = q.acc + (size_t)i * 2 * MM;
-      g.epilogue(q.t0 + i, ac, ac + MM, q.res + i * MM);
+  if (compute) {
+    for (int it = 0; it < q.iters; ++it) {
+      const int i = task_of(q, it);
+      if (i < q.nloc && q.sub == 0) {
+        const float* ac = q.acc + (size_t)i * 2 * MM;
+        g.epilogue(q.t0 + i, ac, ac + MM, q.res + i, q.nloc);
+      }
     }
   }
+  if (trace && tid == 0) gp(trace)[5] = wall_clock64();
   return q.one_slab && g.stage == S_NORM;
 }
 
@@ -894,7 +922,7 @@ __device__ __forceinline__ void rope_pair(const float* table, int t, int j, floa
 
 // GQA split-KV partials. Task (b, g, s): positions [s*C, s*C+C) of sequence b, kv head g, every
 // query head of the group and every new token. New positions in the chunk are appended here.
-__device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev& ly, const Ws& ws, float* smem,
+__device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
                                                const float* rope) {
   const int d = p.hd, nq = p.nh, nkv = p.nkv, T = p.T, cap = p.cap, d2 = d / 2, d4 = d / 4, d8 = d / 8;
   const int npos = p.kv_len + T, C = p.chunk;
@@ -907,8 +935,8 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev& 
   float* Qs = Vs + C * d;       // [T*qg][d]
   float* S = Qs + T * qg * d;   // [T*qg][C]
   const size_t lstride = (size_t)p.Bmax * nkv * cap * d;
-  uint16_t* Kc = p.kv + (size_t)ly.ord * lstride;
-  uint16_t* Vc = p.kv + (size_t)p.L * lstride + (size_t)ly.ord * lstride;
+  uint16_t* Kc = rflp(p.kv) + (size_t)rfl(ly->ord) * lstride;
+  uint16_t* Vc = rflp(p.kv) + (size_t)p.L * lstride + (size_t)rfl(ly->ord) * lstride;
   const float scale = 1.0f / sqrtf((float)d);
   const int stride = d + kPartPad;
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
@@ -1105,45 +1133,49 @@ __device__ __forceinline__ void merge_phase(const Params& p, const Ws& ws, int h
 // MLA split-KV partials over the latent cache. Task (b, s) covers positions [s*C, s*C + C) of
 // sequence b for every head and every new token. Scores use the absorbed query (W_uk^T q_nope)
 // against the latent part and the rotated query against the shared rope key, scaled by
-// 1/sqrt(nope + rope); positions are staged kSub at a time with a running max and sum per head.
-// New entries (normalised latent, rotated rope key, rounded to bf16) are appended to the cache by
-// the task whose range holds their position.
-__device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev& ly, const Ws& ws, float* smem,
-                                               const float* rope) {
+// 1/sqrt(nope + rope); positions are staged kSub at a time (bf16, as stored) with a running max and
+// sum per head. New entries (normalised latent, rotated rope key, rounded to bf16) are appended to
+// the cache by the task whose range holds their position.
+__device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
+                                               const float* rope, uint64_t* trace) {
   static_assert(kSub == 32, "score lanes map one position each in a half wave");
-  const int nh = p.nh, kvl = p.kvl, rd = p.rd, nd = p.nd, T = p.T, cap = p.cap;
-  const int lat = kvl + rd, latp = lat + 4, qd = nd + rd, h2 = rd / 2, half = lat / 2;
-  const int npos = p.kv_len + T, C = p.chunk, nsplit = p.nsplit, ntask = p.B * nsplit;
+  // step values in scalar registers (read from the parameter block in LDS)
+  const int kv_len = rfl(p.kv_len), Bmax = rfl(p.Bmax), B = rfl(p.B);
+  const float eps = rflf(p.eps);
+  const float* a2 = rflp(p.a2);
+  const float* a3 = rflp(p.a3);
+  const float* a4 = rflp(p.a4);
+  float* part = rflp(p.part);
+  uint16_t* kvc = rflp(p.kv);
+  const int nh = rfl(p.nh), kvl = rfl(p.kvl), rd = rfl(p.rd), nd = rfl(p.nd), T = rfl(p.T), cap = rfl(p.cap);
+  const int lat = kvl + rd, qd = nd + rd, h2 = rd / 2, half = lat / 2;
+  const int cst = lat + 8;  // bf16 per staged cache row: 16-byte aligned rows, banks staggered by 4
+  const int npos = kv_len + T, C = rfl(p.chunk), nsplit = rfl(p.nsplit), ntask = B * nsplit;
   const int tid = tid_x(), lane = lane_id(), wave = wave_id();
-  float* Cs = smem;              // [kSub][latp] cache rows
-  float* Qt = Cs + kSub * latp;  // [nh][lat] query of one token
-  float* Nw = Qt + nh * lat;     // [T][lat] new latent rows, rounded
-  float* S = Nw + T * lat;       // [nh][kSub] scores, then weights
-  float* st = S + nh * kSub;     // [nh][4] running max, running sum, rescale
-  float* nrm = st + nh * 4;      // [T] RMS scale of the new rows
-  float* gk = nrm + 8;           // [kvl] latent norm gain
-  uint16_t* Lc = p.kv + (size_t)ly.ord * p.Bmax * cap * lat;
+  uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);  // [kSub][cst] cache rows (bf16)
+  float* Qt = smem + kSub * cst / 2;                  // [nh][lat] query of one token
+  float* Nw = Qt + nh * lat;                          // [T][lat] new latent rows (values of their bf16)
+  float* S = Nw + T * lat;                            // [nh][kSub] scores, then weights
+  float* st = S + nh * kSub;                          // [nh][4] running max, running sum, rescale
+  float* nrm = st + nh * 4;                           // [8] RMS scale of the new rows
+  uint16_t* gk = reinterpret_cast<uint16_t*>(nrm + 8);  // [kvl] latent norm gain (bf16)
+  uint16_t* Lc = kvc + (size_t)rfl(ly->ord) * Bmax * cap * lat;
   const float scale = 1.0f / sqrtf((float)qd);
-  const int lq = lat >> 2, lc = lat >> 3, nq = nh * lq, kq = kvl >> 2, ntile = (nh >> 2) * kq;
+  const int kq = kvl >> 2, ntile = (nh >> 2) * kq;
   const int stride = kvl + kPartPad;
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int s = task % nsplit, b = task / nsplit;
     const int p0 = s * C, p1 = min(npos, p0 + C);
     uint16_t* Lb = Lc + (size_t)b * cap * lat;
-    const int n0 = max(p0, p.kv_len), nnew = max(0, p1 - n0), tA = n0 - p.kv_len;
+    const Rsrc lr = make_rsrc(Lb, (uint32_t)cap * lat * 2);
+    const int n0 = max(p0, kv_len), nnew = max(0, p1 - n0), tA = n0 - kv_len;
     __syncthreads();
-    if (nnew > 0) {
-      for (int j = tid; j < kvl; j += kThreads) gk[j] = bf2f(gp(ly.kv_norm)[j]);
-      copy_units<2>(
-          ws, nnew * lq,
-          [&](int i) {
-            const int r = i / lq;
-            return p.a2 + (size_t)(b * T + tA + r) * lat + 4 * (i - r * lq);
-          },
-          [&](int i) {
-            const int r = i / lq;
-            return Nw + (tA + r) * lat + 4 * (i - r * lq);
-          });
+    if (nnew > 0) {  // raw new rows (kv_a output) and the latent norm gain, then normalise and rotate
+      dma_rows<kCoherent>(ws.r, Nw + tA * lat, nnew, lat >> 2, lat,
+               [&](int r, int c) { return ws.off(a2 + (size_t)(b * T + tA + r) * lat + 4 * c); });
+      const Rsrc gr = make_rsrc(rflp(ly->kv_norm), (uint32_t)kvl * 2);
+      dma_rows<0>(gr, reinterpret_cast<float*>(gk), 1, kvl >> 3, 0, [&](int, int c) { return (uint32_t)c * 16; });
+      wait_vm();
       __syncthreads();
       for (int r = wave; r < nnew; r += kWaves) {
         float ss = 0.f;
@@ -1152,16 +1184,16 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev& 
           ss += v * v;
         }
         ss = wave_sum(ss, 64);
-        if (lane == 0) nrm[r] = 1.0f / sqrtf(ss / (float)kvl + p.eps);
+        if (lane == 0) nrm[r] = 1.0f / sqrtf(ss / (float)kvl + eps);
       }
       __syncthreads();
       const int per = kvl + h2;
       for (int e = tid; e < nnew * per; e += kThreads) {
         const int r = e / per, j = e - r * per, t = tA + r;
         float* row = Nw + t * lat;
-        uint16_t* dst = Lb + (size_t)(p.kv_len + t) * lat;
+        uint16_t* dst = Lb + (size_t)(kv_len + t) * lat;
         if (j < kvl) {
-          const uint16_t v = f2bf(row[j] * nrm[r] * gk[j]);
+          const uint16_t v = f2bf(row[j] * nrm[r] * bf2f(gk[j]));
           row[j] = bf2f(v);
           gp(dst)[j] = v;
         } else {
@@ -1176,34 +1208,32 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev& 
         }
       }
     }
-    // cache row i of a stage: unit (row, 8 values) from the cache, or from the new rows
-    auto put_c = [&](int i, int c0, const uint4& v) {
-      const int r = i / lc, cc = i - r * lc, pos = c0 + r;
-      f32x4* dq = reinterpret_cast<f32x4*>(Cs + r * latp + 8 * cc);
-      if (pos < p.kv_len) {
-        float f[8];
-        unpack8(v, f);
-        dq[0] = f32x4{f[0], f[1], f[2], f[3]};
-        dq[1] = f32x4{f[4], f[5], f[6], f[7]};
-      } else {
-        const f32x4* sq = reinterpret_cast<const f32x4*>(Nw + (pos - p.kv_len) * lat + 8 * cc);
-        dq[0] = sq[0];
-        dq[1] = sq[1];
-      }
+    // Stage cache rows [c0, c0+n): rows already in the cache by direct copy, new rows from Nw
+    // (after the copies have landed: see fill_new).
+    auto issue_c = [&](int c0, int n) {
+      const int nold = max(0, min(kv_len - c0, n));
+      dma_rows<2>(lr, reinterpret_cast<float*>(Cs), nold, lat >> 3, cst / 2,
+               [&](int r, int c) { return (uint32_t)((c0 + r) * lat) * 2 + c * 16; });
     };
-    auto c_addr = [&](int i, int c0) {
-      const int r = i / lc, pos = c0 + r;
-      return Lb + (size_t)(pos < p.kv_len ? pos : 0) * lat + 8 * (i - r * lc);
+    auto fill_new = [&](int c0, int n) {
+      const int r0 = max(0, kv_len - c0);
+      for (int e = tid; e < (n - r0) * (lat >> 2); e += kThreads) {
+        if (r0 >= n) break;
+        const int r = r0 + e / (lat >> 2), c = e - (r - r0) * (lat >> 2);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(Nw + (c0 + r - kv_len) * lat + 4 * c);
+        uint2 w;
+        w.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+        w.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+        *reinterpret_cast<uint2*>(Cs + r * cst + 4 * c) = w;
+      }
     };
     const bool whole = p1 - p0 <= kSub;  // the range is staged once, by the first token that reads it
     bool staged = false;
     for (int t = 0; t < T; ++t) {
-      const int m = b * T + t, qpos = p.kv_len + t, pe = min(p1, qpos + 1);
-      f32x4 u[2][4];
+      const int m = b * T + t, qpos = kv_len + t, pe = min(p1, qpos + 1);
+      f32x4 u[4];
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) u[k][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) u[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
       if (tid < nh) {
         st[tid * 4] = -INFINITY;
@@ -1212,34 +1242,17 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev& 
       }
       if (pe > p0) {
         // the token's query (absorbed latent part | raw rope part) and the first cache rows
-        {
-          const int ncu = (!whole || !staged) ? (whole ? p1 - p0 : min(kSub, pe - p0)) * lc : 0;
-          staged = true;
-          f32x4 qv[kQSlots];
-          uint4 cv[kCSlots];
-#pragma unroll
-          for (int k = 0; k < kQSlots; ++k) {
-            if (k * kThreads < nq) {
-              const int i = min(k * kThreads + tid, nq - 1), h = i / lq, j = 4 * (i - h * lq);
-              qv[k] = ws.ld4(j < kvl ? p.a4 + ((size_t)m * nh + h) * kvl + j
-                                     : p.a3 + ((size_t)m * nh + h) * qd + nd + (j - kvl));
-            }
-          }
-#pragma unroll
-          for (int k = 0; k < kCSlots; ++k)
-            if (k * kThreads < ncu) cv[k] = ldw(c_addr(min(k * kThreads + tid, ncu - 1), p0));
-#pragma unroll
-          for (int k = 0; k < kQSlots; ++k) {
-            const int i = k * kThreads + tid;
-            if (k * kThreads < nq && i < nq) *reinterpret_cast<f32x4*>(Qt + 4 * i) = qv[k];
-          }
-#pragma unroll
-          for (int k = 0; k < kCSlots; ++k) {
-            const int i = k * kThreads + tid;
-            if (k * kThreads < ncu && i < ncu) put_c(i, p0, cv[k]);
-          }
-        }
+        const int nfirst = (!whole || !staged) ? (whole ? p1 - p0 : min(kSub, pe - p0)) : 0;
+        dma_rows<kCoherent>(ws.r, Qt, nh, kvl >> 2, lat,
+                 [&](int h, int c) { return ws.off(a4 + ((size_t)m * nh + h) * kvl + 4 * c); });
+        dma_rows<kCoherent>(ws.r, Qt + kvl, nh, rd >> 2, lat,
+                 [&](int h, int c) { return ws.off(a3 + ((size_t)m * nh + h) * qd + nd + 4 * c); });
+        issue_c(p0, nfirst);
+        wait_vm();
         __syncthreads();
+        fill_new(p0, nfirst);
+        staged = true;
+        if (trace && tid == 0 && task == (int)blockIdx.x && t == 0) gp(trace)[2] = wall_clock64();
         for (int e = tid; e < nh * h2; e += kThreads) {
           const int h = e / h2, jj = e - h * h2;
           float* qr = Qt + h * lat + kvl;
@@ -1252,18 +1265,10 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev& 
           const int n = min(kSub, pe - c0);
           if (c0 != p0) {
             __syncthreads();
-            const int ncu = n * lc;
-            for (int bb = 0; bb < ncu; bb += kCSlots * kThreads) {
-              uint4 cv[kCSlots];
-#pragma unroll
-              for (int k = 0; k < kCSlots; ++k)
-                if (bb + k * kThreads < ncu) cv[k] = ldw(c_addr(min(bb + k * kThreads + tid, ncu - 1), c0));
-#pragma unroll
-              for (int k = 0; k < kCSlots; ++k) {
-                const int i = bb + k * kThreads + tid;
-                if (bb + k * kThreads < ncu && i < ncu) put_c(i, c0, cv[k]);
-              }
-            }
+            issue_c(c0, n);
+            wait_vm();
+            __syncthreads();
+            fill_new(c0, n);
           }
           __syncthreads();
           // scores: a wave per head pair, lane (position, half of the latent)
@@ -1273,11 +1278,14 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev& 
             if (pl < n) {
               const float* q0 = Qt + (2 * hp) * lat + jh * half;
               const float* q1 = q0 + lat;
-              const float* cr = Cs + pl * latp + jh * half;
-              for (int j = 0; j < half; j += 4) {
-                const f32x4 c = *reinterpret_cast<const f32x4*>(cr + j);
-                s0 += dot4(*reinterpret_cast<const f32x4*>(q0 + j), c);
-                s1 += dot4(*reinterpret_cast<const f32x4*>(q1 + j), c);
+              const uint16_t* cr = Cs + pl * cst + jh * half;
+#pragma unroll 4
+              for (int j = 0; j < half; j += 8) {
+                float c[8];
+                unpack8(*reinterpret_cast<const uint4*>(cr + j), c);
+                const f32x4 ca{c[0], c[1], c[2], c[3]}, cb{c[4], c[5], c[6], c[7]};
+                s0 += dot4(*reinterpret_cast<const f32x4*>(q0 + j), ca) + dot4(*reinterpret_cast<const f32x4*>(q0 + j + 4), cb);
+                s1 += dot4(*reinterpret_cast<const f32x4*>(q1 + j), ca) + dot4(*reinterpret_cast<const f32x4*>(q1 + j + 4), cb);
               }
             }
             s0 += __shfl_xor(s0, 32, 64);
@@ -1288,6 +1296,8 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev& 
             }
           }
           __syncthreads();
+          const bool mark = trace && tid == 0 && task == (int)blockIdx.x && t == 0 && c0 == p0;
+          if (mark) gp(trace)[4] = wall_clock64();
           // running max and sum: half a wave per head
           for (int hp = wave; hp < (nh >> 1); hp += kWaves) {
             const int h = 2 * hp + (lane >> 5), pl = lane & 31;
@@ -1306,49 +1316,45 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev& 
             }
           }
           __syncthreads();
+          if (mark) gp(trace)[5] = wall_clock64();
           // values: thread tile of 4 heads x 4 latent columns
+          if (tid < ntile) {
+            const int hg = tid / kq, jt = tid - hg * kq;
 #pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const int tt = tid + k * kThreads;
-            if (tt < ntile) {
-              const int hg = tt / kq, jt = tt - hg * kq;
+            for (int i = 0; i < 4; ++i) u[i] *= st[(4 * hg + i) * 4 + 2];
+#pragma unroll 4
+            for (int pl = 0; pl < n; ++pl) {
+              const uint2 cw = *reinterpret_cast<const uint2*>(Cs + pl * cst + 4 * jt);
+              const f32x4 c{lo_bf(cw.x), hi_bf(cw.x), lo_bf(cw.y), hi_bf(cw.y)};
 #pragma unroll
-              for (int i = 0; i < 4; ++i) u[k][i] *= st[(4 * hg + i) * 4 + 2];
-              for (int pl = 0; pl < n; ++pl) {
-                const f32x4 c = *reinterpret_cast<const f32x4*>(Cs + pl * latp + 4 * jt);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) u[k][i] += S[(4 * hg + i) * kSub + pl] * c;
-              }
+              for (int i = 0; i < 4; ++i) u[i] += S[(4 * hg + i) * kSub + pl] * c;
             }
           }
         }
       }
       __syncthreads();
+      if (trace && tid == 0 && task == (int)blockIdx.x && t == 0) gp(trace)[3] = wall_clock64();
+      if (tid < ntile) {
+        const int hg = tid / kq, jt = tid - hg * kq;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int tt = tid + k * kThreads;
-        if (tt < ntile) {
-          const int hg = tt / kq, jt = tt - hg * kq;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            ws.st4(p.part + ((size_t)(m * nh + 4 * hg + i) * nsplit + s) * stride + kPartPad + 4 * jt, u[k][i]);
-        }
+        for (int i = 0; i < 4; ++i)
+          ws.st4(part + ((size_t)(m * nh + 4 * hg + i) * nsplit + s) * stride + kPartPad + 4 * jt, u[i]);
       }
       if (tid < nh)
-        ws.st4(p.part + ((size_t)(m * nh + tid) * nsplit + s) * stride, f32x4{st[tid * 4], st[tid * 4 + 1], 0.f, 0.f});
+        ws.st4(part + ((size_t)(m * nh + tid) * nsplit + s) * stride, f32x4{st[tid * 4], st[tid * 4 + 1], 0.f, 0.f});
     }
   }
 }
 
 // gated delta rule: task (b, h, cb) owns columns [8cb, 8cb+8) of S_bh, one wave per task
-__device__ __forceinline__ void kda_phase(const Params& p, const LayerDev& ly, const Ws& ws) {
+__device__ __forceinline__ void kda_phase(const Params& p, const LayerDev* ly, const Ws& ws) {
   const int nh = p.nh, dk = p.dk, dv = p.dv, T = p.T;
   const int ncb = dv / 8;
   const int ntask = p.B * nh * ncb;
   const int gw = blockIdx.x * kWaves + wave_id(), tw = gridDim.x * kWaves;
   const int lane = lane_id();
   const int rpl = dk / 64;  // rows per lane (dk is 64 or 128)
-  float* St = p.kda_state + (size_t)ly.ord * p.Bmax * nh * dk * dv;
+  float* St = rflp(p.kda_state) + (size_t)rfl(ly->ord) * p.Bmax * nh * dk * dv;
   for (int task = gw; task < ntask; task += tw) {
     const int cb = task % ncb, h = (task / ncb) % nh, b = task / (ncb * nh);
     float* Sbh = St + ((size_t)b * nh + h) * dk * dv;
@@ -1361,9 +1367,9 @@ __device__ __forceinline__ void kda_phase(const Params& p, const LayerDev& ly, c
       const f32x4 c = *(const GLOBAL f32x4*)(Sbh + (size_t)i * dv + cb * 8 + 4);
       S[r][0] = a.x; S[r][1] = a.y; S[r][2] = a.z; S[r][3] = a.w;
       S[r][4] = c.x; S[r][5] = c.y; S[r][6] = c.z; S[r][7] = c.w;
-      al[r] = gp(ly.alpha)[h * dk + i];
+      al[r] = gp(rflp(ly->alpha))[h * dk + i];
     }
-    const float beta = gp(ly.beta)[h];
+    const float beta = gp(rflp(ly->beta))[h];
     for (int t = 0; t < T; ++t) {
       const int m = b * T + t;
       const float* kv = p.a2 + (size_t)m * nh * dk + h * dk;
@@ -1446,6 +1452,7 @@ struct Smem {
   int rsel[kMaxQueue];
   int cnt[kMaxExperts];
   Route route;
+  LayerDev lyd[2];  // layer table rows of the current and the next layer
   int abort;
 };
 
@@ -1477,9 +1484,9 @@ __device__ __forceinline__ void resid_out(Gemv& g, const Params& p, const uint16
   (void)K;
 }
 
-// Phase i of layer l (l == L: the final norm and LM head). Fills g for GEMV phases; the down
-// projection reads this workgroup's routing of the layer (rt).
-__device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, const Route* rt) {
+// Phase i of layer l (l == L: the final norm and LM head; ly: the layer's table row, in LDS). Fills
+// g for GEMV phases; the down projection reads this workgroup's routing of the layer (rt).
+__device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, const Route* rt, const LayerDev* ly) {
   g.M = p.M;
   g.eps = p.eps;
   g.pairs = 1;
@@ -1494,7 +1501,6 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
     g.ntasks = p.V;
     return PT_GEMV;
   }
-  const GLOBAL LayerDev* ly = gp(p.layers + l);
   const int kind = ly->kind;
   const int na = attn_phases(kind);
   if (i >= na) {
@@ -1647,9 +1653,17 @@ __device__ __forceinline__ void scalarize(Gemv& g) {
   g.rlog = rflp(g.rlog); g.sact = rflp(g.sact); g.eact = rflp(g.eact);
 }
 
-#define MK_SYNC()                                   \
-  do {                                              \
-    if (!grid_sync(p, gen, &sm.abort)) return;      \
+// Copy layer l's table row into LDS slot l % 2 (a direct copy; it has landed by the time the
+// layer starts, after many waits and barriers in between).
+__device__ __forceinline__ void fetch_layer(const Params& p, LayerDev* lyd, int l) {
+  const Rsrc tr = make_rsrc(rflp(p.layers), (uint32_t)(rfl(p.L) * sizeof(LayerDev)));
+  dma_rows<0>(tr, reinterpret_cast<float*>(lyd + (l & 1)), 1, (int)(sizeof(LayerDev) / 16), 0,
+              [&](int, int c) { return (uint32_t)(l * sizeof(LayerDev) + c * 16); });
+}
+
+#define MK_WAIT()                                     \
+  do {                                                \
+    if (!barrier_wait(p, gen, &sm.abort)) return;     \
   } while (0)
 
 template <int MM>
@@ -1693,31 +1707,63 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       sm.rope[(t * kMaxRopePairs + j) * 2] = (float)cos(a);
       sm.rope[(t * kMaxRopePairs + j) * 2 + 1] = (float)sin(a);
     }
+    fetch_layer(p, sm.lyd, 0);
     wait_vm();
+    __syncthreads();
   }
 
   bool resident = false;  // the LDS input buffer holds this layer's normalised MoE input
   for (int l = 0; l <= p.L; ++l) {
-    const int nph = (l == p.L) ? 1 : attn_phases(gp(p.layers + l)->kind) + 3;
+    const LayerDev* ly = &sm.lyd[l & 1];
+    if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
+    const int nph = (l == p.L) ? 1 : attn_phases(ly->kind) + 3;
     for (int i = 0; i < nph; ++i) {
       Gemv g{};
+      Plan q{};
       RowBuf b0, b1;  // per phase: dead outside GEMV phases
-      const int type = rfl(describe(p, l, i, g, &sm.route));
+      // Arrive at the barrier before this phase, then prepare the phase while the others arrive:
+      // its descriptor, its plan and (for GEMV phases) the loads of its first weight rows. The
+      // routed-expert phase waits first (routing needs every router logit). The weight rows are
+      // requested at one place so the buffers are never copied.
+      barrier_arrive(p, gen);
+      uint64_t* trec = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
+      const int type = rfl(describe(p, l, i, g, &sm.route, ly));
       scalarize(g);
-      const int npre = (type == PT_GEMV) ? gemv_preload<MM>(g, sm.buf, b0, b1) : 0;
-      MK_SYNC();
-      // sub-phase stamps of this phase go to the record of the barrier that preceded it
-      uint64_t* trec = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * 4 : nullptr;
+      if (trec && tid_x() == 0) gp(trec)[10] = wall_clock64();
+      const bool early = type == PT_GEMV;  // prepared while waiting
+      if (!early) {
+        MK_WAIT();
+        if (trec && tid_x() == 0) gp(trec)[7] = wall_clock64();
+        if (type == PT_EXPERT) {
+          compute_route(p, ws, l, &sm.route, sm.rsel, sm.rw, sm.cnt);
+          if (trec && tid_x() == 0) gp(trec)[6] = wall_clock64();
+          g.rt = &sm.route;
+          g.ntasks = rfl(sm.route.nu * p.F);
+        }
+      }
+      if (type == PT_GEMV || type == PT_EXPERT) {
+        q = make_plan<MM>(g, sm.buf);
+        if (trec && tid_x() == 0) gp(trec)[11] = wall_clock64();
+        gemv_preload(g, q, b0, b1);
+      }
+      if (early) {
+        if (trec && tid_x() == 0) gp(trec)[9] = wall_clock64();
+        MK_WAIT();
+        if (trec && tid_x() == 0) gp(trec)[7] = wall_clock64();
+      }
       switch (type) {
         case PT_GEMV:
-          resident = gemv_phase<MM>(g, ws, sm.buf, sm.inv, sm.red, b0, b1, npre, false, trec) && g.kind == G_RS;
+        case PT_EXPERT: {
+          const bool keep = type == PT_EXPERT && resident;
+          resident = gemv_phase<MM>(g, q, ws, sm.buf, sm.inv, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
           break;
+        }
         case PT_ATTN_GQA:
-          gqa_attn_phase(p, p.layers[l], ws, sm.buf, sm.rope);
+          gqa_attn_phase(p, ly, ws, sm.buf, sm.rope);
           resident = false;
           break;
         case PT_ATTN_MLA:
-          mla_attn_phase(p, p.layers[l], ws, sm.buf, sm.rope);
+          mla_attn_phase(p, ly, ws, sm.buf, sm.rope, trec);
           resident = false;
           break;
         case PT_MERGE:
@@ -1725,25 +1771,22 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
           resident = false;
           break;
         case PT_KDA:
-          kda_phase(p, p.layers[l], ws);
+          kda_phase(p, ly, ws);
           resident = false;
           break;
-        default:  // PT_EXPERT
-          compute_route(p, ws, l, &sm.route, sm.rsel, sm.rw, sm.cnt);
-          g.rt = &sm.route;
-          g.ntasks = rfl(sm.route.nu * p.F);
-          gemv_phase<MM>(g, ws, sm.buf, sm.inv, sm.red, b0, b1, 0, resident, trec);
-          resident = false;
+        default:
           break;
       }
       wait_vm();
+      if (trec && tid_x() == 0) gp(trec)[8] = wall_clock64();
     }
   }
   if (p.trace) {
     __syncthreads();
     if (tid_x() == 0) {
-      uint64_t* tr = p.trace + ((size_t)gen * gridDim.x + blockIdx.x) * 4;
-      gp(tr)[0] = gp(tr)[1] = gp(tr)[2] = gp(tr)[3] = wall_clock64();
+      uint64_t* tr = p.trace + ((size_t)gen * gridDim.x + blockIdx.x) * kTraceStamps;
+      const uint64_t now = wall_clock64();
+      for (int k = 0; k < kTraceStamps; ++k) gp(tr)[k] = now;
     }
   }
 }

@@ -32,6 +32,7 @@ extern "C" {
 #define MK_MAX_BATCH 8
 #define MK_MAX_NEW_TOKENS 8
 #define MK_DEVICE_NONE (-1)  /* host-only context: validates and lays out, never launches */
+#define MK_TRACE_STAMPS 16   /* wall-clock stamps per trace record */
 
 typedef enum {
   MK_OK = 0,
@@ -139,15 +140,19 @@ int mk_decode_step(mk_ctx* ctx, int batch, int n_new_tokens, int kv_len, const i
  * watchdog timeout or an out-of-range token (the context is then poisoned). */
 int mk_poll(mk_ctx* ctx);
 
-/* Profiling: while enabled, every step records, for each grid barrier and workgroup, four stamps
- * of the device wall clock (wall_clock64, 100 MHz on MI355X): arrival at the barrier, departure,
- * and, for the GEMV phase that follows it, the time its input was staged and the time its dot
- * products were done (0 for other phases). One extra record per workgroup holds the time it
- * finished the step. */
+/* Profiling: while enabled, every step records, for each grid barrier and workgroup,
+ * MK_TRACE_STAMPS stamps of the device wall clock (wall_clock64, 100 MHz on MI355X): 0 arrival at
+ * the barrier (flag published), 1 departure, then marks of the phase that follows it (0 where a
+ * phase has none):
+ * 2 input staged (GEMV) or query and first cache rows staged (attention), 3 dot products done
+ * (GEMV) or values accumulated (attention), 4 first weight loads issued (GEMV), 5 epilogue written
+ * (GEMV), 6 routing done (routed-expert phase), 7 phase entered (the first wave past the barrier),
+ * 8 the phase's stores drained, 9 the phase prepared while waiting at its barrier (descriptor,
+ * plan, first loads issued), 10 descriptor built, 11 plan built, 12-15 reserved. One extra record per workgroup holds
+ * the time it finished the step. */
 int mk_set_trace(mk_ctx* ctx, int enable);
 
-/* Copy the last traced step: out[((barrier * n_blocks) + block) * 4 + {0: arrive, 1: depart,
- * 2: staged, 3: computed}] for
+/* Copy the last traced step: out[((barrier * n_blocks) + block) * MK_TRACE_STAMPS + stamp] for
  * barrier < *n_barriers + 1 (the last record is the end of the step). Call with out == NULL to get
  * the counts; capacity is the number of uint64_t slots in out. Synchronous (after the step's stream
  * has finished). */
