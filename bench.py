@@ -86,6 +86,49 @@ def traffic_from_profiles(B: int):
     return d.get("per_launch_bytes", {}).get(str(B))
 
 
+CALIB_BYTES = 1 << 30  # bytes the calibration kernel reads (and writes)
+
+
+def ingest_pmc(fetch_csv: str, write_csv: str) -> None:
+    """HBM traffic of the megakernel from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the calibration copy (CALIB_BYTES read and
+    written by an elementwise kernel), written to profiles/ with the kernel's source hash."""
+    import csv
+
+    def per_kernel(path: str, counter: str) -> tuple[float, list[float]]:
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        by = {}
+        for r in rows:
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            by[key] = by.get(key, 0.0) + float(r["Counter_Value"])
+        # the calibration multiply (x * 1.0 -> y), not the fills torch runs around it
+        calib = [v for (d, n), v in by.items() if "elementwise" in n and "Fill" not in n and
+                 ("AUnaryFunctor" in n or "Mul" in n)]
+        mk = [v for (d, n), v in sorted(by.items(), key=lambda kv: int(kv[0][0])) if "mk_decode_kernel" in n]
+        if not calib or not mk:
+            raise SystemExit(f"{path}: need the calibration kernel and megakernel dispatches for {counter}")
+        return max(calib), mk
+
+    f_cal, f_mk = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_cal, w_mk = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = CALIB_BYTES / (f_cal * 1024.0)
+    w_scale = CALIB_BYTES / (w_cal * 1024.0)
+    fetch = float(np.median(f_mk)) * 1024.0 * f_scale
+    write = float(np.median(w_mk)) * 1024.0 * w_scale
+    cfg = synth.WORKLOADS[WORKLOAD].model
+    out = {"kernel_hash": kernel_source_hash(), "workload": WORKLOAD, "batch": 1,
+           "calibration": {"bytes": CALIB_BYTES, "fetch_kib": f_cal, "write_kib": w_cal,
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "megakernel": {"dispatches": len(f_mk), "fetch_kib_median": float(np.median(f_mk)),
+                          "write_kib_median": float(np.median(w_mk)), "fetch_bytes": fetch, "write_bytes": write},
+           "per_launch_bytes": {"1": fetch + write}}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "megakernel_k3_pmc_traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+    del cfg
+
+
 # ------------------------------------------------------------------------------------------
 # CPU baseline: the oracle on the host's cores, on a bounded sample of the same step
 # ------------------------------------------------------------------------------------------
@@ -233,7 +276,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--trace", action="store_true", help="print per-phase device timings of one step per batch")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one elementwise copy of CALIB_BYTES (fp32 x*1 -> y) first: the counter calibration "
+                         "kernel for the traffic figure")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 counter_collection CSVs (FETCH_SIZE, WRITE_SIZE) of a --calib-copy "
+                         "run into profiles/megakernel_k3_pmc_traffic.{json,md} and exit")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the decode step; --gpus {args.gpus} is not supported "
               f"(this build runs on exactly one GPU, with no collectives)", file=sys.stderr)
@@ -252,6 +304,13 @@ def main():
     dm.fill_caches(max(batches), w.kv_len)
     print(f"# model loaded in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
+    if args.calib_copy:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     results = {}
     for B in batches:
         toks = synth.tokens(spec.seed, 1, cfg.vocab, B, w.new_tokens)

@@ -95,9 +95,11 @@ int check_config(const mk_config* c) {
         c->v_dim < 8 || c->v_dim % 8 || c->rope_dim < 2 || c->rope_dim % 2 || c->rope_dim > 2 * kMaxRopePairs)
       return fail(MK_E_UNSUPPORTED, "MLA dims must be multiples of 8 (rope_dim even, <= %d)", 2 * kMaxRopePairs);
     const int lat = c->kv_lora + c->rope_dim, nh = c->n_heads;
-    if (c->rope_dim % 8 || nh % 4) return fail(MK_E_UNSUPPORTED, "MLA needs rope_dim % 8 == 0 and n_heads % 4 == 0");
-    if (kSub * (lat + 8) / 2 + nh * lat + c->max_new_tokens * lat + nh * kSub + nh * 4 + 8 + c->kv_lora / 2 > kLdsFloats ||
-        (nh / 4) * (c->kv_lora / 4) > kThreadsHost)
+    // the attention tile: 16 heads x kv_lora = 512 on the matrix cores (4 K groups x 2 position tiles,
+    // 32 value column tiles over 8 waves)
+    if (nh != 16 || c->kv_lora != 512 || lat % 32 || c->rope_dim % 8)
+      return fail(MK_E_UNSUPPORTED, "MLA attention supports 16 heads, kv_lora 512 and rope_dim a multiple of 32");
+    if (kSub * (lat + 8) / 2 + nh * lat + c->max_new_tokens * lat + 5 * nh * kSub + nh * 4 + 8 + c->kv_lora / 2 > kLdsFloats)
       return fail(MK_E_UNSUPPORTED, "MLA heads / latent too wide for the attention tile");
     if (c->attn_kind == MK_ATTN_HYBRID) {
       if (c->hybrid_period < 1) return fail(MK_E_INVAL, "hybrid_period must be positive");

@@ -227,44 +227,47 @@ __device__ __forceinline__ void barrier_arrive(const Params& p, uint32_t& gen) {
   }
 }
 
-__device__ __forceinline__ bool barrier_wait(const Params& p, uint32_t gen, int* s_abort) {
+// The polling wave's half of the wait: poll until every workgroup has arrived (or abort).
+__device__ __forceinline__ void barrier_poll(const Params& p, uint32_t gen, int* s_abort) {
   const uint32_t target = p.epoch + gen;
-  if (wave_id() == kPollWave) {
-    const int lane = lane_id();
-    uint64_t* tr = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
-    const uint64_t t0 = wall_clock64();
-    int abort = 0;
-    while (true) {
-      uint32_t f[kMaxGrid / 64];
+  const int lane = lane_id();
+  uint64_t* tr = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
+  const uint64_t t0 = wall_clock64();
+  int abort = 0;
+  while (true) {
+    uint32_t f[kMaxGrid / 64];
 #pragma unroll
-      for (int k = 0; k < kMaxGrid / 64; ++k) {
-        const int i = lane + 64 * k;
-        f[k] = i < (int)gridDim.x ? ldc_u32(p.flags + i) : target;
-      }
-      int ok = 1;
+    for (int k = 0; k < kMaxGrid / 64; ++k) {
+      const int i = lane + 64 * k;
+      f[k] = i < (int)gridDim.x ? ldc_u32(p.flags + i) : target;
+    }
+    int ok = 1;
 #pragma unroll
-      for (int k = 0; k < kMaxGrid / 64; ++k) ok &= ((int32_t)(f[k] - target) >= 0);
-      if (__all(ok)) break;
-      if (ldc_u32(p.status + 1)) {
-        abort = 1;
-        break;
-      }
-      if (wall_clock64() - t0 > p.watchdog_ticks) {
-        if (lane == 0) {
-          stc_u32(p.status + 0, (uint32_t)(-MK_E_DEVICE));
-          stc_u32(p.status + 2, gen);
-          stc_u32(p.status + 1, 1u);
-        }
-        abort = 1;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+    for (int k = 0; k < kMaxGrid / 64; ++k) ok &= ((int32_t)(f[k] - target) >= 0);
+    if (__all(ok)) break;
+    if (ldc_u32(p.status + 1)) {
+      abort = 1;
+      break;
     }
-    if (lane == 0) {
-      *s_abort = abort;
-      if (tr) gp(tr)[1] = wall_clock64();
+    if (wall_clock64() - t0 > p.watchdog_ticks) {
+      if (lane == 0) {
+        stc_u32(p.status + 0, (uint32_t)(-MK_E_DEVICE));
+        stc_u32(p.status + 2, gen);
+        stc_u32(p.status + 1, 1u);
+      }
+      abort = 1;
+      break;
     }
+    __builtin_amdgcn_s_sleep(1);
   }
+  if (lane == 0) {
+    *s_abort = abort;
+    if (tr) gp(tr)[1] = wall_clock64();
+  }
+}
+
+// Every wave's half: the workgroup leaves together once the polling wave is done.
+__device__ __forceinline__ bool barrier_finish(int* s_abort) {
   wg_barrier();
   return *s_abort == 0;
 }
@@ -1130,12 +1133,26 @@ __device__ __forceinline__ void merge_phase(const Params& p, const Ws& ws, int h
   }
 }
 
+// bf16 vectors for the matrix cores
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) { return as_bf16x8(*reinterpret_cast<const u32x4*>(p)); }
+// two floats as bf16 high parts (packed) and the bf16 of what the high parts leave (low parts):
+// x = hi + lo to about 16 significant bits
+__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
+  const uint16_t l0 = f2bf(x0 - bf2f(h0)), l1 = f2bf(x1 - bf2f(h1));
+  hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  lo = (uint32_t)l0 | ((uint32_t)l1 << 16);
+}
+
 // MLA split-KV partials over the latent cache. Task (b, s) covers positions [s*C, s*C + C) of
 // sequence b for every head and every new token. Scores use the absorbed query (W_uk^T q_nope)
 // against the latent part and the rotated query against the shared rope key, scaled by
 // 1/sqrt(nope + rope); positions are staged kSub at a time (bf16, as stored) with a running max and
-// sum per head. New entries (normalised latent, rotated rope key, rounded to bf16) are appended to
-// the cache by the task whose range holds their position.
+// sum per head; scores (query split into bf16 high and low parts) and value sums (weights split
+// likewise) run on the matrix cores. New entries (normalised latent, rotated rope key, rounded to
+// bf16) are appended to the cache by the task whose range holds their position.
 __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
                                                const float* rope, uint64_t* trace) {
   static_assert(kSub == 32, "score lanes map one position each in a half wave");
@@ -1153,16 +1170,21 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
   const int npos = kv_len + T, C = rfl(p.chunk), nsplit = rfl(p.nsplit), ntask = B * nsplit;
   const int tid = tid_x(), lane = lane_id(), wave = wave_id();
   uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);  // [kSub][cst] cache rows (bf16)
-  float* Qt = smem + kSub * cst / 2;                  // [nh][lat] query of one token
+  float* Qt = smem + kSub * cst / 2;                  // [nh][lat] query of one token (fp32), then
+  uint16_t* Qh = reinterpret_cast<uint16_t*>(Qt);     //   its bf16 high parts [nh][lat]
+  uint16_t* Ql = Qh + nh * lat;                       //   and low parts [nh][lat]; finally values [nh][kvl]
   float* Nw = Qt + nh * lat;                          // [T][lat] new latent rows (values of their bf16)
-  float* S = Nw + T * lat;                            // [nh][kSub] scores, then weights
+  float* Sp = Nw + T * lat;                           // [4][nh][kSub] partial scores of the K groups
+  float* S = Sp + 4 * nh * kSub;                      // [nh][kSub] weights
   float* st = S + nh * kSub;                          // [nh][4] running max, running sum, rescale
   float* nrm = st + nh * 4;                           // [8] RMS scale of the new rows
   uint16_t* gk = reinterpret_cast<uint16_t*>(nrm + 8);  // [kvl] latent norm gain (bf16)
   uint16_t* Lc = kvc + (size_t)rfl(ly->ord) * Bmax * cap * lat;
   const float scale = 1.0f / sqrtf((float)qd);
-  const int kq = kvl >> 2, ntile = (nh >> 2) * kq;
   const int stride = kvl + kPartPad;
+  const int nks = lat / 32;                    // 32-wide K steps of the scores
+  const int kgs = (nks + 3) / 4;               // K steps per group (4 groups x 2 position tiles = 8 waves)
+  const int ml = lane & 15, mq = lane >> 4;    // MFMA lane: row/column l % 16, K octet l / 16
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int s = task % nsplit, b = task / nsplit;
     const int p0 = s * C, p1 = min(npos, p0 + C);
@@ -1231,9 +1253,9 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
     bool staged = false;
     for (int t = 0; t < T; ++t) {
       const int m = b * T + t, qpos = kv_len + t, pe = min(p1, qpos + 1);
-      f32x4 u[4];
+      f32x4 u[4];  // values: column tiles 4*wave + ct, rows 4*mq + i (heads), column ml
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < 4; ++ct) u[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
       if (tid < nh) {
         st[tid * 4] = -INFINITY;
@@ -1244,9 +1266,9 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
         // the token's query (absorbed latent part | raw rope part) and the first cache rows
         const int nfirst = (!whole || !staged) ? (whole ? p1 - p0 : min(kSub, pe - p0)) : 0;
         dma_rows<kCoherent>(ws.r, Qt, nh, kvl >> 2, lat,
-                 [&](int h, int c) { return ws.off(a4 + ((size_t)m * nh + h) * kvl + 4 * c); });
+                            [&](int h, int c) { return ws.off(a4 + ((size_t)m * nh + h) * kvl + 4 * c); });
         dma_rows<kCoherent>(ws.r, Qt + kvl, nh, rd >> 2, lat,
-                 [&](int h, int c) { return ws.off(a3 + ((size_t)m * nh + h) * qd + nd + 4 * c); });
+                            [&](int h, int c) { return ws.off(a3 + ((size_t)m * nh + h) * qd + nd + 4 * c); });
         issue_c(p0, nfirst);
         wait_vm();
         __syncthreads();
@@ -1261,6 +1283,29 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
           qr[jj] = x0;
           qr[jj + h2] = x1;
         }
+        __syncthreads();
+        // query as bf16 high and low parts (q = hi + lo to 16 bits), in place
+        {
+          const int nq4 = nh * lat / 4;
+          f32x4 qv[5];
+#pragma unroll
+          for (int k = 0; k < 5; ++k) {
+            const int i = k * kThreads + tid;
+            if (k * kThreads < nq4) qv[k] = *reinterpret_cast<const f32x4*>(Qt + 4 * min(i, nq4 - 1));
+          }
+          __syncthreads();
+#pragma unroll
+          for (int k = 0; k < 5; ++k) {
+            const int i = k * kThreads + tid;
+            if (k * kThreads < nq4 && i < nq4) {
+              uint32_t h01, h23, l01, l23;
+              split_bf16(qv[k].x, qv[k].y, h01, l01);
+              split_bf16(qv[k].z, qv[k].w, h23, l23);
+              *reinterpret_cast<uint2*>(Qh + 4 * i) = make_uint2(h01, h23);
+              *reinterpret_cast<uint2*>(Ql + 4 * i) = make_uint2(l01, l23);
+            }
+          }
+        }
         for (int c0 = p0; c0 < pe; c0 += kSub) {
           const int n = min(kSub, pe - c0);
           if (c0 != p0) {
@@ -1271,37 +1316,34 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
             fill_new(c0, n);
           }
           __syncthreads();
-          // scores: a wave per head pair, lane (position, half of the latent)
-          for (int it = tid; it < (nh >> 1) * 64; it += kThreads) {
-            const int hp = it >> 6, ln = it & 63, pl = ln & 31, jh = ln >> 5;
-            float s0 = 0.f, s1 = 0.f;
-            if (pl < n) {
-              const float* q0 = Qt + (2 * hp) * lat + jh * half;
-              const float* q1 = q0 + lat;
-              const uint16_t* cr = Cs + pl * cst + jh * half;
-#pragma unroll 4
-              for (int j = 0; j < half; j += 8) {
-                float c[8];
-                unpack8(*reinterpret_cast<const uint4*>(cr + j), c);
-                const f32x4 ca{c[0], c[1], c[2], c[3]}, cb{c[4], c[5], c[6], c[7]};
-                s0 += dot4(*reinterpret_cast<const f32x4*>(q0 + j), ca) + dot4(*reinterpret_cast<const f32x4*>(q0 + j + 4), cb);
-                s1 += dot4(*reinterpret_cast<const f32x4*>(q1 + j), ca) + dot4(*reinterpret_cast<const f32x4*>(q1 + j + 4), cb);
-              }
+          const bool mark = trace && tid == 0 && task == (int)blockIdx.x && t == 0 && c0 == p0;
+          // scores on the matrix cores: wave -> position tile (wave & 1) x K group (wave >> 1)
+          {
+            const int pt = wave & 1, kg = wave >> 1;
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            const uint16_t* brow = Cs + (16 * pt + ml) * cst + 8 * mq;
+            const uint16_t* ahi = Qh + ml * lat + 8 * mq;
+            const uint16_t* alo = Ql + ml * lat + 8 * mq;
+            for (int kk = kg * kgs; kk < min(nks, kg * kgs + kgs); ++kk) {
+              const bf16x8 bv = ld_bf16x8(brow + 32 * kk);
+              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_bf16x8(ahi + 32 * kk), bv, d, 0, 0, 0);
+              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_bf16x8(alo + 32 * kk), bv, d, 0, 0, 0);
             }
-            s0 += __shfl_xor(s0, 32, 64);
-            s1 += __shfl_xor(s1, 32, 64);
-            if (jh == 0) {
-              S[(2 * hp) * kSub + pl] = pl < n ? s0 * scale : -INFINITY;
-              S[(2 * hp + 1) * kSub + pl] = pl < n ? s1 * scale : -INFINITY;
-            }
+            // D: column ml (position 16 pt + ml), rows 4 mq + i (heads 4 mq + i of this 16-head block)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Sp[(kg * nh + 4 * mq + i) * kSub + 16 * pt + ml] = d[i];
           }
           __syncthreads();
-          const bool mark = trace && tid == 0 && task == (int)blockIdx.x && t == 0 && c0 == p0;
           if (mark) gp(trace)[4] = wall_clock64();
           // running max and sum: half a wave per head
           for (int hp = wave; hp < (nh >> 1); hp += kWaves) {
             const int h = 2 * hp + (lane >> 5), pl = lane & 31;
-            const float sv = S[h * kSub + pl];
+            float sv = -INFINITY;
+            if (pl < n) {
+              float a = 0.f;
+              for (int k = 0; k < 4; ++k) a += Sp[(k * nh + h) * kSub + pl];
+              sv = a * scale;
+            }
             const float cm = wave_max(sv, 32);
             const float mo = st[h * 4], lo = st[h * 4 + 1];
             const float mn = fmaxf(mo, cm);
@@ -1317,28 +1359,54 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
           }
           __syncthreads();
           if (mark) gp(trace)[5] = wall_clock64();
-          // values: thread tile of 4 heads x 4 latent columns
-          if (tid < ntile) {
-            const int hg = tid / kq, jt = tid - hg * kq;
+          // values on the matrix cores: A = weights [16 heads][32 positions] (bf16 high and low
+          // parts), B = cache rows [32 positions][16 columns]; wave -> column tiles 4 wave + ct
+          {
+            const f32x4 w0 = *reinterpret_cast<const f32x4*>(S + ml * kSub + 8 * mq);
+            const f32x4 w1 = *reinterpret_cast<const f32x4*>(S + ml * kSub + 8 * mq + 4);
+            uint32_t h0, h1, h2_, h3, l0, l1, l2, l3;
+            split_bf16(w0.x, w0.y, h0, l0);
+            split_bf16(w0.z, w0.w, h1, l1);
+            split_bf16(w1.x, w1.y, h2_, l2);
+            split_bf16(w1.z, w1.w, h3, l3);
+            const bf16x8 whi = as_bf16x8(u32x4{h0, h1, h2_, h3}), wlo = as_bf16x8(u32x4{l0, l1, l2, l3});
 #pragma unroll
-            for (int i = 0; i < 4; ++i) u[i] *= st[(4 * hg + i) * 4 + 2];
-#pragma unroll 4
-            for (int pl = 0; pl < n; ++pl) {
-              const uint2 cw = *reinterpret_cast<const uint2*>(Cs + pl * cst + 4 * jt);
-              const f32x4 c{lo_bf(cw.x), hi_bf(cw.x), lo_bf(cw.y), hi_bf(cw.y)};
+            for (int i = 0; i < 4; ++i) {
+              const float sc = st[(4 * mq + i) * 4 + 2];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) u[i] += S[(4 * hg + i) * kSub + pl] * c;
+              for (int ct = 0; ct < 4; ++ct) u[ct][i] *= sc;
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+              const int col = 16 * (4 * wave + ct) + ml;
+              uint32_t bw[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int r0 = 8 * mq + 2 * j, r1 = r0 + 1;
+                const uint32_t v0 = r0 < n ? Cs[r0 * cst + col] : 0u;
+                const uint32_t v1 = r1 < n ? Cs[r1 * cst + col] : 0u;
+                bw[j] = v0 | (v1 << 16);
+              }
+              const bf16x8 bv = as_bf16x8(u32x4{bw[0], bw[1], bw[2], bw[3]});
+              u[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, bv, u[ct], 0, 0, 0);
+              u[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, bv, u[ct], 0, 0, 0);
             }
           }
         }
       }
       __syncthreads();
       if (trace && tid == 0 && task == (int)blockIdx.x && t == 0) gp(trace)[3] = wall_clock64();
-      if (tid < ntile) {
-        const int hg = tid / kq, jt = tid - hg * kq;
+      // values to LDS [nh][kvl] (the query's space), then to the partials in 16-byte rows
+      float* Ut = Qt;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ws.st4(part + ((size_t)(m * nh + 4 * hg + i) * nsplit + s) * stride + kPartPad + 4 * jt, u[i]);
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ut[(4 * mq + i) * kvl + 16 * (4 * wave + ct) + ml] = u[ct][i];
+      __syncthreads();
+      for (int e = tid; e < nh * (kvl >> 2); e += kThreads) {
+        const int h = e / (kvl >> 2), c = e - h * (kvl >> 2);
+        ws.st4(part + ((size_t)(m * nh + h) * nsplit + s) * stride + kPartPad + 4 * c,
+               *reinterpret_cast<const f32x4*>(Ut + h * kvl + 4 * c));
       }
       if (tid < nh)
         ws.st4(part + ((size_t)(m * nh + tid) * nsplit + s) * stride, f32x4{st[tid * 4], st[tid * 4 + 1], 0.f, 0.f});
@@ -1661,9 +1729,9 @@ __device__ __forceinline__ void fetch_layer(const Params& p, LayerDev* lyd, int 
               [&](int, int c) { return (uint32_t)(l * sizeof(LayerDev) + c * 16); });
 }
 
-#define MK_WAIT()                                     \
+#define MK_FINISH()                                   \
   do {                                                \
-    if (!barrier_wait(p, gen, &sm.abort)) return;     \
+    if (!barrier_finish(&sm.abort)) return;           \
   } while (0)
 
 template <int MM>
@@ -1722,9 +1790,11 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       Plan q{};
       RowBuf b0, b1;  // per phase: dead outside GEMV phases
       // Arrive at the barrier before this phase, then prepare the phase while the others arrive:
-      // its descriptor, its plan and (for GEMV phases) the loads of its first weight rows. The
-      // routed-expert phase waits first (routing needs every router logit). The weight rows are
-      // requested at one place so the buffers are never copied.
+      // its descriptor, its plan and (for GEMV phases) the loads of its first weight rows (on the
+      // polling wave too: its polls then queue behind them, which costs less than holding the
+      // workgroup while it requests them after the poll). The routed-expert phase waits first
+      // (routing needs every router logit). The weight rows are requested at one place so the
+      // buffers are never copied.
       barrier_arrive(p, gen);
       uint64_t* trec = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
       const int type = rfl(describe(p, l, i, g, &sm.route, ly));
@@ -1732,7 +1802,8 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       if (trec && tid_x() == 0) gp(trec)[10] = wall_clock64();
       const bool early = type == PT_GEMV;  // prepared while waiting
       if (!early) {
-        MK_WAIT();
+        if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort);
+        MK_FINISH();
         if (trec && tid_x() == 0) gp(trec)[7] = wall_clock64();
         if (type == PT_EXPERT) {
           compute_route(p, ws, l, &sm.route, sm.rsel, sm.rw, sm.cnt);
@@ -1748,7 +1819,8 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       }
       if (early) {
         if (trec && tid_x() == 0) gp(trec)[9] = wall_clock64();
-        MK_WAIT();
+        if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort);
+        MK_FINISH();
         if (trec && tid_x() == 0) gp(trec)[7] = wall_clock64();
       }
       switch (type) {
