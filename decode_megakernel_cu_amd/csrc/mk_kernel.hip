@@ -872,6 +872,7 @@ __device__ __forceinline__ void compute_route(const Params& p, const Ws& ws, int
     }
   }
   __syncthreads();
+  // counting sort of the pairs by expert: counts, then one wave scans them (R experts per lane)
   const int nq = M * K;
   for (int e = tid; e < E; e += kThreads) {
     int c = 0;
@@ -879,22 +880,41 @@ __device__ __forceinline__ void compute_route(const Params& p, const Ws& ws, int
     cnt[e] = c;
   }
   __syncthreads();
-  if (tid == 0) {
-    int nu = 0, np = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = cnt[e];
-      if (c) {
-        rt->uexp[nu] = e;
-        rt->ustart[nu] = np;
-        cnt[e] = np;
-        np += c;
-        ++nu;
-      } else {
-        cnt[e] = -1;
+  if (wave_id() == 0) {
+    int c[R], s = 0, z = 0;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int e = R * lane + k;
+      c[k] = e < E ? cnt[e] : 0;
+      s += c[k];
+      z += c[k] > 0;
+    }
+    int si = s, zi = z;  // inclusive scans over lanes
+    for (int o = 1; o < 64; o <<= 1) {
+      const int sv = __shfl_up(si, o, 64), zv = __shfl_up(zi, o, 64);
+      if (lane >= o) {
+        si += sv;
+        zi += zv;
       }
     }
-    rt->ustart[nu] = np;
-    rt->nu = nu;
+    int start = si - s, u = zi - z;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int e = R * lane + k;
+      if (c[k] > 0) {
+        rt->uexp[u] = e;
+        rt->ustart[u] = start;
+        cnt[e] = start;
+        ++u;
+      } else if (e < E) {
+        cnt[e] = -1;
+      }
+      start += c[k];
+    }
+    if (lane == 63) {
+      rt->ustart[zi] = si;
+      rt->nu = zi;
+    }
   }
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) {
@@ -1061,45 +1081,43 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
 }
 
 // Merge split-KV partials: out[m][h*dim + j] = sum_s e^{mx_s - M} u_s[j] / sum_s e^{mx_s - M} l_s
-// over the splits s (M the largest mx_s). Task (m, h, 32 values): threads (split lane sl = tid/8,
-// quad q = tid%8) sum splits sl, sl + 64, ... of four values; the splits' statistics are read in
-// the same batch as the first values.
+// over the splits s (M the largest mx_s). Task (m, h, 32 values): every split's statistics and
+// its 32 values are copied straight into LDS in one batch; thread (split lane sl = tid/8, quad
+// q = tid%8) then sums splits sl, sl + 64, ... of four values.
 __device__ __forceinline__ void merge_phase(const Params& p, const Ws& ws, int heads, int dim, float* out,
                                             float* smem) {
-  constexpr int NS = 5;
-  const int nsplit = p.nsplit, stride = dim + kPartPad, nj = (dim + 31) >> 5, ntask = p.M * heads * nj;
+  const int nsplit = rfl(p.nsplit), stride = dim + kPartPad, nj = (dim + 31) >> 5, ntask = rfl(p.M) * heads * nj;
+  const float* part = rflp(p.part);
   const int tid = tid_x(), lane = lane_id(), wave = wave_id(), sl = tid >> 3, qd = tid & 7;
-  float* w = smem;                                                     // [nsplit] split weights
-  f32x4* red = reinterpret_cast<f32x4*>(smem + ((nsplit + 3) & ~3));  // [kWaves][8]
-  float* misc = reinterpret_cast<float*>(red + kWaves * 8);           // [2][kWaves]
+  float* hdr = smem;                                     // [nsplit][4] max, sum
+  float* val = hdr + 4 * nsplit;                         // [nsplit][4 nv] values (dense)
+  float* w = val + 32 * nsplit;                          // [nsplit] split weights
+  f32x4* red = reinterpret_cast<f32x4*>(w + ((nsplit + 3) & ~3));  // [kWaves][8]
+  float* misc = reinterpret_cast<float*>(red + kWaves * 8);       // [2][kWaves]
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int mh = task / nj, j0 = (task - mh * nj) * 32;
-    const float* src = p.part + (size_t)mh * nsplit * stride;
-    const int jq = j0 + 4 * qd < dim ? j0 + 4 * qd : j0;
+    const int nv = min(32, dim - j0) >> 2;  // 16-byte units of values
+    const float* src = part + (size_t)mh * nsplit * stride;
     __syncthreads();
-    f32x4 v[NS];
-#pragma unroll
-    for (int u = 0; u < NS; ++u)
-      if (u * 64 < nsplit) v[u] = ws.ld4(src + (size_t)min(sl + 64 * u, nsplit - 1) * stride + kPartPad + jq);
-    const f32x4 hd = ws.ld4(src + (size_t)min(tid, nsplit - 1) * stride);
-    float mx = tid < nsplit ? hd.x : -INFINITY;
-    for (int s = tid + kThreads; s < nsplit; s += kThreads) mx = fmaxf(mx, ws.ld1(src + (size_t)s * stride));
+    dma_rows<kCoherent>(ws.r, hdr, 1, nsplit, 0, [&](int, int c) { return ws.off(src + (size_t)c * stride); });
+    dma_rows<kCoherent>(ws.r, val, 1, nsplit * nv, 0, [&](int, int u) {
+      const int r = u / nv;
+      return ws.off(src + (size_t)r * stride + kPartPad + j0 + 4 * (u - r * nv));
+    });
+    wait_vm();
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int s = tid; s < nsplit; s += kThreads) mx = fmaxf(mx, hdr[4 * s]);
     mx = wave_max(mx, 64);
     if (lane == 0) misc[wave] = mx;
     __syncthreads();
     float M = misc[0];
     for (int i = 1; i < kWaves; ++i) M = fmaxf(M, misc[i]);
     float lsum = 0.f;
-    if (tid < nsplit) {
-      const float ws_ = hd.x == -INFINITY ? 0.f : __expf(hd.x - M);
-      w[tid] = ws_;
-      lsum += ws_ * hd.y;
-    }
-    for (int s = tid + kThreads; s < nsplit; s += kThreads) {
-      const f32x4 h2 = ws.ld4(src + (size_t)s * stride);
-      const float ws_ = h2.x == -INFINITY ? 0.f : __expf(h2.x - M);
+    for (int s = tid; s < nsplit; s += kThreads) {
+      const float ws_ = hdr[4 * s] == -INFINITY ? 0.f : __expf(hdr[4 * s] - M);
       w[s] = ws_;
-      lsum += ws_ * h2.y;
+      lsum += ws_ * hdr[4 * s + 1];
     }
     lsum = wave_sum(lsum, 64);
     if (lane == 0) misc[kWaves + wave] = lsum;
@@ -1107,15 +1125,8 @@ __device__ __forceinline__ void merge_phase(const Params& p, const Ws& ws, int h
     float L = 0.f;
     for (int i = 0; i < kWaves; ++i) L += misc[kWaves + i];
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int s = sl + 64 * u;
-      if (u * 64 < nsplit && s < nsplit) acc += w[s] * v[u];
-    }
-    for (int sb = NS * 64; sb < nsplit; sb += 64) {
-      const int s = sb + sl;
-      if (s < nsplit) acc += w[s] * ws.ld4(src + (size_t)s * stride + kPartPad + jq);
-    }
+    if (qd < nv)
+      for (int s = sl; s < nsplit; s += 64) acc += w[s] * *reinterpret_cast<const f32x4*>(val + 4 * nv * s + 4 * qd);
     for (int o = 8; o < 64; o <<= 1) {
       acc.x += __shfl_xor(acc.x, o, 64);
       acc.y += __shfl_xor(acc.y, o, 64);
@@ -1124,11 +1135,10 @@ __device__ __forceinline__ void merge_phase(const Params& p, const Ws& ws, int h
     }
     if (lane < 8) red[wave * 8 + lane] = acc;
     __syncthreads();
-    if (tid < 8 && j0 + 4 * tid < dim) {
+    if (tid < nv) {
       f32x4 t = red[tid];
       for (int i = 1; i < kWaves; ++i) t += red[i * 8 + tid];
-      const float il = 1.0f / L;
-      ws.st4(out + (size_t)mh * dim + j0 + 4 * tid, t * il);
+      ws.st4(out + (size_t)mh * dim + j0 + 4 * tid, t * (1.0f / L));
     }
   }
 }
