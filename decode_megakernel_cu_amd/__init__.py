@@ -25,7 +25,7 @@ KIND_ID = {k: i for i, k in enumerate(KINDS)}
 TRACE_STAMPS = 16  # MK_TRACE_STAMPS
 
 EXPORTS = ["mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_poll", "mk_set_trace",
-           "mk_read_trace", "mk_last_error", "mk_destroy"]
+           "mk_read_trace", "mk_set_matrix_cores", "mk_last_error", "mk_destroy"]
 
 
 class MkConfig(ctypes.Structure):
@@ -67,9 +67,10 @@ def _load():
     L.mk_destroy.argtypes = [vp]
     L.mk_destroy.restype = None
     L.mk_set_trace.argtypes = [vp, i32]
+    L.mk_set_matrix_cores.argtypes = [vp, i32]
     L.mk_read_trace.argtypes = [vp, vp, u64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     for f in ("mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_poll", "mk_set_trace",
-              "mk_read_trace"):
+              "mk_read_trace", "mk_set_matrix_cores"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -132,6 +133,10 @@ def tensor_desc(kind: str, layer: int, expert: int, src: int, nbytes: int, on_de
 
 def mk_set_trace(ctx, enable: bool) -> None:
     _check(lib.mk_set_trace(ctx, int(enable)))
+
+
+def mk_set_matrix_cores(ctx, enable: bool) -> None:
+    _check(lib.mk_set_matrix_cores(ctx, int(enable)))
 
 
 def mk_read_trace(ctx):

@@ -17,7 +17,7 @@
 
 namespace mk {
 size_t kernel_lds_bytes();
-hipError_t launch_decode(const Params& p, int nblocks, hipStream_t stream);
+hipError_t launch_decode(const Params& p, int nblocks, bool matrix_cores, hipStream_t stream);
 hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd, int kvl, hipStream_t stream);
 hipError_t occupancy(int* blocks_per_cu);
 int max_grid();
@@ -136,17 +136,68 @@ bool step_fits(const mk_config& c, int M, int nb) {
   return good;
 }
 
+// Whether the matrix-core GEMV executor can run every GEMV phase of this model: row lengths in
+// whole 32-column units, per-head rows in whole groups of 16 inside one head.
+bool mfma_shapes(const mk_config& c) {
+  const long long H = c.hidden, F = c.ffn, SF = c.shared_ffn, nh = c.n_heads;
+  bool ok = H % 32 == 0 && F % 32 == 0 && SF % 32 == 0;
+  if (c.attn_kind == MK_ATTN_GQA) {
+    ok = ok && (nh * c.head_dim) % 32 == 0;
+  } else {
+    ok = ok && c.q_lora % 32 == 0 && c.nope_dim % 32 == 0 && c.kv_lora % 32 == 0 && (nh * c.v_dim) % 32 == 0 &&
+         c.kv_lora % 16 == 0 && c.v_dim % 16 == 0;
+    if (c.attn_kind == MK_ATTN_HYBRID) ok = ok && (nh * c.kda_dv) % 32 == 0;
+  }
+  return ok;
+}
+
+// The same fit for the matrix-core executor: besides the accumulators, one 16x16 partial slot per
+// accumulator tile plus one per wave; staged rows at a stride of (slab + 4) floats, at least one
+// 32-column slab of them, and the whole window of per-head phases.
+bool step_fits_mfma(const mk_config& c, int M, int nb) {
+  if (nb < 1) return true;
+  const long long MM = M <= 8 ? 8 : 16;
+  auto cap_of = [&](long long nloc, long long nat) {
+    return (long long)kLdsFloats - nloc * 3 * MM - (nat + kWaves) * 256 - 8;
+  };
+  // pairs: weight-row kinds per task; down: the down projection (one accumulator tile per group)
+  auto ok = [&](long long ntasks, long long rows, long long pairs, bool norm, bool down = false) {
+    const long long nloc = (ntasks + nb - 1) / nb, ngrp = (nloc + 15) / 16;
+    return cap_of(nloc, down ? ngrp : ngrp * pairs) >= rows * (32 + 4) + (norm ? 16 : 0);
+  };
+  auto ok_off = [&](long long ntasks, long long rph, long long seg) {
+    const long long gmax = (ntasks / 16 + nb - 1) / nb, nloc = 16 * gmax;
+    const long long window = ((nloc + rph - 1) / rph + 1) * seg;
+    return cap_of(nloc, gmax) >= M * (window + 4);
+  };
+  const long long E = c.n_experts, F = c.ffn, SF = c.shared_ffn, H = c.hidden, nh = c.n_heads;
+  const long long np = (long long)M * c.top_k;
+  bool good = ok(c.vocab, M, 1, true) && ok(E + SF, M, SF > 0 ? 2 : 1, true) &&
+              ok(std::min(E, np) * F, M, 2, true) && ok(H, np + M, 1, false, true) && ok(H, M, 1, false);
+  if (c.attn_kind == MK_ATTN_GQA) {
+    good = good && ok(nh * c.head_dim + 2LL * c.n_kv_heads * c.head_dim, M, 1, true);
+  } else {
+    const long long lat = c.kv_lora + c.rope_dim, qd = c.nope_dim + c.rope_dim;
+    good = good && ok(c.q_lora + lat, M, 1, true) && ok(nh * qd, M, 1, true) &&
+           ok_off(nh * c.kv_lora, c.kv_lora, c.nope_dim) && ok_off(nh * c.v_dim, c.v_dim, c.kv_lora);
+    if (c.attn_kind == MK_ATTN_HYBRID) good = good && ok(2 * nh * c.kda_dk + nh * c.kda_dv, M, 1, true);
+  }
+  return good;
+}
+
 Layout make_layout(const mk_config& c) {
   Layout Lt;
   const uint64_t H = c.hidden, V = c.vocab, E = c.n_experts, F = c.ffn, SF = c.shared_ffn;
   uint64_t off = align_up(sizeof(LayerDev) * (uint64_t)c.n_layers);
-  auto put = [&](int kind, int layer, int expert, uint64_t bytes, int repack = 0) {
+  // packed: the next tensor follows without padding (the experts of one pool block are indexed as
+  // one [E][rows][cols] array)
+  auto put = [&](int kind, int layer, int expert, uint64_t bytes, int repack = 0, bool packed = false) {
     Slot s;
     s.off = off;
     s.bytes = bytes;
     s.repack = repack;
     Lt.tensors[Key(kind, layer, expert)] = s;
-    off = align_up(off + bytes);
+    off = packed ? off + bytes : align_up(off + bytes);
     return s.off;
   };
   put(MK_W_EMBED, -1, -1, V * H * 2);
@@ -201,11 +252,11 @@ Layout make_layout(const mk_config& c) {
   std::vector<uint64_t> gbase(nslot), ubase(nslot), dbase(nslot);
   for (int s = 0; s < nslot; ++s) {
     gbase[s] = off;
-    for (int e = 0; e < c.n_experts; ++e) put(MK_W_EXP_GATE, s, e, F * H * 2);
+    for (int e = 0; e < c.n_experts; ++e) put(MK_W_EXP_GATE, s, e, F * H * 2, 0, e + 1 < c.n_experts);
     ubase[s] = off;
-    for (int e = 0; e < c.n_experts; ++e) put(MK_W_EXP_UP, s, e, F * H * 2);
+    for (int e = 0; e < c.n_experts; ++e) put(MK_W_EXP_UP, s, e, F * H * 2, 0, e + 1 < c.n_experts);
     dbase[s] = off;
-    for (int e = 0; e < c.n_experts; ++e) put(MK_W_EXP_DOWN, s, e, H * F * 2);
+    for (int e = 0; e < c.n_experts; ++e) put(MK_W_EXP_DOWN, s, e, H * F * 2, 0, e + 1 < c.n_experts);
   }
   for (int l = 0; l < c.n_layers; ++l) {
     LayerDev& d = Lt.layers[l];
@@ -288,6 +339,7 @@ struct mk_ctx {
   uint64_t watchdog_ticks;
   bool poisoned;
   bool trace;
+  bool matrix_cores;  // GEMV phases of steps with 5..16 rows on the matrix cores when shapes allow
   int last_barriers;
   std::vector<uint8_t> loaded;  // per tensor slot, in map order
   std::map<Key, size_t> index;
@@ -336,6 +388,7 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
   c->launches = 0;
   c->poisoned = false;
   c->trace = false;
+  c->matrix_cores = true;
   c->last_barriers = 0;
   c->n_loaded = 0;
   size_t i = 0;
@@ -441,7 +494,8 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   if (!d_tokens || !d_logits || !d_kv) return fail(MK_E_INVAL, "tokens, kv and logits must be non-NULL");
   if (g.attn_kind == MK_ATTN_HYBRID && !d_kda_state) return fail(MK_E_INVAL, "hybrid model needs the delta-rule state");
   const int M = B * T;
-  if (!step_fits(g, M, c->nblocks))
+  const bool mf = c->matrix_cores && M >= 5 && mfma_shapes(g) && step_fits_mfma(g, M, c->nblocks);
+  if (!mf && !step_fits(g, M, c->nblocks))
     return fail(MK_E_UNSUPPORTED, "a phase of this step does not fit the workgroup's LDS");
   if (c->n_loaded != c->loaded.size())
     return fail(MK_E_STATE, "%zu of %zu weight tensors loaded", c->n_loaded, c->loaded.size());
@@ -484,7 +538,7 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   if ((uint64_t)M * nh * p.nsplit * (dmax + kPartPad) > w.part_floats)
     return fail(MK_E_UNSUPPORTED, "attention partials exceed the workspace");
   hipError_t e = hipSetDevice(c->device);
-  if (e == hipSuccess) e = launch_decode(p, c->nblocks, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = launch_decode(p, c->nblocks, mf, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MK_E_HIP, "launch failed: %s", hipGetErrorString(e));
   c->launches++;
   int nb = 1;
@@ -500,6 +554,13 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
 int mk_set_trace(mk_ctx* c, int enable) {
   if (!c) return fail(MK_E_INVAL, "context is NULL");
   c->trace = enable != 0;
+  g_err.clear();
+  return MK_OK;
+}
+
+int mk_set_matrix_cores(mk_ctx* c, int enable) {
+  if (!c) return fail(MK_E_INVAL, "context is NULL");
+  c->matrix_cores = enable != 0;
   g_err.clear();
   return MK_OK;
 }

@@ -80,6 +80,19 @@ __device__ __forceinline__ void unpack8(const uint4& w, float (&f)[8]) {
   f[4] = lo_bf(w.z); f[5] = hi_bf(w.z); f[6] = lo_bf(w.w); f[7] = hi_bf(w.w);
 }
 
+// bf16 vectors for the matrix cores
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) { return as_bf16x8(*reinterpret_cast<const u32x4*>(p)); }
+// two floats as bf16 high parts (packed) and the bf16 of what the high parts leave (low parts):
+// x = hi + lo to about 16 significant bits
+__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
+  const uint16_t l0 = f2bf(x0 - bf2f(h0)), l1 = f2bf(x1 - bf2f(h1));
+  hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  lo = (uint32_t)l0 | ((uint32_t)l1 << 16);
+}
+
 // Weights and cache rows are read once per step: non-temporal loads keep them from evicting the
 // kernel's code and the activations from L2.
 __device__ __forceinline__ uint4 ldw(const uint16_t* p) {
@@ -181,6 +194,15 @@ __device__ __forceinline__ void dma_rows(Rsrc r_, float* dst, int R, int U, int 
   for (int b = wave_id(); b < nb; b += kWaves) {
     const int r = b / bpr, c0 = (b - r * bpr) << 6, c = c0 + lane;
     if (c < U) __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, (LdsPtr)(dst + r * DS + 4 * c0), 16, off(r, c), 0, 0, AUX);
+  }
+}
+// the same with row r landing at dst + at(r) (floats)
+template <int AUX, class At, class Off>
+__device__ __forceinline__ void dma_rows_at(Rsrc r_, float* dst, int R, int U, At at, Off off) {
+  const int bpr = (U + 63) >> 6, nb = R * bpr, lane = lane_id();
+  for (int b = wave_id(); b < nb; b += kWaves) {
+    const int r = b / bpr, c0 = (b - r * bpr) << 6, c = c0 + lane;
+    if (c < U) __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, (LdsPtr)(dst + at(r) + 4 * c0), 16, off(r, c), 0, 0, AUX);
   }
 }
 // the same with 4-byte units (lane l writes the block's base + 4 l)
@@ -314,6 +336,9 @@ struct RowRef {
 };
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+// by value (a reference-returning min keeps its operands in memory)
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 __device__ __forceinline__ int pow2ceil(int x) {
   int p = 1;
   while (p < x) p <<= 1;
@@ -467,29 +492,58 @@ struct Gemv {
     __syncthreads();
   }
 
-  // Issue the staging of input columns [k0, k0+ks) into dst (LDS) as rows of ks floats, and of
-  // the slab's norm gain (bf16) into gl. Direct memory-to-LDS copies; the caller waits.
-  __device__ __forceinline__ void stage_issue(const Ws& ws, float* dst, uint16_t* gl, int k0, int ks) const {
+  // Issue the staging of input columns [k0, k0+ks) into dst (LDS) as rows of ks floats at a row
+  // stride of DS floats, and of the slab's norm gain (bf16) into gl. Direct memory-to-LDS copies;
+  // the caller waits.
+  __device__ __forceinline__ void stage_issue(const Ws& ws, float* dst, uint16_t* gl, int k0, int ks, int DS) const {
     if (stage == S_DOWN) {  // expert activation rows, then shared activation rows
       const int ue = max(0, min(F - k0, ks)) >> 2, us = max(0, min(SF - k0, ks)) >> 2;
-      dma_rows<kCoherent>(ws.r, dst, np, ue, ks, [&](int r, int c) { return ws.off(src + (size_t)r * F + k0 + 4 * c); });
-      dma_rows<kCoherent>(ws.r, dst + np * ks, M, us, ks,
+      dma_rows<kCoherent>(ws.r, dst, np, ue, DS, [&](int r, int c) { return ws.off(src + (size_t)r * F + k0 + 4 * c); });
+      dma_rows<kCoherent>(ws.r, dst + np * DS, M, us, DS,
                [&](int r, int c) { return ws.off(src2 + (size_t)r * SF + k0 + 4 * c); });
       return;
     }
     if (stage == S_NOPE) {  // the nope parts of the window's heads, from rows [nh][qd]
       const int h0 = k0 / nd, nhw = ks / nd;
-      dma_rows<kCoherent>(ws.r, dst, M * nhw, nd >> 2, nd, [&](int r, int c) {
-        const int m = r / nhw;
-        return ws.off(src + (size_t)m * nh * qd + (h0 + r - m * nhw) * qd + 4 * c);
-      });
+      dma_rows_at<kCoherent>(
+          ws.r, dst, M * nhw, nd >> 2,
+          [&](int r) {
+            const int m = r / nhw;
+            return m * DS + (r - m * nhw) * nd;
+          },
+          [&](int r, int c) {
+            const int m = r / nhw;
+            return ws.off(src + (size_t)m * nh * qd + (h0 + r - m * nhw) * qd + 4 * c);
+          });
       return;
     }
-    dma_rows<kCoherent>(ws.r, dst, M, ks >> 2, ks, [&](int r, int c) { return ws.off(src + (size_t)r * ld + k0 + 4 * c); });
+    dma_rows<kCoherent>(ws.r, dst, M, ks >> 2, DS, [&](int r, int c) { return ws.off(src + (size_t)r * ld + k0 + 4 * c); });
     if (stage == S_NORM) {  // the gain of the slab, 8 bf16 per unit
       const Rsrc gr = make_rsrc(gain + k0, (uint32_t)ks * 2);
       dma_rows<0>(gr, reinterpret_cast<float*>(gl), 1, ks >> 3, 0, [&](int, int c) { return (uint32_t)c * 16; });
     }
+  }
+
+  // inv[m] from the staged rows (row stride DS) when they hold all K columns
+  template <int MM>
+  __device__ __forceinline__ void norm_stats(const float* dst, int ks, int DS, float* inv, float* red) const {
+    const int tid = tid_x();
+    for (int m = 0; m < M; ++m) {
+      float ss = 0.f;
+      for (int k = 4 * tid; k < ks; k += 4 * kThreads) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(dst + m * DS + k);
+        ss += dot4(v, v);
+      }
+      ss = wave_sum(ss, 64);
+      if (lane_id() == 0) red[m * kWaves + wave_id()] = ss;
+    }
+    __syncthreads();
+    if (tid < M) {
+      float t = 0.f;
+      for (int w = 0; w < kWaves; ++w) t += red[tid * kWaves + w];
+      inv[tid] = 1.0f / sqrtf(t / (float)K + eps);
+    }
+    __syncthreads();
   }
 
   // After the staged data has landed (waited and synchronised): S_NORM rows are scaled by their RMS
@@ -499,24 +553,7 @@ struct Gemv {
                                                float* red) const {
     if (stage != S_NORM) return;
     const int tid = tid_x();
-    if (one_slab) {
-      for (int m = 0; m < M; ++m) {
-        float ss = 0.f;
-        for (int k = 4 * tid; k < ks; k += 4 * kThreads) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(dst + m * ks + k);
-          ss += dot4(v, v);
-        }
-        ss = wave_sum(ss, 64);
-        if (lane_id() == 0) red[m * kWaves + wave_id()] = ss;
-      }
-      __syncthreads();
-      if (tid < M) {
-        float t = 0.f;
-        for (int w = 0; w < kWaves; ++w) t += red[tid * kWaves + w];
-        inv[tid] = 1.0f / sqrtf(t / (float)K + eps);
-      }
-      __syncthreads();
-    }
+    if (one_slab) norm_stats<MM>(dst, ks, ks, inv, red);
     for (int o = tid; o < (ks >> 3); o += kThreads) {
       float gf[8];
       unpack8(*reinterpret_cast<const uint4*>(gl + 8 * o), gf);
@@ -773,7 +810,7 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
     uint16_t* gl = reinterpret_cast<uint16_t*>(xin + (g.stage == S_DOWN ? g.np + g.M : g.M) * ks);
     if (!keep) {
       if (g.stage == S_NORM && !q.one_slab && sl == 0) g.row_inv<MM>(ws, inv, red);
-      g.stage_issue(ws, xin, gl, q.wbase + k0, ks);
+      g.stage_issue(ws, xin, gl, q.wbase + k0, ks, ks);
       if (resid && sl == 0)  // this workgroup's residual inputs, [token][task]
         dma_rows4<kCoherent>(ws.r, q.res, g.M, q.nloc, q.nloc,
                   [&](int m, int c) { return ws.off(g.out0 + (size_t)m * g.ldo0 + q.t0 + c); });
@@ -930,6 +967,389 @@ __device__ __forceinline__ void compute_route(const Params& p, const Ws& ws, int
     }
   }
   __syncthreads();
+}
+
+// ----------------------------------------------------------------------------------------------
+// Matrix-core GEMV executor (kernels built for several input rows per step)
+//
+// With eight or more input rows the vector executor above spends more issue slots on
+// multiply-adds and LDS reads than the weight stream allows; here the products run on the matrix
+// cores. Weight rows are taken 16 at a time: for each 32-column unit a lane loads 16 bytes of one
+// row (lane l: row l % 16, columns 8 (l / 16) .. +8 of the unit) -- the A operand of a
+// 16x16x32 bf16 multiply as it comes from memory -- and the B operand holds the same 32 columns of
+// up to 16 input rows. The inputs are staged in LDS as fp32 and then rewritten in place, each run
+// of 8 columns as its bf16 high parts followed by the bf16 of the remainders (x = hi + lo to about
+// 16 significant bits), so two multiplies per unit give the products of the bf16 weights with the
+// fp32 inputs, accumulated in fp32.
+//
+// A tile is one group of 16 output rows and one of its weight-row kinds (SwiGLU gate or up; for
+// the down projection, each routed expert and the shared expert). The tiles' units form one
+// sequence, cut into eight contiguous ranges, one per wave; a wave streams its range in elements
+// of up to kNC units within one tile through the same two register buffers as the vector executor
+// (an element's loads are issued two elements ahead, the first two before the phase's barrier),
+// and writes its partial 16x16 result of each tile (each output group, for the down projection)
+// to its own LDS slot. After a slab the slots of each tile are summed in wave order -- a fixed
+// order, so results do not depend on timing -- into the same per-task accumulators the vector
+// executor fills, and the same epilogues write the outputs.
+//
+// Shapes: every row length and slab width is a multiple of 32 columns, and per-head rows (G_OFF)
+// come in whole groups of 16 inside one head; the host launches this executor only then.
+// ----------------------------------------------------------------------------------------------
+struct MPlan {
+  int t0, nloc, wbase, Wst, KS, DS, nslab, ngrp, nat;
+  bool one_slab;
+  float* acc;    // [nloc][2][MM] task accumulators
+  float* res;    // [M][nloc] residual inputs
+  float* piece;  // [nat + kWaves][16 columns][16 rows] partial tiles, slot = acc tile + wave
+};
+
+// A slab's unit counts: per tile (nuk), or for the down projection per routed-expert tile (ne) and
+// for the shared-expert tile (ns), pg per group; U over all tiles of the workgroup.
+struct MGeo {
+  int k0, ks, nuk, ne, ns, pg, U;
+};
+
+__device__ __forceinline__ MGeo mgeo(const Gemv& g, const MPlan& q, int slab) {
+  MGeo e;
+  e.k0 = slab * q.KS;
+  e.ks = imin(q.KS, q.Wst - e.k0);
+  if (g.kind == G_DOWN) {
+    e.ne = imax(0, imin(g.F - e.k0, e.ks)) >> 5;
+    e.ns = g.SF > 0 ? imax(0, imin(g.SF - e.k0, e.ks)) >> 5 : 0;
+    e.pg = rfl(g.rt->nu) * e.ne + e.ns;
+    e.nuk = 0;
+    e.U = q.ngrp * e.pg;
+  } else {
+    int len = e.ks;
+    if (g.kind == G_OFF) len = g.seg;
+    e.nuk = len >> 5;
+    e.ne = e.ns = 0;
+    e.pg = g.pairs * e.nuk;
+    e.U = q.ngrp * e.pg;
+  }
+  return e;
+}
+
+// (values, not a conditional over fields: a selected field address keeps the struct in memory)
+__device__ __forceinline__ int tile_units(const Gemv& g, const MGeo& e, int j) {
+  if (g.kind != G_DOWN) return e.nuk;
+  int u = e.ns;
+  if (j % g.pairs < rfl(g.rt->nu)) u = e.ne;
+  return u;
+}
+// accumulator tile of tile j: the down projection sums all of a group's tiles into one
+__device__ __forceinline__ int acc_tile(const Gemv& g, int j) { return g.kind == G_DOWN ? j / g.pairs : j; }
+
+// first unit of wave w's range
+__device__ __forceinline__ int wave_start(const MGeo& e, int w) { return (w * e.U) / kWaves; }
+
+template <int MM>
+__device__ __forceinline__ MPlan mmake_plan(const Gemv& g, float* smem) {
+  MPlan q;
+  const unsigned gb = blockIdx.x, gn = gridDim.x;
+  const bool offs = g.kind == G_OFF;
+  int t1;
+  if (offs) {  // whole groups of 16 rows, so that a group never spans two heads
+    const unsigned ng = (unsigned)g.ntasks >> 4;
+    q.t0 = 16 * (int)(ng * gb / gn);
+    t1 = 16 * (int)(ng * (gb + 1) / gn);
+  } else {
+    const unsigned nt = (unsigned)g.ntasks;
+    q.t0 = (int)(nt * gb / gn);
+    t1 = (int)(nt * (gb + 1) / gn);
+  }
+  q.nloc = t1 - q.t0;
+  q.ngrp = (q.nloc + 15) >> 4;
+  q.nat = g.kind == G_DOWN ? q.ngrp : q.ngrp * g.pairs;
+  const int in_cap = (kLdsFloats - q.nloc * 3 * MM - (q.nat + kWaves) * 256) & ~7;
+  q.acc = smem + in_cap;
+  q.res = q.acc + q.nloc * 2 * MM;
+  q.piece = q.res + q.nloc * MM;
+  q.wbase = 0;
+  q.Wst = g.Wst;
+  if (offs && q.nloc > 0) {
+    q.wbase = (q.t0 / g.rph) * g.seg;
+    q.Wst = ((t1 - 1) / g.rph) * g.seg + g.seg - q.wbase;
+  }
+  const int rows = g.stage == S_DOWN ? g.np + g.M : g.M;
+  if (offs) {
+    q.KS = q.Wst;
+    q.nslab = 1;
+  } else {
+    // staged rows at a stride of KS + 4 floats, then (S_NORM) the slab's gain in bf16
+    int cap = ((2 * (in_cap - 4 * rows)) / (2 * rows + (g.stage == S_NORM ? 1 : 0))) & ~31;
+    if (cap < 32) cap = 32;
+    q.nslab = cdiv(q.Wst, cap);
+    q.KS = (cdiv(q.Wst, q.nslab) + 31) & ~31;  // balanced slabs
+  }
+  if (q.nloc == 0) q.nslab = 0;
+  q.DS = q.KS + 4;
+  q.one_slab = q.nslab == 1;
+  return q;
+}
+
+// Position in a wave's element stream (wave-uniform): slab, tile, first unit and unit count of the
+// element (n == 0: the padding element that keeps a slab's element count even), units left in the
+// wave's range of the slab, and the parity of the elements so far in the slab.
+struct MCur {
+  int slab, j, us, n, rem, cnt;
+};
+
+// (The cursor functions take and return cursors by value: stores to different fields of a
+// referenced cursor on different paths would be merged into one store through a selected address,
+// and the cursor would then live in scratch memory.)
+__device__ __forceinline__ MCur mcur_slab(const Gemv& g, const MPlan& q, int slab) {
+  const int w = wave_id();
+  MCur c;
+  for (; slab < q.nslab; ++slab) {
+    const MGeo e = mgeo(g, q, slab);
+    const int s = wave_start(e, w), t = wave_start(e, w + 1);
+    if (t > s) {
+      int j, us;
+      if (g.kind == G_DOWN) {
+        const int nu = rfl(g.rt->nu), gi = s / e.pg, r = s - gi * e.pg, nue = nu * e.ne;
+        const int which = r < nue ? r / e.ne : nu;
+        us = r - which * e.ne;
+        j = gi * g.pairs + which;
+      } else {
+        j = s / e.nuk;
+        us = s - j * e.nuk;
+      }
+      c.slab = slab;
+      c.j = j;
+      c.us = us;
+      c.rem = t - s;
+      c.cnt = 0;
+      c.n = imin(imin(kNC, tile_units(g, e, j) - us), t - s);
+      return c;
+    }
+  }
+  c.slab = q.nslab;
+  c.j = c.us = c.n = c.rem = c.cnt = 0;
+  return c;
+}
+
+__device__ __forceinline__ MCur madvance(const Gemv& g, const MPlan& q, const MCur& c0) {
+  const int slab = c0.slab, n = c0.n;
+  if (slab >= q.nslab) return c0;
+  if (n == 0) return mcur_slab(g, q, slab + 1);  // after the padding element
+  const int rem = c0.rem - n, cnt = c0.cnt ^ 1;
+  if (rem == 0) {
+    if (cnt == 0) return mcur_slab(g, q, slab + 1);
+    MCur c;  // the padding element keeps the slab's element count even
+    c.slab = slab;
+    c.j = c0.j;
+    c.us = c0.us;
+    c.n = 0;
+    c.rem = 0;
+    c.cnt = 0;
+    return c;
+  }
+  const MGeo e = mgeo(g, q, slab);
+  int j = c0.j, us = c0.us + n;
+  if (us == tile_units(g, e, j)) {
+    us = 0;
+    do ++j;
+    while (tile_units(g, e, j) == 0);
+  }
+  MCur c;
+  c.slab = slab;
+  c.j = j;
+  c.us = us;
+  c.n = imin(imin(kNC, tile_units(g, e, j) - us), rem);
+  c.rem = rem;
+  c.cnt = cnt;
+  return c;
+}
+
+// Issue the loads of element c into b: lane l reads row l % 16 of the tile's group at columns
+// 8 (l / 16) .. +8 of each unit (rows the workgroup does not own, and kinds a row lacks, read a
+// valid dummy address; their results are never used).
+__device__ __forceinline__ void mload_element(const Gemv& g, const MPlan& q, const MCur& c, RowBuf& b) {
+  const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
+  const uint16_t* w = g.safe;
+  bool ok = false;
+  if (c.slab < q.nslab && c.n > 0) {
+    const int gi = c.j / g.pairs, which = c.j - gi * g.pairs, i = gi * 16 + r;
+    if (i < q.nloc) {
+      const RowRef rr = g.row(q.t0 + i, which);
+      if (rr.w) {
+        w = rr.w + c.slab * q.KS + 32 * c.us + 8 * kq;
+        ok = true;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kNC; ++u) b.v[u] = ldw(ok && u < c.n ? w + 32 * u : g.safe);
+}
+
+__device__ __forceinline__ void mgemv_preload(const Gemv& g, const MPlan& q, RowBuf& b0, RowBuf& b1) {
+  MCur c = mcur_slab(g, q, 0);
+  mload_element(g, q, c, b0);
+  c = madvance(g, q, c);
+  mload_element(g, q, c, b1);
+}
+
+// Consume the element at cc from b (its slab is staged in xs), then reuse b for the element at pc
+// (two ahead); a partial tile goes to its slot when the next element belongs to another.
+__device__ __forceinline__ void mstep(const Gemv& g, const MPlan& q, MCur& cc, MCur& pc, const float* xs, RowBuf& b,
+                                      f32x4& dt) {
+  const int lane = lane_id(), m = lane & 15, kq = lane >> 4;
+  if (cc.n > 0) {
+    const int gi = cc.j / g.pairs, which = cc.j - gi * g.pairs;
+    int brow = imin(m, g.M - 1);  // columns past the last input row repeat it; their results are unused
+    uint32_t keep = ~0u;
+    int col = 32 * cc.us + 8 * kq;
+    if (g.kind == G_DOWN) {
+      const int nu = rfl(g.rt->nu);
+      if (which < nu) {  // this expert's (token, weight) pair of the column's token, if any
+        const int s0 = rfl(g.rt->ustart[which]), s1 = rfl(g.rt->ustart[which + 1]);
+        bool has = false;
+        int ps = 0;
+        for (int s = s0; s < s1; ++s) {
+          if (g.rt->ptok[s] == m) {
+            ps = s;
+            has = true;
+          }
+        }
+        brow = ps;
+        keep = has ? ~0u : 0u;
+      } else {
+        brow += g.np;
+      }
+    } else if (g.kind == G_OFF) {
+      col += ((q.t0 + 16 * gi) / g.rph) * g.seg - q.wbase;
+    }
+    const float* xp = xs + brow * q.DS + col;
+#pragma unroll
+    for (int u = 0; u < kNC; ++u) {
+      if (u < cc.n) {
+        const u32x4 h = *reinterpret_cast<const u32x4*>(xp + 32 * u) & keep;
+        const u32x4 l = *reinterpret_cast<const u32x4*>(xp + 32 * u + 4) & keep;
+        const bf16x8 a = as_bf16x8(u32x4{b.v[u].x, b.v[u].y, b.v[u].z, b.v[u].w});
+        dt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(h), dt, 0, 0, 0);
+        dt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(l), dt, 0, 0, 0);
+      }
+    }
+  }
+  mload_element(g, q, pc, b);
+  const MCur old = cc;
+  cc = madvance(g, q, cc);
+  pc = madvance(g, q, pc);
+  if (old.n > 0 && (cc.slab != old.slab || cc.n == 0 || acc_tile(g, cc.j) != acc_tile(g, old.j))) {
+    // lane l holds column l % 16, rows 4 (l / 16) .. +4 of the tile
+    f32x4* slot = reinterpret_cast<f32x4*>(q.piece + (size_t)(acc_tile(g, old.j) + wave_id()) * 256 + m * 16 + 4 * kq);
+    *slot = dt;
+    dt = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Staged rows to bf16 high/low parts in place, after the norm scaling (S_NORM) or the router
+// weight of each expert pair row (S_DOWN).
+__device__ __forceinline__ void mconvert(const Gemv& g, float* xs, const uint16_t* gl, int ks, int DS,
+                                         const float* inv) {
+  const int nco = ks >> 3, nr = g.stage == S_DOWN ? g.np + g.M : g.M;
+  for (int e = tid_x(); e < nr * nco; e += kThreads) {
+    const int r = e / nco, o = e - r * nco;
+    f32x4* p = reinterpret_cast<f32x4*>(xs + r * DS + 8 * o);
+    f32x4 a = p[0], b = p[1];
+    if (g.stage == S_NORM) {
+      float gf[8];
+      unpack8(*reinterpret_cast<const uint4*>(gl + 8 * o), gf);
+      const float s = inv[r];
+      a.x *= s * gf[0]; a.y *= s * gf[1]; a.z *= s * gf[2]; a.w *= s * gf[3];
+      b.x *= s * gf[4]; b.y *= s * gf[5]; b.z *= s * gf[6]; b.w *= s * gf[7];
+    } else if (g.stage == S_DOWN && r < g.np) {
+      const float s = g.rt->pw[r];
+      a *= s;
+      b *= s;
+    }
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    split_bf16(a.x, a.y, h0, l0);
+    split_bf16(a.z, a.w, h1, l1);
+    split_bf16(b.x, b.y, h2, l2);
+    split_bf16(b.z, b.w, h3, l3);
+    p[0] = __builtin_bit_cast(f32x4, u32x4{h0, h1, h2, h3});
+    p[1] = __builtin_bit_cast(f32x4, u32x4{l0, l1, l2, l3});
+  }
+}
+
+// Sum each tile's wave slots (in wave order) into the task accumulators; G_EXP keeps, per task,
+// the columns of its expert's tokens in pair order.
+template <int MM>
+__device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGeo& e, bool first) {
+  const int na = g.kind == G_DOWN ? 1 : g.pairs;
+  const int n = na * MM * q.nloc;
+  for (int x = tid_x(); x < n; x += kThreads) {
+    const int ak = x / q.nloc, i = x - ak * q.nloc, a = ak / MM, k = ak - a * MM;
+    int col = k;
+    if (g.kind == G_EXP) {
+      const int u = (q.t0 + i) / g.F, s0 = g.rt->ustart[u];
+      if (k >= g.rt->ustart[u + 1] - s0) continue;
+      col = g.rt->ptok[s0 + k];
+    } else if (k >= g.M) {
+      continue;
+    }
+    const int gi = i >> 4, r = i & 15;
+    const int at = g.kind == G_DOWN ? gi : gi * g.pairs + a;
+    int len = e.nuk;
+    if (g.kind == G_DOWN) len = e.pg;
+    const int u0 = (g.kind == G_DOWN ? gi : at) * len, u1 = u0 + len;
+    float v = 0.f;
+    for (int w = 0; w < kWaves; ++w) {
+      if (wave_start(e, w) < u1 && wave_start(e, w + 1) > u0) v += q.piece[(size_t)(at + w) * 256 + col * 16 + r];
+    }
+    float* ac = q.acc + (size_t)i * 2 * MM + a * MM + k;
+    *ac = first ? v : *ac + v;
+  }
+}
+
+// Returns true when the LDS input buffer ends the phase holding the whole normalised input (in
+// the split bf16 form this executor reads).
+template <int MM>
+__device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const Ws& ws, float* smem, float* inv,
+                                            float* red, RowBuf& b0, RowBuf& b1, bool keep_in, uint64_t* trace) {
+  float* xs = smem;
+  const int tid = tid_x();
+  const bool keep = keep_in && q.one_slab;
+  const bool resid = g.kind == G_RESID || g.kind == G_DOWN;
+  const int rows = g.stage == S_DOWN ? g.np + g.M : g.M;
+  MCur cc = mcur_slab(g, q, 0);
+  MCur pc = madvance(g, q, madvance(g, q, cc));
+  f32x4 dt = {0.f, 0.f, 0.f, 0.f};
+  if (trace && tid == 0) gp(trace)[4] = wall_clock64();
+  for (int sl = 0; sl < q.nslab; ++sl) {
+    const MGeo e = mgeo(g, q, sl);
+    __syncthreads();
+    uint16_t* gl = reinterpret_cast<uint16_t*>(xs + rows * q.DS);
+    if (!keep) {
+      if (g.stage == S_NORM && !q.one_slab && sl == 0) g.row_inv<MM>(ws, inv, red);
+      g.stage_issue(ws, xs, gl, q.wbase + e.k0, e.ks, q.DS);
+      if (resid && sl == 0)
+        dma_rows4<kCoherent>(ws.r, q.res, g.M, q.nloc, q.nloc,
+                             [&](int m, int c) { return ws.off(g.out0 + (size_t)m * g.ldo0 + q.t0 + c); });
+      wait_vm();
+      __syncthreads();
+      if (g.stage == S_NORM && q.one_slab) g.norm_stats<MM>(xs, e.ks, q.DS, inv, red);
+      mconvert(g, xs, gl, e.ks, q.DS, inv);
+    }
+    __syncthreads();
+    if (trace && sl == 0 && tid == 0) gp(trace)[2] = wall_clock64();
+    while (cc.slab == sl) {
+      mstep(g, q, cc, pc, xs, b0, dt);
+      mstep(g, q, cc, pc, xs, b1, dt);
+    }
+    __syncthreads();
+    mreduce<MM>(g, q, e, sl == 0);
+  }
+  if (trace && tid == 0) gp(trace)[3] = wall_clock64();
+  __syncthreads();
+  for (int i = tid; i < q.nloc; i += kThreads) {
+    const float* ac = q.acc + (size_t)i * 2 * MM;
+    g.epilogue(q.t0 + i, ac, ac + MM, q.res + i, q.nloc);
+  }
+  if (trace && tid == 0) gp(trace)[5] = wall_clock64();
+  return q.one_slab && g.stage == S_NORM;
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -1141,19 +1561,6 @@ __device__ __forceinline__ void merge_phase(const Params& p, const Ws& ws, int h
       ws.st4(out + (size_t)mh * dim + j0 + 4 * tid, t * (1.0f / L));
     }
   }
-}
-
-// bf16 vectors for the matrix cores
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) { return as_bf16x8(*reinterpret_cast<const u32x4*>(p)); }
-// two floats as bf16 high parts (packed) and the bf16 of what the high parts leave (low parts):
-// x = hi + lo to about 16 significant bits
-__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
-  const uint16_t l0 = f2bf(x0 - bf2f(h0)), l1 = f2bf(x1 - bf2f(h1));
-  hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
-  lo = (uint32_t)l0 | ((uint32_t)l1 << 16);
 }
 
 // MLA split-KV partials over the latent cache. Task (b, s) covers positions [s*C, s*C + C) of
@@ -1744,7 +2151,17 @@ __device__ __forceinline__ void fetch_layer(const Params& p, LayerDev* lyd, int 
     if (!barrier_finish(&sm.abort)) return;           \
   } while (0)
 
-template <int MM>
+template <bool MF>
+struct PlanOf {
+  typedef Plan type;
+};
+template <>
+struct PlanOf<true> {
+  typedef MPlan type;
+};
+
+// MM: input rows the kernel is built for (at least M); MF: GEMV phases on the matrix cores
+template <int MM, bool MF>
 __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   __shared__ Smem sm;
   // the parameters live in LDS: read where needed instead of pinning ~100 scalar registers
@@ -1793,11 +2210,10 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   bool resident = false;  // the LDS input buffer holds this layer's normalised MoE input
   for (int l = 0; l <= p.L; ++l) {
     const LayerDev* ly = &sm.lyd[l & 1];
-    if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
     const int nph = (l == p.L) ? 1 : attn_phases(ly->kind) + 3;
     for (int i = 0; i < nph; ++i) {
       Gemv g{};
-      Plan q{};
+      typename PlanOf<MF>::type q{};
       RowBuf b0, b1;  // per phase: dead outside GEMV phases
       // Arrive at the barrier before this phase, then prepare the phase while the others arrive:
       // its descriptor, its plan and (for GEMV phases) the loads of its first weight rows (on the
@@ -1823,9 +2239,15 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         }
       }
       if (type == PT_GEMV || type == PT_EXPERT) {
-        q = make_plan<MM>(g, sm.buf);
-        if (trec && tid_x() == 0) gp(trec)[11] = wall_clock64();
-        gemv_preload(g, q, b0, b1);
+        if constexpr (MF) {
+          q = mmake_plan<MM>(g, sm.buf);
+          if (trec && tid_x() == 0) gp(trec)[11] = wall_clock64();
+          mgemv_preload(g, q, b0, b1);
+        } else {
+          q = make_plan<MM>(g, sm.buf);
+          if (trec && tid_x() == 0) gp(trec)[11] = wall_clock64();
+          gemv_preload(g, q, b0, b1);
+        }
       }
       if (early) {
         if (trec && tid_x() == 0) gp(trec)[9] = wall_clock64();
@@ -1837,14 +2259,23 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         case PT_GEMV:
         case PT_EXPERT: {
           const bool keep = type == PT_EXPERT && resident;
-          resident = gemv_phase<MM>(g, q, ws, sm.buf, sm.inv, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
+          if constexpr (MF)
+            resident = mgemv_phase<MM>(g, q, ws, sm.buf, sm.inv, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
+          else
+            resident = gemv_phase<MM>(g, q, ws, sm.buf, sm.inv, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
           break;
         }
+        // The next layer's table row is requested during the layer's attention phase, which waits
+        // for its own copies into LDS anyway: a copy into LDS still in flight when a GEMV phase
+        // starts would make every LDS read of its streaming loop wait for all loads (the compiler
+        // cannot tell the two LDS areas apart).
         case PT_ATTN_GQA:
+          if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
           gqa_attn_phase(p, ly, ws, sm.buf, sm.rope);
           resident = false;
           break;
         case PT_ATTN_MLA:
+          if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
           mla_attn_phase(p, ly, ws, sm.buf, sm.rope, trec);
           resident = false;
           break;
@@ -1853,6 +2284,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
           resident = false;
           break;
         case PT_KDA:
+          if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
           kda_phase(p, ly, ws);
           resident = false;
           break;
@@ -1889,21 +2321,29 @@ namespace mk {
 size_t kernel_lds_bytes() { return sizeof(Smem) + sizeof(Params); }
 int max_grid() { return kMaxGrid; }
 
-hipError_t launch_decode(const Params& p, int nblocks, hipStream_t stream) {
+hipError_t launch_decode(const Params& p, int nblocks, bool matrix_cores, hipStream_t stream) {
   const int mm = p.M <= 1 ? 1 : p.M <= 2 ? 2 : p.M <= 4 ? 4 : p.M <= 8 ? 8 : 16;
+  const dim3 grid(nblocks), block(kThreads);
 #ifdef MK_ONLY_MM1
   if (mm != 1) return hipErrorNotSupported;
-  hipLaunchKernelGGL(mk_decode_kernel<1>, dim3(nblocks), dim3(kThreads), 0, stream, p);
+  (void)matrix_cores;
+  hipLaunchKernelGGL((mk_decode_kernel<1, false>), grid, block, 0, stream, p);
   return hipGetLastError();
-#endif
+#else
+  if (matrix_cores && mm >= 8) {
+    if (mm == 8) hipLaunchKernelGGL((mk_decode_kernel<8, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((mk_decode_kernel<16, true>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
   switch (mm) {
-    case 1: hipLaunchKernelGGL(mk_decode_kernel<1>, dim3(nblocks), dim3(kThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(mk_decode_kernel<2>, dim3(nblocks), dim3(kThreads), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(mk_decode_kernel<4>, dim3(nblocks), dim3(kThreads), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(mk_decode_kernel<8>, dim3(nblocks), dim3(kThreads), 0, stream, p); break;
-    default: hipLaunchKernelGGL(mk_decode_kernel<16>, dim3(nblocks), dim3(kThreads), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((mk_decode_kernel<1, false>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((mk_decode_kernel<2, false>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((mk_decode_kernel<4, false>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((mk_decode_kernel<8, false>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((mk_decode_kernel<16, false>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
+#endif
 }
 
 hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd, int kvl, hipStream_t stream) {
@@ -1913,9 +2353,14 @@ hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int n
 
 hipError_t occupancy(int* blocks_per_cu) {
 #ifdef MK_ONLY_MM1
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_decode_kernel<1>, kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_decode_kernel<1, false>, kThreads, 0);
+#else
+  int a = 0, b = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, mk_decode_kernel<16, false>, kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, mk_decode_kernel<16, true>, kThreads, 0);
+  *blocks_per_cu = a < b ? a : b;
+  return e;
 #endif
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_decode_kernel<16>, kThreads, 0);
 }
 
 }  // namespace mk

@@ -40,12 +40,14 @@ def teardown_module(_):
         _models.pop(k).close()
 
 
-def run_pair(cfg, spec, B, T, kv_len, step=0):
+def run_pair(cfg, spec, B, T, kv_len, step=0, matrix_cores=True):
     import oracle
 
-    print(f"[case] {cfg.name} L={cfg.n_layers} B={B} T={T} kv_len={kv_len} seed={spec.seed}", flush=True)
+    print(f"[case] {cfg.name} L={cfg.n_layers} B={B} T={T} kv_len={kv_len} seed={spec.seed} "
+          f"matrix_cores={matrix_cores}", flush=True)
     toks = synth.tokens(spec.seed, step, cfg.vocab, B, T)
     dm = device_model(cfg, spec)
+    dm.set_matrix_cores(matrix_cores)
     dm.fill_caches(B, kv_len)
     logits, route = dm.step(toks, kv_len)
     torch.cuda.synchronize()
@@ -122,8 +124,8 @@ def check_cache(cfg, dm, caches, init, B, T, kv_len):
             assert err < 1e-4, f"delta-rule state error {err:.3e}"
 
 
-def parity(cfg, spec, B, T, kv_len):
-    dm, got, route, ref, caches, init = run_pair(cfg, spec, B, T, kv_len)
+def parity(cfg, spec, B, T, kv_len, matrix_cores=True):
+    dm, got, route, ref, caches, init = run_pair(cfg, spec, B, T, kv_len, matrix_cores=matrix_cores)
     err = check_logits(got, ref)
     check_route(route, ref)
     check_cache(cfg, dm, caches, init, B, T, kv_len)
@@ -142,6 +144,21 @@ def test_tiny_batch1(seed):
 @pytest.mark.parametrize("B,T,kv_len", [(2, 3, 37), (4, 4, 0), (8, 2, 129), (1, 8, 5)])
 def test_tiny_shapes(B, T, kv_len):
     parity(synth.TINY, synth.Spec(seed=5), B, T, kv_len)
+
+
+@pytest.mark.parametrize("B,T,kv_len", [(8, 2, 129), (1, 8, 5)])
+def test_tiny_shapes_vector_units(B, T, kv_len):
+    # the vector-unit GEMV executor at 5..16 rows (the matrix cores are the default there)
+    parity(synth.TINY, synth.Spec(seed=5), B, T, kv_len, matrix_cores=False)
+
+
+# row lengths that are not whole 32-column units: 5..16 rows fall back to the vector units
+TINY_RAGGED = replace(synth.TINY, name="tiny-ragged", hidden=264, ffn=520, vocab=1000)
+
+
+@pytest.mark.parametrize("B,T,kv_len", [(8, 1, 40), (2, 4, 3)])
+def test_tiny_ragged_rows(B, T, kv_len):
+    parity(TINY_RAGGED, synth.Spec(seed=7), B, T, kv_len)
 
 
 def test_tiny_peaked_attention():
@@ -167,6 +184,10 @@ HYB_SMALL = replace(synth.K3_HYBRID, name="hybrid-4layer", n_layers=4, expert_po
 @pytest.mark.parametrize("B,T,kv_len", [(1, 1, 4096), (3, 2, 1000), (1, 7, 4096), (8, 1, 33)])
 def test_k3_two_layers(B, T, kv_len):
     parity(K3_SMALL, synth.Spec(seed=2), B, T, kv_len)
+
+
+def test_k3_two_layers_batch8_vector_units():
+    parity(K3_SMALL, synth.Spec(seed=2), 8, 1, 33, matrix_cores=False)
 
 
 def test_k3_two_layers_peaked_mla():
