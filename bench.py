@@ -276,6 +276,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--trace", action="store_true", help="print per-phase device timings of one step per batch")
+    ap.add_argument("--mfma-min-rows", type=int, default=None,
+                    help="token rows from which GEMV phases use the matrix cores (library default if omitted)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one elementwise copy of CALIB_BYTES (fp32 x*1 -> y) first: the counter calibration "
                          "kernel for the traffic figure")
@@ -300,6 +302,8 @@ def main():
     spec = synth.Spec(seed=args.seed)
     t0 = time.time()
     dm = DeviceModel(cfg, spec, device=0)
+    if args.mfma_min_rows is not None:
+        dm.set_matrix_cores(args.mfma_min_rows)
     batches = [int(b) for b in args.batches.split(",")]
     dm.fill_caches(max(batches), w.kv_len)
     print(f"# model loaded in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)

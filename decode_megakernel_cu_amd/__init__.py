@@ -135,8 +135,13 @@ def mk_set_trace(ctx, enable: bool) -> None:
     _check(lib.mk_set_trace(ctx, int(enable)))
 
 
-def mk_set_matrix_cores(ctx, enable: bool) -> None:
-    _check(lib.mk_set_matrix_cores(ctx, int(enable)))
+MK_MFMA_MIN_ROWS = 3  # MK_MFMA_MIN_ROWS
+MK_MAX_M = 16
+
+
+def mk_set_matrix_cores(ctx, min_rows: int) -> None:
+    """GEMV phases of steps with at least min_rows token rows on the matrix cores (> MK_MAX_M: never)."""
+    _check(lib.mk_set_matrix_cores(ctx, int(min_rows)))
 
 
 def mk_read_trace(ctx):

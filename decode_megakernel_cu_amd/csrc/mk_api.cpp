@@ -40,6 +40,7 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr uint64_t kAlign = 256;
+constexpr int kMfmaMinRows = MK_MFMA_MIN_ROWS;  // steps of 3..16 token rows on the matrix cores
 constexpr int kThreadsHost = kThreads;
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -110,28 +111,41 @@ int check_config(const mk_config* c) {
   return MK_OK;
 }
 
-// Whether every GEMV phase of a step with M token rows fits the LDS carve-up of the kernel: the
-// task accumulators of a workgroup's share (3 x MM floats per task) at the end of the buffer, the
-// staged input (at least 8 columns of each staged row, the whole window of per-head phases) before.
-bool step_fits(const mk_config& c, int M, int nb) {
+// Whether every GEMV phase of a step with M token rows fits the LDS carve-up of the kernel (mf: the
+// matrix-core executor): per workgroup share of nloc tasks, the task accumulators (3 x MM floats
+// per task) and one partial slot per accumulator tile plus one per wave (MM floats; a 16x16 tile
+// on the matrix cores, whose tiles are groups of 16 tasks) at the end of the buffer; before them
+// the staged input, at least one slab (8 columns; 32 on the matrix cores, rows padded by 4 floats)
+// of each staged row, or the whole window of per-head phases.
+bool step_fits(const mk_config& c, int M, int nb, bool mf) {
   if (nb < 1) return true;
   const long long MM = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
-  auto cap_of = [&](long long ntasks) { return (long long)kLdsFloats - (ntasks + nb - 1) / nb * 3 * MM; };
-  auto ok = [&](long long ntasks, long long rows) { return cap_of(ntasks) >= rows * 8; };
+  const long long pslot = mf ? 256 : MM, pad = mf ? 4 : 0, minw = mf ? 32 : 8;
+  auto cap_of = [&](long long nloc, long long nat) {
+    return (long long)kLdsFloats - nloc * 3 * MM - (nat + kWaves) * pslot - 8;
+  };
+  auto groups = [&](long long nloc) { return mf ? (nloc + 15) / 16 : nloc; };
+  // pairs: weight-row kinds per task; down: the down projection (one accumulator tile per group)
+  auto ok = [&](long long ntasks, long long rows, long long pairs, bool norm, bool down = false) {
+    const long long nloc = (ntasks + nb - 1) / nb, ng = groups(nloc);
+    return cap_of(nloc, down ? ng : ng * pairs) >= rows * (minw + pad) + (norm ? minw / 2 : 0);
+  };
   auto ok_off = [&](long long ntasks, long long rph, long long seg) {
-    const long long nloc = (ntasks + nb - 1) / nb, window = ((nloc + rph - 1) / rph + 1) * seg;
-    return cap_of(ntasks) >= window * M;
+    const long long nloc = mf ? 16 * ((ntasks / 16 + nb - 1) / nb) : (ntasks + nb - 1) / nb;
+    const long long window = ((nloc + rph - 1) / rph + 1) * seg;
+    return cap_of(nloc, groups(nloc)) >= M * (window + pad);
   };
   const long long E = c.n_experts, F = c.ffn, SF = c.shared_ffn, H = c.hidden, nh = c.n_heads;
   const long long np = (long long)M * c.top_k;
-  bool good = ok(c.vocab, M) && ok(H, M) && ok(E + SF, M) && ok(std::min(E, np) * F, M) && ok(H, np + M);
+  bool good = ok(c.vocab, M, 1, true) && ok(E + SF, M, SF > 0 ? 2 : 1, true) &&
+              ok(std::min(E, np) * F, M, 2, true) && ok(H, np + M, 1, false, true) && ok(H, M, 1, false);
   if (c.attn_kind == MK_ATTN_GQA) {
-    good = good && ok(nh * c.head_dim + 2LL * c.n_kv_heads * c.head_dim, M);
+    good = good && ok(nh * c.head_dim + 2LL * c.n_kv_heads * c.head_dim, M, 1, true);
   } else {
     const long long lat = c.kv_lora + c.rope_dim, qd = c.nope_dim + c.rope_dim;
-    good = good && ok(c.q_lora + lat, M) && ok(nh * qd, M) && ok_off(nh * c.kv_lora, c.kv_lora, c.nope_dim) &&
-           ok_off(nh * c.v_dim, c.v_dim, c.kv_lora);
-    if (c.attn_kind == MK_ATTN_HYBRID) good = good && ok(2 * nh * c.kda_dk + nh * c.kda_dv, M);
+    good = good && ok(c.q_lora + lat, M, 1, true) && ok(nh * qd, M, 1, true) &&
+           ok_off(nh * c.kv_lora, c.kv_lora, c.nope_dim) && ok_off(nh * c.v_dim, c.v_dim, c.kv_lora);
+    if (c.attn_kind == MK_ATTN_HYBRID) good = good && ok(2 * nh * c.kda_dk + nh * c.kda_dv, M, 1, true);
   }
   return good;
 }
@@ -149,40 +163,6 @@ bool mfma_shapes(const mk_config& c) {
     if (c.attn_kind == MK_ATTN_HYBRID) ok = ok && (nh * c.kda_dv) % 32 == 0;
   }
   return ok;
-}
-
-// The same fit for the matrix-core executor: besides the accumulators, one 16x16 partial slot per
-// accumulator tile plus one per wave; staged rows at a stride of (slab + 4) floats, at least one
-// 32-column slab of them, and the whole window of per-head phases.
-bool step_fits_mfma(const mk_config& c, int M, int nb) {
-  if (nb < 1) return true;
-  const long long MM = M <= 8 ? 8 : 16;
-  auto cap_of = [&](long long nloc, long long nat) {
-    return (long long)kLdsFloats - nloc * 3 * MM - (nat + kWaves) * 256 - 8;
-  };
-  // pairs: weight-row kinds per task; down: the down projection (one accumulator tile per group)
-  auto ok = [&](long long ntasks, long long rows, long long pairs, bool norm, bool down = false) {
-    const long long nloc = (ntasks + nb - 1) / nb, ngrp = (nloc + 15) / 16;
-    return cap_of(nloc, down ? ngrp : ngrp * pairs) >= rows * (32 + 4) + (norm ? 16 : 0);
-  };
-  auto ok_off = [&](long long ntasks, long long rph, long long seg) {
-    const long long gmax = (ntasks / 16 + nb - 1) / nb, nloc = 16 * gmax;
-    const long long window = ((nloc + rph - 1) / rph + 1) * seg;
-    return cap_of(nloc, gmax) >= M * (window + 4);
-  };
-  const long long E = c.n_experts, F = c.ffn, SF = c.shared_ffn, H = c.hidden, nh = c.n_heads;
-  const long long np = (long long)M * c.top_k;
-  bool good = ok(c.vocab, M, 1, true) && ok(E + SF, M, SF > 0 ? 2 : 1, true) &&
-              ok(std::min(E, np) * F, M, 2, true) && ok(H, np + M, 1, false, true) && ok(H, M, 1, false);
-  if (c.attn_kind == MK_ATTN_GQA) {
-    good = good && ok(nh * c.head_dim + 2LL * c.n_kv_heads * c.head_dim, M, 1, true);
-  } else {
-    const long long lat = c.kv_lora + c.rope_dim, qd = c.nope_dim + c.rope_dim;
-    good = good && ok(c.q_lora + lat, M, 1, true) && ok(nh * qd, M, 1, true) &&
-           ok_off(nh * c.kv_lora, c.kv_lora, c.nope_dim) && ok_off(nh * c.v_dim, c.v_dim, c.kv_lora);
-    if (c.attn_kind == MK_ATTN_HYBRID) good = good && ok(2 * nh * c.kda_dk + nh * c.kda_dv, M, 1, true);
-  }
-  return good;
 }
 
 Layout make_layout(const mk_config& c) {
@@ -339,7 +319,7 @@ struct mk_ctx {
   uint64_t watchdog_ticks;
   bool poisoned;
   bool trace;
-  bool matrix_cores;  // GEMV phases of steps with 5..16 rows on the matrix cores when shapes allow
+  int mfma_min_rows;  // GEMV phases of steps with at least this many rows on the matrix cores
   int last_barriers;
   std::vector<uint8_t> loaded;  // per tensor slot, in map order
   std::map<Key, size_t> index;
@@ -388,7 +368,7 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
   c->launches = 0;
   c->poisoned = false;
   c->trace = false;
-  c->matrix_cores = true;
+  c->mfma_min_rows = kMfmaMinRows;
   c->last_barriers = 0;
   c->n_loaded = 0;
   size_t i = 0;
@@ -494,8 +474,8 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   if (!d_tokens || !d_logits || !d_kv) return fail(MK_E_INVAL, "tokens, kv and logits must be non-NULL");
   if (g.attn_kind == MK_ATTN_HYBRID && !d_kda_state) return fail(MK_E_INVAL, "hybrid model needs the delta-rule state");
   const int M = B * T;
-  const bool mf = c->matrix_cores && M >= 5 && mfma_shapes(g) && step_fits_mfma(g, M, c->nblocks);
-  if (!mf && !step_fits(g, M, c->nblocks))
+  const bool mf = M >= c->mfma_min_rows && mfma_shapes(g) && step_fits(g, M, c->nblocks, true);
+  if (!mf && !step_fits(g, M, c->nblocks, false))
     return fail(MK_E_UNSUPPORTED, "a phase of this step does not fit the workgroup's LDS");
   if (c->n_loaded != c->loaded.size())
     return fail(MK_E_STATE, "%zu of %zu weight tensors loaded", c->n_loaded, c->loaded.size());
@@ -558,9 +538,10 @@ int mk_set_trace(mk_ctx* c, int enable) {
   return MK_OK;
 }
 
-int mk_set_matrix_cores(mk_ctx* c, int enable) {
+int mk_set_matrix_cores(mk_ctx* c, int min_rows) {
   if (!c) return fail(MK_E_INVAL, "context is NULL");
-  c->matrix_cores = enable != 0;
+  if (min_rows < 2) return fail(MK_E_INVAL, "min_rows %d below 2", min_rows);
+  c->mfma_min_rows = min_rows;
   g_err.clear();
   return MK_OK;
 }

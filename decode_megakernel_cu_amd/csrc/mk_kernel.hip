@@ -85,12 +85,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) { return as_bf16x8(*reinterpret_cast<const u32x4*>(p)); }
 // two floats as bf16 high parts (packed) and the bf16 of what the high parts leave (low parts):
-// x = hi + lo to about 16 significant bits
+// x = hi + lo to about 16 significant bits (hardware round-to-nearest-even conversions)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
-  const uint16_t l0 = f2bf(x0 - bf2f(h0)), l1 = f2bf(x1 - bf2f(h1));
-  hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
-  lo = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  const bf16x2 h = {(__bf16)x0, (__bf16)x1};
+  hi = __builtin_bit_cast(uint32_t, h);
+  const bf16x2 l = {(__bf16)(x0 - __uint_as_float(hi << 16)), (__bf16)(x1 - __uint_as_float(hi & 0xFFFF0000u))};
+  lo = __builtin_bit_cast(uint32_t, l);
 }
 
 // Weights and cache rows are read once per step: non-temporal loads keep them from evicting the
@@ -451,47 +452,6 @@ struct Gemv {
     }
   }
 
-  // inv[m] = 1/sqrt(mean(src[m][:K]^2) + eps): one batched pass over every row
-  template <int MM>
-  __device__ __forceinline__ void row_inv(const Ws& ws, float* inv, float* red) const {
-    const int rq = K >> 2, n = M * rq, tid = tid_x();
-    float ss[MM];
-#pragma unroll
-    for (int k = 0; k < MM; ++k) ss[k] = 0.f;
-    for (int b = 0; b < n; b += 8 * kThreads) {
-      f32x4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (b + u * kThreads < n) {
-          const int i = min(b + u * kThreads + tid, n - 1), m = i / rq;
-          v[u] = ws.ld4(src + (size_t)m * ld + 4 * (i - m * rq));
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = b + u * kThreads + tid;
-        if (b + u * kThreads < n && i < n) {
-          const int m = i / rq;
-          const float s = dot4(v[u], v[u]);
-#pragma unroll
-          for (int k = 0; k < MM; ++k) ss[k] += (k == m) ? s : 0.f;
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < MM; ++k) {
-      const float s = wave_sum(ss[k], 64);
-      if (lane_id() == 0 && k < M) red[k * kWaves + wave_id()] = s;
-    }
-    __syncthreads();
-    if (tid < M) {
-      float t = 0.f;
-      for (int w = 0; w < kWaves; ++w) t += red[tid * kWaves + w];
-      inv[tid] = 1.0f / sqrtf(t / (float)K + eps);
-    }
-    __syncthreads();
-  }
-
   // Issue the staging of input columns [k0, k0+ks) into dst (LDS) as rows of ks floats at a row
   // stride of DS floats, and of the slab's norm gain (bf16) into gl. Direct memory-to-LDS copies;
   // the caller waits.
@@ -524,49 +484,64 @@ struct Gemv {
     }
   }
 
-  // inv[m] from the staged rows (row stride DS) when they hold all K columns
+  // RMSNorm is applied as inv[m] * (W (g . x[m])): staging scales the columns by the gain, the
+  // epilogue by the row's factor inv[m] = 1/sqrt(mean(x[m]^2) + eps). The sums of squares come from
+  // the raw staged columns, one partial per wave in red[m][wave] (summed over the slabs).
+  __device__ __forceinline__ float rms_inv(const float* red, int m) const {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += red[m * kWaves + w];
+    return 1.0f / sqrtf(t / (float)K + eps);
+  }
   template <int MM>
-  __device__ __forceinline__ void norm_stats(const float* dst, int ks, int DS, float* inv, float* red) const {
-    const int tid = tid_x();
-    for (int m = 0; m < M; ++m) {
-      float ss = 0.f;
-      for (int k = 4 * tid; k < ks; k += 4 * kThreads) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(dst + m * DS + k);
-        ss += dot4(v, v);
+  __device__ __forceinline__ void add_sumsq(float (&ss)[MM], float* red, bool first) const {
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      if (m < M) {
+        const float s = wave_sum(ss[m], 64);
+        if (lane_id() == 0) red[m * kWaves + wave_id()] = first ? s : red[m * kWaves + wave_id()] + s;
       }
-      ss = wave_sum(ss, 64);
-      if (lane_id() == 0) red[m * kWaves + wave_id()] = ss;
     }
-    __syncthreads();
-    if (tid < M) {
-      float t = 0.f;
-      for (int w = 0; w < kWaves; ++w) t += red[tid * kWaves + w];
-      inv[tid] = 1.0f / sqrtf(t / (float)K + eps);
-    }
-    __syncthreads();
+  }
+  // the token whose input row slot k of task t dotted (G_EXP: its expert's pairs in order), and the
+  // number of slots
+  __device__ __forceinline__ int token_of(int t, int k) const {
+    if (kind != G_EXP) return k;
+    const int s0 = rt->ustart[t / F];
+    return rt->ptok[s0 + k];
+  }
+  __device__ __forceinline__ int slots_of(int t) const {
+    if (kind != G_EXP) return M;
+    const int u = t / F;
+    return rt->ustart[u + 1] - rt->ustart[u];
   }
 
-  // After the staged data has landed (waited and synchronised): S_NORM rows are scaled by their RMS
-  // over all K columns (from the staged rows when there is one slab, else from row_inv) and the gain.
+  // After the staged data has landed (waited and synchronised): S_NORM columns are scaled by the
+  // gain and the rows' sums of squares accumulated (first: the first slab of the phase).
   template <int MM>
-  __device__ __forceinline__ void stage_finish(float* dst, const uint16_t* gl, int ks, bool one_slab, float* inv,
+  __device__ __forceinline__ void stage_finish(float* dst, const uint16_t* gl, int ks, int DS, bool first,
                                                float* red) const {
     if (stage != S_NORM) return;
-    const int tid = tid_x();
-    if (one_slab) norm_stats<MM>(dst, ks, ks, inv, red);
-    for (int o = tid; o < (ks >> 3); o += kThreads) {
+    float ss[MM];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) ss[m] = 0.f;
+    for (int o = tid_x(); o < (ks >> 3); o += kThreads) {
       float gf[8];
       unpack8(*reinterpret_cast<const uint4*>(gl + 8 * o), gf);
-      for (int m = 0; m < M; ++m) {
-        const float s = inv[m];
-        f32x4* d = reinterpret_cast<f32x4*>(dst + m * ks + 8 * o);
-        f32x4 a = d[0], b = d[1];
-        a.x *= s * gf[0]; a.y *= s * gf[1]; a.z *= s * gf[2]; a.w *= s * gf[3];
-        b.x *= s * gf[4]; b.y *= s * gf[5]; b.z *= s * gf[6]; b.w *= s * gf[7];
-        d[0] = a;
-        d[1] = b;
+#pragma unroll
+      for (int m = 0; m < MM; ++m) {
+        if (m < M) {
+          f32x4* d = reinterpret_cast<f32x4*>(dst + m * DS + 8 * o);
+          f32x4 a = d[0], b = d[1];
+          ss[m] += dot4(a, a) + dot4(b, b);
+          a.x *= gf[0]; a.y *= gf[1]; a.z *= gf[2]; a.w *= gf[3];
+          b.x *= gf[4]; b.y *= gf[5]; b.z *= gf[6]; b.w *= gf[7];
+          d[0] = a;
+          d[1] = b;
+        }
       }
     }
+    add_sumsq<MM>(ss, red, first);
   }
 };
 
@@ -707,7 +682,7 @@ __device__ __forceinline__ void load_element(const Gemv& g, const Plan& q, const
   const int i = task_of(q, c.it);
   const uint16_t* w = g.safe;
   int nc = 0;
-  if (c.ei < q.nel && i < q.nloc) {
+  if (c.slab < q.nslab && c.ei < q.nel && i < q.nloc) {
     const RowRef r = g.row(q.t0 + i, c.which);
     if (r.w) {
       w = r.w + k0;
@@ -793,8 +768,8 @@ __device__ __forceinline__ void step_element(const Gemv& g, const Plan& q, int e
 // Returns true when the LDS input buffer ends the phase holding the whole normalised input.
 // The first two elements of the stream were requested by gemv_preload.
 template <int MM>
-__device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const Ws& ws, float* smem, float* inv,
-                                           float* red, RowBuf& b0, RowBuf& b1, bool keep_in, uint64_t* trace) {
+__device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const Ws& ws, float* smem, float* red,
+                                           RowBuf& b0, RowBuf& b1, bool keep_in, uint64_t* trace) {
   float* xin = smem;
   const int tid = tid_x();
   const bool compute = true;
@@ -809,14 +784,13 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
     __syncthreads();
     uint16_t* gl = reinterpret_cast<uint16_t*>(xin + (g.stage == S_DOWN ? g.np + g.M : g.M) * ks);
     if (!keep) {
-      if (g.stage == S_NORM && !q.one_slab && sl == 0) g.row_inv<MM>(ws, inv, red);
       g.stage_issue(ws, xin, gl, q.wbase + k0, ks, ks);
       if (resid && sl == 0)  // this workgroup's residual inputs, [token][task]
         dma_rows4<kCoherent>(ws.r, q.res, g.M, q.nloc, q.nloc,
                   [&](int m, int c) { return ws.off(g.out0 + (size_t)m * g.ldo0 + q.t0 + c); });
       wait_vm();
       __syncthreads();
-      g.stage_finish<MM>(xin, gl, ks, q.one_slab, inv, red);
+      g.stage_finish<MM>(xin, gl, ks, ks, sl == 0, red);
     }
     __syncthreads();
     if (trace && sl == 0 && tid == 0) gp(trace)[2] = wall_clock64();
@@ -837,7 +811,15 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
     for (int it = 0; it < q.iters; ++it) {
       const int i = task_of(q, it);
       if (i < q.nloc && q.sub == 0) {
-        const float* ac = q.acc + (size_t)i * 2 * MM;
+        float* ac = q.acc + (size_t)i * 2 * MM;
+        if (g.stage == S_NORM) {  // the RMS factor of each input row
+          const int n = g.slots_of(q.t0 + i);
+          for (int k = 0; k < n; ++k) {
+            const float s = g.rms_inv(red, g.token_of(q.t0 + i, k));
+            ac[k] *= s;
+            ac[MM + k] *= s;
+          }
+        }
         g.epilogue(q.t0 + i, ac, ac + MM, q.res + i, q.nloc);
       }
     }
@@ -845,6 +827,7 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
   if (trace && tid == 0) gp(trace)[5] = wall_clock64();
   return q.one_slab && g.stage == S_NORM;
 }
+
 
 // ----------------------------------------------------------------------------------------------
 // routing (every workgroup, one wave per token): softmax over the token's router logits, top-k
@@ -970,11 +953,10 @@ __device__ __forceinline__ void compute_route(const Params& p, const Ws& ws, int
 }
 
 // ----------------------------------------------------------------------------------------------
-// Matrix-core GEMV executor (kernels built for several input rows per step)
+// Matrix-core GEMV executor (steps with several input rows)
 //
-// With eight or more input rows the vector executor above spends more issue slots on
-// multiply-adds and LDS reads than the weight stream allows; here the products run on the matrix
-// cores. Weight rows are taken 16 at a time: for each 32-column unit a lane loads 16 bytes of one
+// From a few input rows on, the vector executor above spends more issue slots on multiply-adds
+// and LDS reads than the weight stream allows; here the products run on the matrix cores. Weight rows are taken 16 at a time: for each 32-column unit a lane loads 16 bytes of one
 // row (lane l: row l % 16, columns 8 (l / 16) .. +8 of the unit) -- the A operand of a
 // 16x16x32 bf16 multiply as it comes from memory -- and the B operand holds the same 32 columns of
 // up to 16 input rows. The inputs are staged in LDS as fp32 and then rewritten in place, each run
@@ -1244,21 +1226,29 @@ __device__ __forceinline__ void mstep(const Gemv& g, const MPlan& q, MCur& cc, M
   }
 }
 
-// Staged rows to bf16 high/low parts in place, after the norm scaling (S_NORM) or the router
-// weight of each expert pair row (S_DOWN).
-__device__ __forceinline__ void mconvert(const Gemv& g, float* xs, const uint16_t* gl, int ks, int DS,
-                                         const float* inv) {
+// Staged rows to bf16 high/low parts in place, after the gain (S_NORM; the rows' sums of squares
+// are accumulated from the raw columns, the RMS factor is applied when the tiles are summed) or
+// the router weight of each expert pair row (S_DOWN).
+template <int MM>
+__device__ __forceinline__ void mconvert(const Gemv& g, float* xs, const uint16_t* gl, int ks, int DS, bool first,
+                                         float* red) {
   const int nco = ks >> 3, nr = g.stage == S_DOWN ? g.np + g.M : g.M;
+  const bool norm = g.stage == S_NORM;
+  float ss[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) ss[m] = 0.f;
   for (int e = tid_x(); e < nr * nco; e += kThreads) {
     const int r = e / nco, o = e - r * nco;
     f32x4* p = reinterpret_cast<f32x4*>(xs + r * DS + 8 * o);
     f32x4 a = p[0], b = p[1];
-    if (g.stage == S_NORM) {
+    if (norm) {
+      const float s2 = dot4(a, a) + dot4(b, b);
+#pragma unroll
+      for (int m = 0; m < MM; ++m) ss[m] += m == r ? s2 : 0.f;
       float gf[8];
       unpack8(*reinterpret_cast<const uint4*>(gl + 8 * o), gf);
-      const float s = inv[r];
-      a.x *= s * gf[0]; a.y *= s * gf[1]; a.z *= s * gf[2]; a.w *= s * gf[3];
-      b.x *= s * gf[4]; b.y *= s * gf[5]; b.z *= s * gf[6]; b.w *= s * gf[7];
+      a.x *= gf[0]; a.y *= gf[1]; a.z *= gf[2]; a.w *= gf[3];
+      b.x *= gf[4]; b.y *= gf[5]; b.z *= gf[6]; b.w *= gf[7];
     } else if (g.stage == S_DOWN && r < g.np) {
       const float s = g.rt->pw[r];
       a *= s;
@@ -1272,12 +1262,14 @@ __device__ __forceinline__ void mconvert(const Gemv& g, float* xs, const uint16_
     p[0] = __builtin_bit_cast(f32x4, u32x4{h0, h1, h2, h3});
     p[1] = __builtin_bit_cast(f32x4, u32x4{l0, l1, l2, l3});
   }
+  if (norm) g.add_sumsq<MM>(ss, red, first);
 }
 
 // Sum each tile's wave slots (in wave order) into the task accumulators; G_EXP keeps, per task,
 // the columns of its expert's tokens in pair order.
 template <int MM>
-__device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGeo& e, bool first) {
+__device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGeo& e, bool first, bool last,
+                                        const float* red) {
   const int na = g.kind == G_DOWN ? 1 : g.pairs;
   const int n = na * MM * q.nloc;
   for (int x = tid_x(); x < n; x += kThreads) {
@@ -1296,19 +1288,22 @@ __device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGe
     if (g.kind == G_DOWN) len = e.pg;
     const int u0 = (g.kind == G_DOWN ? gi : at) * len, u1 = u0 + len;
     float v = 0.f;
-    for (int w = 0; w < kWaves; ++w) {
-      if (wave_start(e, w) < u1 && wave_start(e, w + 1) > u0) v += q.piece[(size_t)(at + w) * 256 + col * 16 + r];
+    for (int w = 0; w < kWaves; ++w) {  // the waves whose (non-empty) ranges meet the tile
+      const int ws = wave_start(e, w), we = wave_start(e, w + 1);
+      if (we > ws && ws < u1 && we > u0) v += q.piece[(size_t)(at + w) * 256 + col * 16 + r];
     }
     float* ac = q.acc + (size_t)i * 2 * MM + a * MM + k;
-    *ac = first ? v : *ac + v;
+    if (!first) v += *ac;
+    if (last && g.stage == S_NORM) v *= g.rms_inv(red, col);
+    *ac = v;
   }
 }
 
 // Returns true when the LDS input buffer ends the phase holding the whole normalised input (in
 // the split bf16 form this executor reads).
 template <int MM>
-__device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const Ws& ws, float* smem, float* inv,
-                                            float* red, RowBuf& b0, RowBuf& b1, bool keep_in, uint64_t* trace) {
+__device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const Ws& ws, float* smem, float* red,
+                                            RowBuf& b0, RowBuf& b1, bool keep_in, uint64_t* trace) {
   float* xs = smem;
   const int tid = tid_x();
   const bool keep = keep_in && q.one_slab;
@@ -1317,21 +1312,19 @@ __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const
   MCur cc = mcur_slab(g, q, 0);
   MCur pc = madvance(g, q, madvance(g, q, cc));
   f32x4 dt = {0.f, 0.f, 0.f, 0.f};
-  if (trace && tid == 0) gp(trace)[4] = wall_clock64();
+  if (trace && tid == 0) gp(trace)[4] = gp(trace)[2] = wall_clock64();
   for (int sl = 0; sl < q.nslab; ++sl) {
     const MGeo e = mgeo(g, q, sl);
     __syncthreads();
     uint16_t* gl = reinterpret_cast<uint16_t*>(xs + rows * q.DS);
     if (!keep) {
-      if (g.stage == S_NORM && !q.one_slab && sl == 0) g.row_inv<MM>(ws, inv, red);
       g.stage_issue(ws, xs, gl, q.wbase + e.k0, e.ks, q.DS);
       if (resid && sl == 0)
         dma_rows4<kCoherent>(ws.r, q.res, g.M, q.nloc, q.nloc,
                              [&](int m, int c) { return ws.off(g.out0 + (size_t)m * g.ldo0 + q.t0 + c); });
       wait_vm();
       __syncthreads();
-      if (g.stage == S_NORM && q.one_slab) g.norm_stats<MM>(xs, e.ks, q.DS, inv, red);
-      mconvert(g, xs, gl, e.ks, q.DS, inv);
+      mconvert<MM>(g, xs, gl, e.ks, q.DS, sl == 0, red);
     }
     __syncthreads();
     if (trace && sl == 0 && tid == 0) gp(trace)[2] = wall_clock64();
@@ -1340,7 +1333,7 @@ __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const
       mstep(g, q, cc, pc, xs, b1, dt);
     }
     __syncthreads();
-    mreduce<MM>(g, q, e, sl == 0);
+    mreduce<MM>(g, q, e, sl == 0, sl == q.nslab - 1, red);
   }
   if (trace && tid == 0) gp(trace)[3] = wall_clock64();
   __syncthreads();
@@ -1930,7 +1923,6 @@ __device__ __forceinline__ void kda_phase(const Params& p, const LayerDev* ly, c
 // ----------------------------------------------------------------------------------------------
 struct Smem {
   float buf[kLdsFloats];
-  float inv[MK_MAX_M];
   float red[kWaves * MK_MAX_M];
   float rope[MK_MAX_NEW_TOKENS * kMaxRopePairs * 2];
   float rw[kMaxQueue];
@@ -2260,9 +2252,9 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         case PT_EXPERT: {
           const bool keep = type == PT_EXPERT && resident;
           if constexpr (MF)
-            resident = mgemv_phase<MM>(g, q, ws, sm.buf, sm.inv, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
+            resident = mgemv_phase<MM>(g, q, ws, sm.buf, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
           else
-            resident = gemv_phase<MM>(g, q, ws, sm.buf, sm.inv, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
+            resident = gemv_phase<MM>(g, q, ws, sm.buf, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
           break;
         }
         // The next layer's table row is requested during the layer's attention phase, which waits
@@ -2330,9 +2322,13 @@ hipError_t launch_decode(const Params& p, int nblocks, bool matrix_cores, hipStr
   hipLaunchKernelGGL((mk_decode_kernel<1, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 #else
-  if (matrix_cores && mm >= 8) {
-    if (mm == 8) hipLaunchKernelGGL((mk_decode_kernel<8, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((mk_decode_kernel<16, true>), grid, block, 0, stream, p);
+  if (matrix_cores && mm >= 2) {
+    switch (mm) {
+      case 2: hipLaunchKernelGGL((mk_decode_kernel<2, true>), grid, block, 0, stream, p); break;
+      case 4: hipLaunchKernelGGL((mk_decode_kernel<4, true>), grid, block, 0, stream, p); break;
+      case 8: hipLaunchKernelGGL((mk_decode_kernel<8, true>), grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL((mk_decode_kernel<16, true>), grid, block, 0, stream, p); break;
+    }
     return hipGetLastError();
   }
   switch (mm) {

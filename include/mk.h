@@ -152,17 +152,19 @@ int mk_poll(mk_ctx* ctx);
  * the time it finished the step. */
 int mk_set_trace(mk_ctx* ctx, int enable);
 
-/* Where the GEMV phases (projections, router, experts, LM head) of steps with 5 to 16 token rows
- * run. With enable != 0 (the default) they run on the matrix cores (16x16x32 bf16 multiplies;
- * inputs split into bf16 high and low parts, fp32 accumulation) whenever every row length of the
- * model is a multiple of 32 and every per-head projection comes in whole groups of 16 rows;
- * otherwise, and with enable == 0, on the vector units. Batched rows are what a speculative
- * verify step checks at once (the draft tokens are verified together by the large model: news
- * summary "谷歌TPU v7推理Kimi K3性能超英伟达GB200 57%", background section), and the compute share
- * of a step grows with the batch (German news article, section "Der Trick: 92 Schichten zu einem
- * Programm verschmelzen"). Both paths compute the same products in fp32; they differ only in
- * summation order. Takes effect from the next step; returns MK_E_INVAL for a NULL context. */
-int mk_set_matrix_cores(mk_ctx* ctx, int enable);
+/* Where the GEMV phases (projections, router, experts, LM head) run. Steps with at least min_rows
+ * token rows (batch * n_new_tokens; default MK_MFMA_MIN_ROWS) run them on the matrix cores
+ * (16x16x32 bf16 multiplies of 16 weight rows by up to 16 token rows; inputs split into bf16 high
+ * and low parts, fp32 accumulation) whenever every row length of the model is a multiple of 32 and
+ * every per-head projection comes in whole groups of 16 rows; other steps, and every step when
+ * min_rows > MK_MAX_M, run them on the vector units. Batched rows are what a speculative verify
+ * step checks at once (the draft tokens are verified together by the large model: news summary
+ * "谷歌TPU v7推理Kimi K3性能超英伟达GB200 57%", background section), and the compute share of a step
+ * grows with the batch (German news article, section "Der Trick: 92 Schichten zu einem Programm
+ * verschmelzen"). Both paths compute the same products in fp32 and differ only in summation
+ * order. Takes effect from the next step. MK_E_INVAL for a NULL context or min_rows < 2. */
+#define MK_MFMA_MIN_ROWS 3
+int mk_set_matrix_cores(mk_ctx* ctx, int min_rows);
 
 /* Copy the last traced step: out[((barrier * n_blocks) + block) * MK_TRACE_STAMPS + stamp] for
  * barrier < *n_barriers + 1 (the last record is the end of the step). Call with out == NULL to get

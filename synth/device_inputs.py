@@ -133,8 +133,9 @@ class DeviceModel:
                                rt.data_ptr() if rt is not None else 0, self.stream)
         return logits, rt
 
-    def set_matrix_cores(self, enable: bool):
-        self.mk.mk_set_matrix_cores(self.ctx, enable)
+    def set_matrix_cores(self, min_rows: int):
+        """Steps with at least min_rows token rows run their GEMV phases on the matrix cores."""
+        self.mk.mk_set_matrix_cores(self.ctx, min_rows)
 
     def poll(self):
         self.mk.mk_poll(self.ctx)

@@ -172,3 +172,16 @@ def test_hybrid_needs_state(mk):
 def test_null_context(mk):
     for fn, args in ((mk.lib.mk_poll, (None,)), (mk.lib.mk_load_weights, (None, None, 0, None))):
         assert fn(*args) == mk.MK_E_INVAL
+
+
+def test_matrix_core_threshold_arguments(mk, host_ctx):
+    _, ctx = host_ctx
+    mk.mk_set_matrix_cores(ctx, 2)
+    mk.mk_set_matrix_cores(ctx, mk.MK_MFMA_MIN_ROWS)
+    mk.mk_set_matrix_cores(ctx, mk.MK_MAX_M + 1)  # vector units only
+    for bad in (1, 0, -3):
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_set_matrix_cores(ctx, bad)
+        assert e.value.code == mk.MK_E_INVAL
+    with pytest.raises(mk.MkError):
+        mk.mk_set_matrix_cores(None, 5)

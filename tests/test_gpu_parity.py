@@ -17,6 +17,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
+VECTOR_ONLY = 17  # matrix-core row threshold above the largest step: vector units only
 
 _models = {}
 
@@ -40,14 +41,14 @@ def teardown_module(_):
         _models.pop(k).close()
 
 
-def run_pair(cfg, spec, B, T, kv_len, step=0, matrix_cores=True):
+def run_pair(cfg, spec, B, T, kv_len, step=0, mfma_min_rows=3):
     import oracle
 
     print(f"[case] {cfg.name} L={cfg.n_layers} B={B} T={T} kv_len={kv_len} seed={spec.seed} "
-          f"matrix_cores={matrix_cores}", flush=True)
+          f"mfma_min_rows={mfma_min_rows}", flush=True)
     toks = synth.tokens(spec.seed, step, cfg.vocab, B, T)
     dm = device_model(cfg, spec)
-    dm.set_matrix_cores(matrix_cores)
+    dm.set_matrix_cores(mfma_min_rows)
     dm.fill_caches(B, kv_len)
     logits, route = dm.step(toks, kv_len)
     torch.cuda.synchronize()
@@ -124,8 +125,8 @@ def check_cache(cfg, dm, caches, init, B, T, kv_len):
             assert err < 1e-4, f"delta-rule state error {err:.3e}"
 
 
-def parity(cfg, spec, B, T, kv_len, matrix_cores=True):
-    dm, got, route, ref, caches, init = run_pair(cfg, spec, B, T, kv_len, matrix_cores=matrix_cores)
+def parity(cfg, spec, B, T, kv_len, mfma_min_rows=3):
+    dm, got, route, ref, caches, init = run_pair(cfg, spec, B, T, kv_len, mfma_min_rows=mfma_min_rows)
     err = check_logits(got, ref)
     check_route(route, ref)
     check_cache(cfg, dm, caches, init, B, T, kv_len)
@@ -146,10 +147,16 @@ def test_tiny_shapes(B, T, kv_len):
     parity(synth.TINY, synth.Spec(seed=5), B, T, kv_len)
 
 
+@pytest.mark.parametrize("B,T,kv_len", [(2, 1, 50), (1, 3, 7), (4, 1, 129)])
+def test_tiny_shapes_matrix_cores_small(B, T, kv_len):
+    # the matrix-core executor below its default threshold (2..4 token rows)
+    parity(synth.TINY, synth.Spec(seed=8), B, T, kv_len, mfma_min_rows=2)
+
+
 @pytest.mark.parametrize("B,T,kv_len", [(8, 2, 129), (1, 8, 5)])
 def test_tiny_shapes_vector_units(B, T, kv_len):
     # the vector-unit GEMV executor at 5..16 rows (the matrix cores are the default there)
-    parity(synth.TINY, synth.Spec(seed=5), B, T, kv_len, matrix_cores=False)
+    parity(synth.TINY, synth.Spec(seed=5), B, T, kv_len, mfma_min_rows=VECTOR_ONLY)
 
 
 # row lengths that are not whole 32-column units: 5..16 rows fall back to the vector units
@@ -187,7 +194,7 @@ def test_k3_two_layers(B, T, kv_len):
 
 
 def test_k3_two_layers_batch8_vector_units():
-    parity(K3_SMALL, synth.Spec(seed=2), 8, 1, 33, matrix_cores=False)
+    parity(K3_SMALL, synth.Spec(seed=2), 8, 1, 33, mfma_min_rows=VECTOR_ONLY)
 
 
 def test_k3_two_layers_peaked_mla():
