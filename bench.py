@@ -276,6 +276,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--trace", action="store_true", help="print per-phase device timings of one step per batch")
+    ap.add_argument("--workload", default=WORKLOAD, choices=["c3", "c4", "c5"],
+                    help="c3: K3-scale share (the headline); c4: its 7-token verify step; c5: the hybrid model "
+                         "(for profiling one path; --batches applies)")
+    ap.add_argument("--no-verify", action="store_true",
+                    help="skip the 7-token speculative-verify measurement on the K3-scale share")
     ap.add_argument("--mfma-min-rows", type=int, default=None,
                     help="token rows from which GEMV phases use the matrix cores (library default if omitted)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -290,14 +295,14 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the decode step; --gpus {args.gpus} is not supported "
-              f"(this build runs on exactly one GPU, with no collectives)", file=sys.stderr)
+              f"(it measures exactly one GPU, with no collectives)", file=sys.stderr)
         sys.exit(2)
 
     import torch
 
     from synth.device_inputs import DeviceModel
 
-    w = synth.WORKLOADS[WORKLOAD]
+    w = synth.WORKLOADS[args.workload]
     cfg = w.model
     spec = synth.Spec(seed=args.seed)
     t0 = time.time()
@@ -315,11 +320,10 @@ def main():
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    results = {}
-    for B in batches:
-        toks = synth.tokens(spec.seed, 1, cfg.vocab, B, w.new_tokens)
+    def measure(B: int, T: int, trace: bool) -> dict:
+        toks = synth.tokens(spec.seed, 1, cfg.vocab, B, T)
         d_tok = torch.from_numpy(toks.astype(np.int32)).cuda()
-        logits = torch.empty((B, w.new_tokens, cfg.vocab), dtype=torch.float32, device="cuda")
+        logits = torch.empty((B, T, cfg.vocab), dtype=torch.float32, device="cuda")
         _, route = dm.step(toks, w.kv_len, route=True, logits=logits, d_tokens=d_tok)
         torch.cuda.synchronize()
         dm.poll()
@@ -339,22 +343,29 @@ def main():
         wall = time.perf_counter() - t_wall
         dm.poll()
         kms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-        by = algorithmic_bytes(cfg, B, w.new_tokens, w.kv_len, route)
-        results[B] = {"ms_per_step": wall * 1e3 / args.steps, "kernel_ms_avg": float(kms.mean()),
-                      "kernel_ms_p10": float(np.percentile(kms, 10)), "kernel_ms_p90": float(np.percentile(kms, 90)),
-                      "tokens_per_s": B * w.new_tokens * args.steps / wall, "bytes": by["total"],
-                      "gbs": by["total"] / (kms.mean() * 1e-3) / 1e9}
-        print(f"# B={B}: {results[B]['kernel_ms_avg']:.3f} ms/launch, {results[B]['tokens_per_s']:.1f} tok/s, "
-              f"{results[B]['gbs']:.0f} GB/s ({by['total'] / 1e9:.2f} GB/step)", file=sys.stderr, flush=True)
-        if args.trace:
+        by = algorithmic_bytes(cfg, B, T, w.kv_len, route)
+        r = {"ms_per_step": wall * 1e3 / args.steps, "kernel_ms_avg": float(kms.mean()),
+             "kernel_ms_p10": float(np.percentile(kms, 10)), "kernel_ms_p90": float(np.percentile(kms, 90)),
+             "tokens_per_s": B * T * args.steps / wall, "bytes": by["total"],
+             "gbs": by["total"] / (kms.mean() * 1e-3) / 1e9}
+        print(f"# B={B} T={T}: {r['kernel_ms_avg']:.3f} ms/launch, {r['tokens_per_s']:.1f} tok/s, "
+              f"{r['gbs']:.0f} GB/s ({by['total'] / 1e9:.2f} GB/step)", file=sys.stderr, flush=True)
+        if trace:
             dm.mk.mk_set_trace(dm.ctx, True)
             dm.step(toks, w.kv_len, route=False, logits=logits, d_tokens=d_tok)
             torch.cuda.synchronize()
             summary = trace_summary(cfg, dm.mk.mk_read_trace(dm.ctx))
             dm.mk.mk_set_trace(dm.ctx, False)
-            print(f"# trace B={B}", file=sys.stderr)
+            print(f"# trace B={B} T={T}", file=sys.stderr)
             print_trace(summary)
-            results[B]["trace"] = summary
+            r["trace"] = summary
+        return r
+
+    results = {B: measure(B, w.new_tokens, args.trace) for B in batches}
+    verify = None
+    if args.workload == "c3" and not args.no_verify:
+        v = synth.WORKLOADS["c4"]
+        verify = measure(v.batch, v.new_tokens, False)
     dm.close()
 
     head = results[batches[0]]
@@ -382,6 +393,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(batches[0])},
     }
+    if verify is not None:  # positions verified per second (1 + 6 draft tokens per step)
+        out["verify_t7"] = {"positions_per_s": round(verify["tokens_per_s"], 2),
+                            "kernel_ms": round(verify["kernel_ms_avg"], 4),
+                            "gb_per_step": round(verify["bytes"] / 1e9, 3), "hbm_gbs": round(verify["gbs"], 1),
+                            "hbm_frac": round(verify["gbs"] / HBM_PEAK_GBS, 4)}
+    if args.workload != "c3":
+        out["config"]["workload"] = f"{args.workload}: {w.description} (profiling run, not the headline)"
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))

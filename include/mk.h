@@ -42,7 +42,7 @@ typedef enum {
   MK_E_NOMEM = -4,        /* a caller buffer is smaller than mk_query_sizes requires */
   MK_E_HIP = -5,          /* a HIP runtime call failed (message in mk_last_error) */
   MK_E_DEVICE = -6,       /* the device reported an error (watchdog timeout or bad token id); see mk_poll */
-  MK_E_UNSUPPORTED = -7   /* valid but not supported by this build (e.g. shape limits) */
+  MK_E_UNSUPPORTED = -7   /* valid but not supported by this library (e.g. shape limits) */
 } mk_status;
 
 typedef enum { MK_ATTN_GQA = 0, MK_ATTN_MLA = 1, MK_ATTN_HYBRID = 2 } mk_attn_kind;

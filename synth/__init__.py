@@ -92,7 +92,8 @@ class Workload:
 
 
 # --------------------------------------------------------------------------------------
-# The five workloads (shapes from the task's configuration list).
+# The five workloads: a tiny and a mid-size MoE decoder, the K3-scale one-GPU share at batch 1-8,
+# its speculative-verify step (1 + 6 draft tokens) and the hybrid delta-rule / MLA variant.
 # --------------------------------------------------------------------------------------
 TINY = ModelConfig(
     name="tiny-moe", n_layers=2, hidden=256, vocab=1024, attn_kind=ATTN_GQA,
