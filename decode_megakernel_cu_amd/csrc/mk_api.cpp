@@ -493,8 +493,10 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   // split-KV: GQA uses fixed chunks; MLA sizes them so that the tasks of the step fill the grid
   const int npos = kv_len + T;
   p.chunk = kChunk;
-  if (g.attn_kind != MK_ATTN_GQA && c->nblocks > 0)
-    p.chunk = std::max(kChunk, (int)(((long long)B * npos + c->nblocks - 1) / c->nblocks));
+  if (g.attn_kind != MK_ATTN_GQA && c->nblocks > 0) {  // whole kSub-position tiles per task
+    const int even = (int)(((long long)B * npos + c->nblocks - 1) / c->nblocks);
+    p.chunk = (std::max(kChunk, even) + kSub - 1) / kSub * kSub;
+  }
   p.nsplit = (npos + p.chunk - 1) / p.chunk;
   p.epoch = (uint32_t)(c->launches * 65536ull);
   p.tokens = d_tokens; p.logits = d_logits; p.route = d_route;
