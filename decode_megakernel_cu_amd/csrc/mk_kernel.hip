@@ -1563,6 +1563,23 @@ __device__ __forceinline__ void merge_phase(const Params& p, const Ws& ws, int h
 // sum per head; scores (query split into bf16 high and low parts) and value sums (weights split
 // likewise) run on the matrix cores. New entries (normalised latent, rotated rope key, rounded to
 // bf16) are appended to the cache by the task whose range holds their position.
+// The cache rows the workgroup's first task reads first (the rows already in the cache, direct copies
+// into LDS): issued before the phase's barrier, since they do not depend on the step's earlier phases.
+__device__ __forceinline__ void mla_prefetch_rows(const Params& p, const LayerDev* ly, float* smem) {
+  const int kv_len = rfl(p.kv_len), Bmax = rfl(p.Bmax), B = rfl(p.B), T = rfl(p.T), cap = rfl(p.cap);
+  const int lat = rfl(p.kvl) + rfl(p.rd), cst = lat + 8;
+  const int npos = kv_len + T, C = rfl(p.chunk), nsplit = rfl(p.nsplit), task = blockIdx.x;
+  if (task >= B * nsplit) return;
+  const int s = task % nsplit, b = task / nsplit;
+  const int p0 = s * C, p1 = imin(npos, p0 + C), pe = imin(p1, kv_len + 1);
+  if (pe <= p0) return;
+  const int n = p1 - p0 <= kSub ? p1 - p0 : imin(kSub, pe - p0);
+  const int nold = imax(0, imin(kv_len - p0, n));
+  const uint16_t* Lb = rflp(p.kv) + ((size_t)rfl(ly->ord) * Bmax + b) * cap * lat;
+  const Rsrc lr = make_rsrc(Lb, (uint32_t)cap * lat * 2);
+  dma_rows<2>(lr, smem, nold, lat >> 3, cst / 2, [&](int r, int c) { return (uint32_t)((p0 + r) * lat) * 2 + c * 16; });
+}
+
 __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
                                                const float* rope, uint64_t* trace) {
   static_assert(kSub == 32, "score lanes map one position each in a half wave");
@@ -1679,7 +1696,7 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
                             [&](int h, int c) { return ws.off(a4 + ((size_t)m * nh + h) * kvl + 4 * c); });
         dma_rows<kCoherent>(ws.r, Qt + kvl, nh, rd >> 2, lat,
                             [&](int h, int c) { return ws.off(a3 + ((size_t)m * nh + h) * qd + nd + 4 * c); });
-        issue_c(p0, nfirst);
+        if (task != (int)blockIdx.x || t != 0) issue_c(p0, nfirst);  // else requested before the barrier
         wait_vm();
         __syncthreads();
         fill_new(p0, nfirst);
@@ -2220,6 +2237,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       if (trec && tid_x() == 0) gp(trec)[10] = wall_clock64();
       const bool early = type == PT_GEMV;  // prepared while waiting
       if (!early) {
+        if (type == PT_ATTN_MLA) mla_prefetch_rows(p, ly, sm.buf);
         if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort);
         MK_FINISH();
         if (trec && tid_x() == 0) gp(trec)[7] = wall_clock64();
