@@ -600,8 +600,11 @@ __device__ __forceinline__ void dot_block(const RowBuf& b, const float* xin, int
 // a slab padded to even so that the two register buffers alternate the same way in every slab.
 constexpr int kGemvWaves = kWaves;
 
+// vp: lane-group tasks per task (2: the SwiGLU gate and up rows of router/shared and routed-expert
+// phases go to different lane groups, so few tasks still keep every wave busy); cp: weight rows a
+// lane-group task streams one after the other (the down projection's experts and shared expert)
 struct Plan {
-  int t0, nloc, wbase, Wst, KS, nslab, lg, LPR, G, sub, grp, iters, nblk, per, nel, nelp, ntot;
+  int t0, nloc, wbase, Wst, KS, nslab, lg, LPR, G, sub, grp, iters, nblk, per, nel, nelp, ntot, vp, cp, nv;
   bool one_slab;
   float* acc;  // [nloc][2][MM] task accumulators, at the end of the LDS buffer
   float* res;  // [M][nloc] residual inputs
@@ -636,19 +639,22 @@ __device__ __forceinline__ Plan make_plan(const Gemv& g, float* smem) {
   }
   q.nslab = q.KS > 0 ? (q.Wst + q.KS - 1) / q.KS : 0;
   const int nch = (offs ? g.seg : q.KS) >> 3;
+  q.vp = (g.kind == G_RS || g.kind == G_EXP) && g.pairs == 2 ? 2 : 1;
+  q.cp = q.vp == 2 ? 1 : g.pairs;
+  q.nv = q.nloc * q.vp;
   // lanes per row (a power of two): enough that kNC chunks per lane cover the row, few enough that
   // every wave has a task when the workgroup has few
   const int lo = min(6, log2ceil(cdiv(nch, kNC))), hi = max(lo, min(6, log2ceil(nch)));
-  const int bal = max(0, 6 - log2ceil(max(1, cdiv(q.nloc, kGemvWaves))));
+  const int bal = max(0, 6 - log2ceil(max(1, cdiv(q.nv, kGemvWaves))));
   q.lg = min(max(bal, lo), hi);
   q.LPR = 1 << q.lg;
   q.G = 64 >> q.lg;
   const int lane = lane_id();
   q.sub = lane & (q.LPR - 1);
   q.grp = lane >> q.lg;
-  q.iters = cdiv(q.nloc, kGemvWaves * q.G);
+  q.iters = cdiv(q.nv, kGemvWaves * q.G);
   q.nblk = (nch + (kNC << q.lg) - 1) >> (3 + q.lg);
-  q.per = g.pairs * q.nblk;
+  q.per = q.cp * q.nblk;
   q.nel = q.iters * q.per;
   q.nelp = q.nel + (q.nel & 1);
   q.ntot = q.nslab * q.nelp;
@@ -679,11 +685,11 @@ __device__ __forceinline__ int task_of(const Plan& q, int it) { return (it * kGe
 // Issue the loads of the element at c into b (lanes without a row read a valid dummy address).
 __device__ __forceinline__ void load_element(const Gemv& g, const Plan& q, const Cursor& c, RowBuf& b) {
   const int k0 = c.slab * q.KS, ks = min(q.KS, q.Wst - k0);
-  const int i = task_of(q, c.it);
+  const int v = task_of(q, c.it), i = v >> (q.vp - 1), which = q.vp == 2 ? v & 1 : c.which;
   const uint16_t* w = g.safe;
   int nc = 0;
-  if (c.slab < q.nslab && c.ei < q.nel && i < q.nloc) {
-    const RowRef r = g.row(q.t0 + i, c.which);
+  if (c.slab < q.nslab && c.ei < q.nel && v < q.nv) {
+    const RowRef r = g.row(q.t0 + i, which);
     if (r.w) {
       w = r.w + k0;
       nc = max(0, min(r.len - k0, ks)) >> 3;
@@ -697,26 +703,37 @@ __device__ __forceinline__ void load_element(const Gemv& g, const Plan& q, const
 __device__ __forceinline__ void gemv_preload(const Gemv& g, const Plan& q, RowBuf& b0, RowBuf& b1) {
   Cursor c{0, 0, 0, 0, 0};
   if (q.ntot > 0) load_element(g, q, c, b0);
-  advance(c, q, g.pairs);
+  advance(c, q, q.cp);
   if (q.ntot > 1) load_element(g, q, c, b1);
 }
 
 template <int MM>
-__device__ __forceinline__ void reduce_task(const Gemv& g, const Plan& q, int i, bool first, float (&a0)[MM],
+__device__ __forceinline__ void reduce_task(const Gemv& g, const Plan& q, int v, bool first, float (&a0)[MM],
                                             float (&a1)[MM]) {
   const bool two = g.kind == G_RS || g.kind == G_EXP;
+  if (q.vp == 2) {  // one row of the task: gate (slot 0) or up (slot 1)
+    const int i = v >> 1, w = v & 1;
 #pragma unroll
-  for (int k = 0; k < MM; ++k) a0[k] = wave_sum(a0[k], q.LPR);
-  if (two) {
+    for (int k = 0; k < MM; ++k) a0[k] = wave_sum(w ? a1[k] : a0[k], q.LPR);
+    if (v < q.nv && q.sub == 0) {
+      float* ac = q.acc + (size_t)i * 2 * MM + w * MM;
 #pragma unroll
-    for (int k = 0; k < MM; ++k) a1[k] = wave_sum(a1[k], q.LPR);
-  }
-  if (i < q.nloc && q.sub == 0) {
-    float* ac = q.acc + (size_t)i * 2 * MM;
+      for (int k = 0; k < MM; ++k) ac[k] = first ? a0[k] : ac[k] + a0[k];
+    }
+  } else {
 #pragma unroll
-    for (int k = 0; k < MM; ++k) {
-      ac[k] = first ? a0[k] : ac[k] + a0[k];
-      if (two) ac[MM + k] = first ? a1[k] : ac[MM + k] + a1[k];
+    for (int k = 0; k < MM; ++k) a0[k] = wave_sum(a0[k], q.LPR);
+    if (two) {
+#pragma unroll
+      for (int k = 0; k < MM; ++k) a1[k] = wave_sum(a1[k], q.LPR);
+    }
+    if (v < q.nloc && q.sub == 0) {
+      float* ac = q.acc + (size_t)v * 2 * MM;
+#pragma unroll
+      for (int k = 0; k < MM; ++k) {
+        ac[k] = first ? a0[k] : ac[k] + a0[k];
+        if (two) ac[MM + k] = first ? a1[k] : ac[MM + k] + a1[k];
+      }
     }
   }
 #pragma unroll
@@ -729,10 +746,9 @@ template <int MM>
 __device__ __forceinline__ void step_element(const Gemv& g, const Plan& q, int eg, Cursor& cc, Cursor& pc, int k0,
                                              int ks, const float* xin, RowBuf& b, float (&a0)[MM],
                                              float (&a1)[MM]) {
-  const int which = cc.which;
-  const int i = task_of(q, cc.it);
+  const int v = task_of(q, cc.it), i = v >> (q.vp - 1), which = q.vp == 2 ? v & 1 : cc.which;
   const bool real = cc.ei < q.nel;
-  if (real && i < q.nloc) {
+  if (real && v < q.nv) {
     const RowRef r = g.row(q.t0 + i, which);
     if (r.w) {
       const int nc = max(0, min(r.len - k0, ks)) >> 3;
@@ -758,11 +774,11 @@ __device__ __forceinline__ void step_element(const Gemv& g, const Plan& q, int e
     }
   }
   if (eg + 2 < q.ntot) load_element(g, q, pc, b);
-  const bool task_end = real && which == g.pairs - 1 && cc.blk == q.nblk - 1;
+  const bool task_end = real && cc.which == q.cp - 1 && cc.blk == q.nblk - 1;
   const bool first = cc.slab == 0;
-  advance(cc, q, g.pairs);
-  advance(pc, q, g.pairs);
-  if (task_end) reduce_task<MM>(g, q, i, first, a0, a1);
+  advance(cc, q, q.cp);
+  advance(pc, q, q.cp);
+  if (task_end) reduce_task<MM>(g, q, v, first, a0, a1);
 }
 
 // Returns true when the LDS input buffer ends the phase holding the whole normalised input.
@@ -776,8 +792,8 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
   const bool keep = keep_in && q.one_slab;  // input already staged by the previous phase
   const bool resid = g.kind == G_RESID || g.kind == G_DOWN;
   Cursor cc{0, 0, 0, 0, 0}, pc{0, 0, 0, 0, 0};
-  advance(pc, q, g.pairs);
-  advance(pc, q, g.pairs);
+  advance(pc, q, q.cp);
+  advance(pc, q, q.cp);
   if (trace && tid == 0) gp(trace)[4] = wall_clock64();
   for (int sl = 0; sl < q.nslab; ++sl) {
     const int k0 = sl * q.KS, ks = min(q.KS, q.Wst - k0);
@@ -806,23 +822,19 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
     }
   }
   if (trace && tid == 0) gp(trace)[3] = wall_clock64();
-  // epilogue: each task by the lane that accumulated it
-  if (compute) {
-    for (int it = 0; it < q.iters; ++it) {
-      const int i = task_of(q, it);
-      if (i < q.nloc && q.sub == 0) {
-        float* ac = q.acc + (size_t)i * 2 * MM;
-        if (g.stage == S_NORM) {  // the RMS factor of each input row
-          const int n = g.slots_of(q.t0 + i);
-          for (int k = 0; k < n; ++k) {
-            const float s = g.rms_inv(red, g.token_of(q.t0 + i, k));
-            ac[k] *= s;
-            ac[MM + k] *= s;
-          }
-        }
-        g.epilogue(q.t0 + i, ac, ac + MM, q.res + i, q.nloc);
+  // epilogue: one thread per task (a task's rows may have been reduced by different lane groups)
+  __syncthreads();
+  for (int i = tid; i < q.nloc; i += kThreads) {
+    float* ac = q.acc + (size_t)i * 2 * MM;
+    if (g.stage == S_NORM) {  // the RMS factor of each input row
+      const int n = g.slots_of(q.t0 + i);
+      for (int k = 0; k < n; ++k) {
+        const float s = g.rms_inv(red, g.token_of(q.t0 + i, k));
+        ac[k] *= s;
+        ac[MM + k] *= s;
       }
     }
+    g.epilogue(q.t0 + i, ac, ac + MM, q.res + i, q.nloc);
   }
   if (trace && tid == 0) gp(trace)[5] = wall_clock64();
   return q.one_slab && g.stage == S_NORM;
