@@ -286,7 +286,7 @@ Layout make_layout(const mk_config& c) {
   };
   w.flags = take(kMaxBlocks * 4);
   w.status = take(64 * 4);
-  w.trace_slots = (uint64_t)(2 + 10 * c.n_layers) * kMaxBlocks;
+  w.trace_slots = (uint64_t)(3 + 10 * c.n_layers) * kMaxBlocks;
   w.trace = take(w.trace_slots * kTraceStamps * 8);
   w.rope = take((uint64_t)MK_MAX_NEW_TOKENS * kMaxRopePairs * 2 * 4);
   w.x = take(M * H * 4);
@@ -301,6 +301,7 @@ Layout make_layout(const mk_config& c) {
   w.rlog = take(M * E * 4);
   w.sact = take(M * std::max<uint64_t>(SF, 1) * 4);
   w.eact = take(M * c.top_k * F * 4);
+  w.amax = take(M * 8);
   w.scratch = w.part;
   w.total = o;
   return Lt;
@@ -461,9 +462,11 @@ int mk_load_weights(mk_ctx* c, const mk_tensor_desc* d, int n, void* stream) {
   return MK_OK;
 }
 
-int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens, void* d_kv, float* d_kda_state,
-                   float* d_logits, int32_t* d_route, void* stream) {
+// One decode step (both entry points): validation, parameters, the launch.
+static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens, void* d_kv, float* d_kda_state,
+                float* d_logits, int32_t* d_route, int32_t* d_argmax, int32_t* d_accepted, void* stream) {
   if (!c) return fail(MK_E_INVAL, "context is NULL");
+  const bool greedy = d_argmax != nullptr;
   const mk_config& g = c->cfg;
   if (B < 1 || B > g.max_batch) return fail(MK_E_INVAL, "batch %d outside 1..%d", B, g.max_batch);
   if (T < 1 || T > g.max_new_tokens) return fail(MK_E_INVAL, "n_new_tokens %d outside 1..%d", T, g.max_new_tokens);
@@ -471,7 +474,8 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   if (kv_len < 0) return fail(MK_E_INVAL, "kv_len %d is negative", kv_len);
   if ((long long)kv_len + T > g.kv_capacity)
     return fail(MK_E_KV_OVERFLOW, "kv_len %d + %d new tokens exceeds capacity %d", kv_len, T, g.kv_capacity);
-  if (!d_tokens || !d_logits || !d_kv) return fail(MK_E_INVAL, "tokens, kv and logits must be non-NULL");
+  if (!d_tokens || !d_kv) return fail(MK_E_INVAL, "tokens and kv must be non-NULL");
+  if (!greedy && !d_logits) return fail(MK_E_INVAL, "logits must be non-NULL");
   if (g.attn_kind == MK_ATTN_HYBRID && !d_kda_state) return fail(MK_E_INVAL, "hybrid model needs the delta-rule state");
   const int M = B * T;
   const bool mf = M >= c->mfma_min_rows && mfma_shapes(g) && step_fits(g, M, c->nblocks, true);
@@ -515,6 +519,10 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   p.ws_bytes = (uint32_t)w.total;
   p.watchdog_ticks = c->watchdog_ticks;
   p.trace = c->trace ? reinterpret_cast<uint64_t*>(ws + w.trace) : nullptr;
+  p.greedy = greedy ? 1 : 0;
+  p.amax = reinterpret_cast<unsigned long long*>(ws + w.amax);
+  p.argmax = d_argmax;
+  p.accepted = d_accepted;
   const int nh = g.n_heads;
   const uint64_t dmax = g.attn_kind == MK_ATTN_GQA ? g.head_dim : std::max(g.kv_lora, g.kda_dv);
   if ((uint64_t)M * nh * p.nsplit * (dmax + kPartPad) > w.part_floats)
@@ -523,7 +531,7 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   if (e == hipSuccess) e = launch_decode(p, c->nblocks, mf, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MK_E_HIP, "launch failed: %s", hipGetErrorString(e));
   c->launches++;
-  int nb = 1;
+  int nb = greedy ? 2 : 1;  // the LM head's barrier, and the one before the greedy results
   for (int l = 0; l < g.n_layers; ++l) {
     const int k = layer_kind(g, l);
     nb += k == kGqa ? 7 : k == kMla ? 10 : 6;
@@ -531,6 +539,17 @@ int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens,
   c->last_barriers = nb;
   g_err.clear();
   return MK_OK;
+}
+
+int mk_decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens, void* d_kv, float* d_kda_state,
+                   float* d_logits, int32_t* d_route, void* stream) {
+  return decode_step(c, B, T, kv_len, d_tokens, d_kv, d_kda_state, d_logits, d_route, nullptr, nullptr, stream);
+}
+
+int mk_decode_step_greedy(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens, void* d_kv,
+                          float* d_kda_state, float* d_logits, int32_t* d_argmax, int32_t* d_accepted, void* stream) {
+  if (c && !d_argmax) return fail(MK_E_INVAL, "argmax output must be non-NULL");
+  return decode_step(c, B, T, kv_len, d_tokens, d_kv, d_kda_state, d_logits, nullptr, d_argmax, d_accepted, stream);
 }
 
 int mk_set_trace(mk_ctx* c, int enable) {

@@ -36,7 +36,7 @@ static_assert(sizeof(LayerDev) % 16 == 0, "layer table rows are copied in 16-byt
 
 // Workspace carve-up (byte offsets from the workspace base).
 struct WsLayout {
-  uint64_t flags, status, trace, rope, x, a1, a2, a3, a4, att, o2, part, rlog, sact, eact, scratch, total;
+  uint64_t flags, status, trace, rope, x, a1, a2, a3, a4, att, o2, part, rlog, sact, eact, amax, scratch, total;
   uint64_t part_floats;  // capacity of the partials buffer in floats
   uint64_t trace_slots;  // barriers x blocks the trace region holds
 };
@@ -66,6 +66,11 @@ struct Params {
   uint32_t ws_bytes;  // workspace size (< 2^31)
   uint64_t watchdog_ticks;  // wall-clock ticks a barrier may wait
   uint64_t* trace;          // optional [barrier][block][kTraceStamps] wall-clock stamps
+  // greedy steps: per-row argmax keys (workspace), the argmax tokens and accepted draft counts
+  int32_t greedy;
+  unsigned long long* amax;  // [M] (value, index) keys, largest logit then lowest index
+  int32_t* argmax;           // [M]
+  int32_t* accepted;         // [B] or nullptr
 };
 
 }  // namespace mk

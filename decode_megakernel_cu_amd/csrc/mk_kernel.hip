@@ -337,6 +337,14 @@ struct RowRef {
 };
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+// Greedy selection key of logit v at vocabulary index i: unsigned order of the keys is the order
+// of the logits, ties broken towards the lower index (the float's bits made monotonic, then the
+// index complemented in the low word).
+__device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (uint32_t)i);
+}
 // by value (a reference-returning min keeps its operands in memory)
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
@@ -367,6 +375,7 @@ struct Gemv {
   int E, SF, F, H;  // G_RS / G_EXP / G_DOWN
   float *rlog, *sact, *eact;
   const Route* rt;
+  unsigned long long* hmax;  // LM head of a greedy step: per-row argmax keys of the workgroup (LDS)
 
   __device__ __forceinline__ RowRef row(int t, int which) const {
     RowRef r{nullptr, K, 0, M, 0, nullptr};
@@ -427,7 +436,11 @@ struct Gemv {
           ld_o = ldo1;
           t -= n0;
         }
-        for (int k = 0; k < M; ++k) stc(o + (size_t)k * ld_o + t, a0[k]);
+        if (o)
+          for (int k = 0; k < M; ++k) stc(o + (size_t)k * ld_o + t, a0[k]);
+        if (hmax)
+          for (int k = 0; k < M; ++k)
+            __hip_atomic_fetch_max(hmax + k, argmax_key(a0[k], t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         break;
       }
       case G_RESID:
@@ -1959,6 +1972,8 @@ struct Smem {
   int cnt[kMaxExperts];
   Route route;
   LayerDev lyd[2];  // layer table rows of the current and the next layer
+  unsigned long long hmax[MK_MAX_M];  // greedy steps: this workgroup's argmax keys of the LM head
+  int amx[MK_MAX_M];
   int abort;
 };
 
@@ -2156,7 +2171,7 @@ __device__ __forceinline__ void scalarize(Gemv& g) {
   g.out0 = rflp(g.out0); g.out1 = rflp(g.out1); g.out2 = rflp(g.out2);
   g.ldo0 = rfl(g.ldo0); g.ldo1 = rfl(g.ldo1); g.ldo2 = rfl(g.ldo2); g.rph = rfl(g.rph); g.seg = rfl(g.seg);
   g.E = rfl(g.E); g.SF = rfl(g.SF); g.F = rfl(g.F); g.H = rfl(g.H);
-  g.rlog = rflp(g.rlog); g.sact = rflp(g.sact); g.eact = rflp(g.eact);
+  g.rlog = rflp(g.rlog); g.sact = rflp(g.sact); g.eact = rflp(g.eact); g.hmax = rflp(g.hmax);
 }
 
 // Copy layer l's table row into LDS slot l % 2 (a direct copy; it has landed by the time the
@@ -2224,6 +2239,10 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       sm.rope[(t * kMaxRopePairs + j) * 2 + 1] = (float)sin(a);
     }
     fetch_layer(p, sm.lyd, 0);
+    // greedy steps: clear the device-wide argmax keys (many barriers precede the LM head's updates)
+    if (p.greedy && blockIdx.x == 0 && tid_x() < M)
+      __hip_atomic_store((GLOBAL unsigned long long*)(p.amax + tid_x()), 0ull, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     wait_vm();
     __syncthreads();
   }
@@ -2245,6 +2264,10 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       barrier_arrive(p, gen);
       uint64_t* trec = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
       const int type = rfl(describe(p, l, i, g, &sm.route, ly));
+      if (l == p.L) {  // LM head: logits optional on greedy steps, per-workgroup argmax keys
+        if (tid_x() < MK_MAX_M) sm.hmax[tid_x()] = 0ull;
+        g.hmax = p.greedy ? sm.hmax : nullptr;
+      }
       scalarize(g);
       if (trec && tid_x() == 0) gp(trec)[10] = wall_clock64();
       const bool early = type == PT_GEMV;  // prepared while waiting
@@ -2313,8 +2336,36 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         default:
           break;
       }
+      if (l == p.L && p.greedy) {  // the workgroup's keys into the device-wide ones
+        __syncthreads();
+        if (tid_x() < M && sm.hmax[tid_x()] != 0ull)
+          __hip_atomic_fetch_max((GLOBAL unsigned long long*)(p.amax + tid_x()), sm.hmax[tid_x()], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
       wait_vm();
       if (trec && tid_x() == 0) gp(trec)[8] = wall_clock64();
+    }
+  }
+  if (p.greedy) {  // one more barrier, then workgroup 0 turns the keys into tokens and accepts drafts
+    barrier_arrive(p, gen);
+    if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort);
+    MK_FINISH();
+    if (blockIdx.x == 0) {
+      const int tid = tid_x();
+      if (tid < M) {
+        const unsigned long long key =
+            __hip_atomic_load((GLOBAL unsigned long long*)(p.amax + tid), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int tok = (int)(0xFFFFFFFFu - (uint32_t)key);
+        sm.amx[tid] = tok;
+        gp(p.argmax)[tid] = tok;
+      }
+      __syncthreads();
+      if (p.accepted != nullptr && tid < p.B) {  // drafts accepted while they equal the previous argmax
+        const int T = p.T;
+        int n = 0;
+        while (n + 1 < T && gp(p.tokens)[tid * T + n + 1] == sm.amx[tid * T + n]) ++n;
+        gp(p.accepted)[tid] = n;
+      }
     }
   }
   if (p.trace) {

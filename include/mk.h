@@ -136,6 +136,23 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor_desc* descs, int n, void* hip_s
 int mk_decode_step(mk_ctx* ctx, int batch, int n_new_tokens, int kv_len, const int32_t* d_tokens, void* d_kv,
                    float* d_kda_state, float* d_logits, int32_t* d_route, void* hip_stream);
 
+/* The same step with greedy selection fused after the LM head (the pages' serving loop picks the
+ * next token on the device: tpu-megakernels README, section on the servers' generation modes;
+ * drafts verified in one step: news summary "谷歌TPU v7推理Kimi K3性能超英伟达GB200 57%", background
+ * section). d_argmax [batch][n_new_tokens] int32 (device, required) receives, for every new
+ * position, the index of its largest logit (the lowest such index on ties). d_logits may be NULL:
+ * the logits are then not written. d_accepted [batch] int32 (device, may be NULL) receives, for
+ * each sequence, the number of draft tokens accepted by greedy verification: tokens[b][1..T-1] are
+ * drafts, and draft j is accepted while tokens[b][j] == argmax[b][j-1] for every j up to it. The
+ * step then yields accepted + 1 tokens for the sequence -- the accepted drafts and
+ * argmax[b][accepted] -- and the caller continues from kv_len + accepted + 1 (the cache entries of
+ * the accepted positions are already written; later ones are overwritten by the next step). One
+ * kernel launch, asynchronous on hip_stream; same errors as mk_decode_step, plus MK_E_INVAL for a
+ * NULL d_argmax. */
+int mk_decode_step_greedy(mk_ctx* ctx, int batch, int n_new_tokens, int kv_len, const int32_t* d_tokens, void* d_kv,
+                          float* d_kda_state, float* d_logits, int32_t* d_argmax, int32_t* d_accepted,
+                          void* hip_stream);
+
 /* After the caller synchronised the step's stream: MK_OK, or MK_E_DEVICE if the kernel reported a
  * watchdog timeout or an out-of-range token (the context is then poisoned). */
 int mk_poll(mk_ctx* ctx);

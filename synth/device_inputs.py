@@ -133,6 +133,23 @@ class DeviceModel:
                                rt.data_ptr() if rt is not None else 0, self.stream)
         return logits, rt
 
+    def step_greedy(self, tokens: np.ndarray, kv_len: int, logits: torch.Tensor | None = None,
+                    d_tokens: torch.Tensor | None = None, argmax: torch.Tensor | None = None,
+                    accepted: torch.Tensor | None = None):
+        """A greedy step: returns (argmax [B][T] int32, accepted [B] int32); logits are written only if given."""
+        B, T = tokens.shape
+        if d_tokens is None:
+            d_tokens = torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).to(self.device)
+        if argmax is None:
+            argmax = torch.full((B, T), -1, dtype=torch.int32, device=self.device)
+        if accepted is None:
+            accepted = torch.full((B,), -1, dtype=torch.int32, device=self.device)
+        self.mk.mk_decode_step_greedy(self.ctx, B, T, kv_len, d_tokens.data_ptr(), self.kv.data_ptr(),
+                                      self.state.data_ptr() if self.state is not None else 0,
+                                      logits.data_ptr() if logits is not None else 0, argmax.data_ptr(),
+                                      accepted.data_ptr(), self.stream)
+        return argmax, accepted
+
     def set_matrix_cores(self, min_rows: int):
         """Steps with at least min_rows token rows run their GEMV phases on the matrix cores."""
         self.mk.mk_set_matrix_cores(self.ctx, min_rows)

@@ -185,3 +185,28 @@ def test_matrix_core_threshold_arguments(mk, host_ctx):
         assert e.value.code == mk.MK_E_INVAL
     with pytest.raises(mk.MkError):
         mk.mk_set_matrix_cores(None, 5)
+
+
+def test_greedy_step_argument_errors(mk, host_ctx):
+    cfg, ctx = host_ctx
+    ok = dict(batch=2, n_new_tokens=3, kv_len=10, tokens=1, kv=1, kda_state=0, logits=0, argmax=1, accepted=0)
+
+    def step(**kw):
+        a = dict(ok)
+        a.update(kw)
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_decode_step_greedy(ctx, **a)
+        return e.value.code
+
+    assert step(argmax=0) == mk.MK_E_INVAL
+    assert step(batch=0) == mk.MK_E_INVAL
+    assert step(n_new_tokens=cfg.max_new_tokens + 1) == mk.MK_E_INVAL
+    assert step(tokens=0) == mk.MK_E_INVAL
+    assert step(kv=0) == mk.MK_E_INVAL
+    assert step(kv_len=cfg.kv_capacity - 1) == mk.MK_E_KV_OVERFLOW
+    # logits and accepted are optional: the arguments are valid, the weights are missing
+    assert step() == mk.MK_E_STATE
+    assert step(logits=1, accepted=1) == mk.MK_E_STATE
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_decode_step_greedy(None, 1, 1, 0, 1, 1, 0, 0, 1)
+    assert e.value.code == mk.MK_E_INVAL

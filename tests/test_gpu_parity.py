@@ -228,3 +228,67 @@ def test_k3_full_batch8():
 def test_hybrid_full_batch8():
     w = synth.WORKLOADS["c5"]
     parity(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
+
+
+# --------------------------------------------------------------------------------------------
+# greedy steps: argmax fused after the LM head, draft acceptance on the device
+# --------------------------------------------------------------------------------------------
+def oracle_greedy(cfg, spec, toks, kv_len):
+    import oracle
+
+    from greedy_ref import greedy_tokens
+
+    caches = synth.host_caches(cfg, spec, toks.shape[0], kv_len, cache_batch=cfg.max_batch)
+    ref = oracle.decode_step(cfg, oracle.Provider(cfg, spec), toks, kv_len, caches, cache_batch=cfg.max_batch)
+    return greedy_tokens(ref["logits"])
+
+
+def greedy_check(cfg, spec, toks, kv_len, expect_accepted=None):
+    from greedy_ref import accepted_drafts, greedy_tokens
+
+    B, T = toks.shape
+    print(f"[case] greedy {cfg.name} B={B} T={T} kv_len={kv_len} seed={spec.seed}", flush=True)
+    dm = device_model(cfg, spec)
+    dm.set_matrix_cores(3)
+    dm.fill_caches(B, kv_len)
+    logits = torch.empty((B, T, cfg.vocab), dtype=torch.float32, device="cuda")
+    am, acc = dm.step_greedy(toks, kv_len, logits=logits)
+    torch.cuda.synchronize()
+    dm.poll()
+    am, acc = am.cpu().numpy(), acc.cpu().numpy()
+    # the fused selection agrees with the logits the same step wrote, and with the oracle's
+    assert np.array_equal(am, greedy_tokens(logits.cpu().numpy())), "fused argmax differs from the step's logits"
+    ref = oracle_greedy(cfg, spec, toks, kv_len)
+    assert np.array_equal(am, ref), f"greedy tokens differ: gpu {am.ravel()} oracle {ref.ravel()}"
+    assert np.array_equal(acc, accepted_drafts(toks, ref)), f"accepted {acc} vs {accepted_drafts(toks, ref)}"
+    if expect_accepted is not None:
+        assert acc.tolist() == list(expect_accepted)
+    # the same step without writing logits gives the same selection
+    am2, acc2 = dm.step_greedy(toks, kv_len)
+    torch.cuda.synchronize()
+    dm.poll()
+    assert np.array_equal(am2.cpu().numpy(), am) and np.array_equal(acc2.cpu().numpy(), acc)
+    print(f"[ok] greedy {cfg.name} B={B} T={T}: accepted {acc.tolist()}", flush=True)
+
+
+@pytest.mark.parametrize("B,T,kv_len", [(1, 1, 64), (2, 4, 37), (8, 2, 100)])
+def test_greedy_tiny(B, T, kv_len):
+    spec = synth.Spec(seed=9)
+    greedy_check(synth.TINY, spec, synth.tokens(spec.seed, 0, synth.TINY.vocab, B, T), kv_len)
+
+
+def test_greedy_acceptance_tiny():
+    """Drafts built from the oracle's own greedy continuation are accepted up to the first planted
+    mismatch."""
+    cfg, spec, B, T, kv_len = synth.TINY, synth.Spec(seed=10), 3, 5, 40
+    toks = synth.tokens(spec.seed, 0, cfg.vocab, B, 1)
+    for _ in range(T - 1):  # extend every sequence by the oracle's greedy token for its prefix
+        toks = np.concatenate([toks, oracle_greedy(cfg, spec, toks, kv_len)[:, -1:]], axis=1)
+    toks[0, 3] = (toks[0, 3] + 1) % cfg.vocab  # sequence 0: drafts 1 and 2 accepted
+    toks[1, 1] = (toks[1, 1] + 1) % cfg.vocab  # sequence 1: none
+    greedy_check(cfg, spec, toks, kv_len, expect_accepted=[2, 0, 4])
+
+
+def test_greedy_k3_two_layers_verify():
+    spec = synth.Spec(seed=2)
+    greedy_check(K3_SMALL, spec, synth.tokens(spec.seed, 3, K3_SMALL.vocab, 1, 7), 4096)
