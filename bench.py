@@ -267,6 +267,61 @@ def print_trace(summary: dict) -> None:
 
 
 # ------------------------------------------------------------------------------------------
+# Speculative decoding around the verify step, with synthetic drafts: the target's own greedy
+# continuation (T=1 greedy steps) supplies drafts that are accepted; mismatching drafts after the
+# first L-1 make the step yield L tokens (L-1 accepted drafts and the bonus token).
+# ------------------------------------------------------------------------------------------
+def speculative(dm, cfg, spec, v, steps: int, warmup: int, stream) -> dict:
+    import torch
+
+    T, kv_len = v.new_tokens, v.kv_len
+    tok = synth.tokens(spec.seed, 7, cfg.vocab, 1, 1)
+    cont = [int(tok[0, 0])]
+    for j in range(T - 1):  # greedy continuation, one token per step
+        am, _ = dm.step_greedy(np.array([[cont[-1]]], dtype=np.int32), kv_len + j)
+        torch.cuda.synchronize()
+        cont.append(int(am.cpu().numpy()[0, 0]))
+    dm.poll()
+    out = {"new_tokens_per_step": T, "drafts": "the target's greedy continuation, then mismatching tokens",
+           "lengths": {}}
+    # plain greedy decode (one token, no logits written) for comparison
+    one = np.array([[cont[0]]], dtype=np.int32)
+    d_one = torch.from_numpy(one).cuda()
+    am1 = torch.empty((1, 1), dtype=torch.int32, device="cuda")
+    acc1 = torch.empty((1,), dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        dm.step_greedy(one, kv_len, d_tokens=d_one, argmax=am1, accepted=acc1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dm.step_greedy(one, kv_len, d_tokens=d_one, argmax=am1, accepted=acc1)
+    torch.cuda.synchronize()
+    ms1 = (time.perf_counter() - t0) * 1e3 / steps
+    out["greedy_decode_b1"] = {"ms_per_step": round(ms1, 4), "tokens_per_s": round(1e3 / ms1, 2)}
+    for L in (3, 6):  # tokens yielded per step
+        toks = np.array([cont[:L] + [(c + 1) % cfg.vocab for c in cont[L:T]]], dtype=np.int32)
+        d_tok = torch.from_numpy(toks).cuda()
+        am = torch.empty((1, T), dtype=torch.int32, device="cuda")
+        acc = torch.empty((1,), dtype=torch.int32, device="cuda")
+        for _ in range(warmup):
+            dm.step_greedy(toks, kv_len, d_tokens=d_tok, argmax=am, accepted=acc)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            dm.step_greedy(toks, kv_len, d_tokens=d_tok, argmax=am, accepted=acc)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        dm.poll()
+        yielded = int(acc.cpu().numpy()[0]) + 1
+        out["lengths"][str(L)] = {"accepted_drafts": yielded - 1, "tokens_per_step": yielded,
+                                  "ms_per_step": round(ms, 4), "accepted_tokens_per_s": round(yielded * 1e3 / ms, 2)}
+        print(f"# speculative T={T} length {L}: {yielded} tokens/step, {ms:.3f} ms, "
+              f"{yielded * 1e3 / ms:.1f} accepted tok/s", file=sys.stderr, flush=True)
+    print(f"# greedy decode B=1: {ms1:.3f} ms, {1e3 / ms1:.1f} tok/s", file=sys.stderr, flush=True)
+    return out
+
+
+# ------------------------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,10 +417,11 @@ def main():
         return r
 
     results = {B: measure(B, w.new_tokens, args.trace) for B in batches}
-    verify = None
+    verify = spec_dec = None
     if args.workload == "c3" and not args.no_verify:
         v = synth.WORKLOADS["c4"]
         verify = measure(v.batch, v.new_tokens, False)
+        spec_dec = speculative(dm, cfg, spec, v, args.steps, args.warmup, stream)
     dm.close()
 
     head = results[batches[0]]
@@ -393,6 +449,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(batches[0])},
     }
+    if spec_dec is not None:
+        out["speculative"] = spec_dec
     if verify is not None:  # positions verified per second (1 + 6 draft tokens per step)
         out["verify_t7"] = {"positions_per_s": round(verify["tokens_per_s"], 2),
                             "kernel_ms": round(verify["kernel_ms_avg"], 4),
