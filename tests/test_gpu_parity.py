@@ -26,7 +26,8 @@ def device_model(cfg, spec):
     """One resident model at a time (the K3-scale arenas take ~200 GB each)."""
     from synth.device_inputs import DeviceModel
 
-    key = (cfg, spec.seed, tuple(sorted(spec.sigma_by_kind.items())))
+    key = (cfg, spec.seed, spec.sigma, spec.gain_sigma, spec.cache_sigma, spec.state_sigma,
+           tuple(sorted(spec.sigma_by_kind.items())))
     if key not in _models:
         for k in list(_models):
             _models.pop(k).close()
@@ -292,3 +293,87 @@ def test_greedy_acceptance_tiny():
 def test_greedy_k3_two_layers_verify():
     spec = synth.Spec(seed=2)
     greedy_check(K3_SMALL, spec, synth.tokens(spec.seed, 3, K3_SMALL.vocab, 1, 7), 4096)
+
+
+# --------------------------------------------------------------------------------------------
+# speculative decoding loop: verify steps with fused acceptance, kv_len rolled back to the
+# accepted prefix between rounds
+# --------------------------------------------------------------------------------------------
+MLA_SMALL = replace(synth.K3, name="mla-small", n_layers=2, hidden=1024, vocab=4096, q_lora=512, n_experts=8,
+                    ffn=512, shared_ffn=256, expert_pool_layers=0, max_batch=1, kv_capacity=160)
+
+
+def oracle_greedy_continuation(cfg, spec, first, kv_len, n):
+    """The target's plain greedy decode: n tokens after `first`, one oracle step per token, the
+    oracle's cache growing by one row per step. Returns the tokens, the oracle's caches and the
+    smallest top-2 logit margin (relative to the row's largest logit)."""
+    import oracle
+
+    from greedy_ref import greedy_tokens
+
+    caches = synth.host_caches(cfg, spec, 1, kv_len, cache_batch=cfg.max_batch)
+    prov = oracle.Provider(cfg, spec)
+    seq, margin = [first], np.inf
+    for j in range(n):
+        ref = oracle.decode_step(cfg, prov, np.array([[seq[-1]]], dtype=np.int32), kv_len + j, caches,
+                                 cache_batch=cfg.max_batch)
+        lg = ref["logits"][0, 0]
+        top = np.sort(lg)[-2:]
+        margin = min(margin, (top[1] - top[0]) / np.abs(lg).max())
+        seq.append(int(greedy_tokens(lg)))
+    return np.array(seq, dtype=np.int32), caches, margin
+
+
+def speculative_loop(cfg, spec, T, kv_len, keep):
+    """Round r verifies the last yielded token followed by T-1 drafts: the target's own greedy
+    continuation with draft keep[r]+1 changed, so exactly keep[r] drafts are accepted (the drafts
+    after the changed one are right again: acceptance stops at the first mismatch). The round
+    yields the accepted drafts and the target's token after them, and the next round starts at
+    kv_len + the tokens yielded so far, overwriting the cache rows of the rejected drafts. The
+    yielded tokens must be the plain greedy continuation, and the cache rows of the yielded
+    positions those of the plain decode."""
+    n = sum(k + 1 for k in keep)
+    assert kv_len + n + T <= cfg.kv_capacity
+    first = int(synth.tokens(spec.seed, 11, cfg.vocab, 1, 1)[0, 0])
+    seq, caches, margin = oracle_greedy_continuation(cfg, spec, first, kv_len, n + T - 1)
+    print(f"[case] speculative {cfg.name} T={T} kv_len={kv_len} keep={keep} seed={spec.seed} "
+          f"oracle top-2 margin {margin:.2e}", flush=True)
+    dm = device_model(cfg, spec)
+    dm.set_matrix_cores(3)
+    dm.fill_caches(1, kv_len)
+    pos = 0
+    for r, k in enumerate(keep):
+        toks = seq[pos:pos + T].copy()
+        if k + 1 < T:
+            toks[k + 1] = (toks[k + 1] + 1) % cfg.vocab
+        am, acc = dm.step_greedy(toks[None, :], kv_len + pos)
+        torch.cuda.synchronize()
+        dm.poll()
+        am, acc = am.cpu().numpy()[0], int(acc.cpu().numpy()[0])
+        assert acc == k, f"round {r}: {acc} drafts accepted, expected {k} (gpu tokens {am}, drafts {toks})"
+        want = seq[pos + 1:pos + acc + 2]
+        assert np.array_equal(am[:acc + 1], want), f"round {r}: yielded {am[:acc + 1]}, greedy decode {want}"
+        pos += acc + 1
+    assert pos == n
+    rows = slice(kv_len, kv_len + pos)
+    if cfg.attn_kind == synth.ATTN_GQA:
+        gk, gv = dm.gqa_cache()
+        pairs = [(gk[:, :1, :, rows], caches["k"][:, :1, :, rows]), (gv[:, :1, :, rows], caches["v"][:, :1, :, rows])]
+    else:
+        pairs = [(dm.latent_cache()[:, :1, rows], caches["latent"][:, :1, rows])]
+    for g, o in pairs:  # a row left from a rejected draft would differ at O(1)
+        a, b = bf(g), bf(o)
+        err = (np.abs(a - b).max(axis=-1) / np.abs(b).max(axis=-1)).max()
+        assert err < 2e-2, f"cache rows of the yielded tokens differ from the greedy decode's: {err:.3e}"
+    print(f"[ok] speculative {cfg.name}: {len(keep)} rounds yielded {pos} tokens", flush=True)
+
+
+def test_speculative_loop_tiny_t8():
+    # one anchor + 7 drafts per round
+    # weights at sigma 0.05: a greedy continuation that does not settle into a repeated token
+    speculative_loop(synth.TINY, synth.Spec(seed=12, sigma=0.05), 8, 40, [7, 0, 3, 1, 6, 2])
+
+
+def test_speculative_loop_mla_t7():
+    # the verify workload's shape: one anchor + 6 drafts, latent cache
+    speculative_loop(MLA_SMALL, synth.Spec(seed=15, sigma=0.05), 7, 64, [6, 2, 0, 5, 3])
