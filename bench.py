@@ -185,13 +185,17 @@ PHASES = {
     "kda": ["qkv", "delta_rule", "w_o"],
 }
 MOE_PHASES = ["router+shared_up", "experts_up", "experts_down"]
+DENSE_PHASES = ["gate+up", "down"]  # n_experts = 0: the SwiGLU block alone
 
 
 def phase_names(cfg) -> list[str]:
     names = ["embed"]
     for l in range(cfg.n_layers):
         kind = cfg.layer_kind(l)
-        names += [f"{kind}:{p}" for p in PHASES[kind]] + [f"moe:{p}" for p in MOE_PHASES]
+        if cfg.n_experts:
+            names += [f"{kind}:{p}" for p in PHASES[kind]] + [f"moe:{p}" for p in MOE_PHASES]
+        else:
+            names += [f"{kind}:{p}" for p in PHASES[kind]] + [f"ffn:{p}" for p in DENSE_PHASES]
     return names + ["lm_head"]
 
 
@@ -331,11 +335,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--trace", action="store_true", help="print per-phase device timings of one step per batch")
-    ap.add_argument("--workload", default=WORKLOAD, choices=["c3", "c4", "c5"],
-                    help="c3: K3-scale share (the headline); c4: its 7-token verify step; c5: the hybrid model "
-                         "(for profiling one path; --batches applies)")
+    ap.add_argument("--workload", default=WORKLOAD, choices=["c3", "c4", "c5", "dense"],
+                    help="c3: K3-scale share (the headline); c4: its 7-token verify step; c5: the hybrid model; "
+                         "dense: the dense 27B-class decoder (for profiling one path; --batches applies)")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the 7-token speculative-verify measurement on the K3-scale share")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-decoder measurement that follows the K3-scale share")
     ap.add_argument("--mfma-min-rows", type=int, default=None,
                     help="token rows from which GEMV phases use the matrix cores (library default if omitted)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -375,7 +381,7 @@ def main():
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    def measure(B: int, T: int, trace: bool) -> dict:
+    def measure(B: int, T: int, trace: bool, dm=dm, cfg=cfg, w=w) -> dict:
         toks = synth.tokens(spec.seed, 1, cfg.vocab, B, T)
         d_tok = torch.from_numpy(toks.astype(np.int32)).cuda()
         logits = torch.empty((B, T, cfg.vocab), dtype=torch.float32, device="cuda")
@@ -423,6 +429,17 @@ def main():
         verify = measure(v.batch, v.new_tokens, False)
         spec_dec = speculative(dm, cfg, spec, v, args.steps, args.warmup, stream)
     dm.close()
+    dense = None
+    if args.workload == "c3" and not args.no_dense:  # the dense second model, after the share is freed
+        wd = synth.WORKLOADS["dense"]
+        t0 = time.time()
+        dmd = DeviceModel(wd.model, spec, device=0)
+        if args.mfma_min_rows is not None:
+            dmd.set_matrix_cores(args.mfma_min_rows)
+        dmd.fill_caches(max(batches), wd.kv_len)
+        print(f"# dense model loaded in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+        dense = {B: measure(B, 1, False, dm=dmd, cfg=wd.model, w=wd) for B in batches}
+        dmd.close()
 
     head = results[batches[0]]
     achieved = head["gbs"]
@@ -451,6 +468,16 @@ def main():
     }
     if spec_dec is not None:
         out["speculative"] = spec_dec
+    if dense is not None:
+        dc = synth.WORKLOADS["dense"].model
+        out["dense"] = {
+            "workload": f"dense GQA decoder: {dc.n_layers} layers, hidden {dc.hidden}, {dc.n_heads} query / "
+                        f"{dc.n_kv_heads} KV heads of {dc.head_dim}, SwiGLU {dc.shared_ffn}, vocab {dc.vocab} "
+                        f"({sum(synth.numel(t.shape) for t in synth.tensor_list(dc)) / 1e9:.1f} B parameters), "
+                        f"KV cache {synth.WORKLOADS['dense'].kv_len}",
+            "batches": {str(B): {"tokens_per_s": round(r["tokens_per_s"], 2), "kernel_ms": round(r["kernel_ms_avg"], 4),
+                                 "gb_per_step": round(r["bytes"] / 1e9, 3), "hbm_gbs": round(r["gbs"], 1),
+                                 "hbm_frac": round(r["gbs"] / HBM_PEAK_GBS, 4)} for B, r in dense.items()}}
     if verify is not None:  # positions verified per second (1 + 6 draft tokens per step)
         out["verify_t7"] = {"positions_per_s": round(verify["tokens_per_s"], 2),
                             "kernel_ms": round(verify["kernel_ms_avg"], 4),

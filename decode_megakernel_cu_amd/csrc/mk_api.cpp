@@ -76,11 +76,16 @@ int check_config(const mk_config* c) {
   if (c->max_new_tokens < 1 || c->max_new_tokens > MK_MAX_NEW_TOKENS)
     return fail(MK_E_INVAL, "max_new_tokens must be in 1..%d", MK_MAX_NEW_TOKENS);
   if (c->kv_capacity < c->max_new_tokens) return fail(MK_E_INVAL, "kv_capacity below max_new_tokens");
-  if (c->n_experts < 1 || c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 8)
-    return fail(MK_E_INVAL, "need 1 <= top_k <= min(n_experts, 8)");
-  if (c->n_experts > kMaxExperts) return fail(MK_E_UNSUPPORTED, "at most %d experts", kMaxExperts);
-  if (c->ffn < 8 || c->ffn % 8 || c->shared_ffn < 0 || c->shared_ffn % 8)
-    return fail(MK_E_UNSUPPORTED, "ffn and shared_ffn must be multiples of 8");
+  if (c->n_experts == 0) {  // dense: the feed-forward block is the shared SwiGLU block alone
+    if (c->top_k != 0 || c->shared_ffn < 8 || c->shared_ffn % 8)
+      return fail(MK_E_INVAL, "a dense model (n_experts 0) needs top_k 0 and shared_ffn a positive multiple of 8");
+  } else {
+    if (c->n_experts < 1 || c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 8)
+      return fail(MK_E_INVAL, "need 1 <= top_k <= min(n_experts, 8)");
+    if (c->n_experts > kMaxExperts) return fail(MK_E_UNSUPPORTED, "at most %d experts", kMaxExperts);
+    if (c->ffn < 8 || c->ffn % 8 || c->shared_ffn < 0 || c->shared_ffn % 8)
+      return fail(MK_E_UNSUPPORTED, "ffn and shared_ffn must be multiples of 8");
+  }
   if (c->expert_pool_layers < 0) return fail(MK_E_INVAL, "expert_pool_layers must be >= 0");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(MK_E_INVAL, "rms_eps / rope_theta out of range");
   if (c->n_heads < 1) return fail(MK_E_INVAL, "n_heads must be positive");
@@ -88,8 +93,10 @@ int check_config(const mk_config* c) {
     if (c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return fail(MK_E_INVAL, "n_heads must be a multiple of n_kv_heads");
     if (c->head_dim < 8 || c->head_dim % 8 || c->head_dim > 2 * kMaxRopePairs)
       return fail(MK_E_UNSUPPORTED, "head_dim must be a multiple of 8 and at most %d", 2 * kMaxRopePairs);
-    const int qg = c->n_heads / c->n_kv_heads;
-    if ((2 * kChunk + c->max_new_tokens * qg) * c->head_dim + c->max_new_tokens * qg * kChunk > kLdsFloats)
+    // the attention tile: bf16 keys and values of kGSub positions, then per query row (new token x
+    // head of the group) the rotated query, the scores, the value sums and two running statistics
+    const int nr = c->max_new_tokens * (c->n_heads / c->n_kv_heads);
+    if (kGSub * c->head_dim + nr * (2 * c->head_dim + kGSub + 2) > kLdsFloats)
       return fail(MK_E_UNSUPPORTED, "GQA group too large for the attention tile");
   } else {
     if (c->kv_lora < 8 || c->kv_lora % 8 || c->q_lora < 8 || c->q_lora % 8 || c->nope_dim < 8 || c->nope_dim % 8 ||
@@ -220,7 +227,7 @@ Layout make_layout(const mk_config& c) {
       d.wo = rel(put(MK_W_WO, l, -1, H * nh * dv * 2));
     }
     d.moe_norm = rel(put(MK_W_MOE_NORM, l, -1, H * 2));
-    d.router = rel(put(MK_W_ROUTER, l, -1, E * H * 2));
+    if (E) d.router = rel(put(MK_W_ROUTER, l, -1, E * H * 2));
     if (SF) {
       d.sh_gate = rel(put(MK_W_SH_GATE, l, -1, SF * H * 2));
       d.sh_up = rel(put(MK_W_SH_UP, l, -1, SF * H * 2));
@@ -494,12 +501,15 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   p.SF = g.shared_ffn; p.norm_topk = g.norm_topk; p.cap = g.kv_capacity; p.Bmax = g.max_batch;
   p.eps = g.rms_eps; p.rope_theta = g.rope_theta;
   p.B = B; p.T = T; p.M = M; p.kv_len = kv_len;
-  // split-KV: GQA uses fixed chunks; MLA sizes them so that the tasks of the step fill the grid
+  // split-KV: chunks (at least kChunk positions) sized so that the tasks of the step about fill the grid
   const int npos = kv_len + T;
   p.chunk = kChunk;
   if (g.attn_kind != MK_ATTN_GQA && c->nblocks > 0) {  // whole kSub-position tiles per task
     const int even = (int)(((long long)B * npos + c->nblocks - 1) / c->nblocks);
     p.chunk = (std::max(kChunk, even) + kSub - 1) / kSub * kSub;
+  } else if (c->nblocks > 0) {  // GQA: tasks (sequence, kv head, split) about fill the grid
+    const int even = (int)(((long long)B * g.n_kv_heads * npos + c->nblocks - 1) / c->nblocks);
+    p.chunk = (std::max(kChunk, even) + kChunk - 1) / kChunk * kChunk;
   }
   p.nsplit = (npos + p.chunk - 1) / p.chunk;
   p.epoch = (uint32_t)(c->launches * 65536ull);
@@ -532,9 +542,9 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   if (e != hipSuccess) return fail(MK_E_HIP, "launch failed: %s", hipGetErrorString(e));
   c->launches++;
   int nb = greedy ? 2 : 1;  // the LM head's barrier, and the one before the greedy results
-  for (int l = 0; l < g.n_layers; ++l) {
+  for (int l = 0; l < g.n_layers; ++l) {  // attention phases, then 3 MoE phases (dense: 2)
     const int k = layer_kind(g, l);
-    nb += k == kGqa ? 7 : k == kMla ? 10 : 6;
+    nb += (k == kGqa ? 4 : k == kMla ? 7 : 3) + (g.n_experts ? 3 : 2);
   }
   c->last_barriers = nb;
   g_err.clear();

@@ -1381,138 +1381,164 @@ __device__ __forceinline__ void rope_pair(const float* table, int t, int j, floa
   x1 = b * c + a * s;
 }
 
-// GQA split-KV partials. Task (b, g, s): positions [s*C, s*C+C) of sequence b, kv head g, every
-// query head of the group and every new token. New positions in the chunk are appended here.
+// GQA split-KV partials (flash decoding). Task (b, g, s): positions [s*C, s*C+C) of sequence b,
+// kv head g, every query head of the group and every new token (rows r = t*qg + head in group).
+// The task streams its positions in sub-tiles of kGSub: the cache rows of the next sub-tile are
+// requested (into registers) while the current one is scored, and each row keeps a running
+// maximum, sum of weights and unnormalised value sum (online softmax), so the task writes one
+// partial whatever its length. New positions in the chunk are rotated, rounded to bf16, appended
+// to the cache and attended from the rounded values.
 __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
                                                const float* rope) {
   const int d = p.hd, nq = p.nh, nkv = p.nkv, T = p.T, cap = p.cap, d2 = d / 2, d4 = d / 4, d8 = d / 8;
-  const int npos = p.kv_len + T, C = p.chunk;
-  const int nsplit = p.nsplit;
-  const int qg = nq / nkv;
+  const int npos = p.kv_len + T, C = p.chunk, nsplit = p.nsplit, kvl = p.kv_len;
+  const int qg = nq / nkv, nr = T * qg;
   const int ntask = p.B * nkv * nsplit;
-  const int tid = tid_x();
-  float* Ks = smem;             // [C][d]
-  float* Vs = Ks + C * d;       // [C][d]
-  float* Qs = Vs + C * d;       // [T*qg][d]
-  float* S = Qs + T * qg * d;   // [T*qg][C]
+  const int tid = tid_x(), lane = lane_id();
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(smem);  // [kGSub][d] bf16
+  uint16_t* Vb = Kb + kGSub * d;                     // [kGSub][d] bf16
+  float* Qs = smem + kGSub * d;                      // [nr][d] rotated queries
+  float* S = Qs + nr * d;                            // [nr][kGSub] scores, then weights
+  float* Acc = S + nr * kGSub;                       // [nr][d] unnormalised value sums
+  float* Mx = Acc + nr * d;                          // [nr] running maximum
+  float* Ls = Mx + nr;                               // [nr] running sum of weights
   const size_t lstride = (size_t)p.Bmax * nkv * cap * d;
   uint16_t* Kc = rflp(p.kv) + (size_t)rfl(ly->ord) * lstride;
   uint16_t* Vc = rflp(p.kv) + (size_t)p.L * lstride + (size_t)rfl(ly->ord) * lstride;
   const float scale = 1.0f / sqrtf((float)d);
-  const int stride = d + kPartPad;
+  const int stride = d + kPartPad, U = kGSub * d8;  // U: 16-byte units of K (and of V) per sub-tile
+  constexpr int kU = kGSub * 16 / kThreads;         // units per thread (head_dim <= 128)
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int s = task % nsplit, g = (task / nsplit) % nkv, b = task / (nsplit * nkv);
-    const int p0 = s * C, p1 = min(npos, p0 + C), np = p1 - p0;
-    const size_t row0 = ((size_t)b * nkv + g) * cap;  // cache row of position 0
-    __syncthreads();
-    // cached rows (bf16, 8 per load), then the raw queries and new rows (coherent)
-    {
-      const int ncu = np * d8;
-      for (int b0 = 0; b0 < ncu; b0 += 2 * kThreads) {
-        uint4 kv4[2], vv4[2];
+    const int p0 = s * C, p1 = min(npos, p0 + C), pc = min(p1, kvl);  // [p0, pc): cached positions
+    const size_t row0 = ((size_t)b * nkv + g) * cap;                     // cache row of position 0
+    uint4 kr[kU], vr[kU];
+    auto issue = [&](int q0) {  // the cached rows of the sub-tile at q0 (others read row 0)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          if (b0 + u * kThreads < ncu) {
-            const int i = min(b0 + u * kThreads + tid, ncu - 1), pl = i / d8, c = i - pl * d8, pos = p0 + pl;
-            const size_t off = (row0 + (pos < p.kv_len ? pos : 0)) * d + 8 * c;
-            kv4[u] = ldw(Kc + off);
-            vv4[u] = ldw(Vc + off);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int i = b0 + u * kThreads + tid;
-          if (b0 + u * kThreads < ncu && i < ncu) {
-            const int pl = i / d8, c = i - pl * d8;
-            if (p0 + pl < p.kv_len) {
-              float f[8];
-              unpack8(kv4[u], f);
-              for (int j = 0; j < 8; ++j) Ks[pl * d + 8 * c + j] = f[j];
-              unpack8(vv4[u], f);
-              for (int j = 0; j < 8; ++j) Vs[pl * d + 8 * c + j] = f[j];
-            }
-          }
-        }
+      for (int u = 0; u < kU; ++u) {
+        const int i = u * kThreads + tid, pl = i / d8, c = i - pl * d8, pos = q0 + pl;
+        const size_t off = (row0 + ((i < U && pos < pc) ? pos : 0)) * d + 8 * (i < U ? c : 0);
+        kr[u] = ldw(Kc + off);
+        vr[u] = ldw(Vc + off);
       }
-    }
+    };
+    __syncthreads();
+    issue(p0);
     copy_units<4>(
-        ws, T * qg * d4,
+        ws, nr * d4,
         [&](int i) {
           const int r = i / d4, t = r / qg, hq = g * qg + (r - t * qg);
           return p.a1 + (size_t)(b * T + t) * nq * d + hq * d + 4 * (i - r * d4);
         },
         [&](int i) { return Qs + 4 * i; });
-    const int n0 = max(p0, p.kv_len), nnew = max(0, p1 - n0);
-    copy_units<2>(
-        ws, nnew * 2 * d4,
-        [&](int i) {
-          const int r = i / (2 * d4), c = i - r * 2 * d4, m = b * T + (n0 - p.kv_len) + r;
-          return (c < d4 ? p.a2 : p.a3) + (size_t)m * nkv * d + g * d + 4 * (c < d4 ? c : c - d4);
-        },
-        [&](int i) {
-          const int r = i / (2 * d4), c = i - r * 2 * d4, pl = n0 - p0 + r;
-          return (c < d4 ? Ks : Vs) + pl * d + 4 * (c < d4 ? c : c - d4);
-        });
+    for (int e = tid; e < nr * d; e += kThreads) Acc[e] = 0.f;
+    for (int e = tid; e < nr; e += kThreads) {
+      Mx[e] = -INFINITY;
+      Ls[e] = 0.f;
+    }
     __syncthreads();
-    // rotate the queries and the new keys; round new rows to bf16 and append them
-    for (int e = tid; e < T * qg * d2; e += kThreads) {
+    for (int e = tid; e < nr * d2; e += kThreads) {  // rotate the queries
       const int r = e / d2, j = e - r * d2, t = r / qg;
       float q0 = Qs[r * d + j], q1 = Qs[r * d + j + d2];
       rope_pair(rope, t, j, q0, q1);
       Qs[r * d + j] = q0;
       Qs[r * d + j + d2] = q1;
     }
-    for (int e = tid; e < nnew * d2; e += kThreads) {
-      const int r = e / d2, j = e - r * d2, pl = n0 - p0 + r, t = n0 - p.kv_len + r;
-      float k0 = Ks[pl * d + j], k1 = Ks[pl * d + j + d2];
-      rope_pair(rope, t, j, k0, k1);
-      const uint16_t kb0 = f2bf(k0), kb1 = f2bf(k1);
-      const uint16_t vb0 = f2bf(Vs[pl * d + j]), vb1 = f2bf(Vs[pl * d + j + d2]);
-      const size_t ci = (row0 + n0 + r) * d;
-      gp(Kc)[ci + j] = kb0;
-      gp(Kc)[ci + j + d2] = kb1;
-      gp(Vc)[ci + j] = vb0;
-      gp(Vc)[ci + j + d2] = vb1;
-      Ks[pl * d + j] = bf2f(kb0);
-      Ks[pl * d + j + d2] = bf2f(kb1);
-      Vs[pl * d + j] = bf2f(vb0);
-      Vs[pl * d + j + d2] = bf2f(vb1);
-    }
-    __syncthreads();
-    const int nr = T * qg;
-    for (int e = tid; e < nr * C; e += kThreads) {
-      const int r = e / C, pl = e - r * C, t = r / qg;
-      float sc = -INFINITY;
-      if (pl < np && p0 + pl <= p.kv_len + t) {
-        float acc = 0.f;
-        for (int j = 0; j < d; j += 4)
-          acc += dot4(*reinterpret_cast<const f32x4*>(Qs + r * d + j), *reinterpret_cast<const f32x4*>(Ks + pl * d + j));
-        sc = acc * scale;
-      }
-      S[r * C + pl] = sc;
-    }
-    __syncthreads();
-    for (int r = wave_id(); r < nr; r += kWaves) {
-      const int t = r / qg, hq = g * qg + (r - t * qg), m = b * T + t;
-      float mx = -INFINITY;
-      for (int pl = 0; pl < C; ++pl) mx = fmaxf(mx, S[r * C + pl]);
-      float* dst = p.part + ((size_t)(m * nq + hq) * nsplit + s) * stride;
-      float l = 0.f;
-      for (int j = lane_id(); j < d; j += 64) {
-        float acc = 0.f;
-        l = 0.f;
-        if (mx != -INFINITY) {
-          for (int pl = 0; pl < np; ++pl) {
-            const float w = (S[r * C + pl] == -INFINITY) ? 0.f : __expf(S[r * C + pl] - mx);
-            l += w;
-            acc += w * Vs[pl * d + j];
-          }
+    for (int q0 = p0; q0 < p1; q0 += kGSub) {
+      const int ns = min(kGSub, p1 - q0);
+      __syncthreads();  // the previous sub-tile is consumed
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {  // cached rows into LDS
+        const int i = u * kThreads + tid, pl = i / d8, c = i - pl * d8;
+        if (i < U && q0 + pl < pc) {
+          *reinterpret_cast<uint4*>(Kb + pl * d + 8 * c) = kr[u];
+          *reinterpret_cast<uint4*>(Vb + pl * d + 8 * c) = vr[u];
         }
-        stc(dst + kPartPad + j, acc);
       }
-      if (lane_id() == 0) {
-        stc(dst, mx);
-        stc(dst + 1, l);
+      if (q0 + kGSub < pc) issue(q0 + kGSub);
+      // new positions of the sub-tile: rotate the key, round to bf16, append, stage
+      const int n0 = max(q0, kvl), nn = max(0, q0 + ns - n0);
+      for (int e = tid; e < nn * d2; e += kThreads) {
+        const int r = e / d2, j = e - r * d2, pl = n0 - q0 + r, t = n0 - kvl + r, m = b * T + t;
+        const float* kp = p.a2 + (size_t)m * nkv * d + g * d;
+        const float* vp = p.a3 + (size_t)m * nkv * d + g * d;
+        float k0 = ws.ld1(kp + j), k1 = ws.ld1(kp + j + d2);
+        const float v0 = ws.ld1(vp + j), v1 = ws.ld1(vp + j + d2);
+        rope_pair(rope, t, j, k0, k1);
+        const uint16_t kb0 = f2bf(k0), kb1 = f2bf(k1), vb0 = f2bf(v0), vb1 = f2bf(v1);
+        const size_t ci = (row0 + n0 + r) * d;
+        gp(Kc)[ci + j] = kb0;
+        gp(Kc)[ci + j + d2] = kb1;
+        gp(Vc)[ci + j] = vb0;
+        gp(Vc)[ci + j + d2] = vb1;
+        Kb[pl * d + j] = kb0;
+        Kb[pl * d + j + d2] = kb1;
+        Vb[pl * d + j] = vb0;
+        Vb[pl * d + j + d2] = vb1;
+      }
+      __syncthreads();
+      for (int e = tid; e < nr * kGSub; e += kThreads) {  // scores, causal among the new positions
+        const int r = e / kGSub, pl = e - r * kGSub, t = r / qg;
+        float sc = -INFINITY;
+        if (pl < ns && q0 + pl <= kvl + t) {
+          float acc = 0.f;
+#pragma unroll 4
+          for (int j = 0; j < d; j += 8) {
+            float kf[8];
+            unpack8(*reinterpret_cast<const uint4*>(Kb + pl * d + j), kf);
+            const f32x4 qa = *reinterpret_cast<const f32x4*>(Qs + r * d + j);
+            const f32x4 qb = *reinterpret_cast<const f32x4*>(Qs + r * d + j + 4);
+            acc += qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3] + qb.x * kf[4] + qb.y * kf[5] +
+                   qb.z * kf[6] + qb.w * kf[7];
+          }
+          sc = acc * scale;
+        }
+        S[r * kGSub + pl] = sc;
+      }
+      __syncthreads();
+      for (int r = wave_id(); r < nr; r += kWaves) {  // online softmax: one wave per row
+        const float sv = S[r * kGSub + lane];
+        const float mold = Mx[r], mnew = fmaxf(mold, wave_max(sv, 64));
+        if (mnew == -INFINITY) continue;  // nothing visible to this row yet
+        const float alpha = mold == -INFINITY ? 0.f : __expf(mold - mnew);
+        const float w = sv == -INFINITY ? 0.f : __expf(sv - mnew);
+        const float ls = wave_sum(w, 64);
+        S[r * kGSub + lane] = w;  // read back by the same wave: its LDS accesses stay in order
+        __builtin_amdgcn_wave_barrier();
+        if (2 * lane < d) {  // eight positions per step: their loads are in flight together
+          float a0 = 0.f, a1 = 0.f;
+          const uint16_t* vcol = Vb + 2 * lane;
+          for (int pl0 = 0; pl0 < ns; pl0 += 8) {
+            const f32x4 wa = *reinterpret_cast<const f32x4*>(S + r * kGSub + pl0);
+            const f32x4 wb = *reinterpret_cast<const f32x4*>(S + r * kGSub + pl0 + 4);
+            const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+            uint32_t v2[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)  // rows past ns hold stale values: weight 0, value not read
+              v2[k] = pl0 + k < ns ? *reinterpret_cast<const uint32_t*>(vcol + (pl0 + k) * d) : 0u;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              a0 += wv[k] * __uint_as_float(v2[k] << 16);
+              a1 += wv[k] * __uint_as_float(v2[k] & 0xFFFF0000u);
+            }
+          }
+          Acc[r * d + 2 * lane] = alpha * Acc[r * d + 2 * lane] + a0;
+          Acc[r * d + 2 * lane + 1] = alpha * Acc[r * d + 2 * lane + 1] + a1;
+        }
+        if (lane == 0) {
+          Mx[r] = mnew;
+          Ls[r] = alpha * Ls[r] + ls;
+        }
+      }
+    }
+    __syncthreads();
+    for (int r = wave_id(); r < nr; r += kWaves) {  // the task's partial: max, sum, values
+      const int t = r / qg, hq = g * qg + (r - t * qg), m = b * T + t;
+      float* dst = p.part + ((size_t)(m * nq + hq) * nsplit + s) * stride;
+      for (int j = lane; j < d; j += 64) stc(dst + kPartPad + j, Acc[r * d + j]);
+      if (lane == 0) {
+        stc(dst, Mx[r]);
+        stc(dst + 1, Ls[r]);
       }
     }
   }
@@ -2030,7 +2056,8 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
       g.kind = G_RS;
       g.E = p.E;
       g.SF = p.SF;
-      g.W0 = g.safe = ly->router;
+      g.W0 = ly->router;
+      g.safe = p.E ? ly->router : ly->sh_gate;  // dense: no router rows
       g.Wg = ly->sh_gate;
       g.Wu = ly->sh_up;
       g.rlog = p.rlog;
@@ -2039,7 +2066,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
       g.pairs = p.SF > 0 ? 2 : 1;
       return PT_GEMV;
     }
-    if (i == na + 1) {
+    if (i == na + 1 && p.E > 0) {  // a dense model has no routed-expert phase
       norm_input(g, p.x, p.H, p.H, ly->moe_norm);
       g.kind = G_EXP;
       g.F = p.F;
@@ -2061,7 +2088,8 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
     g.SF = p.SF;
     g.H = p.H;
     g.K = g.Wst = p.F > p.SF ? p.F : p.SF;
-    g.Wg = g.safe = ly->exp_down;
+    g.Wg = ly->exp_down;
+    g.safe = p.E ? ly->exp_down : ly->sh_down;  // dense: the (empty) expert pool has no rows
     g.Wu = ly->sh_down;
     g.out0 = p.x;
     g.ldo0 = p.H;
@@ -2239,6 +2267,10 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       sm.rope[(t * kMaxRopePairs + j) * 2 + 1] = (float)sin(a);
     }
     fetch_layer(p, sm.lyd, 0);
+    if (tid_x() == 0) {  // no routed experts until a routing phase fills the queues (dense: never)
+      sm.route.nu = 0;
+      sm.route.ustart[0] = 0;
+    }
     // greedy steps: clear the device-wide argmax keys (many barriers precede the LM head's updates)
     if (p.greedy && blockIdx.x == 0 && tid_x() < M)
       __hip_atomic_store((GLOBAL unsigned long long*)(p.amax + tid_x()), 0ull, __ATOMIC_RELAXED,
@@ -2250,7 +2282,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   bool resident = false;  // the LDS input buffer holds this layer's normalised MoE input
   for (int l = 0; l <= p.L; ++l) {
     const LayerDev* ly = &sm.lyd[l & 1];
-    const int nph = (l == p.L) ? 1 : attn_phases(ly->kind) + 3;
+    const int nph = (l == p.L) ? 1 : attn_phases(ly->kind) + (p.E ? 3 : 2);
     for (int i = 0; i < nph; ++i) {
       Gemv g{};
       typename PlanOf<MF>::type q{};

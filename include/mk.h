@@ -55,6 +55,10 @@ typedef enum { MK_ATTN_GQA = 0, MK_ATTN_MLA = 1, MK_ATTN_HYBRID = 2 } mk_attn_ki
  * Every layer has a MoE block: n_experts routed SwiGLU experts of width ffn, top_k chosen by a
  * softmax router (weights are the chosen probabilities; renormalised over the chosen set when
  * norm_topk != 0), plus a shared SwiGLU expert of width shared_ffn (0 = none).
+ * n_experts = 0 (with top_k = 0, ffn ignored, shared_ffn > 0) describes a dense decoder: its
+ * feed-forward block is the shared SwiGLU block alone and there is no router ("tpu-megakernels
+ * README", FAQ: the dense BF16 decoder served beside the MoE model). Its layers have one grid
+ * phase fewer (no routed-expert phase).
  * expert_pool_layers > 0: layer l uses the expert weights of pool slot l % expert_pool_layers. */
 typedef struct {
   int32_t n_layers, hidden, vocab, attn_kind;
@@ -76,7 +80,7 @@ typedef struct {
 
 /* Weight kinds. Shapes (row-major) for mk_load_weights:
  *   EMBED [vocab][hidden]  FINAL_NORM [hidden]  LM_HEAD [vocab][hidden]
- *   per layer: ATTN_NORM, MOE_NORM [hidden]; ROUTER [n_experts][hidden];
+ *   per layer: ATTN_NORM, MOE_NORM [hidden]; ROUTER [n_experts][hidden] (none when n_experts = 0);
  *     SH_GATE, SH_UP [shared_ffn][hidden]; SH_DOWN [hidden][shared_ffn]
  *     GQA: WQ [n_heads*head_dim][hidden], WK, WV [n_kv_heads*head_dim][hidden], WO [hidden][n_heads*head_dim]
  *     MLA: W_DQ [q_lora][hidden], Q_NORM [q_lora], W_UQ [n_heads*(nope_dim+rope_dim)][q_lora]

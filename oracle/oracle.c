@@ -7,6 +7,11 @@
  * delta rule, a softmax router with top-k, and SwiGLU experts. Loops are in the
  * textbook order; each output element is summed by one thread in index order,
  * so results do not depend on the thread count.
+ *
+ * A model with n_experts = 0 is a dense decoder: its feed-forward block is the
+ * one SwiGLU block of width shared_ffn, applied to every token with weight 1
+ * (the dense BF16 decoder the pages serve beside the MoE model:
+ * "tpu-megakernels README", FAQ on DSpark and DFlash2).
  */
 #include "oracle.h"
 
@@ -397,15 +402,16 @@ static void swiglu(const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, i
   free(u);
 }
 
-static void moe_block(const orc_config* c, const provider* P, int l, int M, const double* h, orc_io* io,
-                      double* out) {
+/* router (softmax over fp32 logits, top-k) and the selected experts, each weighted by its
+ * probability (renormalised over the chosen ones when norm_topk), added into out */
+static void routed_experts(const orc_config* c, const provider* P, int l, int M, const double* h, orc_io* io,
+                           double* y, double* out) {
   const int H = c->hidden, E = c->n_experts, K = c->top_k, F = c->ffn;
   uint16_t* Wr = get_bf16(P, ORC_ROUTER, l, -1, (size_t)E * H);
   double* r = (double*)malloc(sizeof(double) * M * E);
   double* p = (double*)malloc(sizeof(double) * M * E);
   int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * M * K);
   double* w = (double*)malloc(sizeof(double) * M * K);
-  double* y = (double*)malloc(sizeof(double) * H);
   matmat(Wr, E, H, h, H, M, r, E);
   for (int m = 0; m < M; ++m) {
     double* rm = r + (size_t)m * E;
@@ -424,7 +430,6 @@ static void moe_block(const orc_config* c, const provider* P, int l, int M, cons
   }
   if (io->sel) memcpy(io->sel + (size_t)l * M * K, sel, sizeof(int32_t) * M * K);
   if (io->probs) memcpy(io->probs + (size_t)l * M * E, p, sizeof(double) * M * E);
-  memset(out, 0, sizeof(double) * M * H);
   int slot = c->expert_pool_layers ? l % c->expert_pool_layers : l;
   for (int e = 0; e < E; ++e) {
     int used = 0;
@@ -441,6 +446,16 @@ static void moe_block(const orc_config* c, const provider* P, int l, int M, cons
         }
     free(Wg); free(Wu); free(Wd);
   }
+  free(Wr); free(r); free(p); free(sel); free(w);
+}
+
+/* the feed-forward block: routed experts (none in a dense model) plus the shared SwiGLU block */
+static void moe_block(const orc_config* c, const provider* P, int l, int M, const double* h, orc_io* io,
+                      double* out) {
+  const int H = c->hidden;
+  double* y = (double*)malloc(sizeof(double) * H);
+  memset(out, 0, sizeof(double) * M * H);
+  if (c->n_experts > 0) routed_experts(c, P, l, M, h, io, y, out);
   if (c->shared_ffn) {
     const int S = c->shared_ffn;
     uint16_t* Wg = get_bf16(P, ORC_SH_GATE, l, -1, (size_t)S * H);
@@ -452,7 +467,7 @@ static void moe_block(const orc_config* c, const provider* P, int l, int M, cons
     }
     free(Wg); free(Wu); free(Wd);
   }
-  free(Wr); free(r); free(p); free(sel); free(w); free(y);
+  free(y);
 }
 
 int orc_decode_step(const orc_config* c, orc_fill_fn fill, void* user, int B, int T, int kv_len,

@@ -52,7 +52,7 @@ typedef struct {
   int32_t n_heads, n_kv_heads, head_dim;
   int32_t q_lora, kv_lora, rope_dim, nope_dim, v_dim;
   int32_t kda_dk, kda_dv, hybrid_period;
-  int32_t n_experts, top_k, ffn, shared_ffn, norm_topk;
+  int32_t n_experts, top_k, ffn, shared_ffn, norm_topk; /* n_experts = 0: dense (shared block only) */
   int32_t expert_pool_layers; /* 0: every layer has its own experts */
   int32_t kv_capacity;        /* positions per cache row */
   int32_t mla_explicit;       /* 1: MLA in the explicit (non-absorbed) form */

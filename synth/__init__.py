@@ -114,6 +114,15 @@ K3 = ModelConfig(
 K3_HYBRID = replace(
     K3, name="k3-hybrid", attn_kind=ATTN_HYBRID, kda_dk=128, kda_dv=128, hybrid_period=4)
 
+# The dense second model: a MoE-free bf16 GQA decoder of about 27 B parameters, the size of the
+# dense decoder the pages serve next to the MoE model. The pages give no dimensions; these are
+# synthetic choices. n_experts = 0: the feed-forward block is the one SwiGLU block of width
+# shared_ffn. The whole model fits one GPU (about 53 GB of bf16 weights).
+DENSE = ModelConfig(
+    name="dense-27b", n_layers=64, hidden=5120, vocab=151936, attn_kind=ATTN_GQA,
+    n_heads=40, n_kv_heads=8, head_dim=128, n_experts=0, top_k=0, ffn=0, shared_ffn=21504,
+    max_batch=8, max_new_tokens=8, kv_capacity=4104, rope_theta=1e6)
+
 WORKLOADS = {
     "c1": Workload("c1", TINY, 1, 1, 128, "tiny MoE decoder, batch 1"),
     "c2": Workload("c2", MID, 1, 1, 2048, "mid-size GQA MoE, batch 1"),
@@ -124,6 +133,7 @@ WORKLOADS = {
     "c3b8": Workload("c3b8", K3, 8, 1, 4096, "K3-scale one-GPU share, batch 8"),
     "c4": Workload("c4", K3, 1, 7, 4096, "speculative verify: 1 + 6 draft tokens"),
     "c5": Workload("c5", K3_HYBRID, 8, 1, 4096, "hybrid delta-rule / MLA, batch 8"),
+    "dense": Workload("dense", DENSE, 1, 1, 4096, "dense 27B-class GQA decoder, batch 1"),
 }
 
 
@@ -193,7 +203,8 @@ def tensor_list(cfg: ModelConfig) -> list[TensorSpec]:
                 t("wo", (H, nh * dv)),
             ]
         out.append(t("moe_norm", (H,), "gain"))
-        out.append(t("router", (cfg.n_experts, H)))
+        if cfg.n_experts:
+            out.append(t("router", (cfg.n_experts, H)))
         if cfg.shared_ffn:
             out += [t("sh_gate", (cfg.shared_ffn, H)), t("sh_up", (cfg.shared_ffn, H)),
                     t("sh_down", (H, cfg.shared_ffn))]

@@ -100,6 +100,41 @@ def load_all(mk, cfg, ctx):
     mk.mk_load_weights(ctx, descs)
 
 
+@pytest.mark.parametrize("kw", [dict(top_k=1), dict(shared_ffn=0), dict(shared_ffn=12)])
+def test_bad_dense_configs(mk, kw):
+    # n_experts = 0 is a dense model: top_k 0 and a shared (dense) block of a multiple of 8
+    base = dict(n_experts=0, top_k=0, ffn=0, shared_ffn=512)
+    base.update(kw)
+    with pytest.raises(mk.MkError) as e:
+        sizes(mk, replace(synth.TINY, **base))
+    assert e.value.code == mk.MK_E_INVAL
+
+
+def test_dense_layout_and_loading(mk):
+    """A dense model's arena holds exactly its tensors (no router, no expert pool); a step is
+    refused until every one of them is loaded, and a router tensor is rejected."""
+    for c in (synth.DENSE, replace(synth.TINY, n_experts=0, top_k=0, ffn=0, shared_ffn=512)):
+        s = sizes(mk, c)
+        tl = synth.tensor_list(c)
+        assert not any(t.kind in ("router", "exp_gate", "exp_up", "exp_down") for t in tl)
+        total = sum(synth.numel(t.shape) * 2 for t in tl)
+        assert total <= s.arena_bytes <= total + 256 * (len(tl) + 1) + c.n_layers * 256
+    assert sizes(mk, synth.DENSE).arena_bytes < 60e9
+    cfg = replace(synth.TINY, n_experts=0, top_k=0, ffn=0, shared_ffn=512)
+    s = sizes(mk, cfg)
+    ctx = mk.mk_create(mk.config(cfg), mk.MK_DEVICE_NONE, 0, s.arena_bytes, 0, s.workspace_bytes)
+    try:
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_load_weights(ctx, [mk.tensor_desc("router", 0, -1, 1, cfg.hidden * 2, False)])
+        assert e.value.code == mk.MK_E_INVAL
+        load_all(mk, cfg, ctx)
+        with pytest.raises(mk.MkError) as e:  # loaded, but a host-only context cannot launch
+            mk.mk_decode_step(ctx, 1, 1, 3, 1, 1, 0, 1, 0, 0)
+        assert e.value.code == mk.MK_E_STATE and "host-only" in mk.mk_last_error()
+    finally:
+        mk.mk_destroy(ctx)
+
+
 def test_create_rejects_small_buffers(mk):
     cfg = synth.TINY
     s = sizes(mk, cfg)

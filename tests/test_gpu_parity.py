@@ -208,6 +208,27 @@ def test_hybrid_four_layers(B, T):
     parity(HYB_SMALL, synth.Spec(seed=4), B, T, 517)
 
 
+# dense decoders (n_experts = 0): no router, the SwiGLU block alone, one phase fewer per layer
+TINY_DENSE = replace(synth.TINY, name="tiny-dense", n_experts=0, top_k=0, ffn=0, shared_ffn=512)
+DENSE_SMALL = replace(synth.DENSE, name="dense-2layer", n_layers=2)
+
+
+@pytest.mark.parametrize("B,T,kv_len,rows", [(1, 1, 64, 3), (2, 3, 37, 3), (8, 2, 100, 3), (8, 2, 100, VECTOR_ONLY),
+                                             (1, 8, 5, 3)])
+def test_tiny_dense(B, T, kv_len, rows):
+    parity(TINY_DENSE, synth.Spec(seed=19), B, T, kv_len, mfma_min_rows=rows)
+
+
+def test_tiny_dense_ragged_rows():
+    # a dense width that is not whole 32-column units: every step on the vector units
+    parity(replace(TINY_DENSE, name="tiny-dense-ragged", shared_ffn=520), synth.Spec(seed=19), 4, 2, 21)
+
+
+@pytest.mark.parametrize("B,T", [(1, 1), (8, 1), (1, 7)])
+def test_dense_two_layers(B, T):
+    parity(DENSE_SMALL, synth.Spec(seed=20), B, T, 4096)
+
+
 # --------------------------------------------------------------------------------------------
 # full sizes, the launch configuration the benchmark times
 # --------------------------------------------------------------------------------------------
@@ -228,6 +249,11 @@ def test_k3_full_batch8():
 
 def test_hybrid_full_batch8():
     w = synth.WORKLOADS["c5"]
+    parity(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
+
+
+def test_dense_full_batch1():
+    w = synth.WORKLOADS["dense"]
     parity(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
 
 

@@ -388,6 +388,46 @@ def test_expert_weighting_and_routing_trace():
     np.testing.assert_allclose(out2["x"][1, 0], x0 + p[3] * 4 * f + p[0] * 1 * f, rtol=1e-12, atol=1e-14)
 
 
+def test_dense_swiglu_closed_form():
+    """A dense model (n_experts = 0) has no router: with W_g = W_u = W_d = I (width H) its
+    feed-forward block adds silu(h) * h to every token."""
+    cfg = tiny_gqa(n_experts=0, top_k=0, ffn=0, shared_ffn=256)
+    H = cfg.hidden
+    spec = synth.Spec(seed=17)
+    ov = identity_overrides(cfg)
+    ov.update({"L0.wo": zeros_bits(H, H), "L0.sh_gate": eye_bits(H, H), "L0.sh_up": eye_bits(H, H),
+               "L0.sh_down": eye_bits(H, H)})
+    toks = np.array([[5], [6]], dtype=np.int32)
+    out, _ = run(cfg, ov, toks, 4, spec=spec)
+    assert out["sel"].shape[-1] == 0
+    for b in range(2):
+        x0 = embed_rows(spec, cfg, toks[b])[0]
+        h = rmsnorm_ref(x0)
+        np.testing.assert_allclose(out["x"][1, b], x0 + h / (1.0 + np.exp(-h)) * h, rtol=1e-12, atol=1e-14)
+
+
+def test_dense_equals_single_expert_moe():
+    """One routed expert chosen with probability 1 (E = k = 1: the softmax of one logit) is the
+    dense block: a dense model and a one-expert MoE whose expert holds the dense weights give the
+    same logits, whatever the router weights."""
+    dense = tiny_gqa(n_experts=0, top_k=0, ffn=0, shared_ffn=384, n_layers=2)
+    moe = tiny_gqa(n_experts=1, top_k=1, ffn=384, shared_ffn=0, n_layers=2)
+    spec = synth.Spec(seed=18, sigma=0.05)
+    H = dense.hidden
+    ov = {}
+    for l in range(2):
+        for a, b in (("sh_gate", "gate"), ("sh_up", "up"), ("sh_down", "down")):
+            shape = (384, H) if a != "sh_down" else (H, 384)
+            w = synth.normal_bf16(spec.seed, f"L{l}.{a}", shape[0] * shape[1], spec.sigma)
+            ov[f"X{l}.0.{b}"] = w
+    toks = np.array([[3, 40, 7]], dtype=np.int32)
+    a, _ = run(dense, {}, toks, 6, spec=spec)
+    b, _ = run(moe, ov, toks, 6, spec=spec)
+    np.testing.assert_array_equal(b["sel"], np.zeros((2, 3, 1), dtype=np.int32))
+    np.testing.assert_allclose(b["probs"], 1.0, rtol=0, atol=0)
+    np.testing.assert_allclose(a["logits"], b["logits"], rtol=1e-13, atol=1e-13)
+
+
 def test_causal_mask_among_new_tokens():
     cfg = replace(synth.TINY, n_layers=2)
     spec = synth.Spec(seed=17)
