@@ -148,12 +148,38 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Reductions over aligned groups of `width` lanes (a power of two up to 64); every lane of a group
+// receives the result. Lane pairs are combined by data-parallel moves inside rows of 16 (swap
+// neighbours, swap pairs, mirror half-rows, mirror rows), a swizzle that swaps halves of 32 lanes,
+// and, for the whole wave, the sum of lanes 0 and 32 read as scalars: one instruction per step where
+// a chain of LDS permutes would wait on each. The whole wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {  // lane l's value, wave-uniform
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float swap16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
 __device__ __forceinline__ float wave_sum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (width >= 2) v += dpp_mov<0xB1>(0.f, v);   // lanes 2i <-> 2i+1
+  if (width >= 4) v += dpp_mov<0x4E>(0.f, v);   // pairs of a quad
+  if (width >= 8) v += dpp_mov<0x141>(0.f, v);  // mirror within 8 lanes
+  if (width >= 16) v += dpp_mov<0x140>(0.f, v); // mirror within 16 lanes
+  if (width >= 32) v += swap16(v);
+  if (width >= 64) v = lane_f(v, 0) + lane_f(v, 32);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if (width >= 2) v = fmaxf(v, dpp_mov<0xB1>(v, v));
+  if (width >= 4) v = fmaxf(v, dpp_mov<0x4E>(v, v));
+  if (width >= 8) v = fmaxf(v, dpp_mov<0x141>(v, v));
+  if (width >= 16) v = fmaxf(v, dpp_mov<0x140>(v, v));
+  if (width >= 32) v = fmaxf(v, swap16(v));
+  if (width >= 64) v = fmaxf(lane_f(v, 0), lane_f(v, 32));
   return v;
 }
 
@@ -1389,7 +1415,7 @@ __device__ __forceinline__ void rope_pair(const float* table, int t, int j, floa
 // partial whatever its length. New positions in the chunk are rotated, rounded to bf16, appended
 // to the cache and attended from the rounded values.
 __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
-                                               const float* rope) {
+                                               const float* rope, uint64_t* trace) {
   const int d = p.hd, nq = p.nh, nkv = p.nkv, T = p.T, cap = p.cap, d2 = d / 2, d4 = d / 4, d8 = d / 8;
   const int npos = p.kv_len + T, C = p.chunk, nsplit = p.nsplit, kvl = p.kv_len;
   const int qg = nq / nkv, nr = T * qg;
@@ -1444,6 +1470,8 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
       Qs[r * d + j] = q0;
       Qs[r * d + j + d2] = q1;
     }
+    const bool first = task == (int)blockIdx.x && trace && tid == 0;  // stamps of the first task
+    if (first) gp(trace)[2] = wall_clock64();
     for (int q0 = p0; q0 < p1; q0 += kGSub) {
       const int ns = min(kGSub, p1 - q0);
       __syncthreads();  // the previous sub-tile is consumed
@@ -1496,6 +1524,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
         S[r * kGSub + pl] = sc;
       }
       __syncthreads();
+      if (first && q0 == p0) gp(trace)[4] = wall_clock64();
       for (int r = wave_id(); r < nr; r += kWaves) {  // online softmax: one wave per row
         const float sv = S[r * kGSub + lane];
         const float mold = Mx[r], mnew = fmaxf(mold, wave_max(sv, 64));
@@ -1530,8 +1559,10 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
           Ls[r] = alpha * Ls[r] + ls;
         }
       }
+      if (first && q0 == p0) gp(trace)[5] = wall_clock64();
     }
     __syncthreads();
+    if (first) gp(trace)[3] = wall_clock64();
     for (int r = wave_id(); r < nr; r += kWaves) {  // the task's partial: max, sum, values
       const int t = r / qg, hq = g * qg + (r - t * qg), m = b * T + t;
       float* dst = p.part + ((size_t)(m * nq + hq) * nsplit + s) * stride;
@@ -2348,7 +2379,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         // cannot tell the two LDS areas apart).
         case PT_ATTN_GQA:
           if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
-          gqa_attn_phase(p, ly, ws, sm.buf, sm.rope);
+          gqa_attn_phase(p, ly, ws, sm.buf, sm.rope, trec);
           resident = false;
           break;
         case PT_ATTN_MLA:
