@@ -302,6 +302,27 @@ def speculative(dm, cfg, spec, v, steps: int, warmup: int, stream) -> dict:
     torch.cuda.synchronize()
     ms1 = (time.perf_counter() - t0) * 1e3 / steps
     out["greedy_decode_b1"] = {"ms_per_step": round(ms1, 4), "tokens_per_s": round(1e3 / ms1, 2)}
+    # temperature / top-p sampling fused after the LM head (the caller's uniform numbers on the device)
+    d_u = torch.full((1, 1), 0.5, dtype=torch.float32, device="cuda")
+    smp = torch.empty((1, 1), dtype=torch.int32, device="cuda")
+    lg1 = torch.empty((1, 1, cfg.vocab), dtype=torch.float32, device="cuda")
+    def sample_step():
+        dm.mk.mk_decode_step_sample(dm.ctx, 1, 1, kv_len, d_one.data_ptr(), dm.kv.data_ptr(),
+                                    dm.state.data_ptr() if dm.state is not None else 0, lg1.data_ptr(), 1.0, 0.9,
+                                    d_u.data_ptr(), smp.data_ptr(), dm.stream)
+    for _ in range(warmup):
+        sample_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sample_step()
+    torch.cuda.synchronize()
+    mss = (time.perf_counter() - t0) * 1e3 / steps
+    dm.poll()
+    out["sampled_decode_b1"] = {"temperature": 1.0, "top_p": 0.9, "ms_per_step": round(mss, 4),
+                                "tokens_per_s": round(1e3 / mss, 2)}
+    print(f"# sampled decode B=1 (temperature 1, top-p 0.9): {mss:.3f} ms, {1e3 / mss:.1f} tok/s", file=sys.stderr,
+          flush=True)
     for L in (3, 6):  # tokens yielded per step
         toks = np.array([cont[:L] + [(c + 1) % cfg.vocab for c in cont[L:T]]], dtype=np.int32)
         d_tok = torch.from_numpy(toks).cuda()

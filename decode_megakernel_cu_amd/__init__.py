@@ -24,8 +24,9 @@ KIND_ID = {k: i for i, k in enumerate(KINDS)}
 
 TRACE_STAMPS = 16  # MK_TRACE_STAMPS
 
-EXPORTS = ["mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_greedy", "mk_poll",
-           "mk_set_trace", "mk_read_trace", "mk_set_matrix_cores", "mk_last_error", "mk_destroy"]
+EXPORTS = ["mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_greedy",
+           "mk_decode_step_sample", "mk_poll", "mk_set_trace", "mk_read_trace", "mk_set_matrix_cores", "mk_last_error",
+           "mk_destroy"]
 
 
 class MkConfig(ctypes.Structure):
@@ -62,6 +63,7 @@ def _load():
     L.mk_load_weights.argtypes = [vp, ctypes.POINTER(MkTensorDesc), i32, vp]
     L.mk_decode_step.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     L.mk_decode_step_greedy.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.mk_decode_step_sample.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp]
     L.mk_poll.argtypes = [vp]
     L.mk_last_error.restype = ctypes.c_char_p
     L.mk_last_error.argtypes = []
@@ -70,8 +72,8 @@ def _load():
     L.mk_set_trace.argtypes = [vp, i32]
     L.mk_set_matrix_cores.argtypes = [vp, i32]
     L.mk_read_trace.argtypes = [vp, vp, u64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
-    for f in ("mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_greedy", "mk_poll",
-              "mk_set_trace", "mk_read_trace", "mk_set_matrix_cores"):
+    for f in ("mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_greedy",
+              "mk_decode_step_sample", "mk_poll", "mk_set_trace", "mk_read_trace", "mk_set_matrix_cores"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -125,6 +127,14 @@ def mk_decode_step_greedy(ctx, batch: int, n_new_tokens: int, kv_len: int, token
     """The step with greedy selection fused after the LM head (logits and accepted may be 0)."""
     _check(lib.mk_decode_step_greedy(ctx, batch, n_new_tokens, kv_len, tokens, kv, kda_state or None, logits or None,
                                      argmax or None, accepted or None, stream))
+
+
+def mk_decode_step_sample(ctx, batch: int, n_new_tokens: int, kv_len: int, tokens: int, kv: int, kda_state: int,
+                          logits: int, temperature: float, top_p: float, uniform: int, sampled: int,
+                          stream: int = 0) -> None:
+    """The step with temperature / top-p sampling fused after the LM head (uniform: the caller's numbers)."""
+    _check(lib.mk_decode_step_sample(ctx, batch, n_new_tokens, kv_len, tokens, kv, kda_state or None, logits or None,
+                                     float(temperature), float(top_p), uniform or None, sampled or None, stream))
 
 
 def mk_poll(ctx) -> None:

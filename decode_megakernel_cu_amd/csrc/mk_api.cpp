@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <string>
@@ -470,10 +471,25 @@ int mk_load_weights(mk_ctx* c, const mk_tensor_desc* d, int n, void* stream) {
 }
 
 // One decode step (both entry points): validation, parameters, the launch.
+// A sampling step: temperature, top_p and the caller's uniform numbers in, tokens out.
+struct SampleArgs {
+  float temperature, top_p;
+  const float* uniform;
+  int32_t* sampled;
+};
+
 static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens, void* d_kv, float* d_kda_state,
-                float* d_logits, int32_t* d_route, int32_t* d_argmax, int32_t* d_accepted, void* stream) {
+                       float* d_logits, int32_t* d_route, int32_t* d_argmax, int32_t* d_accepted, void* stream,
+                       const SampleArgs* smp = nullptr) {
   if (!c) return fail(MK_E_INVAL, "context is NULL");
   const bool greedy = d_argmax != nullptr;
+  if (smp) {
+    if (!(smp->temperature > 0.f) || !std::isfinite(smp->temperature))
+      return fail(MK_E_INVAL, "temperature must be positive and finite");
+    if (!(smp->top_p > 0.f && smp->top_p <= 1.f)) return fail(MK_E_INVAL, "top_p must be in (0, 1]");
+    if (!smp->uniform || !smp->sampled || !d_logits)
+      return fail(MK_E_INVAL, "a sampling step needs logits, uniform and sampled buffers");
+  }
   const mk_config& g = c->cfg;
   if (B < 1 || B > g.max_batch) return fail(MK_E_INVAL, "batch %d outside 1..%d", B, g.max_batch);
   if (T < 1 || T > g.max_new_tokens) return fail(MK_E_INVAL, "n_new_tokens %d outside 1..%d", T, g.max_new_tokens);
@@ -533,6 +549,13 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   p.amax = reinterpret_cast<unsigned long long*>(ws + w.amax);
   p.argmax = d_argmax;
   p.accepted = d_accepted;
+  if (smp) {
+    p.sample = 1;
+    p.temperature = smp->temperature;
+    p.top_p = smp->top_p;
+    p.uniform = smp->uniform;
+    p.sampled = smp->sampled;
+  }
   const int nh = g.n_heads;
   const uint64_t dmax = g.attn_kind == MK_ATTN_GQA ? g.head_dim : std::max(g.kv_lora, g.kda_dv);
   if ((uint64_t)M * nh * p.nsplit * (dmax + kPartPad) > w.part_floats)
@@ -541,7 +564,7 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   if (e == hipSuccess) e = launch_decode(p, c->nblocks, mf, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MK_E_HIP, "launch failed: %s", hipGetErrorString(e));
   c->launches++;
-  int nb = greedy ? 2 : 1;  // the LM head's barrier, and the one before the greedy results
+  int nb = (greedy || smp) ? 2 : 1;  // the LM head's barrier, and the one before greedy or sampled tokens
   for (int l = 0; l < g.n_layers; ++l) {  // attention phases, then 3 MoE phases (dense: 2)
     const int k = layer_kind(g, l);
     nb += (k == kGqa ? 4 : k == kMla ? 7 : 3) + (g.n_experts ? 3 : 2);
@@ -560,6 +583,13 @@ int mk_decode_step_greedy(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_
                           float* d_kda_state, float* d_logits, int32_t* d_argmax, int32_t* d_accepted, void* stream) {
   if (c && !d_argmax) return fail(MK_E_INVAL, "argmax output must be non-NULL");
   return decode_step(c, B, T, kv_len, d_tokens, d_kv, d_kda_state, d_logits, nullptr, d_argmax, d_accepted, stream);
+}
+
+int mk_decode_step_sample(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens, void* d_kv,
+                          float* d_kda_state, float* d_logits, float temperature, float top_p, const float* d_uniform,
+                          int32_t* d_sampled, void* stream) {
+  const SampleArgs smp{temperature, top_p, d_uniform, d_sampled};
+  return decode_step(c, B, T, kv_len, d_tokens, d_kv, d_kda_state, d_logits, nullptr, nullptr, nullptr, stream, &smp);
 }
 
 int mk_set_trace(mk_ctx* c, int enable) {

@@ -72,6 +72,11 @@ struct Params {
   unsigned long long* amax;  // [M] (value, index) keys, largest logit then lowest index
   int32_t* argmax;           // [M]
   int32_t* accepted;         // [B] or nullptr
+  // sampling steps: temperature / nucleus sampling of every row after the LM head
+  int32_t sample;
+  float temperature, top_p;
+  const float* uniform;  // [M] the caller's uniform numbers in [0, 1)
+  int32_t* sampled;      // [M]
 };
 
 }  // namespace mk

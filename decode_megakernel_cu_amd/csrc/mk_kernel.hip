@@ -1532,8 +1532,10 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
         const float alpha = mold == -INFINITY ? 0.f : __expf(mold - mnew);
         const float w = sv == -INFINITY ? 0.f : __expf(sv - mnew);
         const float ls = wave_sum(w, 64);
-        S[r * kGSub + lane] = w;  // read back by the same wave: its LDS accesses stay in order
+        S[r * kGSub + lane] = w;  // read back by the whole wave: ordered by wavefront-scope fences
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         if (2 * lane < d) {  // eight positions per step: their loads are in flight together
           float a0 = 0.f, a1 = 0.f;
           const uint16_t* vcol = Vb + 2 * lane;
@@ -2246,6 +2248,169 @@ __device__ __forceinline__ void fetch_layer(const Params& p, LayerDev* lyd, int 
     if (!barrier_finish(&sm.abort)) return;           \
   } while (0)
 
+// ----------------------------------------------------------------------------------------------
+// temperature / nucleus (top-p) sampling of one row of logits by one workgroup, after the LM head
+// (the MoE model's server offers greedy or temperature/top-p generation: "tpu-megakernels README",
+// section "OpenAI-compatible servers"). With e = exp((logit - max) / temperature) and Z its sum,
+// the kept set is every token with e >= tau, tau the largest value whose kept sum reaches
+// top_p * Z (found by bisection on the bits of tau: the kept sum only changes at the values of e,
+// so the bisection ends on one of them and keeps every token tied with it); the token is the
+// first, in index order, at which the running kept sum exceeds u * (kept sum), u the caller's
+// uniform number. Thread t holds kSR consecutive logits of each tile of kThreads * kSR (the whole
+// row when the vocabulary fits one tile); every sum is taken in a fixed order, so the result does
+// not change from run to run.
+// ----------------------------------------------------------------------------------------------
+constexpr int kSR = 80;  // logits per thread and tile
+
+// sum / maximum over the workgroup (every thread receives it); red holds kWaves floats
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v, 64);
+  __syncthreads();
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < kWaves; ++w) t += red[w];
+  return t;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v, 64);
+  __syncthreads();
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  float t = red[0];
+  for (int w = 1; w < kWaves; ++w) t = fmaxf(t, red[w]);
+  return t;
+}
+
+__device__ __noinline__ void sample_row(const Params& p, int m, float* lds) {
+  const int V = p.V, tid = tid_x(), lane = lane_id();
+  const int tile = kThreads * kSR, ntile = (V + tile - 1) / tile;
+  const float* row = p.logits + (size_t)m * V;
+  const Rsrc lr = make_rsrc(row, (uint32_t)V * 4u);  // loads past the row read zero
+  float* red = lds;       // [16] reductions and flags
+  float* pre = lds + 16;  // [kThreads + 1] per-thread kept sums, then their prefixes
+  float x[kSR];
+  auto load = [&](int t) __attribute__((always_inline)) {
+    const int base = t * tile + tid * kSR;
+#pragma unroll
+    for (int k = 0; k < kSR; k += 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(lr, (uint32_t)(base + k) * 4u, 0, kCoherent);
+      x[k] = __uint_as_float(v.x);
+      x[k + 1] = __uint_as_float(v.y);
+      x[k + 2] = __uint_as_float(v.z);
+      x[k + 3] = __uint_as_float(v.w);
+    }
+  };
+  const float invt = 1.0f / p.temperature;
+  float mx = -INFINITY;
+  for (int t = 0; t < ntile; ++t) {
+    load(t);
+#pragma unroll
+    for (int k = 0; k < kSR; ++k)
+      if (t * tile + tid * kSR + k < V) mx = fmaxf(mx, x[k]);
+  }
+  mx = block_max(mx, red);
+  // e in place (the last tile stays resident; with one tile, the whole row)
+  auto weights = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kSR; ++k) x[k] = t * tile + tid * kSR + k < V ? __expf((x[k] - mx) * invt) : 0.f;
+  };
+  auto tile_e = [&](int t) __attribute__((always_inline)) {
+    if (ntile > 1) {
+      load(t);
+      weights(t);
+    }
+  };
+  if (ntile == 1) weights(0);
+  auto kept_sum = [&](float tau) __attribute__((always_inline)) {  // sum of e >= tau over the row
+    float s = 0.f;
+    for (int t = 0; t < ntile; ++t) {
+      tile_e(t);
+#pragma unroll
+      for (int k = 0; k < kSR; ++k) s += x[k] >= tau ? x[k] : 0.f;
+    }
+    return block_sum(s, red);
+  };
+  const float Z = kept_sum(0.f);
+  const float goal = p.top_p * Z;
+  uint32_t lo = 0u, hi = __float_as_uint(1.0f) + 1u;  // kept_sum(lo) >= goal > kept_sum(hi)
+  float mass = Z;
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    const float s = kept_sum(__uint_as_float(mid));
+    if (s >= goal) {
+      lo = mid;
+      mass = s;
+    } else {
+      hi = mid;
+    }
+  }
+  const float tau = __uint_as_float(lo);
+  const float target = gp(p.uniform)[m] * mass;
+  // the running kept sum in index order: per-thread kept sums, then one non-decreasing sequence of
+  // prefixes pre[0..kThreads] (group sums chained by one lane, each clamped to the next group's
+  // start), so the half-open ranges [pre[t], pre[t+1]) tile [0, total) and exactly one thread holds
+  // the target; it scans its own logits
+  int tok = -1, last = -1;
+  float base = 0.f;
+  for (int t = 0; t < ntile && tok < 0; ++t) {
+    tile_e(t);
+    float sk = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSR; ++k) sk += x[k] >= tau ? x[k] : 0.f;
+    __syncthreads();
+    pre[tid] = sk;
+    __syncthreads();
+    if (wave_id() == 0) {  // lane j: threads 8j .. 8j+7
+      float g = 0.f;
+      for (int i = 0; i < 8; ++i) g += pre[8 * lane + i];
+      // group starts: one sequential chain, run identically by every lane on scalar reads of the
+      // group sums, so every lane sees the same values (no exchange through memory)
+      float g0 = 0.f, g1 = 0.f, chain = 0.f;
+      for (int j = 0; j < 64; ++j) {
+        if (lane == j) g0 = chain;
+        chain += lane_f(g, j);
+        if (lane == j) g1 = chain;
+      }
+      float run = g0;
+      for (int i = 0; i < 8; ++i) {
+        const float v = pre[8 * lane + i];
+        pre[8 * lane + i] = fminf(run, g1);
+        run += v;
+      }
+      if (lane == 63) pre[kThreads] = g1;
+    }
+    __syncthreads();
+    const float start = base + pre[tid], next = base + pre[tid + 1];
+    int mine = -1, lastk = -1;
+    if (start <= target && target < next) {
+      float c = start;
+#pragma unroll
+      for (int k = 0; k < kSR; ++k) {
+        if (x[k] >= tau && x[k] > 0.f) {
+          c += x[k];
+          lastk = t * tile + tid * kSR + k;
+          if (mine < 0 && c > target) mine = lastk;
+        }
+      }
+      if (mine < 0) mine = lastk;  // rounding: the range's last kept token
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSR; ++k)
+        if (x[k] >= tau && x[k] > 0.f) lastk = t * tile + tid * kSR + k;
+    }
+    base += pre[kThreads];
+    __syncthreads();
+    if (tid == 0) red[9] = -1.f;
+    __syncthreads();
+    if (mine >= 0) red[9] = (float)mine;  // at most one thread
+    __syncthreads();
+    tok = (int)red[9];
+    last = max(last, (int)block_max((float)lastk, red));
+  }
+  if (tid == 0) gp(p.sampled)[m] = tok >= 0 ? tok : last;  // rounding past the end: the last kept
+}
+
 template <bool MF>
 struct PlanOf {
   typedef Plan type;
@@ -2409,10 +2574,15 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       if (trec && tid_x() == 0) gp(trec)[8] = wall_clock64();
     }
   }
-  if (p.greedy) {  // one more barrier, then workgroup 0 turns the keys into tokens and accepts drafts
+  if (p.greedy || p.sample) {  // one more barrier: every row's logits (or argmax keys) are complete
     barrier_arrive(p, gen);
     if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort);
     MK_FINISH();
+  }
+  if (p.sample) {
+    for (int m = blockIdx.x; m < M; m += gridDim.x) sample_row(p, m, sm.buf);
+  }
+  if (p.greedy) {  // workgroup 0 turns the keys into tokens and accepts drafts
     if (blockIdx.x == 0) {
       const int tid = tid_x();
       if (tid < M) {

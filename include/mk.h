@@ -157,6 +157,23 @@ int mk_decode_step_greedy(mk_ctx* ctx, int batch, int n_new_tokens, int kv_len, 
                           float* d_kda_state, float* d_logits, int32_t* d_argmax, int32_t* d_accepted,
                           void* hip_stream);
 
+/* mk_decode_step followed, in the same launch, by temperature / nucleus (top-p) sampling of every
+ * position's next token (the MoE model's server offers greedy or temperature/top-p generation:
+ * "tpu-megakernels README", section "OpenAI-compatible servers"). With p = softmax(logits /
+ * temperature) per position, the kept set is every token whose p is at least tau, tau the largest
+ * value at which the kept probability mass reaches top_p (tokens tied with tau are all kept); the
+ * sampled token is the first, in index order, at which the running sum of kept probabilities
+ * exceeds u times their total, u = d_uniform[b][t]. The library draws no random numbers:
+ * d_uniform [batch][n_new_tokens] fp32 in [0, 1) (device) is the caller's. d_logits is required
+ * (written as by mk_decode_step, then read back by the sampler); d_sampled [batch][n_new_tokens]
+ * int32 (device). One workgroup samples each position: logits in registers, the threshold by
+ * bisection on its bits, every sum in a fixed order (the tokens do not vary from run to run).
+ * MK_E_INVAL for temperature <= 0 or not finite, top_p outside (0, 1], or a NULL d_logits,
+ * d_uniform or d_sampled; otherwise as mk_decode_step. */
+int mk_decode_step_sample(mk_ctx* ctx, int batch, int n_new_tokens, int kv_len, const int32_t* d_tokens, void* d_kv,
+                          float* d_kda_state, float* d_logits, float temperature, float top_p,
+                          const float* d_uniform, int32_t* d_sampled, void* hip_stream);
+
 /* After the caller synchronised the step's stream: MK_OK, or MK_E_DEVICE if the kernel reported a
  * watchdog timeout or an out-of-range token (the context is then poisoned). */
 int mk_poll(mk_ctx* ctx);

@@ -150,6 +150,22 @@ class DeviceModel:
                                       accepted.data_ptr(), self.stream)
         return argmax, accepted
 
+    def step_sample(self, tokens: np.ndarray, kv_len: int, temperature: float, top_p: float, uniform: np.ndarray,
+                    logits: torch.Tensor | None = None, d_tokens: torch.Tensor | None = None):
+        """A sampling step: returns (sampled [B][T] int32, logits [B][T][V] fp32)."""
+        B, T = tokens.shape
+        if d_tokens is None:
+            d_tokens = torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).to(self.device)
+        if logits is None:
+            logits = torch.empty((B, T, self.cfg.vocab), dtype=torch.float32, device=self.device)
+        d_u = torch.from_numpy(np.ascontiguousarray(uniform, dtype=np.float32).reshape(B, T)).to(self.device)
+        sampled = torch.full((B, T), -1, dtype=torch.int32, device=self.device)
+        self.mk.mk_decode_step_sample(self.ctx, B, T, kv_len, d_tokens.data_ptr(), self.kv.data_ptr(),
+                                      self.state.data_ptr() if self.state is not None else 0, logits.data_ptr(),
+                                      temperature, top_p, d_u.data_ptr(), sampled.data_ptr(), self.stream)
+        self._keep = d_u  # alive until the caller synchronises
+        return sampled, logits
+
     def set_matrix_cores(self, min_rows: int):
         """Steps with at least min_rows token rows run their GEMV phases on the matrix cores."""
         self.mk.mk_set_matrix_cores(self.ctx, min_rows)

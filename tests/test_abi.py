@@ -245,3 +245,24 @@ def test_greedy_step_argument_errors(mk, host_ctx):
     with pytest.raises(mk.MkError) as e:
         mk.mk_decode_step_greedy(None, 1, 1, 0, 1, 1, 0, 0, 1)
     assert e.value.code == mk.MK_E_INVAL
+
+
+def test_sample_step_argument_errors(mk, host_ctx):
+    _, ctx = host_ctx
+    ok = dict(batch=1, n_new_tokens=1, kv_len=10, tokens=1, kv=1, kda_state=0, logits=1, temperature=0.8, top_p=0.9,
+              uniform=1, sampled=1)
+
+    def step(**kw):
+        a = dict(ok)
+        a.update(kw)
+        mk.mk_decode_step_sample(ctx, **a)
+
+    for kw in (dict(temperature=0.0), dict(temperature=-1.0), dict(temperature=float("inf")),
+               dict(temperature=float("nan")), dict(top_p=0.0), dict(top_p=1.5), dict(uniform=0), dict(sampled=0),
+               dict(logits=0)):
+        with pytest.raises(mk.MkError) as e:
+            step(**kw)
+        assert e.value.code == mk.MK_E_INVAL, kw
+    with pytest.raises(mk.MkError) as e:  # valid arguments: the weights are not loaded yet
+        step(top_p=1.0)
+    assert e.value.code == mk.MK_E_STATE

@@ -6,6 +6,7 @@ one bf16 rounding of the oracle's, untouched cache entries bitwise unchanged, an
 delta-rule state within fp32 accumulation error.
 """
 import gc
+import math
 from dataclasses import replace
 
 import numpy as np
@@ -206,6 +207,78 @@ def test_k3_two_layers_peaked_mla():
 @pytest.mark.parametrize("B,T", [(8, 1), (2, 3)])
 def test_hybrid_four_layers(B, T):
     parity(HYB_SMALL, synth.Spec(seed=4), B, T, 517)
+
+
+# --------------------------------------------------------------------------------------------
+# temperature / top-p sampling fused after the LM head
+# --------------------------------------------------------------------------------------------
+SAMPLE_LOGIT_TOL = 2e-3  # logit error (relative to the row's largest logit) the sampling check allows for
+
+
+def sample_check(cfg, spec, B, T, kv_len, temperature, top_p, useed, exact_all=False):
+    """Every sampled token must be the oracle's draw, or differ from it only where the draw sits
+    on a decision boundary within what the logits' error (and fp32 sums over the vocabulary) can
+    move: the oracle's running kept mass around the token must straddle u * mass within that
+    slack, and the token must be kept or within the slack of the threshold. Most positions (all,
+    for sharp distributions) must match exactly."""
+    import oracle
+    from oracle import sampling
+
+    toks = synth.tokens(spec.seed, 4, cfg.vocab, B, T)
+    u = np.random.default_rng(useed).random((B, T))  # the caller's uniform numbers (seeded)
+    print(f"[case] sample {cfg.name} B={B} T={T} kv_len={kv_len} temperature={temperature} top_p={top_p}",
+          flush=True)
+    dm = device_model(cfg, spec)
+    dm.set_matrix_cores(3)
+    dm.fill_caches(B, kv_len)
+    got, logits = dm.step_sample(toks, kv_len, temperature, top_p, u)
+    torch.cuda.synchronize()
+    dm.poll()
+    got = got.cpu().numpy()
+    caches = synth.host_caches(cfg, spec, B, kv_len, cache_batch=cfg.max_batch)
+    ref = oracle.decode_step(cfg, oracle.Provider(cfg, spec), toks, kv_len, caches, cache_batch=cfg.max_batch)
+    check_logits(logits.cpu().numpy(), ref)
+    exact = 0
+    for b in range(B):
+        for t in range(T):
+            lg = ref["logits"][b, t]
+            r = sampling.sample(lg, temperature, top_p, u[b, t])
+            s = int(got[b, t])
+            assert 0 <= s < cfg.vocab
+            if s == r["token"]:
+                exact += 1
+                continue
+            # p moves by up to a factor exp(+-2 eps / temperature) when each logit moves by eps
+            rel = math.expm1(2 * SAMPLE_LOGIT_TOL * np.abs(lg).max() / temperature) + 1e-4
+            p, tau = r["p"], r["tau"]
+            near = np.abs(p - tau) <= rel * tau
+            slack = rel * r["mass"] + p[near].sum()
+            kp = np.where(r["kept"] | near, p, 0.0)
+            before, after = kp[:s].sum(), kp[:s + 1].sum()
+            assert r["kept"][s] or near[s], f"({b},{t}): token {s} outside the nucleus (p {p[s]:.3e}, tau {tau:.3e})"
+            assert before - slack <= r["target"] <= after + slack, (
+                f"({b},{t}): token {s} covers [{before:.6f}, {after:.6f}], the draw is {r['target']:.6f} "
+                f"(oracle token {r['token']}, slack {slack:.2e})")
+    need = B * T if exact_all else int(0.75 * B * T)
+    assert exact >= need, f"only {exact} of {B * T} draws equal the oracle's"
+    print(f"[ok] sample {cfg.name}: {exact}/{B * T} draws equal the oracle's", flush=True)
+
+
+@pytest.mark.parametrize("temperature,top_p,exact_all", [(1.0, 0.9, False), (0.7, 0.5, False), (1.5, 1.0, False),
+                                                         (0.01, 0.9, True), (0.03, 0.3, True)])
+def test_sample_tiny(temperature, top_p, exact_all):
+    sample_check(synth.TINY, synth.Spec(seed=21, sigma=0.05), 4, 2, 30, temperature, top_p, 5, exact_all)
+
+
+@pytest.mark.parametrize("temperature,top_p,exact_all", [(1.0, 0.95, False), (0.005, 0.8, True)])
+def test_sample_k3_two_layers(temperature, top_p, exact_all):
+    # a vocabulary slice of exactly one register tile (40960 = 512 threads x 80)
+    sample_check(K3_SMALL, synth.Spec(seed=22), 1, 7, 4096, temperature, top_p, 6, exact_all)
+
+
+def test_sample_dense_two_layers():
+    # a vocabulary of several tiles (151936 logits)
+    sample_check(DENSE_SMALL, synth.Spec(seed=23), 2, 2, 1000, 0.02, 0.9, 7, False)
 
 
 # dense decoders (n_experts = 0): no router, the SwiGLU block alone, one phase fewer per layer
