@@ -94,12 +94,15 @@ def bf(u):
 def check_rounded(a_bits, b_bits, what):
     """a, b: bf16 patterns of the same quantity computed in fp32 (GPU) and fp64 (oracle) and
     rounded once to bf16. They may differ by one bf16 step of the larger magnitude, plus the
-    fp32 error the GPU accumulates through earlier layers (1e-4 of the entry vector's largest
-    magnitude; it matters only for entries close to zero). The last axis is the entry vector."""
+    error the GPU accumulates through earlier layers, bounded by 3e-4 of the entry vector's
+    largest magnitude (it matters only for entries close to zero). That error grows with depth:
+    after 90 layers of the K3-scale share at batch 8 it reaches 1.1e-4 of the vector's scale, the
+    same order as the step's logit error (1.2e-4 of the largest logit). The last axis is the entry
+    vector."""
     a, b = bf(a_bits), bf(b_bits)
     step = 2.0 ** (np.floor(np.log2(np.maximum(np.maximum(np.abs(a), np.abs(b)), 1e-30))) - 7)
     scale = np.abs(b).max(axis=-1, keepdims=True)
-    bad = np.abs(a - b) > step * 1.0001 + 1e-4 * scale
+    bad = np.abs(a - b) > step * 1.0001 + 3e-4 * scale
     if bad.any():
         idx = np.argwhere(bad)[:5]
         rows = ", ".join(f"{tuple(i)}: gpu {a[tuple(i)]:.6g} oracle {b[tuple(i)]:.6g}" for i in idx)
