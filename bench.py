@@ -74,9 +74,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(B: int):
+PMC_FILES = {"c3": "megakernel_k3_pmc_traffic.json", "dense": "megakernel_dense_pmc_traffic.json"}
+
+
+def traffic_from_profiles(B: int, workload: str = WORKLOAD):
     """HBM bytes per launch from the committed PMC summary, if it was taken on this kernel."""
-    path = os.path.join(ROOT, "profiles", "megakernel_k3_pmc_traffic.json")
+    path = os.path.join(ROOT, "profiles", PMC_FILES[workload])
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -89,7 +92,7 @@ def traffic_from_profiles(B: int):
 CALIB_BYTES = 1 << 30  # bytes the calibration kernel reads (and writes)
 
 
-def ingest_pmc(fetch_csv: str, write_csv: str) -> None:
+def ingest_pmc(fetch_csv: str, write_csv: str, workload: str = WORKLOAD) -> None:
     """HBM traffic of the megakernel from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the calibration copy (CALIB_BYTES read and
     written by an elementwise kernel), written to profiles/ with the kernel's source hash."""
@@ -115,18 +118,16 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> None:
     w_scale = CALIB_BYTES / (w_cal * 1024.0)
     fetch = float(np.median(f_mk)) * 1024.0 * f_scale
     write = float(np.median(w_mk)) * 1024.0 * w_scale
-    cfg = synth.WORKLOADS[WORKLOAD].model
-    out = {"kernel_hash": kernel_source_hash(), "workload": WORKLOAD, "batch": 1,
+    out = {"kernel_hash": kernel_source_hash(), "workload": workload, "batch": 1,
            "calibration": {"bytes": CALIB_BYTES, "fetch_kib": f_cal, "write_kib": w_cal,
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "megakernel": {"dispatches": len(f_mk), "fetch_kib_median": float(np.median(f_mk)),
                           "write_kib_median": float(np.median(w_mk)), "fetch_bytes": fetch, "write_bytes": write},
            "per_launch_bytes": {"1": fetch + write}}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "megakernel_k3_pmc_traffic.json"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", PMC_FILES[workload]), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
-    del cfg
 
 
 # ------------------------------------------------------------------------------------------
@@ -370,10 +371,10 @@ def main():
                          "kernel for the traffic figure")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 counter_collection CSVs (FETCH_SIZE, WRITE_SIZE) of a --calib-copy "
-                         "run into profiles/megakernel_k3_pmc_traffic.{json,md} and exit")
+                         "run into profiles/megakernel_{k3,dense}_pmc_traffic.json (by --workload) and exit")
     args = ap.parse_args()
     if args.ingest_pmc:
-        ingest_pmc(*args.ingest_pmc)
+        ingest_pmc(*args.ingest_pmc, workload="dense" if args.workload == "dense" else "c3")
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the decode step; --gpus {args.gpus} is not supported "
@@ -499,6 +500,10 @@ def main():
             "batches": {str(B): {"tokens_per_s": round(r["tokens_per_s"], 2), "kernel_ms": round(r["kernel_ms_avg"], 4),
                                  "gb_per_step": round(r["bytes"] / 1e9, 3), "hbm_gbs": round(r["gbs"], 1),
                                  "hbm_frac": round(r["gbs"] / HBM_PEAK_GBS, 4)} for B, r in dense.items()}}
+        d0 = dense[batches[0]]
+        out["dense"]["roofline"] = {"bound": "hbm", "achieved": round(d0["gbs"], 1), "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": round(d0["gbs"] / HBM_PEAK_GBS, 4),
+                                    "traffic": traffic_from_profiles(batches[0], "dense")}
     if verify is not None:  # positions verified per second (1 + 6 draft tokens per step)
         out["verify_t7"] = {"positions_per_s": round(verify["tokens_per_s"], 2),
                             "kernel_ms": round(verify["kernel_ms_avg"], 4),
