@@ -94,10 +94,11 @@ int check_config(const mk_config* c) {
     if (c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return fail(MK_E_INVAL, "n_heads must be a multiple of n_kv_heads");
     if (c->head_dim < 8 || c->head_dim % 8 || c->head_dim > 2 * kMaxRopePairs)
       return fail(MK_E_UNSUPPORTED, "head_dim must be a multiple of 8 and at most %d", 2 * kMaxRopePairs);
-    // the attention tile: bf16 keys and values of kGSub positions, then per query row (new token x
-    // head of the group) the rotated query, the scores, the value sums and two running statistics
+    // the attention tile: bf16 keys (rows padded by 8) and values of kGSub positions, then per query
+    // row (new token x head of the group) the rotated query, the scores, the value sums and two
+    // running statistics
     const int nr = c->max_new_tokens * (c->n_heads / c->n_kv_heads);
-    if (kGSub * c->head_dim + nr * (2 * c->head_dim + kGSub + 2) > kLdsFloats)
+    if (kGSub * (c->head_dim + 4) + nr * (2 * c->head_dim + kGSub + 2) > kLdsFloats)
       return fail(MK_E_UNSUPPORTED, "GQA group too large for the attention tile");
   } else {
     if (c->kv_lora < 8 || c->kv_lora % 8 || c->q_lora < 8 || c->q_lora % 8 || c->nope_dim < 8 || c->nope_dim % 8 ||

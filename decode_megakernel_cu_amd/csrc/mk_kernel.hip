@@ -1421,9 +1421,12 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
   const int qg = nq / nkv, nr = T * qg;
   const int ntask = p.B * nkv * nsplit;
   const int tid = tid_x(), lane = lane_id();
-  uint16_t* Kb = reinterpret_cast<uint16_t*>(smem);  // [kGSub][d] bf16
-  uint16_t* Vb = Kb + kGSub * d;                     // [kGSub][d] bf16
-  float* Qs = smem + kGSub * d;                      // [nr][d] rotated queries
+  // key rows padded by 16 bytes: the score loop reads one key row per lane, and rows 256 bytes
+  // apart would all start in the same LDS bank
+  const int dk = d + 8;
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(smem);  // [kGSub][dk] bf16
+  uint16_t* Vb = Kb + kGSub * dk;                    // [kGSub][d] bf16
+  float* Qs = smem + kGSub * (d + 4);                // [nr][d] rotated queries
   float* S = Qs + nr * d;                            // [nr][kGSub] scores, then weights
   float* Acc = S + nr * kGSub;                       // [nr][d] unnormalised value sums
   float* Mx = Acc + nr * d;                          // [nr] running maximum
@@ -1479,7 +1482,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
       for (int u = 0; u < kU; ++u) {  // cached rows into LDS
         const int i = u * kThreads + tid, pl = i / d8, c = i - pl * d8;
         if (i < U && q0 + pl < pc) {
-          *reinterpret_cast<uint4*>(Kb + pl * d + 8 * c) = kr[u];
+          *reinterpret_cast<uint4*>(Kb + pl * dk + 8 * c) = kr[u];
           *reinterpret_cast<uint4*>(Vb + pl * d + 8 * c) = vr[u];
         }
       }
@@ -1499,8 +1502,8 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
         gp(Kc)[ci + j + d2] = kb1;
         gp(Vc)[ci + j] = vb0;
         gp(Vc)[ci + j + d2] = vb1;
-        Kb[pl * d + j] = kb0;
-        Kb[pl * d + j + d2] = kb1;
+        Kb[pl * dk + j] = kb0;
+        Kb[pl * dk + j + d2] = kb1;
         Vb[pl * d + j] = vb0;
         Vb[pl * d + j + d2] = vb1;
       }
@@ -1513,7 +1516,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
 #pragma unroll 4
           for (int j = 0; j < d; j += 8) {
             float kf[8];
-            unpack8(*reinterpret_cast<const uint4*>(Kb + pl * d + j), kf);
+            unpack8(*reinterpret_cast<const uint4*>(Kb + pl * dk + j), kf);
             const f32x4 qa = *reinterpret_cast<const f32x4*>(Qs + r * d + j);
             const f32x4 qb = *reinterpret_cast<const f32x4*>(Qs + r * d + j + 4);
             acc += qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3] + qb.x * kf[4] + qb.y * kf[5] +
