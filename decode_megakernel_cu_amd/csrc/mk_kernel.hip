@@ -638,6 +638,7 @@ __device__ __forceinline__ void dot_block(const RowBuf& b, const float* xin, int
 // group streams elements (slab, task it, row which, block blk) in that order, the element count of
 // a slab padded to even so that the two register buffers alternate the same way in every slab.
 constexpr int kGemvWaves = kWaves;
+static_assert(kGemvWaves == 8 && kNC == 8, "make_plan's width choice shifts by log2(8)");
 
 // vp: lane-group tasks per task (2: the SwiGLU gate and up rows of router/shared and routed-expert
 // phases go to different lane groups, so few tasks still keep every wave busy); cp: weight rows a
@@ -686,6 +687,24 @@ __device__ __forceinline__ Plan make_plan(const Gemv& g, float* smem) {
   const int lo = min(6, log2ceil(cdiv(nch, kNC))), hi = max(lo, min(6, log2ceil(nch)));
   const int bal = max(0, 6 - log2ceil(max(1, cdiv(q.nv, kGemvWaves))));
   q.lg = min(max(bal, lo), hi);
+  // rows that fill their blocks poorly at this width (a 640-chunk row on 64 lanes: 8 chunks per lane,
+  // then 2) keep fewer bytes in flight; narrower lane groups with fewer block rounds per lane
+  // group (iterations x blocks per row) stream them with full blocks
+  // (every divisor is a power of two: shifts; kGemvWaves = kNC = 8)
+  if (nch * 4 < 3 * ((nch + (kNC << q.lg) - 1) >> (3 + q.lg)) * (kNC << q.lg)) {
+    auto rounds = [&](int lg) {
+      return ((q.nv + (8 << (6 - lg)) - 1) >> (9 - lg)) * ((nch + (8 << lg) - 1) >> (3 + lg));
+    };
+    int best = q.lg, cost = rounds(q.lg);
+    for (int lg = q.lg - 1; lg >= max(0, q.lg - 3); --lg) {
+      const int c = rounds(lg);
+      if (c < cost) {
+        cost = c;
+        best = lg;
+      }
+    }
+    q.lg = best;
+  }
   q.LPR = 1 << q.lg;
   q.G = 64 >> q.lg;
   const int lane = lane_id();
