@@ -371,6 +371,37 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (uint32_t)i);
 }
+// the value of a key (the inverse of the order-preserving map above)
+__device__ __forceinline__ float key_value(unsigned long long k) {
+  const uint32_t u = (uint32_t)(k >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long k) {
+  return ((unsigned long long)dpp_u32<CTRL>((uint32_t)(k >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)k);
+}
+// the largest key of the wave, in every lane (the same lane moves as wave_max)
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+  auto mx = [](unsigned long long a, unsigned long long b) { return a > b ? a : b; };
+  k = mx(k, dpp_u64<0xB1>(k));
+  k = mx(k, dpp_u64<0x4E>(k));
+  k = mx(k, dpp_u64<0x141>(k));
+  k = mx(k, dpp_u64<0x140>(k));
+  const uint32_t sh = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(k >> 32), 0x401F);
+  const uint32_t sl = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)k, 0x401F);
+  k = mx(k, ((unsigned long long)sh << 32) | sl);
+  const unsigned long long k0 =
+      ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(k >> 32), 0) << 32) |
+      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 0);
+  const unsigned long long k1 =
+      ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(k >> 32), 32) << 32) |
+      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 32);
+  return mx(k0, k1);
+}
 // by value (a reference-returning min keeps its operands in memory)
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
@@ -928,24 +959,19 @@ __device__ __forceinline__ void compute_route(const Params& p, const Ws& ws, int
     unsigned taken = 0;
     float tot = 0.f;
     for (int j = 0; j < K; ++j) {
-      float bv = 0.f;
-      int be = -1;
+      // the lane's best untaken expert, then the wave's: keys order by logit, then lower index
+      unsigned long long best = 0ull;
 #pragma unroll
       for (int k = 0; k < R; ++k) {
         const int e = lane + 64 * k;
-        if (e < E && !((taken >> k) & 1u) && (be < 0 || r[k] > bv)) {
-          bv = r[k];
-          be = e;
+        if (e < E && !((taken >> k) & 1u)) {
+          const unsigned long long key = argmax_key(r[k], e);
+          best = key > best ? key : best;
         }
       }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oe = __shfl_xor(be, o, 64);
-        if (oe >= 0 && (be < 0 || ov > bv || (ov == bv && oe < be))) {
-          bv = ov;
-          be = oe;
-        }
-      }
+      best = wave_max_key(best);
+      const int be = (int)(0xFFFFFFFFu - (uint32_t)best);
+      const float bv = key_value(best);
       if ((be & 63) == lane) taken |= 1u << (be >> 6);
       const float pe = __expf(bv - mx) / sum;
       tot += pe;
