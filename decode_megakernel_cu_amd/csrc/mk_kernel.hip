@@ -1486,8 +1486,10 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
     const int s = task % nsplit, g = (task / nsplit) % nkv, b = task / (nsplit * nkv);
     const int p0 = s * C, p1 = min(npos, p0 + C), pc = min(p1, kvl);  // [p0, pc): cached positions
     const size_t row0 = ((size_t)b * nkv + g) * cap;                     // cache row of position 0
-    uint4 kr[kU], vr[kU];
-    auto issue = [&](int q0) {  // the cached rows of the sub-tile at q0 (others read row 0)
+    // two register sets: the rows of the next two sub-tiles are in flight while one is scored
+    uint4 kra[kU], vra[kU], krb[kU], vrb[kU];
+    auto issue = [&](int q0, uint4(&kr)[kU], uint4(&vr)[kU]) __attribute__((always_inline)) {
+      // the cached rows of the sub-tile at q0 (others read row 0)
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i = u * kThreads + tid, pl = i / d8, c = i - pl * d8, pos = q0 + pl;
@@ -1497,7 +1499,8 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
       }
     };
     __syncthreads();
-    issue(p0);
+    issue(p0, kra, vra);
+    if (p0 + kGSub < pc) issue(p0 + kGSub, krb, vrb);
     copy_units<4>(
         ws, nr * d4,
         [&](int i) {
@@ -1520,7 +1523,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
     }
     const bool first = task == (int)blockIdx.x && trace && tid == 0;  // stamps of the first task
     if (first) gp(trace)[2] = wall_clock64();
-    for (int q0 = p0; q0 < p1; q0 += kGSub) {
+    auto subtile = [&](int q0, uint4(&kr)[kU], uint4(&vr)[kU]) __attribute__((always_inline)) {
       const int ns = min(kGSub, p1 - q0);
       __syncthreads();  // the previous sub-tile is consumed
 #pragma unroll
@@ -1531,7 +1534,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
           *reinterpret_cast<uint4*>(Vb + pl * d + 8 * c) = vr[u];
         }
       }
-      if (q0 + kGSub < pc) issue(q0 + kGSub);
+      if (q0 + 2 * kGSub < pc) issue(q0 + 2 * kGSub, kr, vr);
       // new positions of the sub-tile: rotate the key, round to bf16, append, stage
       const int n0 = max(q0, kvl), nn = max(0, q0 + ns - n0);
       for (int e = tid; e < nn * d2; e += kThreads) {
@@ -1610,6 +1613,10 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
         }
       }
       if (first && q0 == p0) gp(trace)[5] = wall_clock64();
+    };
+    for (int q0 = p0; q0 < p1; q0 += 2 * kGSub) {
+      subtile(q0, kra, vra);
+      if (q0 + kGSub < p1) subtile(q0 + kGSub, krb, vrb);
     }
     __syncthreads();
     if (first) gp(trace)[3] = wall_clock64();
