@@ -117,6 +117,10 @@ int check_config(const mk_config* c) {
         return fail(MK_E_UNSUPPORTED, "kda_dk must be 64 or 128 and kda_dv a multiple of 8");
     }
   }
+  // the split-KV merge holds in LDS, for one task, the statistics of every split of two (m, head)
+  // units (4 floats each) and 32 values per split
+  if (40LL * ((c->kv_capacity + kChunk - 1) / kChunk) > kLdsFloats)
+    return fail(MK_E_UNSUPPORTED, "kv_capacity %d too large for the split-KV merge", c->kv_capacity);
   return MK_OK;
 }
 

@@ -1632,66 +1632,76 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
   }
 }
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 // Merge split-KV partials: out[m][h*dim + j] = sum_s e^{mx_s - M} u_s[j] / sum_s e^{mx_s - M} l_s
-// over the splits s (M the largest mx_s). Task (m, h, 32 values): every split's statistics and
-// its 32 values are copied straight into LDS in one batch; thread (split lane sl = tid/8, quad
-// q = tid%8) then sums splits sl, sl + 64, ... of four values.
+// over the splits s (M the largest mx_s). Task = (m, h, 32 values); a workgroup takes a contiguous
+// range of tasks, so its tasks share few (m, h) units. As many of them as LDS holds are one batch:
+// the statistics of the batch's units and every split's values of its tasks are copied into LDS
+// together (one memory round trip per batch, not per task). A group of P lanes then owns four
+// values of a task: it takes the unit's maximum over splits r, r + P, ... (lane r), then the split
+// weights, weighted values and weighted sums over the same splits, and reduces each over the group
+// (P = 64 for a batch of one task, else 8).
 __device__ __forceinline__ void merge_phase(const Params& p, const Ws& ws, int heads, int dim, float* out,
                                             float* smem) {
   const int nsplit = rfl(p.nsplit), stride = dim + kPartPad, nj = (dim + 31) >> 5, ntask = rfl(p.M) * heads * nj;
   const float* part = rflp(p.part);
-  const int tid = tid_x(), lane = lane_id(), wave = wave_id(), sl = tid >> 3, qd = tid & 7;
-  float* hdr = smem;                                     // [nsplit][4] max, sum
-  float* val = hdr + 4 * nsplit;                         // [nsplit][4 nv] values (dense)
-  float* w = val + 32 * nsplit;                          // [nsplit] split weights
-  f32x4* red = reinterpret_cast<f32x4*>(w + ((nsplit + 3) & ~3));  // [kWaves][8]
-  float* misc = reinterpret_cast<float*>(red + kWaves * 8);       // [2][kWaves]
-  for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
-    const int mh = task / nj, j0 = (task - mh * nj) * 32;
-    const int nv = min(32, dim - j0) >> 2;  // 16-byte units of values
-    const float* src = part + (size_t)mh * nsplit * stride;
-    __syncthreads();
-    dma_rows<kCoherent>(ws.r, hdr, 1, nsplit, 0, [&](int, int c) { return ws.off(src + (size_t)c * stride); });
-    dma_rows<kCoherent>(ws.r, val, 1, nsplit * nv, 0, [&](int, int u) {
-      const int r = u / nv;
-      return ws.off(src + (size_t)r * stride + kPartPad + j0 + 4 * (u - r * nv));
+  const int tid = tid_x();
+  const int t0 = (int)((unsigned)ntask * blockIdx.x / gridDim.x), t1 = (int)((unsigned)ntask * (blockIdx.x + 1) / gridDim.x);
+  // tasks per batch: a batch of tb tasks spans at most tb + 1 units of 4 statistics per split; a
+  // task holds 32 values per split
+  const int tb = max(1, (kLdsFloats - 4 * nsplit) / (36 * nsplit));
+  for (int b0 = t0; b0 < t1; b0 += tb) {
+    const int nt = min(tb, t1 - b0), u0 = b0 / nj, nu = (b0 + nt - 1) / nj - u0 + 1;
+    float* hdr = smem;                  // [nu][nsplit][4] max, sum
+    float* val = hdr + 4 * nu * nsplit;  // [nt][nsplit][32] values
+    __syncthreads();  // the previous batch is consumed
+    dma_rows<kCoherent>(ws.r, hdr, nu, nsplit, 4 * nsplit,
+                        [&](int r, int c) { return ws.off(part + ((size_t)(u0 + r) * nsplit + c) * stride); });
+    dma_rows<kCoherent>(ws.r, val, nt, 8 * nsplit, 32 * nsplit, [&](int r, int c) {
+      const int t = b0 + r, u = t / nj, j0 = (t - u * nj) * 32, nv = min(32, dim - j0) >> 2, q = c & 7;
+      return ws.off(part + ((size_t)u * nsplit + (c >> 3)) * stride + kPartPad + j0 + 4 * min(q, nv - 1));
     });
     wait_vm();
     __syncthreads();
-    float mx = -INFINITY;
-    for (int s = tid; s < nsplit; s += kThreads) mx = fmaxf(mx, hdr[4 * s]);
-    mx = wave_max(mx, 64);
-    if (lane == 0) misc[wave] = mx;
-    __syncthreads();
-    float M = misc[0];
-    for (int i = 1; i < kWaves; ++i) M = fmaxf(M, misc[i]);
-    float lsum = 0.f;
-    for (int s = tid; s < nsplit; s += kThreads) {
-      const float ws_ = hdr[4 * s] == -INFINITY ? 0.f : __expf(hdr[4 * s] - M);
-      w[s] = ws_;
-      lsum += ws_ * hdr[4 * s + 1];
-    }
-    lsum = wave_sum(lsum, 64);
-    if (lane == 0) misc[kWaves + wave] = lsum;
-    __syncthreads();
-    float L = 0.f;
-    for (int i = 0; i < kWaves; ++i) L += misc[kWaves + i];
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (qd < nv)
-      for (int s = sl; s < nsplit; s += 64) acc += w[s] * *reinterpret_cast<const f32x4*>(val + 4 * nv * s + 4 * qd);
-    for (int o = 8; o < 64; o <<= 1) {
-      acc.x += __shfl_xor(acc.x, o, 64);
-      acc.y += __shfl_xor(acc.y, o, 64);
-      acc.z += __shfl_xor(acc.z, o, 64);
-      acc.w += __shfl_xor(acc.w, o, 64);
-    }
-    if (lane < 8) red[wave * 8 + lane] = acc;
-    __syncthreads();
-    if (tid < nv) {
-      f32x4 t = red[tid];
-      for (int i = 1; i < kWaves; ++i) t += red[i * 8 + tid];
-      ws.st4(out + (size_t)mh * dim + j0 + 4 * tid, t * (1.0f / L));
-    }
+    // items (task, quad of values), P lanes per item: 64 when the batch is one task, else 8
+    const int G = nt * 8;
+    auto items = [&](auto pc) __attribute__((always_inline)) {
+      constexpr int P = decltype(pc)::value;
+      const int r = tid & (P - 1);
+      for (int g0 = 0; g0 < G; g0 += kThreads / P) {
+        const int g = g0 + tid / P, tl = min(g, G - 1) >> 3, q = g & 7;
+        const int t = b0 + tl, u = t / nj, j0 = (t - u * nj) * 32, nv = min(32, dim - j0) >> 2;
+        const float* hu = hdr + 4 * (u - u0) * nsplit;
+        float mx = -INFINITY;
+#pragma unroll 4
+        for (int s = r; s < nsplit; s += P) mx = fmaxf(mx, hu[4 * s]);
+        mx = wave_max(mx, P);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        float lsum = 0.f;
+        const float* vt = val + 32 * tl * nsplit + 4 * q;
+#pragma unroll 4
+        for (int s = r; s < nsplit; s += P) {
+          const float2 st = *reinterpret_cast<const float2*>(hu + 4 * s);
+          const float w = st.x == -INFINITY ? 0.f : __expf(st.x - mx);
+          lsum += w * st.y;
+          acc += w * *reinterpret_cast<const f32x4*>(vt + 32 * s);
+        }
+        lsum = wave_sum(lsum, P);
+        acc.x = wave_sum(acc.x, P);
+        acc.y = wave_sum(acc.y, P);
+        acc.z = wave_sum(acc.z, P);
+        acc.w = wave_sum(acc.w, P);
+        if (g < G && q < nv && r == 0) ws.st4(out + (size_t)u * dim + j0 + 4 * q, acc * (1.0f / lsum));
+      }
+    };
+    if (nt == 1)
+      items(IntC<64>{});
+    else
+      items(IntC<8>{});
   }
 }
 

@@ -59,7 +59,10 @@ typedef enum { MK_ATTN_GQA = 0, MK_ATTN_MLA = 1, MK_ATTN_HYBRID = 2 } mk_attn_ki
  * feed-forward block is the shared SwiGLU block alone and there is no router ("tpu-megakernels
  * README", FAQ: the dense BF16 decoder served beside the MoE model). Its layers have one grid
  * phase fewer (no routed-expert phase).
- * expert_pool_layers > 0: layer l uses the expert weights of pool slot l % expert_pool_layers. */
+ * expert_pool_layers > 0: layer l uses the expert weights of pool slot l % expert_pool_layers.
+ * kv_capacity is at most 14736 positions (921 split-KV chunks of 16): the merge of the chunks'
+ * partial softmax results holds one task's statistics and values for every chunk in LDS;
+ * larger capacities return MK_E_UNSUPPORTED. */
 typedef struct {
   int32_t n_layers, hidden, vocab, attn_kind;
   int32_t n_heads, n_kv_heads, head_dim;

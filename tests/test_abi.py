@@ -110,6 +110,17 @@ def test_bad_dense_configs(mk, kw):
     assert e.value.code == mk.MK_E_INVAL
 
 
+def test_kv_capacity_limit(mk):
+    # the split-KV merge keeps one task's statistics and values for every split (at least 16
+    # positions each) in LDS: 921 splits fit, 922 do not
+    sizes(mk, replace(synth.TINY, kv_capacity=921 * 16))
+    sizes(mk, replace(synth.K3, kv_capacity=921 * 16))
+    for c in (synth.TINY, synth.K3):
+        with pytest.raises(mk.MkError) as e:
+            sizes(mk, replace(c, kv_capacity=921 * 16 + 1))
+        assert e.value.code == mk.MK_E_UNSUPPORTED
+
+
 def test_dense_layout_and_loading(mk):
     """A dense model's arena holds exactly its tensors (no router, no expert pool); a step is
     refused until every one of them is loaded, and a router tensor is rejected."""
