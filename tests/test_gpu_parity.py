@@ -193,7 +193,9 @@ K3_SMALL = replace(synth.K3, name="k3-2layer", n_layers=2, expert_pool_layers=0)
 HYB_SMALL = replace(synth.K3_HYBRID, name="hybrid-4layer", n_layers=4, expert_pool_layers=0)
 
 
-@pytest.mark.parametrize("B,T,kv_len", [(1, 1, 4096), (3, 2, 1000), (1, 7, 4096), (8, 1, 33)])
+# (2, 8, 4096): 16 token rows over 65 splits of 64 positions; the split-KV merge gives each
+# workgroup 16 (row, head, 32-value) tasks, more than one LDS batch holds (15)
+@pytest.mark.parametrize("B,T,kv_len", [(1, 1, 4096), (3, 2, 1000), (1, 7, 4096), (8, 1, 33), (2, 8, 4096)])
 def test_k3_two_layers(B, T, kv_len):
     parity(K3_SMALL, synth.Spec(seed=2), B, T, kv_len)
 
