@@ -1632,6 +1632,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
   }
 }
 
+// an int as a type: the lane-group width of a generic lambda, fixed at compile time
 template <int N>
 struct IntC {
   static constexpr int value = N;
