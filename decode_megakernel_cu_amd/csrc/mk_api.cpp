@@ -92,13 +92,16 @@ int check_config(const mk_config* c) {
   if (c->n_heads < 1) return fail(MK_E_INVAL, "n_heads must be positive");
   if (c->attn_kind == MK_ATTN_GQA) {
     if (c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return fail(MK_E_INVAL, "n_heads must be a multiple of n_kv_heads");
-    if (c->head_dim < 8 || c->head_dim % 8 || c->head_dim > 2 * kMaxRopePairs)
-      return fail(MK_E_UNSUPPORTED, "head_dim must be a multiple of 8 and at most %d", 2 * kMaxRopePairs);
-    // the attention tile: bf16 keys (rows padded by 8) and values of kGSub positions, then per query
-    // row (new token x head of the group) the rotated query, the scores, the value sums and two
-    // running statistics
-    const int nr = c->max_new_tokens * (c->n_heads / c->n_kv_heads);
-    if (kGSub * (c->head_dim + 4) + nr * (2 * c->head_dim + kGSub + 2) > kLdsFloats)
+    if (c->head_dim < 32 || c->head_dim % 32 || c->head_dim > 128)
+      return fail(MK_E_UNSUPPORTED, "head_dim must be 32, 64, 96 or 128 (matrix-core attention)");
+    // the attention tile: bf16 keys (rows padded by 8) and values (by 16) of kGSub positions, then
+    // per query row (new token x head of the group, in tiles of 16) the query's bf16 high and low
+    // parts (padded by 8), the rotated query, the scores (padded by 4) and three statistics; the
+    // value sums of row tiles x 16-column tiles stay in registers, at most kGqaTiles per wave
+    const int nr = c->max_new_tokens * (c->n_heads / c->n_kv_heads), nrp = (nr + 15) / 16 * 16;
+    const int d = c->head_dim;
+    if (kGSub * (2 * d + 24) / 2 + nrp * (d + 8) + nrp * d + nrp * (kGSub + 4) + 3 * nrp > kLdsFloats ||
+        (nrp / 16) * (d / 16) > kWaves * kGqaTiles)
       return fail(MK_E_UNSUPPORTED, "GQA group too large for the attention tile");
   } else {
     if (c->kv_lora < 8 || c->kv_lora % 8 || c->q_lora < 8 || c->q_lora % 8 || c->nope_dim < 8 || c->nope_dim % 8 ||

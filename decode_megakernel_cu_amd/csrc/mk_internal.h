@@ -14,6 +14,7 @@ constexpr int kLdsFloats = 36 * 1024;    // 144 KiB of LDS per workgroup
 constexpr int kChunk = 16;               // minimum cache positions per split-KV task
 constexpr int kSub = 32;                 // cache positions an MLA task stages at once
 constexpr int kGSub = 64;                // cache positions a GQA task stages at once (one per lane)
+constexpr int kGqaTiles = 3;             // GQA value-sum tiles (16 rows x 16 columns) per wave
 constexpr int kPartPad = 4;              // a partial is [max, sum, pad, pad, values...]: values 16-byte aligned
 constexpr int kMaxExperts = 256;
 constexpr int kTraceStamps = MK_TRACE_STAMPS;

@@ -1453,29 +1453,39 @@ __device__ __forceinline__ void rope_pair(const float* table, int t, int j, floa
 }
 
 // GQA split-KV partials (flash decoding). Task (b, g, s): positions [s*C, s*C+C) of sequence b,
-// kv head g, every query head of the group and every new token (rows r = t*qg + head in group).
-// The task streams its positions in sub-tiles of kGSub: the cache rows of the next sub-tile are
-// requested (into registers) while the current one is scored, and each row keeps a running
-// maximum, sum of weights and unnormalised value sum (online softmax), so the task writes one
+// kv head g, every query head of the group and every new token (rows r = t*qg + head in group,
+// nr of them, in tiles of 16). The task streams its positions in sub-tiles of kGSub: the cache
+// rows of the next sub-tile are in flight in registers while the current one is scored, and
+// each row keeps a running maximum and sum of weights (online softmax), so the task writes one
 // partial whatever its length. New positions in the chunk are rotated, rounded to bf16, appended
 // to the cache and attended from the rounded values.
+// Scores and value sums run on the matrix cores (16x16x32 bf16 multiplies): the queries and the
+// softmax weights enter as bf16 high and low parts (two multiplies each), the keys and values as
+// stored. A value multiply takes 32 positions as its K dimension in the order p = k/8 + 4 (k%8)
+// (k the operand index), so that the four lane groups read staged value rows 1 apart; value rows
+// are padded to 8 LDS banks apart and key, query and score rows to 4, which keeps every operand
+// read free of bank conflicts. The unnormalised value sums stay in registers: tile j of the
+// (row tile, 16-column tile) grid belongs to wave j % 8, rescaled as each row's maximum moves.
 __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
                                                const float* rope, uint64_t* trace) {
   const int d = p.hd, nq = p.nh, nkv = p.nkv, T = p.T, cap = p.cap, d2 = d / 2, d4 = d / 4, d8 = d / 8;
   const int npos = p.kv_len + T, C = p.chunk, nsplit = p.nsplit, kvl = p.kv_len;
-  const int qg = nq / nkv, nr = T * qg;
+  const int qg = nq / nkv, nr = T * qg, nrt = (nr + 15) >> 4, nrp = 16 * nrt;
+  const int nct = d >> 4, nvt = nrt * nct;  // value tiles: row tiles x column tiles
   const int ntask = p.B * nkv * nsplit;
-  const int tid = tid_x(), lane = lane_id();
-  // key rows padded by 16 bytes: the score loop reads one key row per lane, and rows 256 bytes
-  // apart would all start in the same LDS bank
-  const int dk = d + 8;
-  uint16_t* Kb = reinterpret_cast<uint16_t*>(smem);  // [kGSub][dk] bf16
-  uint16_t* Vb = Kb + kGSub * dk;                    // [kGSub][d] bf16
-  float* Qs = smem + kGSub * (d + 4);                // [nr][d] rotated queries
-  float* S = Qs + nr * d;                            // [nr][kGSub] scores, then weights
-  float* Acc = S + nr * kGSub;                       // [nr][d] unnormalised value sums
-  float* Mx = Acc + nr * d;                          // [nr] running maximum
-  float* Ls = Mx + nr;                               // [nr] running sum of weights
+  const int tid = tid_x(), lane = lane_id(), wave = wave_id(), ml = lane & 15, mq = lane >> 4;
+  const int dk = d + 8;   // bf16 per staged key row and per query row (hi, lo)
+  const int dv = d + 16;  // bf16 per staged value row
+  const int ss = kGSub + 4;  // floats per score row
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(smem);  // [kGSub][dk] bf16 keys
+  uint16_t* Vb = Kb + kGSub * dk;                    // [kGSub][dv] bf16 values
+  uint16_t* Qh = Vb + kGSub * dv;                    // [nrp][dk] query high parts
+  uint16_t* Ql = Qh + nrp * dk;                      // [nrp][dk] query low parts
+  float* Qs = reinterpret_cast<float*>(Ql + nrp * dk);  // [nr][d] rotated queries; at the end the value sums [nrp][d]
+  float* S = Qs + nrp * d;                           // [nrp][ss] scores, then weights
+  float* Mx = S + nrp * ss;                          // [nrp] running maximum
+  float* Ls = Mx + nrp;                              // [nrp] running sum of weights
+  float* Sc = Ls + nrp;                              // [nrp] rescale of the value sums this sub-tile
   const size_t lstride = (size_t)p.Bmax * nkv * cap * d;
   uint16_t* Kc = rflp(p.kv) + (size_t)rfl(ly->ord) * lstride;
   uint16_t* Vc = rflp(p.kv) + (size_t)p.L * lstride + (size_t)rfl(ly->ord) * lstride;
@@ -1486,8 +1496,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
     const int s = task % nsplit, g = (task / nsplit) % nkv, b = task / (nsplit * nkv);
     const int p0 = s * C, p1 = min(npos, p0 + C), pc = min(p1, kvl);  // [p0, pc): cached positions
     const size_t row0 = ((size_t)b * nkv + g) * cap;                     // cache row of position 0
-    // two register sets: the rows of the next two sub-tiles are in flight while one is scored
-    uint4 kra[kU], vra[kU], krb[kU], vrb[kU];
+    uint4 kra[kU], vra[kU];  // the rows of the next sub-tile, in flight while one is scored
     auto issue = [&](int q0, uint4(&kr)[kU], uint4(&vr)[kU]) __attribute__((always_inline)) {
       // the cached rows of the sub-tile at q0 (others read row 0)
 #pragma unroll
@@ -1500,7 +1509,6 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
     };
     __syncthreads();
     issue(p0, kra, vra);
-    if (p0 + kGSub < pc) issue(p0 + kGSub, krb, vrb);
     copy_units<4>(
         ws, nr * d4,
         [&](int i) {
@@ -1508,8 +1516,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
           return p.a1 + (size_t)(b * T + t) * nq * d + hq * d + 4 * (i - r * d4);
         },
         [&](int i) { return Qs + 4 * i; });
-    for (int e = tid; e < nr * d; e += kThreads) Acc[e] = 0.f;
-    for (int e = tid; e < nr; e += kThreads) {
+    for (int e = tid; e < nrp; e += kThreads) {
       Mx[e] = -INFINITY;
       Ls[e] = 0.f;
     }
@@ -1521,6 +1528,17 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
       Qs[r * d + j] = q0;
       Qs[r * d + j + d2] = q1;
     }
+    __syncthreads();
+    for (int e = tid; e < nrp * d2; e += kThreads) {  // queries as bf16 high and low parts (rows past nr: 0)
+      const int r = e / d2, j = 2 * (e - r * d2);
+      uint32_t hi = 0u, lo = 0u;
+      if (r < nr) split_bf16(Qs[r * d + j], Qs[r * d + j + 1], hi, lo);
+      *reinterpret_cast<uint32_t*>(Qh + r * dk + j) = hi;
+      *reinterpret_cast<uint32_t*>(Ql + r * dk + j) = lo;
+    }
+    f32x4 u[kGqaTiles];  // value sums of this wave's tiles (rows 4 mq + i, column ml)
+#pragma unroll
+    for (int k = 0; k < kGqaTiles; ++k) u[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool first = task == (int)blockIdx.x && trace && tid == 0;  // stamps of the first task
     if (first) gp(trace)[2] = wall_clock64();
     auto subtile = [&](int q0, uint4(&kr)[kU], uint4(&vr)[kU]) __attribute__((always_inline)) {
@@ -1531,10 +1549,10 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
         const int i = u * kThreads + tid, pl = i / d8, c = i - pl * d8;
         if (i < U && q0 + pl < pc) {
           *reinterpret_cast<uint4*>(Kb + pl * dk + 8 * c) = kr[u];
-          *reinterpret_cast<uint4*>(Vb + pl * d + 8 * c) = vr[u];
+          *reinterpret_cast<uint4*>(Vb + pl * dv + 8 * c) = vr[u];
         }
       }
-      if (q0 + 2 * kGSub < pc) issue(q0 + 2 * kGSub, kr, vr);
+      if (q0 + kGSub < pc) issue(q0 + kGSub, kr, vr);
       // new positions of the sub-tile: rotate the key, round to bf16, append, stage
       const int n0 = max(q0, kvl), nn = max(0, q0 + ns - n0);
       for (int e = tid; e < nn * d2; e += kThreads) {
@@ -1552,75 +1570,99 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
         gp(Vc)[ci + j + d2] = vb1;
         Kb[pl * dk + j] = kb0;
         Kb[pl * dk + j + d2] = kb1;
-        Vb[pl * d + j] = vb0;
-        Vb[pl * d + j + d2] = vb1;
+        Vb[pl * dv + j] = vb0;
+        Vb[pl * dv + j + d2] = vb1;
       }
       __syncthreads();
-      for (int e = tid; e < nr * kGSub; e += kThreads) {  // scores, causal among the new positions
-        const int r = e / kGSub, pl = e - r * kGSub, t = r / qg;
-        float sc = -INFINITY;
-        if (pl < ns && q0 + pl <= kvl + t) {
-          float acc = 0.f;
-#pragma unroll 4
-          for (int j = 0; j < d; j += 8) {
-            float kf[8];
-            unpack8(*reinterpret_cast<const uint4*>(Kb + pl * dk + j), kf);
-            const f32x4 qa = *reinterpret_cast<const f32x4*>(Qs + r * d + j);
-            const f32x4 qb = *reinterpret_cast<const f32x4*>(Qs + r * d + j + 4);
-            acc += qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3] + qb.x * kf[4] + qb.y * kf[5] +
-                   qb.z * kf[6] + qb.w * kf[7];
-          }
-          sc = acc * scale;
+      // scores: tile (row tile rt, position tile pt) per wave; D rows 4 mq + i, column ml
+      for (int jt = wave; jt < nrt * (kGSub / 16); jt += kWaves) {
+        const int rt = jt / (kGSub / 16), pt = jt - rt * (kGSub / 16);
+        const uint16_t* ah = Qh + (16 * rt + ml) * dk + 8 * mq;
+        const uint16_t* al = Ql + (16 * rt + ml) * dk + 8 * mq;
+        const uint16_t* bk = Kb + (16 * pt + ml) * dk + 8 * mq;
+        f32x4 dd = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < d; kk += 32) {
+          const bf16x8 bv = ld_bf16x8(bk + kk);
+          dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_bf16x8(ah + kk), bv, dd, 0, 0, 0);
+          dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_bf16x8(al + kk), bv, dd, 0, 0, 0);
         }
-        S[r * kGSub + pl] = sc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[(16 * rt + 4 * mq + i) * ss + 16 * pt + ml] = dd[i] * scale;
       }
       __syncthreads();
       if (first && q0 == p0) gp(trace)[4] = wall_clock64();
-      for (int r = wave_id(); r < nr; r += kWaves) {  // online softmax: one wave per row
-        const float sv = S[r * kGSub + lane];
+      // online softmax: one wave per row, lane = position; rows past nr and rows that see no
+      // position yet get weight 0 and keep their sums (rescale 1)
+      for (int r = wave; r < nrp; r += kWaves) {
+        const int t = r / qg;
+        const float sv = (r < nr && lane < ns && q0 + lane <= kvl + t) ? S[r * ss + lane] : -INFINITY;
         const float mold = Mx[r], mnew = fmaxf(mold, wave_max(sv, 64));
-        if (mnew == -INFINITY) continue;  // nothing visible to this row yet
-        const float alpha = mold == -INFINITY ? 0.f : __expf(mold - mnew);
-        const float w = sv == -INFINITY ? 0.f : __expf(sv - mnew);
-        const float ls = wave_sum(w, 64);
-        S[r * kGSub + lane] = w;  // read back by the whole wave: ordered by wavefront-scope fences
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (2 * lane < d) {  // eight positions per step: their loads are in flight together
-          float a0 = 0.f, a1 = 0.f;
-          const uint16_t* vcol = Vb + 2 * lane;
-          for (int pl0 = 0; pl0 < ns; pl0 += 8) {
-            const f32x4 wa = *reinterpret_cast<const f32x4*>(S + r * kGSub + pl0);
-            const f32x4 wb = *reinterpret_cast<const f32x4*>(S + r * kGSub + pl0 + 4);
-            const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-            uint32_t v2[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)  // rows past ns hold stale values: weight 0, value not read
-              v2[k] = pl0 + k < ns ? *reinterpret_cast<const uint32_t*>(vcol + (pl0 + k) * d) : 0u;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              a0 += wv[k] * __uint_as_float(v2[k] << 16);
-              a1 += wv[k] * __uint_as_float(v2[k] & 0xFFFF0000u);
-            }
-          }
-          Acc[r * d + 2 * lane] = alpha * Acc[r * d + 2 * lane] + a0;
-          Acc[r * d + 2 * lane + 1] = alpha * Acc[r * d + 2 * lane + 1] + a1;
+        float w = 0.f, alpha = 1.f;
+        if (mnew != -INFINITY) {
+          alpha = mold == -INFINITY ? 0.f : __expf(mold - mnew);
+          w = sv == -INFINITY ? 0.f : __expf(sv - mnew);
         }
+        const float ls = wave_sum(w, 64);
+        S[r * ss + lane] = w;
         if (lane == 0) {
-          Mx[r] = mnew;
-          Ls[r] = alpha * Ls[r] + ls;
+          if (mnew != -INFINITY) {
+            Mx[r] = mnew;
+            Ls[r] = alpha * Ls[r] + ls;
+          }
+          Sc[r] = alpha;
         }
       }
+      __syncthreads();
       if (first && q0 == p0) gp(trace)[5] = wall_clock64();
+      // value sums: A = weights [16 rows][32 positions] (high, low), B = value rows [32][16 columns]
+#pragma unroll
+      for (int k = 0; k < kGqaTiles; ++k) {
+        const int jt = wave + kWaves * k;
+        if (jt < nvt) {
+          const int rt = jt / nct, ct = jt - rt * nct, col = 16 * ct + ml;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) u[k][i] *= Sc[16 * rt + 4 * mq + i];
+          const float* wr = S + (16 * rt + ml) * ss + mq;
+#pragma unroll
+          for (int ks = 0; ks < kGSub; ks += 32) {
+            float wv[8];
+            uint32_t vv[4];
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+              const int pa = ks + mq + 4 * i, pb = pa + 4;
+              wv[i] = wr[ks + 4 * i];
+              wv[i + 1] = wr[ks + 4 * i + 4];
+              const uint32_t va = pa < ns ? Vb[pa * dv + col] : 0u;
+              const uint32_t vb = pb < ns ? Vb[pb * dv + col] : 0u;
+              vv[i >> 1] = va | (vb << 16);
+            }
+            uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+            split_bf16(wv[0], wv[1], h0, l0);
+            split_bf16(wv[2], wv[3], h1, l1);
+            split_bf16(wv[4], wv[5], h2, l2);
+            split_bf16(wv[6], wv[7], h3, l3);
+            const bf16x8 bv = as_bf16x8(u32x4{vv[0], vv[1], vv[2], vv[3]});
+            u[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{h0, h1, h2, h3}), bv, u[k], 0, 0, 0);
+            u[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{l0, l1, l2, l3}), bv, u[k], 0, 0, 0);
+          }
+        }
+      }
     };
-    for (int q0 = p0; q0 < p1; q0 += 2 * kGSub) {
-      subtile(q0, kra, vra);
-      if (q0 + kGSub < p1) subtile(q0 + kGSub, krb, vrb);
+    for (int q0 = p0; q0 < p1; q0 += kGSub) subtile(q0, kra, vra);
+    if (first) gp(trace)[3] = wall_clock64();
+    // the value sums to LDS (over the queries, no longer read), then the task's partial
+    float* Acc = Qs;
+#pragma unroll
+    for (int k = 0; k < kGqaTiles; ++k) {
+      const int jt = wave + kWaves * k;
+      if (jt < nvt) {
+        const int rt = jt / nct, ct = jt - rt * nct;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Acc[(16 * rt + 4 * mq + i) * d + 16 * ct + ml] = u[k][i];
+      }
     }
     __syncthreads();
-    if (first) gp(trace)[3] = wall_clock64();
-    for (int r = wave_id(); r < nr; r += kWaves) {  // the task's partial: max, sum, values
+    for (int r = wave; r < nr; r += kWaves) {  // the task's partial: max, sum, values
       const int t = r / qg, hq = g * qg + (r - t * qg), m = b * T + t;
       float* dst = p.part + ((size_t)(m * nq + hq) * nsplit + s) * stride;
       for (int j = lane; j < d; j += 64) stc(dst + kPartPad + j, Acc[r * d + j]);
@@ -2132,6 +2174,8 @@ __device__ __forceinline__ void resid_out(Gemv& g, const Params& p, const uint16
 
 // Phase i of layer l (l == L: the final norm and LM head; ly: the layer's table row, in LDS). Fills
 // g for GEMV phases; the down projection reads this workgroup's routing of the layer (rt).
+// G: a GQA model (every layer GQA), else MLA or hybrid (MLA and delta-rule layers).
+template <bool G>
 __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, const Route* rt, const LayerDev* ly) {
   g.M = p.M;
   g.eps = p.eps;
@@ -2196,7 +2240,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
     g.pairs = rt->nu + (p.SF > 0 ? 1 : 0);
     return PT_GEMV;
   }
-  if (kind == kGqa) {
+  if constexpr (G) {
     const int dq = p.nh * p.hd, dkv = p.nkv * p.hd;
     if (i == 0) {
       norm_input(g, p.x, p.H, p.H, ly->attn_norm);
@@ -2213,7 +2257,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
     plain_input(g, p.att, dq, dq);
     resid_out(g, p, ly->wo, dq);
     return PT_GEMV;
-  }
+  } else {
   if (kind == kMla) {
     const int lat = p.kvl + p.rd, qd = p.nd + p.rd;
     switch (i) {
@@ -2286,6 +2330,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
   plain_input(g, p.att, dvv, dvv);
   resid_out(g, p, ly->wo, dvv);
   return PT_GEMV;
+  }
 }
 
 __device__ __forceinline__ void scalarize(Gemv& g) {
@@ -2487,7 +2532,9 @@ struct PlanOf<true> {
 };
 
 // MM: input rows the kernel is built for (at least M); MF: GEMV phases on the matrix cores
-template <int MM, bool MF>
+// G: the model's attention family (true: GQA; false: MLA or hybrid); each instance holds only
+// its family's attention code, which keeps the other family's registers out of its allocation
+template <int MM, bool MF, bool G>
 __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   __shared__ Smem sm;
   // the parameters live in LDS: read where needed instead of pinning ~100 scalar registers
@@ -2557,7 +2604,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       // buffers are never copied.
       barrier_arrive(p, gen);
       uint64_t* trec = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
-      const int type = rfl(describe(p, l, i, g, &sm.route, ly));
+      const int type = rfl(describe<G>(p, l, i, g, &sm.route, ly));
       if (l == p.L) {  // LM head: logits optional on greedy steps, per-workgroup argmax keys
         if (tid_x() < MK_MAX_M) sm.hmax[tid_x()] = 0ull;
         g.hmax = p.greedy ? sm.hmax : nullptr;
@@ -2566,7 +2613,8 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       if (trec && tid_x() == 0) gp(trec)[10] = wall_clock64();
       const bool early = type == PT_GEMV;  // prepared while waiting
       if (!early) {
-        if (type == PT_ATTN_MLA) mla_prefetch_rows(p, ly, sm.buf);
+        if constexpr (!G)
+          if (type == PT_ATTN_MLA) mla_prefetch_rows(p, ly, sm.buf);
         if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort);
         MK_FINISH();
         if (trec && tid_x() == 0) gp(trec)[7] = wall_clock64();
@@ -2609,23 +2657,29 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         // starts would make every LDS read of its streaming loop wait for all loads (the compiler
         // cannot tell the two LDS areas apart).
         case PT_ATTN_GQA:
-          if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
-          gqa_attn_phase(p, ly, ws, sm.buf, sm.rope, trec);
-          resident = false;
+          if constexpr (G) {
+            if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
+            gqa_attn_phase(p, ly, ws, sm.buf, sm.rope, trec);
+            resident = false;
+          }
           break;
         case PT_ATTN_MLA:
-          if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
-          mla_attn_phase(p, ly, ws, sm.buf, sm.rope, trec);
-          resident = false;
+          if constexpr (!G) {
+            if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
+            mla_attn_phase(p, ly, ws, sm.buf, sm.rope, trec);
+            resident = false;
+          }
           break;
         case PT_MERGE:
           merge_phase(p, ws, p.nh, p.kvl > 0 ? p.kvl : p.hd, p.att, sm.buf);
           resident = false;
           break;
         case PT_KDA:
-          if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
-          kda_phase(p, ly, ws);
-          resident = false;
+          if constexpr (!G) {
+            if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
+            kda_phase(p, ly, ws);
+            resident = false;
+          }
           break;
         default:
           break;
@@ -2693,32 +2747,39 @@ namespace mk {
 size_t kernel_lds_bytes() { return sizeof(Smem) + sizeof(Params); }
 int max_grid() { return kMaxGrid; }
 
+// the instance for the model's attention family (a GQA model has no latent rank)
+template <int MM, bool MF>
+hipError_t launch_family(const Params& p, dim3 grid, dim3 block, hipStream_t stream) {
+  if (p.kvl == 0)
+    hipLaunchKernelGGL((mk_decode_kernel<MM, MF, true>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((mk_decode_kernel<MM, MF, false>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const Params& p, int nblocks, bool matrix_cores, hipStream_t stream) {
   const int mm = p.M <= 1 ? 1 : p.M <= 2 ? 2 : p.M <= 4 ? 4 : p.M <= 8 ? 8 : 16;
   const dim3 grid(nblocks), block(kThreads);
 #ifdef MK_ONLY_MM1
   if (mm != 1) return hipErrorNotSupported;
   (void)matrix_cores;
-  hipLaunchKernelGGL((mk_decode_kernel<1, false>), grid, block, 0, stream, p);
-  return hipGetLastError();
+  return launch_family<1, false>(p, grid, block, stream);
 #else
   if (matrix_cores && mm >= 2) {
     switch (mm) {
-      case 2: hipLaunchKernelGGL((mk_decode_kernel<2, true>), grid, block, 0, stream, p); break;
-      case 4: hipLaunchKernelGGL((mk_decode_kernel<4, true>), grid, block, 0, stream, p); break;
-      case 8: hipLaunchKernelGGL((mk_decode_kernel<8, true>), grid, block, 0, stream, p); break;
-      default: hipLaunchKernelGGL((mk_decode_kernel<16, true>), grid, block, 0, stream, p); break;
+      case 2: return launch_family<2, true>(p, grid, block, stream);
+      case 4: return launch_family<4, true>(p, grid, block, stream);
+      case 8: return launch_family<8, true>(p, grid, block, stream);
+      default: return launch_family<16, true>(p, grid, block, stream);
     }
-    return hipGetLastError();
   }
   switch (mm) {
-    case 1: hipLaunchKernelGGL((mk_decode_kernel<1, false>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((mk_decode_kernel<2, false>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((mk_decode_kernel<4, false>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((mk_decode_kernel<8, false>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((mk_decode_kernel<16, false>), grid, block, 0, stream, p); break;
+    case 1: return launch_family<1, false>(p, grid, block, stream);
+    case 2: return launch_family<2, false>(p, grid, block, stream);
+    case 4: return launch_family<4, false>(p, grid, block, stream);
+    case 8: return launch_family<8, false>(p, grid, block, stream);
+    default: return launch_family<16, false>(p, grid, block, stream);
   }
-  return hipGetLastError();
 #endif
 }
 
@@ -2729,12 +2790,16 @@ hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int n
 
 hipError_t occupancy(int* blocks_per_cu) {
 #ifdef MK_ONLY_MM1
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_decode_kernel<1, false>, kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_decode_kernel<1, false, false>, kThreads, 0);
 #else
-  int a = 0, b = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, mk_decode_kernel<16, false>, kThreads, 0);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, mk_decode_kernel<16, true>, kThreads, 0);
-  *blocks_per_cu = a < b ? a : b;
+  int n[4] = {0, 0, 0, 0};
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[0], mk_decode_kernel<16, false, false>, kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], mk_decode_kernel<16, true, false>, kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[2], mk_decode_kernel<16, false, true>, kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[3], mk_decode_kernel<16, true, true>, kThreads, 0);
+  int m = n[0];
+  for (int k = 1; k < 4; ++k) m = n[k] < m ? n[k] : m;
+  *blocks_per_cu = m;
   return e;
 #endif
 }
