@@ -48,8 +48,8 @@ typedef enum {
 typedef enum { MK_ATTN_GQA = 0, MK_ATTN_MLA = 1, MK_ATTN_HYBRID = 2 } mk_attn_kind;
 
 /* Model and capacity description. Matrices are bf16, stored [out][in] (row = output feature).
- * attn_kind GQA: n_heads query heads and n_kv_heads key/value heads of head_dim, RoPE over the
- *   whole head. MLA: n_heads heads, q_lora / kv_lora latent ranks, rope_dim + nope_dim query-key
+ * attn_kind GQA: n_heads query heads and n_kv_heads key/value heads of head_dim (32, 64, 96 or
+ *   128: the attention runs on the matrix cores), RoPE over the whole head. MLA: n_heads heads, q_lora / kv_lora latent ranks, rope_dim + nope_dim query-key
  *   width per head, v_dim value width. HYBRID: layer l is MLA when l % hybrid_period ==
  *   hybrid_period - 1, otherwise a gated delta-rule layer with n_heads heads of kda_dk x kda_dv.
  * Every layer has a MoE block: n_experts routed SwiGLU experts of width ffn, top_k chosen by a
