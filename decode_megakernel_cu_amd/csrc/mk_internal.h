@@ -47,6 +47,7 @@ struct WsLayout {
 struct Params {
   // model
   int32_t L, H, V, nh, nkv, hd, ql, kvl, rd, nd, vd, dk, dv, E, topk, F, SF, norm_topk, cap, Bmax;
+  int32_t family;  // attention family: MK_ATTN_GQA, MK_ATTN_MLA or MK_ATTN_HYBRID (the kernel instance)
   float eps, rope_theta;
   // step
   int32_t B, T, M, kv_len, nsplit, chunk;  // chunk: cache positions per split

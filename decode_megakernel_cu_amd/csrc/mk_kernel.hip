@@ -2174,8 +2174,9 @@ __device__ __forceinline__ void resid_out(Gemv& g, const Params& p, const uint16
 
 // Phase i of layer l (l == L: the final norm and LM head; ly: the layer's table row, in LDS). Fills
 // g for GEMV phases; the down projection reads this workgroup's routing of the layer (rt).
-// G: a GQA model (every layer GQA), else MLA or hybrid (MLA and delta-rule layers).
-template <bool G>
+// Fam: the model's attention family (MK_ATTN_GQA: every layer GQA; MK_ATTN_MLA: every layer MLA;
+// MK_ATTN_HYBRID: MLA and delta-rule layers).
+template <int Fam>
 __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, const Route* rt, const LayerDev* ly) {
   g.M = p.M;
   g.eps = p.eps;
@@ -2240,7 +2241,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
     g.pairs = rt->nu + (p.SF > 0 ? 1 : 0);
     return PT_GEMV;
   }
-  if constexpr (G) {
+  if constexpr (Fam == MK_ATTN_GQA) {
     const int dq = p.nh * p.hd, dkv = p.nkv * p.hd;
     if (i == 0) {
       norm_input(g, p.x, p.H, p.H, ly->attn_norm);
@@ -2315,6 +2316,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
     }
   }
   // gated delta rule
+  if constexpr (Fam != MK_ATTN_HYBRID) return PT_GEMV;  // (no such layer)
   const int dq = p.nh * p.dk, dvv = p.nh * p.dv;
   if (i == 0) {
     norm_input(g, p.x, p.H, p.H, ly->attn_norm);
@@ -2532,9 +2534,9 @@ struct PlanOf<true> {
 };
 
 // MM: input rows the kernel is built for (at least M); MF: GEMV phases on the matrix cores
-// G: the model's attention family (true: GQA; false: MLA or hybrid); each instance holds only
-// its family's attention code, which keeps the other family's registers out of its allocation
-template <int MM, bool MF, bool G>
+// AF: the model's attention family (MK_ATTN_GQA, MK_ATTN_MLA, MK_ATTN_HYBRID); each instance holds
+// only its family's attention code, which keeps the others' registers out of its allocation
+template <int MM, bool MF, int AF>
 __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   __shared__ Smem sm;
   // the parameters live in LDS: read where needed instead of pinning ~100 scalar registers
@@ -2604,7 +2606,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       // buffers are never copied.
       barrier_arrive(p, gen);
       uint64_t* trec = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
-      const int type = rfl(describe<G>(p, l, i, g, &sm.route, ly));
+      const int type = rfl(describe<AF>(p, l, i, g, &sm.route, ly));
       if (l == p.L) {  // LM head: logits optional on greedy steps, per-workgroup argmax keys
         if (tid_x() < MK_MAX_M) sm.hmax[tid_x()] = 0ull;
         g.hmax = p.greedy ? sm.hmax : nullptr;
@@ -2613,7 +2615,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       if (trec && tid_x() == 0) gp(trec)[10] = wall_clock64();
       const bool early = type == PT_GEMV;  // prepared while waiting
       if (!early) {
-        if constexpr (!G)
+        if constexpr (AF != MK_ATTN_GQA)
           if (type == PT_ATTN_MLA) mla_prefetch_rows(p, ly, sm.buf);
         if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort);
         MK_FINISH();
@@ -2657,14 +2659,14 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         // starts would make every LDS read of its streaming loop wait for all loads (the compiler
         // cannot tell the two LDS areas apart).
         case PT_ATTN_GQA:
-          if constexpr (G) {
+          if constexpr (AF == MK_ATTN_GQA) {
             if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
             gqa_attn_phase(p, ly, ws, sm.buf, sm.rope, trec);
             resident = false;
           }
           break;
         case PT_ATTN_MLA:
-          if constexpr (!G) {
+          if constexpr (AF != MK_ATTN_GQA) {
             if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
             mla_attn_phase(p, ly, ws, sm.buf, sm.rope, trec);
             resident = false;
@@ -2675,7 +2677,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
           resident = false;
           break;
         case PT_KDA:
-          if constexpr (!G) {
+          if constexpr (AF == MK_ATTN_HYBRID) {
             if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
             kda_phase(p, ly, ws);
             resident = false;
@@ -2747,13 +2749,15 @@ namespace mk {
 size_t kernel_lds_bytes() { return sizeof(Smem) + sizeof(Params); }
 int max_grid() { return kMaxGrid; }
 
-// the instance for the model's attention family (a GQA model has no latent rank)
+// the instance for the model's attention family
 template <int MM, bool MF>
 hipError_t launch_family(const Params& p, dim3 grid, dim3 block, hipStream_t stream) {
-  if (p.kvl == 0)
-    hipLaunchKernelGGL((mk_decode_kernel<MM, MF, true>), grid, block, 0, stream, p);
+  if (p.family == MK_ATTN_GQA)
+    hipLaunchKernelGGL((mk_decode_kernel<MM, MF, MK_ATTN_GQA>), grid, block, 0, stream, p);
+  else if (p.family == MK_ATTN_MLA)
+    hipLaunchKernelGGL((mk_decode_kernel<MM, MF, MK_ATTN_MLA>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((mk_decode_kernel<MM, MF, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((mk_decode_kernel<MM, MF, MK_ATTN_HYBRID>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -2790,15 +2794,17 @@ hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int n
 
 hipError_t occupancy(int* blocks_per_cu) {
 #ifdef MK_ONLY_MM1
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_decode_kernel<1, false, false>, kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_decode_kernel<1, false, MK_ATTN_HYBRID>, kThreads, 0);
 #else
-  int n[4] = {0, 0, 0, 0};
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[0], mk_decode_kernel<16, false, false>, kThreads, 0);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], mk_decode_kernel<16, true, false>, kThreads, 0);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[2], mk_decode_kernel<16, false, true>, kThreads, 0);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[3], mk_decode_kernel<16, true, true>, kThreads, 0);
+  int n[6] = {0, 0, 0, 0, 0, 0};
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[0], mk_decode_kernel<16, false, MK_ATTN_GQA>, kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], mk_decode_kernel<16, true, MK_ATTN_GQA>, kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[2], mk_decode_kernel<16, false, MK_ATTN_MLA>, kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[3], mk_decode_kernel<16, true, MK_ATTN_MLA>, kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[4], mk_decode_kernel<16, false, MK_ATTN_HYBRID>, kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[5], mk_decode_kernel<16, true, MK_ATTN_HYBRID>, kThreads, 0);
   int m = n[0];
-  for (int k = 1; k < 4; ++k) m = n[k] < m ? n[k] : m;
+  for (int k = 1; k < 6; ++k) m = n[k] < m ? n[k] : m;
   *blocks_per_cu = m;
   return e;
 #endif
