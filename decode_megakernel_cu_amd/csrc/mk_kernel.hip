@@ -21,10 +21,11 @@
 // microsecond, so activations are moved with 16-byte agent-scope buffer loads issued in batches
 // (up to eight per lane in flight before the first is consumed), never one load per loop trip.
 //
-// Prefetch. The weights of a phase do not depend on activations, so every wave except the
-// polling one issues the loads of its first rows of the next phase before it arrives at the
-// barrier ("layer n+1 loads while layer n computes", the news digests' account of the design);
-// the barrier wait and the input staging then overlap the HBM latency.
+// Prefetch. The weights of a phase do not depend on activations, so as soon as the workgroup has
+// arrived at the barrier before a GEMV phase, every wave (the polling one included) issues the
+// loads of its first rows of that phase, and only then waits ("layer n+1 loads while layer n
+// computes", the news digests' account of the design); the barrier wait and the input staging
+// then overlap the HBM latency.
 //
 // Nothing uses float atomics: every output element is owned by exactly one lane, so results are
 // bitwise reproducible from run to run.
