@@ -189,6 +189,17 @@ def test_mid_batch4():
     parity(w.model, synth.Spec(seed=1), w.batch, w.new_tokens, w.kv_len)
 
 
+MID_SMALL = replace(synth.MID, name="mid-2layer", n_layers=2)
+
+
+# 4 query heads per KV head: T = 4 fills one 16-row attention tile exactly, T = 5 spills 4 rows into
+# a second; peaked attention so that score errors reach the logits
+@pytest.mark.parametrize("B,T,kv_len", [(2, 4, 300), (2, 5, 300)])
+def test_mid_attention_row_tiles(B, T, kv_len):
+    spec = synth.Spec(seed=8, sigma_by_kind={"wq": 0.1, "wk": 0.1})
+    parity(MID_SMALL, spec, B, T, kv_len)
+
+
 K3_SMALL = replace(synth.K3, name="k3-2layer", n_layers=2, expert_pool_layers=0)
 HYB_SMALL = replace(synth.K3_HYBRID, name="hybrid-4layer", n_layers=4, expert_pool_layers=0)
 
