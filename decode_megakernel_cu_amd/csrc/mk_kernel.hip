@@ -1869,6 +1869,29 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
         *reinterpret_cast<uint2*>(Cs + r * cst + 4 * c) = w;
       }
     };
+    // The rows of the next sub-tile are in flight in registers while the current one is scored: a
+    // direct copy into LDS would make every LDS read of the scoring wait for it (LDS reads after a
+    // copy into LDS wait for the copy). lat <= 576: at most 72 units of 16 bytes per row.
+    constexpr int kMU = (kSub * 72 + kThreads - 1) / kThreads;
+    const int lu = lat >> 3;
+    uint4 cr[kMU];
+    auto issue_r = [&](int c0, int n) __attribute__((always_inline)) {
+      const int nold = max(0, min(kv_len - c0, n));
+#pragma unroll
+      for (int u = 0; u < kMU; ++u) {
+        const int i = u * kThreads + tid, r = i / lu, c = i - r * lu;
+        const bool ok = r < nold;  // (other lanes read row 0)
+        cr[u] = ldw(Lb + (size_t)(ok ? c0 + r : 0) * lat + 8 * (ok ? c : 0));
+      }
+    };
+    auto store_r = [&](int c0, int n) __attribute__((always_inline)) {
+      const int nold = max(0, min(kv_len - c0, n));
+#pragma unroll
+      for (int u = 0; u < kMU; ++u) {
+        const int i = u * kThreads + tid, r = i / lu, c = i - r * lu;
+        if (r < nold) *reinterpret_cast<uint4*>(Cs + r * cst + 8 * c) = cr[u];
+      }
+    };
     const bool whole = p1 - p0 <= kSub;  // the range is staged once, by the first token that reads it
     bool staged = false;
     for (int t = 0; t < T; ++t) {
@@ -1929,13 +1952,12 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
         for (int c0 = p0; c0 < pe; c0 += kSub) {
           const int n = min(kSub, pe - c0);
           if (c0 != p0) {
-            __syncthreads();
-            issue_c(c0, n);
-            wait_vm();
-            __syncthreads();
+            __syncthreads();  // the previous sub-tile is consumed
+            store_r(c0, n);
             fill_new(c0, n);
           }
           __syncthreads();
+          if (c0 + kSub < pe) issue_r(c0 + kSub, min(kSub, pe - c0 - kSub));
           const bool mark = trace && tid == 0 && task == (int)blockIdx.x && t == 0 && c0 == p0;
           // scores on the matrix cores: wave -> position tile (wave & 1) x K group (wave >> 1)
           {
