@@ -1871,8 +1871,9 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
     };
     // The rows of the next sub-tile are in flight in registers while the current one is scored: a
     // direct copy into LDS would make every LDS read of the scoring wait for it (LDS reads after a
-    // copy into LDS wait for the copy). lat <= 576: at most 72 units of 16 bytes per row.
-    constexpr int kMU = (kSub * 72 + kThreads - 1) / kThreads;
+    // copy into LDS wait for the copy). The host admits kv_lora 512 and rope_dim <= 2 kMaxRopePairs,
+    // so a row has at most (512 + 2 kMaxRopePairs) / 8 units of 16 bytes.
+    constexpr int kMU = (kSub * ((512 + 2 * kMaxRopePairs) / 8) + kThreads - 1) / kThreads;
     const int lu = lat >> 3;
     uint4 cr[kMU];
     auto issue_r = [&](int c0, int n) __attribute__((always_inline)) {

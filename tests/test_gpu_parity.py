@@ -211,6 +211,14 @@ def test_k3_two_layers(B, T, kv_len):
     parity(K3_SMALL, synth.Spec(seed=2), B, T, kv_len)
 
 
+def test_k3_two_layers_widest_rope():
+    # rope_dim 128, the widest the host admits: 640-wide latent rows fill the register prefetch of
+    # the next 32-position sub-tile exactly (2560 units of 16 bytes); batch 4 over 4097 positions
+    # gives splits of 96 positions (three sub-tiles), so later sub-tiles go through it
+    cfg = replace(K3_SMALL, name="k3-2layer-rope128", rope_dim=128)
+    parity(cfg, synth.Spec(seed=9), 4, 1, 4096)
+
+
 def test_k3_two_layers_batch8_vector_units():
     parity(K3_SMALL, synth.Spec(seed=2), 8, 1, 33, mfma_min_rows=VECTOR_ONLY)
 
