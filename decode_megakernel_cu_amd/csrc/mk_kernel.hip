@@ -1770,7 +1770,15 @@ __device__ __forceinline__ void mla_prefetch_rows(const Params& p, const LayerDe
   const int nold = imax(0, imin(kv_len - p0, n));
   const uint16_t* Lb = rflp(p.kv) + ((size_t)rfl(ly->ord) * Bmax + b) * cap * lat;
   const Rsrc lr = make_rsrc(Lb, (uint32_t)cap * lat * 2);
-  dma_rows<2>(lr, smem, nold, lat >> 3, cst / 2, [&](int r, int c) { return (uint32_t)((p0 + r) * lat) * 2 + c * 16; });
+  // every wave but the polling one: its polls would complete only after its copies
+  const int w = wave_id(), lane = lane_id(), U = lat >> 3, bpr = (U + 63) >> 6, nb = nold * bpr;
+  if (w == kPollWave) return;
+  for (int bk = w; bk < nb; bk += kWaves - 1) {
+    const int r = bk / bpr, c0 = (bk - r * bpr) << 6, c = c0 + lane;
+    if (c < U)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (LdsPtr)(smem + r * (cst / 2) + 4 * c0), 16,
+                                               (uint32_t)((p0 + r) * lat) * 2 + c * 16, 0, 0, 2);
+  }
 }
 
 __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
