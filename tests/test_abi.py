@@ -110,6 +110,16 @@ def test_bad_dense_configs(mk, kw):
     assert e.value.code == mk.MK_E_INVAL
 
 
+@pytest.mark.parametrize("head_dim", [8, 48, 160])
+def test_gqa_head_dim_limits(mk, head_dim):
+    # GQA attention runs on the matrix cores in 32-column steps, with at most 128 columns per head
+    with pytest.raises(mk.MkError) as e:
+        sizes(mk, replace(synth.TINY, head_dim=head_dim))
+    assert e.value.code == mk.MK_E_UNSUPPORTED
+    for ok in (32, 64, 96, 128):
+        sizes(mk, replace(synth.TINY, head_dim=ok))
+
+
 def test_kv_capacity_limit(mk):
     # the split-KV merge keeps one task's statistics and values for every split (at least 16
     # positions each) in LDS: 921 splits fit, 922 do not
