@@ -173,6 +173,14 @@ def test_tiny_ragged_rows(B, T, kv_len):
     parity(TINY_RAGGED, synth.Spec(seed=7), B, T, kv_len)
 
 
+# head dims the host admits besides 64 and 128: one and three 32-column steps per score multiply,
+# two and six 16-column value tiles
+@pytest.mark.parametrize("head_dim", [32, 96])
+def test_tiny_head_dims(head_dim):
+    cfg = replace(synth.TINY, name=f"tiny-hd{head_dim}", head_dim=head_dim)
+    parity(cfg, synth.Spec(seed=10), 2, 3, 70)
+
+
 def test_tiny_peaked_attention():
     # larger query/key weights make attention sharply peaked, so attention errors reach the logits
     spec = synth.Spec(seed=6, sigma_by_kind={"wq": 0.25, "wk": 0.25, "wv": 0.1, "wo": 0.1})
