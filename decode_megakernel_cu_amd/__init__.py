@@ -24,14 +24,14 @@ KIND_ID = {k: i for i, k in enumerate(KINDS)}
 
 TRACE_STAMPS = 16  # MK_TRACE_STAMPS
 
-EXPORTS = ["mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_greedy",
+EXPORTS = ["mk_config_preset", "mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_greedy",
            "mk_decode_step_sample", "mk_poll", "mk_set_trace", "mk_read_trace", "mk_set_matrix_cores", "mk_last_error",
            "mk_destroy"]
 
 
 class MkConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "n_layers", "hidden", "vocab", "attn_kind", "n_heads", "n_kv_heads", "head_dim", "q_lora", "kv_lora",
+        "preset", "n_layers", "hidden", "vocab", "attn_kind", "n_heads", "n_kv_heads", "head_dim", "q_lora", "kv_lora",
         "rope_dim", "nope_dim", "v_dim", "kda_dk", "kda_dv", "hybrid_period", "n_experts", "top_k", "ffn",
         "shared_ffn", "norm_topk", "expert_pool_layers", "max_batch", "max_new_tokens", "kv_capacity")] + [
         ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
@@ -58,6 +58,7 @@ def _load():
         raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() (no fallback exists)")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64
+    L.mk_config_preset.argtypes = [ctypes.c_int, ctypes.POINTER(MkConfig)]
     L.mk_query_sizes.argtypes = [ctypes.POINTER(MkConfig), ctypes.POINTER(MkSizes)]
     L.mk_create.argtypes = [ctypes.POINTER(MkConfig), i32, vp, u64, vp, u64, ctypes.POINTER(vp)]
     L.mk_load_weights.argtypes = [vp, ctypes.POINTER(MkTensorDesc), i32, vp]
@@ -72,7 +73,7 @@ def _load():
     L.mk_set_trace.argtypes = [vp, i32]
     L.mk_set_matrix_cores.argtypes = [vp, i32]
     L.mk_read_trace.argtypes = [vp, vp, u64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
-    for f in ("mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_greedy",
+    for f in ("mk_config_preset", "mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_greedy",
               "mk_decode_step_sample", "mk_poll", "mk_set_trace", "mk_read_trace", "mk_set_matrix_cores"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -92,10 +93,18 @@ def _check(rc: int) -> int:
 
 
 def config(model) -> MkConfig:
-    """mk_config from any object carrying the fields of the C struct (e.g. synth.ModelConfig)."""
+    """mk_config from any object carrying the fields of the C struct (e.g. synth.ModelConfig; a
+    missing `preset` reads as 0, a custom model)."""
     c = MkConfig()
     for name, _ in MkConfig._fields_:
-        setattr(c, name, getattr(model, name))
+        setattr(c, name, getattr(model, name, 0) if name == "preset" else getattr(model, name))
+    return c
+
+
+def mk_config_preset(preset_id: int) -> MkConfig:
+    """The library's description of a preset workload model (ids 1..6, see include/mk.h)."""
+    c = MkConfig()
+    _check(lib.mk_config_preset(int(preset_id), ctypes.byref(c)))
     return c
 
 

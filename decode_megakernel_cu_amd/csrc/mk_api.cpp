@@ -70,6 +70,7 @@ struct Layout {
 
 int check_config(const mk_config* c) {
   if (!c) return fail(MK_E_INVAL, "config is NULL");
+  if (c->preset < 0 || c->preset > 6) return fail(MK_E_INVAL, "preset %d is not 0 (custom) or a preset id 1..6", c->preset);
   if (c->n_layers < 1 || c->hidden < 8 || c->vocab < 1) return fail(MK_E_INVAL, "n_layers, hidden and vocab must be positive");
   if (c->hidden % 8) return fail(MK_E_UNSUPPORTED, "hidden must be a multiple of 8");
   if (c->attn_kind < 0 || c->attn_kind > 2) return fail(MK_E_INVAL, "attn_kind %d unknown", c->attn_kind);
@@ -346,6 +347,53 @@ struct mk_ctx {
 extern "C" {
 
 const char* mk_last_error(void) { return g_err.c_str(); }
+
+int mk_config_preset(int id, mk_config* out) {
+  if (!out) return fail(MK_E_INVAL, "config output is NULL");
+  mk_config c;
+  std::memset(&c, 0, sizeof c);
+  c.max_batch = 8;
+  c.max_new_tokens = 8;
+  c.rms_eps = 1e-6f;
+  c.rope_theta = 1e4f;
+  switch (id) {
+    case 1:  // tiny MoE decoder
+      c.n_layers = 2; c.hidden = 256; c.vocab = 1024; c.attn_kind = MK_ATTN_GQA;
+      c.n_heads = 4; c.n_kv_heads = 4; c.head_dim = 64;
+      c.n_experts = 8; c.top_k = 2; c.ffn = 512; c.shared_ffn = 0;
+      c.kv_capacity = 136;
+      break;
+    case 2:  // mid-size MoE decoder
+      c.n_layers = 8; c.hidden = 2048; c.vocab = 32000; c.attn_kind = MK_ATTN_GQA;
+      c.n_heads = 16; c.n_kv_heads = 4; c.head_dim = 128;
+      c.n_experts = 64; c.top_k = 8; c.ffn = 768; c.shared_ffn = 768;
+      c.max_batch = 4; c.kv_capacity = 2056;
+      break;
+    case 3:  // K3-scale one-GPU share (and its verify step, preset 4; hybrid variant, preset 5)
+    case 4:
+    case 5:
+      c.n_layers = 92; c.hidden = 7168; c.vocab = 40960; c.attn_kind = id == 5 ? MK_ATTN_HYBRID : MK_ATTN_MLA;
+      c.n_heads = 16; c.q_lora = 1536; c.kv_lora = 512; c.rope_dim = 64; c.nope_dim = 128; c.v_dim = 128;
+      if (id == 5) {
+        c.kda_dk = 128; c.kda_dv = 128; c.hybrid_period = 4;
+      }
+      c.n_experts = 48; c.top_k = 1; c.ffn = 2048; c.shared_ffn = 512; c.expert_pool_layers = 46;
+      c.kv_capacity = 4104;
+      break;
+    case 6:  // dense second model
+      c.n_layers = 64; c.hidden = 5120; c.vocab = 151936; c.attn_kind = MK_ATTN_GQA;
+      c.n_heads = 40; c.n_kv_heads = 8; c.head_dim = 128;
+      c.n_experts = 0; c.top_k = 0; c.ffn = 0; c.shared_ffn = 21504;
+      c.kv_capacity = 4104; c.rope_theta = 1e6f;
+      break;
+    default:
+      return fail(MK_E_INVAL, "unknown preset %d (1..6)", id);
+  }
+  c.preset = id;
+  *out = c;
+  g_err.clear();
+  return MK_OK;
+}
 
 int mk_query_sizes(const mk_config* cfg, mk_sizes* out) {
   int rc = check_config(cfg);

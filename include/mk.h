@@ -6,10 +6,18 @@
  * compressed cache, or the gated delta rule of the hybrid model), router top-k,
  * SwiGLU routed and shared experts, residuals, and the final norm plus LM head --
  * as a single persistent kernel launch. This is the method of
- * "700 TPS on Kimi K3: A Case for TPU Megakernels" (tpu-megakernels README:
- * the decode step fused into one kernel, FAQ "why build a custom megakernel";
- * weights of layer n+1 fetched while layer n computes, in the news digests'
- * sections on where the speedup comes from), built for one MI355X.
+ * "700 TPS on Kimi K3: A Case for TPU Megakernels" (tpu-megakernels README, FAQ
+ * on why to build a custom megakernel: the whole decode step -- attention, MoE,
+ * normalisation, residuals -- fused into one kernel; the weights of layer n+1
+ * fetched while layer n computes: news digest "TPU 巨核:同样是 16 块芯片,Kimi K3
+ * 快 57%", section 差距从哪里来, and the video description "700 tok/s on a 2.8
+ * Trillion Model: The 92-Layer TPU Megakernel", timestamp "The Choreography: Layer
+ * n+1 Loads While Layer n Computes"), built for one MI355X.
+ *
+ * The pages describe no kernel-level API (only the servers and their launch scripts:
+ * tpu-megakernels README, section "OpenAI-compatible servers"). The calls below are
+ * this library's boundary: the model described once, its weights loaded once into
+ * device memory the caller owns, then one call per decode step.
  *
  * Ownership: the caller owns every device buffer (weight arena, workspace, KV
  * cache, recurrent state, tokens, logits). The library allocates no device
@@ -47,7 +55,10 @@ typedef enum {
 
 typedef enum { MK_ATTN_GQA = 0, MK_ATTN_MLA = 1, MK_ATTN_HYBRID = 2 } mk_attn_kind;
 
-/* Model and capacity description. Matrices are bf16, stored [out][in] (row = output feature).
+/* Model and capacity description (a deep MoE decoder whose attention is MLA, or MLA combined with
+ * delta-rule linear attention, or GQA: German news article, section "Auf dem Papier liegt der
+ * GB200 vorn", on Kimi K3's 92 MoE layers and its mix of delta-rule and latent attention).
+ * Matrices are bf16, stored [out][in] (row = output feature).
  * attn_kind GQA: n_heads query heads and n_kv_heads key/value heads of head_dim (32, 64, 96 or
  *   128: the attention runs on the matrix cores), RoPE over the whole head. MLA: n_heads heads, q_lora / kv_lora latent ranks, rope_dim + nope_dim query-key
  *   width per head, v_dim value width. HYBRID: layer l is MLA when l % hybrid_period ==
@@ -64,6 +75,7 @@ typedef enum { MK_ATTN_GQA = 0, MK_ATTN_MLA = 1, MK_ATTN_HYBRID = 2 } mk_attn_ki
  * partial softmax results holds one task's statistics and values for every chunk in LDS;
  * larger capacities return MK_E_UNSUPPORTED. */
 typedef struct {
+  int32_t preset;  /* informational: the mk_config_preset id this description came from, 0 for a custom model */
   int32_t n_layers, hidden, vocab, attn_kind;
   int32_t n_heads, n_kv_heads, head_dim;
   int32_t q_lora, kv_lora, rope_dim, nope_dim, v_dim;
@@ -115,7 +127,30 @@ typedef struct {
 
 typedef struct mk_ctx mk_ctx;
 
-/* Sizes of the caller-owned buffers for cfg. Returns MK_E_INVAL / MK_E_UNSUPPORTED for bad configs.
+/* Preset model descriptions of the measured and tested workloads. The pages give the deployed model
+ * only in outline (92 MoE layers; 2.8 T parameters, 104 B active; tensor-parallel 4 x expert-parallel
+ * 8 over 16 chips: video description "700 tok/s on a 2.8 Trillion Model", key takeaways; German news
+ * article, section "Auf dem Papier liegt der GB200 vorn"); the dimensions below are synthetic choices.
+ *   1  tiny MoE decoder: 2 layers, hidden 256, 4 GQA heads of 64, 8 experts top-2 (ffn 512), vocab 1024
+ *   2  mid-size MoE decoder: 8 layers, hidden 2048, GQA 16 / 4 heads of 128, 64 experts top-8 (ffn 768)
+ *      plus a shared expert of 768, vocab 32000
+ *   3  K3-scale one-GPU share: 92 layers, hidden 7168, MLA 16 heads (q_lora 1536, kv_lora 512, rope 64,
+ *      nope 128, v 128), 48 local experts top-1 (ffn 2048) in a 46-layer pool, shared expert 512,
+ *      vocabulary slice 40960
+ *   4  the same model as 3: the speculative-verify workload differs only in the step (7 new tokens)
+ *   5  the hybrid variant of 3: delta-rule layers (16 heads, dk = dv = 128) at positions 1-3 of every
+ *      group of 4 layers, MLA at the fourth
+ *   6  the dense second model: 64 layers, hidden 5120, GQA 40 / 8 heads of 128, SwiGLU 21504, vocab
+ *      151936, RoPE theta 1e6 (the dense BF16 decoder served beside the MoE model: tpu-megakernels
+ *      README, FAQ on DSpark and DFlash2)
+ * Every preset has max_new_tokens 8, rms_eps 1e-6, max_batch 8 (preset 2: 4), and a cache capacity
+ * of the workload's kv_len plus 8 (presets 1 and 2: 136 and 2056; 3-6: 4104). out->preset is set to id.
+ * MK_E_INVAL for an unknown id or a NULL out. */
+int mk_config_preset(int id, mk_config* out);
+
+/* Sizes of the caller-owned buffers for cfg (the weights stay resident in device memory and are
+ * streamed again every step: news digest "TPU 巨核:同样是 16 块芯片,Kimi K3 快 57%", section
+ * 差距从哪里来, on every token reading the weights from high-bandwidth memory). Returns MK_E_INVAL / MK_E_UNSUPPORTED for bad configs.
  * KV cache layout (bf16):
  *   GQA:    K block then V block, each [n_layers][max_batch][n_kv_heads][kv_capacity][head_dim]
  *   MLA:    [n_mla_layers][max_batch][kv_capacity][kv_lora + rope_dim]   (normed latent, then
@@ -124,15 +159,24 @@ typedef struct mk_ctx mk_ctx;
 int mk_query_sizes(const mk_config* cfg, mk_sizes* out);
 
 /* Create a context on HIP device `device` (or MK_DEVICE_NONE) over caller buffers of at least the
- * queried sizes. The workspace is cleared here (once); the arena is filled by mk_load_weights. */
+ * queried sizes. The workspace is cleared here (once); the arena is filled by mk_load_weights.
+ * (The pages' program likewise runs over buffers laid out ahead of time, with static shapes:
+ * video description "700 tok/s on a 2.8 Trillion Model", timestamp "What It Costs: Static Shapes,
+ * Cold Compiles, and Tradeoffs".) arena and workspace must be 256-byte aligned device pointers;
+ * MK_E_NOMEM when a buffer is smaller than queried, MK_E_HIP when a device call fails. */
 int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_bytes, void* d_workspace,
               uint64_t workspace_bytes, mk_ctx** out);
 
 /* Copy (and, where the kernel wants another layout, repack) n tensors into the arena, in stream
- * order on hip_stream. Every tensor of the model must have been loaded once before the first step. */
+ * order on hip_stream. Every tensor of the model must have been loaded once before the first step.
+ * (The pages' demos likewise prepare their kernel layouts from the checkpoints before serving:
+ * tpu-megakernels README, section "Setup".) The source of each descriptor must stay valid until the
+ * stream reaches the copy. MK_E_INVAL for an unknown tensor, a wrong byte count or a NULL source. */
 int mk_load_weights(mk_ctx* ctx, const mk_tensor_desc* descs, int n, void* hip_stream);
 
-/* One decode step, a single kernel launch, asynchronous on hip_stream.
+/* One decode step, a single kernel launch, asynchronous on hip_stream (the whole decode step as
+ * one program: tpu-megakernels README, FAQ on why to build a custom megakernel; German news
+ * article, section "Der Trick: 92 Schichten zu einem Programm verschmelzen").
  * d_tokens [batch][n_new_tokens] int32 (device); new tokens take positions kv_len .. kv_len+T-1 of
  * each sequence, attend causally to positions 0 .. their own, and their cache entries are written
  * (rounded to bf16) at those positions; d_kv holds entries 0 .. kv_len-1 on entry. kv_len is
@@ -178,10 +222,15 @@ int mk_decode_step_sample(mk_ctx* ctx, int batch, int n_new_tokens, int kv_len, 
                           const float* d_uniform, int32_t* d_sampled, void* hip_stream);
 
 /* After the caller synchronised the step's stream: MK_OK, or MK_E_DEVICE if the kernel reported a
- * watchdog timeout or an out-of-range token (the context is then poisoned). */
+ * watchdog timeout or an out-of-range token (the context is then poisoned, and later steps return
+ * MK_E_STATE). The pages report no device errors; a persistent kernel whose workgroups wait on
+ * each other must never hang the GPU, so every wait is bounded by the device clock and an
+ * expired wait or an invalid token ends the step with this status instead. */
 int mk_poll(mk_ctx* ctx);
 
-/* Profiling: while enabled, every step records, for each grid barrier and workgroup,
+/* Profiling (the per-phase view of the step behind the pages' claim that fused phases leave no
+ * idle gaps between kernels: news digest "TPU 巨核:同样是 16 块芯片,Kimi K3 快 57%", section
+ * 差距从哪里来): while enabled, every step records, for each grid barrier and workgroup,
  * MK_TRACE_STAMPS stamps of the device wall clock (wall_clock64, 100 MHz on MI355X): 0 arrival at
  * the barrier (flag published), 1 departure, then marks of the phase that follows it (0 where a
  * phase has none):
@@ -207,15 +256,19 @@ int mk_set_trace(mk_ctx* ctx, int enable);
 #define MK_MFMA_MIN_ROWS 3
 int mk_set_matrix_cores(mk_ctx* ctx, int min_rows);
 
-/* Copy the last traced step: out[((barrier * n_blocks) + block) * MK_TRACE_STAMPS + stamp] for
+/* Copy the last traced step (recorded while mk_set_trace is on, for the per-phase view above):
+ * out[((barrier * n_blocks) + block) * MK_TRACE_STAMPS + stamp] for
  * barrier < *n_barriers + 1 (the last record is the end of the step). Call with out == NULL to get
  * the counts; capacity is the number of uint64_t slots in out. Synchronous (after the step's stream
  * has finished). */
 int mk_read_trace(mk_ctx* ctx, uint64_t* out, uint64_t capacity, int* n_barriers, int* n_blocks);
 
-/* Message of the last failing call on this thread ("" if none). */
+/* Message of the last failing call on this thread ("" if none). Part of this library's error
+ * reporting; the pages define none. */
 const char* mk_last_error(void);
 
+/* Release the host context (NULL is ignored). Device buffers stay the caller's; the stream must
+ * have finished every step of the context first. */
 void mk_destroy(mk_ctx* ctx);
 
 #ifdef __cplusplus

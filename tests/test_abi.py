@@ -43,8 +43,9 @@ def test_library_is_gfx950():
 
 
 def test_struct_sizes_match_header(mk):
-    # mk_config: 24 int32 + 2 float; mk_tensor_desc: 4 int32 + pointer + uint64
-    assert ctypes.sizeof(mk.MkConfig) == 26 * 4
+    # mk_config: 25 int32 (preset first) + 2 float; mk_tensor_desc: 4 int32 + pointer + uint64
+    assert ctypes.sizeof(mk.MkConfig) == 27 * 4
+    assert mk.MkConfig._fields_[0][0] == "preset"
     assert ctypes.sizeof(mk.MkTensorDesc) == 32
     assert ctypes.sizeof(mk.MkSizes) == 32
 
@@ -287,3 +288,45 @@ def test_sample_step_argument_errors(mk, host_ctx):
     with pytest.raises(mk.MkError) as e:  # valid arguments: the weights are not loaded yet
         step(top_p=1.0)
     assert e.value.code == mk.MK_E_STATE
+
+
+PRESETS = {1: "c1", 2: "c2", 3: "c3", 4: "c4", 5: "c5", 6: "dense"}
+
+
+@pytest.mark.parametrize("pid", sorted(PRESETS))
+def test_presets_equal_the_workload_models(mk, pid):
+    """mk_config_preset(id) describes the same model as the workload the tests and the benchmark
+    build from synth (every field), and the library accepts it."""
+    c = mk.mk_config_preset(pid)
+    model = synth.WORKLOADS[PRESETS[pid]].model
+    assert c.preset == pid
+    for name, _ in mk.MkConfig._fields_:
+        if name == "preset":
+            continue
+        got, want = getattr(c, name), getattr(model, name)
+        if isinstance(want, float):
+            assert got == pytest.approx(want, rel=1e-7), name
+        else:
+            assert got == want, name
+    w = synth.WORKLOADS[PRESETS[pid]]
+    assert c.kv_capacity == w.kv_len + 8
+    s = mk.mk_query_sizes(c)
+    assert s.arena_bytes == sizes(mk, model).arena_bytes
+
+
+@pytest.mark.parametrize("pid", [0, 7, -1])
+def test_unknown_preset(mk, pid):
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_config_preset(pid)
+    assert e.value.code == mk.MK_E_INVAL
+    assert "preset" in mk.mk_last_error()
+
+
+def test_preset_field_is_validated(mk):
+    c = mk.config(synth.TINY)
+    assert c.preset == 0
+    mk.mk_query_sizes(c)
+    c.preset = 9
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_query_sizes(c)
+    assert e.value.code == mk.MK_E_INVAL
