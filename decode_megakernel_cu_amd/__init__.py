@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmk.so")
+# MK_LIBRARY: another build of the same library (e.g. one compiled with different options);
+# default: the in-tree build
+LIB_PATH = os.environ.get("MK_LIBRARY") or os.path.join(_HERE, "libmk.so")
 
 MK_OK, MK_E_INVAL, MK_E_STATE, MK_E_KV_OVERFLOW, MK_E_NOMEM, MK_E_HIP, MK_E_DEVICE, MK_E_UNSUPPORTED = (
     0, -1, -2, -3, -4, -5, -6, -7)

@@ -508,3 +508,113 @@ def test_speculative_loop_tiny_t8():
 def test_speculative_loop_mla_t7():
     # the verify workload's shape: one anchor + 6 drafts, latent cache
     speculative_loop(MLA_SMALL, synth.Spec(seed=15, sigma=0.05), 7, 64, [6, 2, 0, 5, 3])
+
+
+# --------------------------------------------------------------------------------------------
+# the vector-unit instances built for 2 and 4 token rows (batch 2 runs on them by default)
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,B,kv_len,rows", [
+    (K3_SMALL, 2, 4096, 3), (synth.TINY, 2, 50, 3), (DENSE_SMALL, 2, 4096, 3),
+    (K3_SMALL, 4, 4096, VECTOR_ONLY), (synth.TINY, 4, 77, VECTOR_ONLY)], ids=lambda v: getattr(v, "name", v))
+def test_vector_instances_two_and_four_rows(cfg, B, kv_len, rows):
+    parity(cfg, synth.Spec(seed=24), B, 1, kv_len, mfma_min_rows=rows)
+
+
+# --------------------------------------------------------------------------------------------
+# seeds 1 and 2 on every workload's shape (2- and 4-layer versions of the large models)
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [1, 2])
+@pytest.mark.parametrize("wl", ["c2", "c3", "c4", "c5"])
+def test_workload_seeds(wl, seed):
+    w = synth.WORKLOADS[wl]
+    cfg = {"c2": w.model, "c3": K3_SMALL, "c4": K3_SMALL, "c5": HYB_SMALL}[wl]
+    parity(cfg, synth.Spec(seed=seed), w.batch, w.new_tokens, w.kv_len)
+
+
+def test_k3_full_batch2():
+    w = synth.WORKLOADS["c3b2"]
+    parity(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
+
+
+def test_k3_full_batch4():
+    w = synth.WORKLOADS["c3b4"]
+    parity(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
+
+
+# --------------------------------------------------------------------------------------------
+# run-to-run reproducibility: every output element is owned by one lane and every sum runs in a
+# fixed order, so the same step on the same inputs gives the same bits
+# --------------------------------------------------------------------------------------------
+def bitwise_repeat(cfg, spec, B, T, kv_len, mfma_min_rows=3):
+    print(f"[case] repeat {cfg.name} B={B} T={T} kv_len={kv_len} seed={spec.seed}", flush=True)
+    dm = device_model(cfg, spec)
+    dm.set_matrix_cores(mfma_min_rows)
+    dm.fill_caches(B, kv_len)
+    kv0 = dm.kv.clone()
+    st0 = dm.state.clone() if dm.state is not None else None
+    toks = synth.tokens(spec.seed, 6, cfg.vocab, B, T)
+    l1, r1 = dm.step(toks, kv_len)
+    torch.cuda.synchronize()
+    dm.poll()
+    kv1 = dm.kv.clone()
+    st1 = dm.state.clone() if st0 is not None else None
+    # snapshot restore: the cache rows past kv_len and the delta-rule state go back to the snapshot
+    dm.kv.copy_(kv0)
+    if st0 is not None:
+        dm.state.copy_(st0)
+    l2, r2 = dm.step(toks, kv_len)
+    torch.cuda.synchronize()
+    dm.poll()
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), "logits differ between two runs of one step"
+    assert torch.equal(r1, r2), "routes differ between two runs of one step"
+    assert torch.equal(dm.kv, kv1), "appended cache rows differ between two runs"
+    if st0 is not None:
+        assert torch.equal(dm.state.view(torch.int32), st1.view(torch.int32)), "delta-rule state differs"
+    print(f"[ok] repeat {cfg.name} B={B} T={T}: bitwise equal", flush=True)
+
+
+@pytest.mark.parametrize("cfg,B,T,kv_len,rows", [
+    (K3_SMALL, 8, 1, 4096, 3), (K3_SMALL, 1, 1, 4096, 3), (HYB_SMALL, 8, 1, 517, 3), (MID_SMALL, 4, 1, 2048, 3),
+    (MID_SMALL, 2, 1, 2048, 3), (synth.TINY, 8, 2, 100, VECTOR_ONLY)], ids=lambda v: getattr(v, "name", v))
+def test_bitwise_run_to_run(cfg, B, T, kv_len, rows):
+    bitwise_repeat(cfg, synth.Spec(seed=25), B, T, kv_len, rows)
+
+
+def test_bitwise_run_to_run_full_verify():
+    w = synth.WORKLOADS["c4"]
+    bitwise_repeat(w.model, synth.Spec(seed=0), w.batch, w.new_tokens, w.kv_len)
+
+
+# --------------------------------------------------------------------------------------------
+# device-side errors: a token outside the vocabulary is reported by mk_poll, which poisons the
+# context; the step itself completes (the token is read as token 0), so nothing faults or hangs
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("bad", ["vocab", "negative"])
+def test_out_of_vocabulary_token_poisons_context(bad):
+    import decode_megakernel_cu_amd as mk
+    from synth.device_inputs import DeviceModel
+
+    cfg, spec = synth.TINY, synth.Spec(seed=26)
+    for k in list(_models):  # a context of its own: this one ends poisoned
+        _models.pop(k).close()
+    print(f"[case] bad token ({bad}) {cfg.name}", flush=True)
+    dm = DeviceModel(cfg, spec, device=0)
+    try:
+        dm.fill_caches(2, 10)
+        toks = np.array([[5], [cfg.vocab if bad == "vocab" else -3]], dtype=np.int32)
+        dm.step(toks, 10)
+        torch.cuda.synchronize()
+        with pytest.raises(mk.MkError) as e:
+            dm.poll()
+        assert e.value.code == mk.MK_E_DEVICE
+        assert "token 1 of the step" in str(e.value)
+        with pytest.raises(mk.MkError) as e:  # the context stays poisoned
+            dm.poll()
+        assert e.value.code == mk.MK_E_DEVICE
+        with pytest.raises(mk.MkError) as e:
+            dm.step(np.array([[5], [6]], dtype=np.int32), 10)
+        assert e.value.code == mk.MK_E_STATE
+        assert "poisoned" in mk.mk_last_error()
+    finally:
+        dm.close()
+    print(f"[ok] bad token ({bad}): MK_E_DEVICE, then MK_E_STATE", flush=True)
