@@ -26,8 +26,8 @@ KIND_ID = {k: i for i, k in enumerate(KINDS)}
 
 TRACE_STAMPS = 16  # MK_TRACE_STAMPS
 
-EXPORTS = ["mk_config_preset", "mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_greedy",
-           "mk_decode_step_sample", "mk_poll", "mk_set_trace", "mk_read_trace", "mk_set_matrix_cores", "mk_last_error",
+EXPORTS = ["mk_config_preset", "mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_static",
+           "mk_decode_step_greedy", "mk_decode_step_sample", "mk_poll", "mk_set_trace", "mk_read_trace", "mk_set_matrix_cores", "mk_last_error",
            "mk_destroy"]
 
 
@@ -65,6 +65,7 @@ def _load():
     L.mk_create.argtypes = [ctypes.POINTER(MkConfig), i32, vp, u64, vp, u64, ctypes.POINTER(vp)]
     L.mk_load_weights.argtypes = [vp, ctypes.POINTER(MkTensorDesc), i32, vp]
     L.mk_decode_step.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    L.mk_decode_step_static.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     L.mk_decode_step_greedy.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.mk_decode_step_sample.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp]
     L.mk_poll.argtypes = [vp]
@@ -75,7 +76,8 @@ def _load():
     L.mk_set_trace.argtypes = [vp, i32]
     L.mk_set_matrix_cores.argtypes = [vp, i32]
     L.mk_read_trace.argtypes = [vp, vp, u64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
-    for f in ("mk_config_preset", "mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_greedy",
+    for f in ("mk_config_preset", "mk_query_sizes", "mk_create", "mk_load_weights", "mk_decode_step",
+              "mk_decode_step_static", "mk_decode_step_greedy",
               "mk_decode_step_sample", "mk_poll", "mk_set_trace", "mk_read_trace", "mk_set_matrix_cores"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -131,6 +133,13 @@ def mk_decode_step(ctx, batch: int, n_new_tokens: int, kv_len: int, tokens: int,
                    logits: int, route: int = 0, stream: int = 0) -> None:
     _check(lib.mk_decode_step(ctx, batch, n_new_tokens, kv_len, tokens, kv, kda_state or None, logits,
                               route or None, stream))
+
+
+def mk_decode_step_static(ctx, batch: int, n_new_tokens: int, kv_len: int, tokens: int, kv: int, kda_state: int,
+                          logits: int, route: int = 0, stream: int = 0) -> None:
+    """mk_decode_step on the library's static per-GPU workspace (allocates nothing)."""
+    _check(lib.mk_decode_step_static(ctx, batch, n_new_tokens, kv_len, tokens, kv, kda_state or None, logits,
+                                     route or None, stream))
 
 
 def mk_decode_step_greedy(ctx, batch: int, n_new_tokens: int, kv_len: int, tokens: int, kv: int, kda_state: int,

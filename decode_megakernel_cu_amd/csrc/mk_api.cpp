@@ -22,6 +22,8 @@ hipError_t launch_decode(const Params& p, int nblocks, bool matrix_cores, hipStr
 hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd, int kvl, hipStream_t stream);
 hipError_t occupancy(int* blocks_per_cu);
 int max_grid();
+hipError_t static_scratch(int device, void** out);
+hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t stream);
 }  // namespace mk
 
 using namespace mk;
@@ -182,6 +184,8 @@ bool mfma_shapes(const mk_config& c) {
   return ok;
 }
 
+WsLayout ws_layout(const mk_config& c, uint64_t M, uint64_t nsplit, bool trace);
+
 Layout make_layout(const mk_config& c) {
   Layout Lt;
   const uint64_t H = c.hidden, V = c.vocab, E = c.n_experts, F = c.ffn, SF = c.shared_ffn;
@@ -271,8 +275,16 @@ Layout make_layout(const mk_config& c) {
     Lt.kv = (uint64_t)Lt.n_mla * Bm * cap * (c.kv_lora + c.rope_dim) * 2;
   Lt.state = (uint64_t)Lt.n_kda * Bm * c.n_heads * c.kda_dk * c.kda_dv * 4;
 
-  // workspace
-  const uint64_t M = (uint64_t)std::min(MK_MAX_M, c.max_batch * c.max_new_tokens);
+  // workspace: sized for the largest step of the model
+  Lt.nsplit_max = (c.kv_capacity + kChunk - 1) / kChunk;
+  Lt.ws = ws_layout(c, (uint64_t)std::min(MK_MAX_M, c.max_batch * c.max_new_tokens), Lt.nsplit_max, true);
+  return Lt;
+}
+
+// The workspace carve-up for steps of at most M token rows and nsplit split-KV partials per
+// (row, head); trace: room for the per-barrier wall-clock stamps.
+WsLayout ws_layout(const mk_config& c, uint64_t M, uint64_t nsplit, bool trace) {
+  const uint64_t H = c.hidden, E = c.n_experts, F = c.ffn, SF = c.shared_ffn;
   const uint64_t nh = c.n_heads;
   uint64_t w1 = 0, w2 = 0, w3 = 0, dmax = 0, w4 = 0, wo2 = 0;
   if (c.attn_kind == MK_ATTN_GQA) {
@@ -287,14 +299,13 @@ Layout make_layout(const mk_config& c) {
     wo2 = nh * c.v_dim;
     dmax = std::max<uint64_t>(c.kv_lora, c.kda_dv);
   }
-  Lt.nsplit_max = (c.kv_capacity + kChunk - 1) / kChunk;
-  uint64_t part = M * nh * Lt.nsplit_max * (dmax + kPartPad);
-  if (c.attn_kind != MK_ATTN_GQA) {
-    // the W_uk repack stages a host tensor here
+  uint64_t part = M * nh * nsplit * (dmax + kPartPad);
+  if (c.attn_kind != MK_ATTN_GQA && trace) {
+    // the W_uk repack stages a host tensor here (the context's workspace only)
     const uint64_t uk = nh * c.nope_dim * c.kv_lora * 2 / 4 + 64;
     part = std::max(part, uk);
   }
-  WsLayout& w = Lt.ws;
+  WsLayout w{};
   uint64_t o = 0;
   auto take = [&](uint64_t bytes) {
     uint64_t at = o;
@@ -303,7 +314,7 @@ Layout make_layout(const mk_config& c) {
   };
   w.flags = take(kMaxBlocks * 4);
   w.status = take(64 * 4);
-  w.trace_slots = (uint64_t)(3 + 10 * c.n_layers) * kMaxBlocks;
+  w.trace_slots = trace ? (uint64_t)(3 + 10 * c.n_layers) * kMaxBlocks : 0;
   w.trace = take(w.trace_slots * kTraceStamps * 8);
   w.rope = take((uint64_t)MK_MAX_NEW_TOKENS * kMaxRopePairs * 2 * 4);
   w.x = take(M * H * 4);
@@ -321,7 +332,7 @@ Layout make_layout(const mk_config& c) {
   w.amax = take(M * 8);
   w.scratch = w.part;
   w.total = o;
-  return Lt;
+  return w;
 }
 
 }  // namespace
@@ -339,6 +350,7 @@ struct mk_ctx {
   bool trace;
   int mfma_min_rows;  // GEMV phases of steps with at least this many rows on the matrix cores
   int last_barriers;
+  const uint8_t* last_status;  // status words of the last step (the workspace's, or the static scratch's)
   std::vector<uint8_t> loaded;  // per tensor slot, in map order
   std::map<Key, size_t> index;
   size_t n_loaded;
@@ -415,14 +427,16 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
   if (!out) return fail(MK_E_INVAL, "context output is NULL");
   *out = nullptr;
   Layout lt = make_layout(*cfg);
+  // a device context without a workspace (NULL, 0 bytes) steps only through mk_decode_step_static
+  const bool no_ws = device != MK_DEVICE_NONE && !d_workspace && workspace_bytes == 0;
   if (device != MK_DEVICE_NONE) {
-    if (!d_arena || !d_workspace) return fail(MK_E_INVAL, "arena and workspace must be device pointers");
+    if (!d_arena || (!d_workspace && !no_ws)) return fail(MK_E_INVAL, "arena and workspace must be device pointers");
     if ((reinterpret_cast<uintptr_t>(d_arena) | reinterpret_cast<uintptr_t>(d_workspace)) & (kAlign - 1))
       return fail(MK_E_INVAL, "arena and workspace must be 256-byte aligned");
   }
   if (arena_bytes < lt.arena) return fail(MK_E_NOMEM, "arena has %llu bytes, needs %llu", (unsigned long long)arena_bytes, (unsigned long long)lt.arena);
   if (lt.ws.total >= (1ull << 31)) return fail(MK_E_UNSUPPORTED, "workspace above 2 GiB");
-  if (workspace_bytes < lt.ws.total)
+  if (!no_ws && workspace_bytes < lt.ws.total)
     return fail(MK_E_NOMEM, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes, (unsigned long long)lt.ws.total);
   mk_ctx* c = new mk_ctx();
   c->cfg = *cfg;
@@ -435,6 +449,7 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
   c->trace = false;
   c->mfma_min_rows = kMfmaMinRows;
   c->last_barriers = 0;
+  c->last_status = nullptr;
   c->n_loaded = 0;
   size_t i = 0;
   for (auto& kv : c->lt.tensors) c->index[kv.first] = i++;
@@ -471,7 +486,7 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
       if (d.beta) d.beta = reinterpret_cast<const float*>(base + reinterpret_cast<uintptr_t>(d.beta));
     }
     e = hipMemcpy(c->arena, tab.data(), sizeof(LayerDev) * tab.size(), hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipMemset(c->ws, 0, c->lt.ws.total);
+    if (e == hipSuccess && c->ws) e = hipMemset(c->ws, 0, c->lt.ws.total);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
       delete c;
@@ -504,6 +519,8 @@ int mk_load_weights(mk_ctx* c, const mk_tensor_desc* d, int n, void* stream) {
       hipError_t e;
       if (it->second.repack == 1) {
         const void* src = t.src;
+        if (!t.src_on_device && !c->ws)
+          return fail(MK_E_INVAL, "tensor %d: a context without a workspace takes W_uk from device memory only", i);
         if (!t.src_on_device) {
           e = hipMemcpyAsync(c->ws + c->lt.ws.scratch, t.src, t.bytes, hipMemcpyHostToDevice, st);
           if (e != hipSuccess) return fail(MK_E_HIP, "copy of tensor %d failed: %s", i, hipGetErrorString(e));
@@ -534,9 +551,11 @@ struct SampleArgs {
   int32_t* sampled;
 };
 
+// use_static: the step's workspace is the library's static scratch array on the context's device
+// (sized for this step), instead of the context's workspace.
 static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens, void* d_kv, float* d_kda_state,
                        float* d_logits, int32_t* d_route, int32_t* d_argmax, int32_t* d_accepted, void* stream,
-                       const SampleArgs* smp = nullptr) {
+                       const SampleArgs* smp = nullptr, bool use_static = false) {
   if (!c) return fail(MK_E_INVAL, "context is NULL");
   const bool greedy = d_argmax != nullptr;
   if (smp) {
@@ -560,12 +579,37 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   const bool mf = M >= c->mfma_min_rows && mfma_shapes(g) && step_fits(g, M, c->nblocks, true);
   if (!mf && !step_fits(g, M, c->nblocks, false))
     return fail(MK_E_UNSUPPORTED, "a phase of this step does not fit the workgroup's LDS");
+  // split-KV: chunks (at least kChunk positions) sized so that the tasks of the step about fill the grid
+  const int npos = kv_len + T;
+  int chunk = kChunk;
+  if (g.attn_kind != MK_ATTN_GQA && c->nblocks > 0) {  // whole kSub-position tiles per task
+    const int even = (int)(((long long)B * npos + c->nblocks - 1) / c->nblocks);
+    chunk = (std::max(kChunk, even) + kSub - 1) / kSub * kSub;
+  } else if (c->nblocks > 0) {  // GQA: tasks (sequence, kv head, split) about fill the grid
+    const int even = (int)(((long long)B * g.n_kv_heads * npos + c->nblocks - 1) / c->nblocks);
+    chunk = (std::max(kChunk, even) + kChunk - 1) / kChunk * kChunk;
+  }
+  const int nsplit = (npos + chunk - 1) / chunk;
+  WsLayout w = c->lt.ws;
+  if (use_static) {
+    w = ws_layout(g, (uint64_t)M, (uint64_t)nsplit, false);
+    if (w.total > kStaticScratchBytes)
+      return fail(MK_E_UNSUPPORTED, "this step needs %llu bytes of workspace; the static scratch holds %llu",
+                  (unsigned long long)w.total, (unsigned long long)kStaticScratchBytes);
+  }
   if (c->n_loaded != c->loaded.size())
     return fail(MK_E_STATE, "%zu of %zu weight tensors loaded", c->n_loaded, c->loaded.size());
   if (c->poisoned) return fail(MK_E_STATE, "context poisoned by an earlier device error");
   if (c->device == MK_DEVICE_NONE) return fail(MK_E_STATE, "host-only context cannot launch");
+  if (!use_static && !c->ws) return fail(MK_E_STATE, "context has no workspace: steps go through mk_decode_step_static");
+  uint8_t* ws = c->ws;
+  if (use_static) {
+    void* base = nullptr;
+    hipError_t e = static_scratch(c->device, &base);
+    if (e != hipSuccess) return fail(MK_E_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+    ws = static_cast<uint8_t*>(base);
+  }
 
-  const WsLayout& w = c->lt.ws;
   Params p{};
   p.L = g.n_layers; p.H = g.hidden; p.V = g.vocab; p.nh = g.n_heads; p.nkv = g.n_kv_heads; p.hd = g.head_dim;
   p.ql = g.q_lora; p.kvl = g.attn_kind == MK_ATTN_GQA ? 0 : g.kv_lora; p.rd = g.rope_dim; p.nd = g.nope_dim;
@@ -574,25 +618,16 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   p.family = g.attn_kind;
   p.eps = g.rms_eps; p.rope_theta = g.rope_theta;
   p.B = B; p.T = T; p.M = M; p.kv_len = kv_len;
-  // split-KV: chunks (at least kChunk positions) sized so that the tasks of the step about fill the grid
-  const int npos = kv_len + T;
-  p.chunk = kChunk;
-  if (g.attn_kind != MK_ATTN_GQA && c->nblocks > 0) {  // whole kSub-position tiles per task
-    const int even = (int)(((long long)B * npos + c->nblocks - 1) / c->nblocks);
-    p.chunk = (std::max(kChunk, even) + kSub - 1) / kSub * kSub;
-  } else if (c->nblocks > 0) {  // GQA: tasks (sequence, kv head, split) about fill the grid
-    const int even = (int)(((long long)B * g.n_kv_heads * npos + c->nblocks - 1) / c->nblocks);
-    p.chunk = (std::max(kChunk, even) + kChunk - 1) / kChunk * kChunk;
-  }
-  p.nsplit = (npos + p.chunk - 1) / p.chunk;
-  p.epoch = (uint32_t)(c->launches * 65536ull);
+  p.chunk = chunk;
+  p.nsplit = nsplit;
+  // the context's flags count up across its steps; the static scratch's are cleared before each step
+  p.epoch = use_static ? 0u : (uint32_t)(c->launches * 65536ull);
   p.tokens = d_tokens; p.logits = d_logits; p.route = d_route;
   p.layers = reinterpret_cast<const LayerDev*>(c->arena);
   auto wt = [&](int kind) { return reinterpret_cast<const uint16_t*>(c->arena + c->lt.tensors.at(Key(kind, -1, -1)).off); };
   p.embed = wt(MK_W_EMBED); p.final_norm = wt(MK_W_FINAL_NORM); p.lm_head = wt(MK_W_LM_HEAD);
   p.kv = static_cast<uint16_t*>(d_kv);
   p.kda_state = d_kda_state;
-  uint8_t* ws = c->ws;
   p.flags = reinterpret_cast<uint32_t*>(ws + w.flags);
   p.status = reinterpret_cast<uint32_t*>(ws + w.status);
   auto f = [&](uint64_t o) { return reinterpret_cast<float*>(ws + o); };
@@ -601,7 +636,7 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   p.wsb = reinterpret_cast<const char*>(ws);
   p.ws_bytes = (uint32_t)w.total;
   p.watchdog_ticks = c->watchdog_ticks;
-  p.trace = c->trace ? reinterpret_cast<uint64_t*>(ws + w.trace) : nullptr;
+  p.trace = c->trace && !use_static ? reinterpret_cast<uint64_t*>(ws + w.trace) : nullptr;
   p.greedy = greedy ? 1 : 0;
   p.amax = reinterpret_cast<unsigned long long*>(ws + w.amax);
   p.argmax = d_argmax;
@@ -618,15 +653,18 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   if ((uint64_t)M * nh * p.nsplit * (dmax + kPartPad) > w.part_floats)
     return fail(MK_E_UNSUPPORTED, "attention partials exceed the workspace");
   hipError_t e = hipSetDevice(c->device);
+  if (e == hipSuccess && use_static)  // barrier flags and status words start at zero
+    e = launch_clear_words(p.flags, (int)((w.status + 64 * 4 - w.flags) / 4), static_cast<hipStream_t>(stream));
   if (e == hipSuccess) e = launch_decode(p, c->nblocks, mf, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MK_E_HIP, "launch failed: %s", hipGetErrorString(e));
-  c->launches++;
+  if (!use_static) c->launches++;
+  c->last_status = ws + w.status;
   int nb = (greedy || smp) ? 2 : 1;  // the LM head's barrier, and the one before greedy or sampled tokens
   for (int l = 0; l < g.n_layers; ++l) {  // attention phases, then 3 MoE phases (dense: 2)
     const int k = layer_kind(g, l);
     nb += (k == kGqa ? 4 : k == kMla ? 7 : 3) + (g.n_experts ? 3 : 2);
   }
-  c->last_barriers = nb;
+  c->last_barriers = use_static ? 0 : nb;  // a static step records no trace
   g_err.clear();
   return MK_OK;
 }
@@ -649,6 +687,12 @@ int mk_decode_step_sample(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_
   return decode_step(c, B, T, kv_len, d_tokens, d_kv, d_kda_state, d_logits, nullptr, nullptr, nullptr, stream, &smp);
 }
 
+int mk_decode_step_static(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tokens, void* d_kv, float* d_kda_state,
+                          float* d_logits, int32_t* d_route, void* stream) {
+  return decode_step(c, B, T, kv_len, d_tokens, d_kv, d_kda_state, d_logits, d_route, nullptr, nullptr, stream, nullptr,
+                     true);
+}
+
 int mk_set_trace(mk_ctx* c, int enable) {
   if (!c) return fail(MK_E_INVAL, "context is NULL");
   c->trace = enable != 0;
@@ -667,7 +711,7 @@ int mk_set_matrix_cores(mk_ctx* c, int min_rows) {
 int mk_read_trace(mk_ctx* c, uint64_t* out, uint64_t capacity, int* n_barriers, int* n_blocks) {
   if (!c || !n_barriers || !n_blocks) return fail(MK_E_INVAL, "NULL argument");
   if (c->device == MK_DEVICE_NONE) return fail(MK_E_STATE, "host-only context has no trace");
-  if (!c->trace || c->last_barriers == 0) return fail(MK_E_STATE, "no traced step since tracing was enabled");
+  if (!c->trace || c->last_barriers == 0 || !c->ws) return fail(MK_E_STATE, "no traced step since tracing was enabled");
   const uint64_t n = (uint64_t)(c->last_barriers + 1) * c->nblocks * kTraceStamps;
   *n_barriers = c->last_barriers;
   *n_blocks = c->nblocks;
@@ -683,7 +727,12 @@ int mk_poll(mk_ctx* c) {
   if (!c) return fail(MK_E_INVAL, "context is NULL");
   if (c->device == MK_DEVICE_NONE) return c->poisoned ? fail(MK_E_DEVICE, "context poisoned") : MK_OK;
   uint32_t st[4] = {0, 0, 0, 0};
-  hipError_t e = hipMemcpy(st, c->ws + c->lt.ws.status, sizeof st, hipMemcpyDeviceToHost);
+  if (!c->last_status) {  // no step yet
+    if (c->poisoned) return fail(MK_E_DEVICE, "context poisoned");
+    g_err.clear();
+    return MK_OK;
+  }
+  hipError_t e = hipMemcpy(st, c->last_status, sizeof st, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(MK_E_HIP, "status read failed: %s", hipGetErrorString(e));
   if (st[0] != 0 || c->poisoned) {
     c->poisoned = true;

@@ -20,6 +20,10 @@ constexpr int kMaxExperts = 256;
 constexpr int kTraceStamps = MK_TRACE_STAMPS;
 constexpr int kMaxRopePairs = 64;
 constexpr int kMaxQueue = MK_MAX_M * 8;  // token-expert pairs per step (top_k <= 8)
+// The allocation-free step's workspace: a device array of the library, one per GPU, held until the
+// process ends (mk_decode_step_static). 64 MiB covers every step of the preset models.
+constexpr uint64_t kStaticScratchBytes = 64ull << 20;
+constexpr int kMaxDevices = 64;
 
 enum LayerKind : int32_t { kGqa = 0, kMla = 1, kKda = 2 };
 

@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mk_internal.h"
 
 using namespace mk;
@@ -2765,6 +2767,12 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   }
 }
 
+// words [0, n) of p to zero (the static workspace's barrier flags and status before a step: a fill
+// kernel, not a memset, so that a caller may capture the step in a graph)
+__global__ void clear_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + tid_x(); i < n; i += gridDim.x * blockDim.x) gp(p)[i] = 0u;
+}
+
 // W_uk [h][nope][kv_lora] -> W_ukT [h][kv_lora][nope]
 __global__ void transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd, int kvl) {
   const size_t n = (size_t)nh * nd * kvl;
@@ -2776,7 +2784,40 @@ __global__ void transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd,
 
 }  // namespace
 
+// The workspace of mk_decode_step_static: one copy of this array on every GPU the library runs on.
+// In host code `scratch` only names the symbol; its device address (a different one on every GPU)
+// comes from hipGetSymbolAddress with that GPU current, and only that address is ever passed on.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 namespace mk {
+
+// The device address of `scratch` on `device`, looked up once per device (with that device
+// current) and kept for the life of the process.
+hipError_t static_scratch(int device, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipSetDevice(device);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t back = hipSetDevice(cur);
+    if (e == hipSuccess) e = back;
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    addr[device] = ptr;
+  }
+  *out = addr[device];
+  return hipSuccess;
+}
+
+hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_words, dim3(1), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 size_t kernel_lds_bytes() { return sizeof(Smem) + sizeof(Params); }
 int max_grid() { return kMaxGrid; }

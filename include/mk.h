@@ -187,6 +187,23 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor_desc* descs, int n, void* hip_s
 int mk_decode_step(mk_ctx* ctx, int batch, int n_new_tokens, int kv_len, const int32_t* d_tokens, void* d_kv,
                    float* d_kda_state, float* d_logits, int32_t* d_route, void* hip_stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc -- mk_decode_step without the context's workspace: the
+ * step's activations, split-KV partials, barrier flags and status words live in a device array of
+ * the library instead (one per GPU, 64 MiB, held until the process ends; its address on each GPU
+ * is looked up once). The call allocates nothing. It launches two kernels on hip_stream: a fill
+ * kernel that zeroes the array's barrier flags and status words, then the step. Arguments, outputs
+ * and errors are those of mk_decode_step, plus MK_E_UNSUPPORTED when the step needs more workspace
+ * than the array holds (activations of batch * n_new_tokens rows and split-KV partials over kv_len +
+ * n_new_tokens positions; every step of the preset models fits). The context may have been created
+ * without a workspace (NULL, 0 bytes). Every static step on one GPU uses the same array, which
+ * keeps the last step's contents: static steps that overlap in time on one GPU (other streams,
+ * other threads, other contexts) race, and must not be issued. mk_poll reports the device status
+ * of the context's last step as long as no other static step has run on that GPU since. Static
+ * steps record no trace. */
+int mk_decode_step_static(mk_ctx* ctx, int batch, int n_new_tokens, int kv_len, const int32_t* d_tokens, void* d_kv,
+                          float* d_kda_state, float* d_logits, int32_t* d_route, void* hip_stream);
+
 /* The same step with greedy selection fused after the LM head (the pages' serving loop picks the
  * next token on the device: tpu-megakernels README, section on the servers' generation modes;
  * drafts verified in one step: news summary "谷歌TPU v7推理Kimi K3性能超英伟达GB200 57%", background

@@ -24,7 +24,10 @@ def _dev_alloc(nbytes: int, device) -> torch.Tensor:
 class DeviceModel:
     """Arena, workspace, cache and state of one model on one GPU, filled from `spec`."""
 
-    def __init__(self, cfg: synth.ModelConfig, spec: synth.Spec, device: int = 0, load: bool = True):
+    def __init__(self, cfg: synth.ModelConfig, spec: synth.Spec, device: int = 0, load: bool = True,
+                 workspace: bool = True):
+        """workspace=False: a context without a workspace, which steps only through
+        mk_decode_step_static."""
         import decode_megakernel_cu_amd as mk
 
         self.mk = mk
@@ -33,12 +36,12 @@ class DeviceModel:
         self.sizes = mk.mk_query_sizes(self.mcfg)
         s = self.sizes
         self.arena = _dev_alloc(s.arena_bytes, self.device)
-        self.ws = _dev_alloc(s.workspace_bytes, self.device)
+        self.ws = _dev_alloc(s.workspace_bytes, self.device) if workspace else None
         self.kv = torch.zeros(max(s.kv_bytes // 2, 128), dtype=torch.int16, device=self.device)
         self.state = (torch.zeros(s.kda_state_bytes // 4, dtype=torch.float32, device=self.device)
                       if s.kda_state_bytes else None)
-        self.ctx = mk.mk_create(self.mcfg, device, self.arena.data_ptr(), s.arena_bytes, self.ws.data_ptr(),
-                                s.workspace_bytes)
+        self.ctx = mk.mk_create(self.mcfg, device, self.arena.data_ptr(), s.arena_bytes,
+                                self.ws.data_ptr() if workspace else 0, s.workspace_bytes if workspace else 0)
         self.stream = torch.cuda.current_stream(self.device).cuda_stream
         if load:
             self.load_weights()
@@ -131,6 +134,22 @@ class DeviceModel:
         self.mk.mk_decode_step(self.ctx, B, T, kv_len, d_tokens.data_ptr(), self.kv.data_ptr(),
                                self.state.data_ptr() if self.state is not None else 0, logits.data_ptr(),
                                rt.data_ptr() if rt is not None else 0, self.stream)
+        return logits, rt
+
+    def step_static(self, tokens: np.ndarray, kv_len: int, route: bool = True, logits: torch.Tensor | None = None,
+                    d_tokens: torch.Tensor | None = None):
+        """mk_decode_step on the library's static per-GPU workspace."""
+        B, T = tokens.shape
+        cfg = self.cfg
+        if d_tokens is None:
+            d_tokens = torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).to(self.device)
+        if logits is None:
+            logits = torch.empty((B, T, cfg.vocab), dtype=torch.float32, device=self.device)
+        rt = torch.full((cfg.n_layers, B * T, cfg.top_k), -1, dtype=torch.int32, device=self.device) if route else None
+        self.mk.mk_decode_step_static(self.ctx, B, T, kv_len, d_tokens.data_ptr(), self.kv.data_ptr(),
+                                      self.state.data_ptr() if self.state is not None else 0, logits.data_ptr(),
+                                      rt.data_ptr() if rt is not None else 0, self.stream)
+        self._keep_tok = d_tokens
         return logits, rt
 
     def step_greedy(self, tokens: np.ndarray, kv_len: int, logits: torch.Tensor | None = None,

@@ -330,3 +330,28 @@ def test_preset_field_is_validated(mk):
     with pytest.raises(mk.MkError) as e:
         mk.mk_query_sizes(c)
     assert e.value.code == mk.MK_E_INVAL
+
+
+def test_static_step_limits_on_host(mk):
+    """mk_decode_step_static refuses, before any launch, a step whose workspace exceeds the static
+    array (here 8 new tokens over 9000 positions of latent cache: split-KV partials of ~135 MB on a
+    host-only context, which splits into 16-position chunks); a step that fits reaches the
+    host-only check."""
+    cfg = replace(synth.K3, n_layers=2, expert_pool_layers=0, kv_capacity=9008)
+    s = sizes(mk, cfg)
+    ctx = mk.mk_create(mk.config(cfg), mk.MK_DEVICE_NONE, 0, s.arena_bytes, 0, s.workspace_bytes)
+    try:
+        load_all(mk, cfg, ctx)
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_decode_step_static(ctx, 1, 8, 9000, 1, 1, 0, 1)
+        assert e.value.code == mk.MK_E_UNSUPPORTED
+        assert "static scratch" in mk.mk_last_error()
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_decode_step_static(ctx, 1, 1, 100, 1, 1, 0, 1)
+        assert e.value.code == mk.MK_E_STATE
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_decode_step_static(ctx, 1, 1, 9008, 1, 1, 0, 1)
+        assert e.value.code == mk.MK_E_KV_OVERFLOW
+    finally:
+        mk.mk_destroy(ctx)
+
