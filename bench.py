@@ -1,14 +1,20 @@
 """Benchmark: one-launch MoE decode step on the K3-scale one-GPU share (MI355X).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--batches 1,2,4,8] [--no-cpu-baseline]
+                [--no-others] [--no-verify] [--no-read-probe] [--trace [--trace-out F]]
+python bench.py --calib                      (one pass of the copy and read probes, for counters)
+python bench.py --ingest-pmc FETCH.csv WRITE.csv   (turn two rocprofv3 --pmc runs into traffic)
 
 Prints ONE JSON line. `value` is decode tokens/s at batch 1 (the headline configuration:
 92 layers, hidden 7168, MLA with a 4096-long latent cache, 48 local experts top-1 plus a
-shared expert, LM-head slice 7168 x 40960); the other batch sizes of the metric are reported
-under "batches". Inputs are synthetic and seeded and already resident in HBM when the timed
-region starts. "roofline" divides the step's algorithmic bytes (the weights the step must
-read given its routing, the cache read and written, and the logits) by the megakernel's
-average duration, measured with HIP events on the launch stream, against 8 TB/s.
+shared expert, LM-head slice 7168 x 40960); the other batch sizes are under "batches", the
+7-token verify step under "verify", the other workloads under "workloads". Inputs are
+synthetic and seeded and already resident in HBM when the timed region starts. "roofline"
+divides the step's algorithmic bytes (the weights the step must read given its routing, the
+cache read and written, and the logits) by the megakernel's average duration, measured with
+HIP events on the launch stream, against 8 TB/s; "read_probe" is the rate a plain streaming
+read of 4 GiB reaches with each of the megakernel's load kinds on the same GPU, and
+"roofline_measured_read" states the megakernel against the fastest of them.
 """
 from __future__ import annotations
 
@@ -89,38 +95,95 @@ def traffic_from_profiles(B: int, workload: str = WORKLOAD):
     return d.get("per_launch_bytes", {}).get(str(B))
 
 
-CALIB_BYTES = 1 << 30  # bytes the calibration kernel reads (and writes)
+CALIB_BYTES = 1 << 30  # bytes the elementwise copy reads and writes (the WRITE_SIZE calibration)
+STREAM_BYTES = 4 << 30  # bytes the read probe reads per load kind (the FETCH_SIZE calibration)
+STREAM_KINDS = {0: "weights (16-byte non-temporal global loads)", 1: "activations (16-byte coherent buffer loads)",
+                2: "staging (16-byte memory-to-LDS copies)"}
+
+
+def stream_probe():
+    """ctypes handle of libmkstream.so (include/mk_stream.h)."""
+    import ctypes
+
+    path = os.path.join(ROOT, "decode_megakernel_cu_amd", "libmkstream.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    L.mk_stream_read.restype = ctypes.c_int
+    L.mk_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return L
+
+
+def measure_read_bandwidth(reps: int = 10) -> dict:
+    """GB/s of one read pass over STREAM_BYTES with each of the megakernel's load kinds (median of
+    reps passes, HIP events on the launch stream)."""
+    import torch
+
+    L = stream_probe()
+    buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    out = {}
+    for kind, what in STREAM_KINDS.items():
+        ms = []
+        for i in range(reps + 2):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            rc = L.mk_stream_read(buf.data_ptr(), STREAM_BYTES, kind, sink.data_ptr(), st.cuda_stream)
+            b.record(st)
+            if rc != 0:
+                raise RuntimeError(f"mk_stream_read failed: {rc}")
+            torch.cuda.synchronize()
+            if i >= 2:
+                ms.append(a.elapsed_time(b))
+        t = float(np.median(ms))
+        out[str(kind)] = {"what": what, "ms": round(t, 4), "gbs": round(STREAM_BYTES / (t * 1e-3) / 1e9, 1)}
+        print(f"# read probe, {what}: {out[str(kind)]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    del buf
+    torch.cuda.empty_cache()
+    return {"bytes": STREAM_BYTES, "kinds": out}
 
 
 def ingest_pmc(fetch_csv: str, write_csv: str, workload: str = WORKLOAD) -> None:
-    """HBM traffic of the megakernel from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
-    each scaled by what the same counter reads for the calibration copy (CALIB_BYTES read and
-    written by an elementwise kernel), written to profiles/ with the kernel's source hash."""
+    """HBM traffic of the megakernel from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch).
+    FETCH_SIZE is scaled by what the counter reads for the read probe's pass over STREAM_BYTES with
+    the weight-stream load kind (the megakernel's reads are almost all weight and cache rows read
+    that way; the factors of the other two kinds are recorded beside it); WRITE_SIZE by what it reads
+    for the elementwise copy of CALIB_BYTES. Written to profiles/ with the kernel's source hash."""
     import csv
 
-    def per_kernel(path: str, counter: str) -> tuple[float, list[float]]:
+    def per_kernel(path: str, counter: str) -> tuple[dict, float | None, list[float]]:
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         by = {}
         for r in rows:
             key = (r["Dispatch_Id"], r["Kernel_Name"])
             by[key] = by.get(key, 0.0) + float(r["Counter_Value"])
+        probe = {}
+        for (d, n), v in by.items():
+            for k in STREAM_KINDS:
+                if f"stream_read<{k}>" in n:
+                    probe.setdefault(k, []).append(v)
         # the calibration multiply (x * 1.0 -> y), not the fills torch runs around it
-        calib = [v for (d, n), v in by.items() if "elementwise" in n and "Fill" not in n and
-                 ("AUnaryFunctor" in n or "Mul" in n)]
+        copy = [v for (d, n), v in by.items() if "elementwise" in n and "Fill" not in n and
+                ("AUnaryFunctor" in n or "Mul" in n)]
         mk = [v for (d, n), v in sorted(by.items(), key=lambda kv: int(kv[0][0])) if "mk_decode_kernel" in n]
-        if not calib or not mk:
-            raise SystemExit(f"{path}: need the calibration kernel and megakernel dispatches for {counter}")
-        return max(calib), mk
+        if not mk:
+            raise SystemExit(f"{path}: no megakernel dispatches for {counter}")
+        return ({k: float(np.median(v)) for k, v in probe.items()}, max(copy) if copy else None, mk)
 
-    f_cal, f_mk = per_kernel(fetch_csv, "FETCH_SIZE")
-    w_cal, w_mk = per_kernel(write_csv, "WRITE_SIZE")
-    f_scale = CALIB_BYTES / (f_cal * 1024.0)
-    w_scale = CALIB_BYTES / (w_cal * 1024.0)
-    fetch = float(np.median(f_mk)) * 1024.0 * f_scale
+    f_probe, _, f_mk = per_kernel(fetch_csv, "FETCH_SIZE")
+    _, w_copy, w_mk = per_kernel(write_csv, "WRITE_SIZE")
+    if 0 not in f_probe or w_copy is None:
+        raise SystemExit("need the read probe's weight-kind dispatch (FETCH_SIZE) and the copy (WRITE_SIZE)")
+    f_scale = {k: STREAM_BYTES / (v * 1024.0) for k, v in f_probe.items()}
+    w_scale = CALIB_BYTES / (w_copy * 1024.0)
+    fetch = float(np.median(f_mk)) * 1024.0 * f_scale[0]
     write = float(np.median(w_mk)) * 1024.0 * w_scale
     out = {"kernel_hash": kernel_source_hash(), "workload": workload, "batch": 1,
-           "calibration": {"bytes": CALIB_BYTES, "fetch_kib": f_cal, "write_kib": w_cal,
-                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "calibration": {"fetch": {"bytes": STREAM_BYTES, "probe_kib": {str(k): v for k, v in f_probe.items()},
+                                     "scale_by_kind": {str(k): v for k, v in f_scale.items()}, "applied_kind": 0},
+                           "write": {"bytes": CALIB_BYTES, "copy_kib": w_copy, "scale": w_scale}},
            "megakernel": {"dispatches": len(f_mk), "fetch_kib_median": float(np.median(f_mk)),
                           "write_kib_median": float(np.median(w_mk)), "fetch_bytes": fetch, "write_bytes": write},
            "per_launch_bytes": {"1": fetch + write}}
@@ -172,6 +235,7 @@ def cpu_baseline(sample_layers: int = 8, budget_s: float = 12.0) -> dict:
     step = t_head + per_layer * w.model.n_layers
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(w.batch * w.new_tokens / step, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{sample_layers} of {w.model.n_layers} layers of the batch-1 step (+ embedding and LM head), "
                       f"median of {len(times)} runs, weights served from host memory; per-layer time scaled to "
                       f"{w.model.n_layers} layers (step {step:.2f} s)"}
@@ -348,6 +412,31 @@ def speculative(dm, cfg, spec, v, steps: int, warmup: int, stream) -> dict:
 
 
 # ------------------------------------------------------------------------------------------
+# the measured rows: the headline share at batch 1/2/4/8, its verify step, the other workloads
+# ------------------------------------------------------------------------------------------
+OTHER_ROWS = [("c1", [1]), ("c2", [1, 4]), ("c5", [8]), ("dense", [1, 2, 4, 8])]
+
+
+def row_of(r: dict, read_gbs: float | None) -> dict:
+    out = {"tokens_per_s": round(r["tokens_per_s"], 2), "kernel_ms": round(r["kernel_ms_avg"], 4),
+           "kernel_ms_p10": round(r["kernel_ms_p10"], 4), "kernel_ms_p90": round(r["kernel_ms_p90"], 4),
+           "gb_per_step": round(r["bytes"] / 1e9, 4), "hbm_gbs": round(r["gbs"], 1),
+           "hbm_frac": round(r["gbs"] / HBM_PEAK_GBS, 4)}
+    if read_gbs:
+        out["read_probe_frac"] = round(r["gbs"] / read_gbs, 4)
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -357,21 +446,23 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--trace", action="store_true", help="print per-phase device timings of one step per batch")
-    ap.add_argument("--workload", default=WORKLOAD, choices=["c3", "c4", "c5", "dense"],
-                    help="c3: K3-scale share (the headline); c4: its 7-token verify step; c5: the hybrid model; "
-                         "dense: the dense 27B-class decoder (for profiling one path; --batches applies)")
+    ap.add_argument("--trace-out", default=None, help="with --trace: write the per-phase summary (JSON) here")
+    ap.add_argument("--workload", default=WORKLOAD, choices=["c1", "c2", "c3", "c4", "c5", "dense"],
+                    help="c3: the K3-scale share (the headline, followed by every other row); any other: that "
+                         "workload alone (for profiling one path; --batches applies)")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the 7-token speculative-verify measurement on the K3-scale share")
-    ap.add_argument("--no-dense", action="store_true",
-                    help="skip the dense-decoder measurement that follows the K3-scale share")
+    ap.add_argument("--no-others", "--no-dense", dest="no_others", action="store_true",
+                    help="skip the rows after the K3-scale share (tiny, mid-size, hybrid, dense)")
+    ap.add_argument("--no-read-probe", action="store_true", help="skip the read-bandwidth probe")
     ap.add_argument("--mfma-min-rows", type=int, default=None,
                     help="token rows from which GEMV phases use the matrix cores (library default if omitted)")
-    ap.add_argument("--calib-copy", action="store_true",
-                    help="run one elementwise copy of CALIB_BYTES (fp32 x*1 -> y) first: the counter calibration "
-                         "kernel for the traffic figure")
+    ap.add_argument("--calib", action="store_true",
+                    help="first run the counter calibration kernels: one elementwise copy of CALIB_BYTES (fp32 "
+                         "x*1 -> y) and one read-probe pass of STREAM_BYTES per load kind")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 counter_collection CSVs (FETCH_SIZE, WRITE_SIZE) of a --calib-copy "
-                         "run into profiles/megakernel_{k3,dense}_pmc_traffic.json (by --workload) and exit")
+                    help="turn two rocprofv3 counter_collection CSVs (FETCH_SIZE, WRITE_SIZE) of a --calib run "
+                         "into profiles/megakernel_{k3,dense}_pmc_traffic.json (by --workload) and exit")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(*args.ingest_pmc, workload="dense" if args.workload == "dense" else "c3")
@@ -385,25 +476,27 @@ def main():
 
     from synth.device_inputs import DeviceModel
 
-    w = synth.WORKLOADS[args.workload]
-    cfg = w.model
     spec = synth.Spec(seed=args.seed)
-    t0 = time.time()
-    dm = DeviceModel(cfg, spec, device=0)
-    if args.mfma_min_rows is not None:
-        dm.set_matrix_cores(args.mfma_min_rows)
-    batches = [int(b) for b in args.batches.split(",")]
-    dm.fill_caches(max(batches), w.kv_len)
-    print(f"# model loaded in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
-    if args.calib_copy:
+    if args.calib:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    def measure(B: int, T: int, trace: bool, dm=dm, cfg=cfg, w=w) -> dict:
+        L = stream_probe()
+        buf = torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device="cuda")
+        sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+        for kind in STREAM_KINDS:
+            assert L.mk_stream_read(buf.data_ptr(), STREAM_BYTES, kind, sink.data_ptr(), stream.cuda_stream) == 0
+            torch.cuda.synchronize()
+        del buf
+        torch.cuda.empty_cache()
+    read = None if args.no_read_probe else measure_read_bandwidth()
+    read_gbs = read["kinds"]["0"]["gbs"] if read else None
+
+    def measure(dm, cfg, w, B: int, T: int, trace: bool) -> dict:
         toks = synth.tokens(spec.seed, 1, cfg.vocab, B, T)
         d_tok = torch.from_numpy(toks.astype(np.int32)).cuda()
         logits = torch.empty((B, T, cfg.vocab), dtype=torch.float32, device="cuda")
@@ -431,37 +524,57 @@ def main():
              "kernel_ms_p10": float(np.percentile(kms, 10)), "kernel_ms_p90": float(np.percentile(kms, 90)),
              "tokens_per_s": B * T * args.steps / wall, "bytes": by["total"],
              "gbs": by["total"] / (kms.mean() * 1e-3) / 1e9}
-        print(f"# B={B} T={T}: {r['kernel_ms_avg']:.3f} ms/launch, {r['tokens_per_s']:.1f} tok/s, "
-              f"{r['gbs']:.0f} GB/s ({by['total'] / 1e9:.2f} GB/step)", file=sys.stderr, flush=True)
+        print(f"# {w.name} B={B} T={T}: {r['kernel_ms_avg']:.3f} ms/launch (p10 {r['kernel_ms_p10']:.3f}, p90 "
+              f"{r['kernel_ms_p90']:.3f}), {r['tokens_per_s']:.1f} tok/s, {r['gbs']:.0f} GB/s "
+              f"({by['total'] / 1e9:.3f} GB/step)", file=sys.stderr, flush=True)
         if trace:
             dm.mk.mk_set_trace(dm.ctx, True)
             dm.step(toks, w.kv_len, route=False, logits=logits, d_tokens=d_tok)
             torch.cuda.synchronize()
             summary = trace_summary(cfg, dm.mk.mk_read_trace(dm.ctx))
             dm.mk.mk_set_trace(dm.ctx, False)
-            print(f"# trace B={B} T={T}", file=sys.stderr)
+            print(f"# trace {w.name} B={B} T={T}", file=sys.stderr)
             print_trace(summary)
             r["trace"] = summary
         return r
 
-    results = {B: measure(B, w.new_tokens, args.trace) for B in batches}
+    def load(wname: str, batches: list[int]):
+        w = synth.WORKLOADS[wname]
+        t0 = time.time()
+        dm = DeviceModel(w.model, spec, device=0)
+        if args.mfma_min_rows is not None:
+            dm.set_matrix_cores(args.mfma_min_rows)
+        dm.fill_caches(max(batches), w.kv_len)
+        print(f"# {w.name} model loaded in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+        return w, dm
+
+    batches = [int(b) for b in args.batches.split(",")]
+    w, dm = load(args.workload, batches)
+    cfg = w.model
+    results = {B: measure(dm, cfg, w, B, w.new_tokens, args.trace) for B in batches}
+    if args.trace and args.trace_out:
+        with open(args.trace_out, "w") as fh:
+            json.dump({str(B): r["trace"] for B, r in results.items()}, fh, indent=1)
     verify = spec_dec = None
     if args.workload == "c3" and not args.no_verify:
         v = synth.WORKLOADS["c4"]
-        verify = measure(v.batch, v.new_tokens, False)
+        verify = measure(dm, cfg, v, v.batch, v.new_tokens, False)
         spec_dec = speculative(dm, cfg, spec, v, args.steps, args.warmup, stream)
     dm.close()
-    dense = None
-    if args.workload == "c3" and not args.no_dense:  # the dense second model, after the share is freed
-        wd = synth.WORKLOADS["dense"]
-        t0 = time.time()
-        dmd = DeviceModel(wd.model, spec, device=0)
-        if args.mfma_min_rows is not None:
-            dmd.set_matrix_cores(args.mfma_min_rows)
-        dmd.fill_caches(max(batches), wd.kv_len)
-        print(f"# dense model loaded in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
-        dense = {B: measure(B, 1, False, dm=dmd, cfg=wd.model, w=wd) for B in batches}
-        dmd.close()
+    del dm  # the K3-scale arena (193 GB) must be freed before the next model is loaded
+    import gc
+
+    gc.collect()
+    torch.cuda.empty_cache()
+    others = {}
+    if args.workload == "c3" and not args.no_others:  # each model loaded after the previous one is freed
+        for wname, bs in OTHER_ROWS:
+            wo, dmo = load(wname, bs)
+            others[wname] = (wo, {B: measure(dmo, wo.model, wo, B, wo.new_tokens, False) for B in bs})
+            dmo.close()
+            del dmo
+            gc.collect()
+            torch.cuda.empty_cache()
 
     head = results[batches[0]]
     achieved = head["gbs"]
@@ -482,33 +595,34 @@ def main():
                                "rope 64), latent cache 4096, 48 experts top-1 ffn 2048 + shared 512, vocab slice "
                                "40960", "batch": batches[0], "new_tokens": w.new_tokens, "kv_len": w.kv_len,
                    "launches_per_step": 1},
-        "batches": {str(B): {"tokens_per_s": round(r["tokens_per_s"], 2), "kernel_ms": round(r["kernel_ms_avg"], 4),
-                             "gb_per_step": round(r["bytes"] / 1e9, 3), "hbm_gbs": round(r["gbs"], 1),
-                             "hbm_frac": round(r["gbs"] / HBM_PEAK_GBS, 4)} for B, r in results.items()},
+        "batches": {str(B): row_of(r, read_gbs) for B, r in results.items()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(batches[0])},
     }
+    if read is not None:
+        out["read_probe"] = read
+        out["roofline_measured_read"] = {"achieved": round(achieved, 1), "read_gbs": read_gbs,
+                                         "frac": round(achieved / read_gbs, 4)}
     if spec_dec is not None:
         out["speculative"] = spec_dec
-    if dense is not None:
-        dc = synth.WORKLOADS["dense"].model
-        out["dense"] = {
-            "workload": f"dense GQA decoder: {dc.n_layers} layers, hidden {dc.hidden}, {dc.n_heads} query / "
-                        f"{dc.n_kv_heads} KV heads of {dc.head_dim}, SwiGLU {dc.shared_ffn}, vocab {dc.vocab} "
-                        f"({sum(synth.numel(t.shape) for t in synth.tensor_list(dc)) / 1e9:.1f} B parameters), "
-                        f"KV cache {synth.WORKLOADS['dense'].kv_len}",
-            "batches": {str(B): {"tokens_per_s": round(r["tokens_per_s"], 2), "kernel_ms": round(r["kernel_ms_avg"], 4),
-                                 "gb_per_step": round(r["bytes"] / 1e9, 3), "hbm_gbs": round(r["gbs"], 1),
-                                 "hbm_frac": round(r["gbs"] / HBM_PEAK_GBS, 4)} for B, r in dense.items()}}
-        d0 = dense[batches[0]]
-        out["dense"]["roofline"] = {"bound": "hbm", "achieved": round(d0["gbs"], 1), "peak": HBM_PEAK_GBS,
-                                    "unit": "GB/s", "frac": round(d0["gbs"] / HBM_PEAK_GBS, 4),
-                                    "traffic": traffic_from_profiles(batches[0], "dense")}
     if verify is not None:  # positions verified per second (1 + 6 draft tokens per step)
-        out["verify_t7"] = {"positions_per_s": round(verify["tokens_per_s"], 2),
-                            "kernel_ms": round(verify["kernel_ms_avg"], 4),
-                            "gb_per_step": round(verify["bytes"] / 1e9, 3), "hbm_gbs": round(verify["gbs"], 1),
-                            "hbm_frac": round(verify["gbs"] / HBM_PEAK_GBS, 4)}
+        vr = row_of(verify, read_gbs)
+        vr["positions_per_s"] = vr.pop("tokens_per_s")
+        out["verify_t7"] = vr
+    if others:
+        out["workloads"] = {}
+        for wname, (wo, rs) in others.items():
+            entry = {"description": wo.description, "kv_len": wo.kv_len,
+                     "batches": {str(B): row_of(r, read_gbs) for B, r in rs.items()}}
+            if wname == "c1":  # 14.7 MB of weights: resident in the 256 MB last-level cache, latency only
+                entry["note"] = "weights fit the last-level cache; tokens/s and latency only, HBM fraction not meaningful"
+            out["workloads"][wname] = entry
+        if "dense" in others:
+            d0 = others["dense"][1][1]
+            out["workloads"]["dense"]["roofline"] = {"bound": "hbm", "achieved": round(d0["gbs"], 1),
+                                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                     "frac": round(d0["gbs"] / HBM_PEAK_GBS, 4),
+                                                     "traffic": traffic_from_profiles(1, "dense")}
     if args.workload != "c3":
         out["config"]["workload"] = f"{args.workload}: {w.description} (profiling run, not the headline)"
     if not args.no_cpu_baseline:

@@ -212,6 +212,10 @@ __device__ __forceinline__ T* rflp(T* ptr) {
 }
 
 typedef __attribute__((address_space(3))) void* LdsPtr;
+// Trace stamps are written to LDS during a phase (a store to memory would count against the
+// writing wave's vector-memory counter, and that wave's next wait for its weight loads would then
+// also wait for the store to be acknowledged) and copied out by the polling wave at the next barrier.
+typedef __attribute__((address_space(3))) uint64_t LdsU64;
 
 // Direct memory-to-LDS copies (buffer_load ... lds): no registers hold the data, so nothing forces
 // a wait on earlier loads (prefetched weights) before the copies are issued. Rows r < R of U
@@ -269,21 +273,30 @@ __device__ __forceinline__ void copy_units(const Ws& ws, int n, Src src, Dst dst
 // wait: the polling wave polls all flags with independent loads (four per lane) until every
 //   workgroup has arrived, or the abort flag or the watchdog ends the step.
 // ----------------------------------------------------------------------------------------------
-__device__ __forceinline__ void barrier_arrive(const Params& p, uint32_t& gen) {
+// stamps: [2][kTraceStamps] in LDS, record r in row r % 2 (the row of the previous record is copied
+// to memory here: every wave has finished the phase that record covers)
+__device__ __forceinline__ void barrier_arrive(const Params& p, uint32_t& gen, LdsU64* stamps) {
   gen += 1;
   wg_barrier();
-  if (wave_id() == kPollWave && lane_id() == 0) {
-    uint64_t* tr = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
-    if (tr) gp(tr)[0] = wall_clock64();
-    stc_u32(p.flags + blockIdx.x, p.epoch + gen);
+  if (wave_id() == kPollWave) {
+    const int lane = lane_id();
+    if (p.trace) {  // copy out the previous record and clear its row for the record after this one
+      if (lane < kTraceStamps) {
+        LdsU64* prev = stamps + (gen & 1) * kTraceStamps;
+        if (gen >= 2) gp(p.trace)[((size_t)(gen - 2) * gridDim.x + blockIdx.x) * kTraceStamps + lane] = prev[lane];
+        prev[lane] = 0;
+      }
+      if (lane == 0) stamps[((gen - 1) & 1) * kTraceStamps] = wall_clock64();
+    }
+    if (lane == 0) stc_u32(p.flags + blockIdx.x, p.epoch + gen);
   }
 }
 
 // The polling wave's half of the wait: poll until every workgroup has arrived (or abort).
-__device__ __forceinline__ void barrier_poll(const Params& p, uint32_t gen, int* s_abort) {
+__device__ __forceinline__ void barrier_poll(const Params& p, uint32_t gen, int* s_abort, LdsU64* stamps) {
   const uint32_t target = p.epoch + gen;
   const int lane = lane_id();
-  uint64_t* tr = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
+  LdsU64* tr = p.trace ? stamps + ((gen - 1) & 1) * kTraceStamps : nullptr;
   const uint64_t t0 = wall_clock64();
   int abort = 0;
   while (true) {
@@ -314,7 +327,7 @@ __device__ __forceinline__ void barrier_poll(const Params& p, uint32_t gen, int*
   }
   if (lane == 0) {
     *s_abort = abort;
-    if (tr) gp(tr)[1] = wall_clock64();
+    if (tr) tr[1] = wall_clock64();
   }
 }
 
@@ -877,7 +890,7 @@ __device__ __forceinline__ void step_element(const Gemv& g, const Plan& q, int e
 // The first two elements of the stream were requested by gemv_preload.
 template <int MM>
 __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const Ws& ws, float* smem, float* red,
-                                           RowBuf& b0, RowBuf& b1, bool keep_in, uint64_t* trace) {
+                                           RowBuf& b0, RowBuf& b1, bool keep_in, LdsU64* trace) {
   float* xin = smem;
   const int tid = tid_x();
   const bool compute = true;
@@ -886,7 +899,7 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
   Cursor cc{0, 0, 0, 0, 0}, pc{0, 0, 0, 0, 0};
   advance(pc, q, q.cp);
   advance(pc, q, q.cp);
-  if (trace && tid == 0) gp(trace)[4] = wall_clock64();
+  if (trace && tid == 0) trace[4] = wall_clock64();
   for (int sl = 0; sl < q.nslab; ++sl) {
     const int k0 = sl * q.KS, ks = min(q.KS, q.Wst - k0);
     __syncthreads();
@@ -897,11 +910,12 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
         dma_rows4<kCoherent>(ws.r, q.res, g.M, q.nloc, q.nloc,
                   [&](int m, int c) { return ws.off(g.out0 + (size_t)m * g.ldo0 + q.t0 + c); });
       wait_vm();
+      if (trace && sl == 0 && tid == 0) trace[12] = wall_clock64();
       __syncthreads();
       g.stage_finish<MM>(xin, gl, ks, ks, sl == 0, red);
     }
     __syncthreads();
-    if (trace && sl == 0 && tid == 0) gp(trace)[2] = wall_clock64();
+    if (trace && sl == 0 && tid == 0) trace[2] = wall_clock64();
     if (compute) {
       float a0[MM], a1[MM];
 #pragma unroll
@@ -910,12 +924,14 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
       for (int e = 0; e < q.nelp; e += 2) {
         step_element<MM>(g, q, eg0 + e, cc, pc, k0, ks, xin, b0, a0, a1);
         step_element<MM>(g, q, eg0 + e + 1, cc, pc, k0, ks, xin, b1, a0, a1);
+        if (trace && sl == 0 && e == 0 && tid == 0) trace[13] = wall_clock64();
       }
     }
   }
-  if (trace && tid == 0) gp(trace)[3] = wall_clock64();
+  if (trace && tid == 0) trace[3] = wall_clock64();
   // epilogue: one thread per task (a task's rows may have been reduced by different lane groups)
   __syncthreads();
+  if (trace && tid == 0) trace[14] = wall_clock64();
   for (int i = tid; i < q.nloc; i += kThreads) {
     float* ac = q.acc + (size_t)i * 2 * MM;
     if (g.stage == S_NORM) {  // the RMS factor of each input row
@@ -928,7 +944,7 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
     }
     g.epilogue(q.t0 + i, ac, ac + MM, q.res + i, q.nloc);
   }
-  if (trace && tid == 0) gp(trace)[5] = wall_clock64();
+  if (trace && tid == 0) trace[5] = wall_clock64();
   return q.one_slab && g.stage == S_NORM;
 }
 
@@ -1402,7 +1418,7 @@ __device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGe
 // the split bf16 form this executor reads).
 template <int MM>
 __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const Ws& ws, float* smem, float* red,
-                                            RowBuf& b0, RowBuf& b1, bool keep_in, uint64_t* trace) {
+                                            RowBuf& b0, RowBuf& b1, bool keep_in, LdsU64* trace) {
   float* xs = smem;
   const int tid = tid_x();
   const bool keep = keep_in && q.one_slab;
@@ -1411,7 +1427,7 @@ __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const
   MCur cc = mcur_slab(g, q, 0);
   MCur pc = madvance(g, q, madvance(g, q, cc));
   f32x4 dt = {0.f, 0.f, 0.f, 0.f};
-  if (trace && tid == 0) gp(trace)[4] = gp(trace)[2] = wall_clock64();
+  if (trace && tid == 0) trace[4] = trace[2] = wall_clock64();
   for (int sl = 0; sl < q.nslab; ++sl) {
     const MGeo e = mgeo(g, q, sl);
     __syncthreads();
@@ -1426,7 +1442,7 @@ __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const
       mconvert<MM>(g, xs, gl, e.ks, q.DS, sl == 0, red);
     }
     __syncthreads();
-    if (trace && sl == 0 && tid == 0) gp(trace)[2] = wall_clock64();
+    if (trace && sl == 0 && tid == 0) trace[2] = wall_clock64();
     while (cc.slab == sl) {
       mstep(g, q, cc, pc, xs, b0, dt);
       mstep(g, q, cc, pc, xs, b1, dt);
@@ -1434,13 +1450,13 @@ __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const
     __syncthreads();
     mreduce<MM>(g, q, e, sl == 0, sl == q.nslab - 1, red);
   }
-  if (trace && tid == 0) gp(trace)[3] = wall_clock64();
+  if (trace && tid == 0) trace[3] = wall_clock64();
   __syncthreads();
   for (int i = tid; i < q.nloc; i += kThreads) {
     const float* ac = q.acc + (size_t)i * 2 * MM;
     g.epilogue(q.t0 + i, ac, ac + MM, q.res + i, q.nloc);
   }
-  if (trace && tid == 0) gp(trace)[5] = wall_clock64();
+  if (trace && tid == 0) trace[5] = wall_clock64();
   return q.one_slab && g.stage == S_NORM;
 }
 
@@ -1470,7 +1486,7 @@ __device__ __forceinline__ void rope_pair(const float* table, int t, int j, floa
 // read free of bank conflicts. The unnormalised value sums stay in registers: tile j of the
 // (row tile, 16-column tile) grid belongs to wave j % 8, rescaled as each row's maximum moves.
 __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
-                                               const float* rope, uint64_t* trace) {
+                                               const float* rope, LdsU64* trace) {
   const int d = p.hd, nq = p.nh, nkv = p.nkv, T = p.T, cap = p.cap, d2 = d / 2, d4 = d / 4, d8 = d / 8;
   const int npos = p.kv_len + T, C = p.chunk, nsplit = p.nsplit, kvl = p.kv_len;
   const int qg = nq / nkv, nr = T * qg, nrt = (nr + 15) >> 4, nrp = 16 * nrt;
@@ -1543,7 +1559,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
 #pragma unroll
     for (int k = 0; k < kGqaTiles; ++k) u[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool first = task == (int)blockIdx.x && trace && tid == 0;  // stamps of the first task
-    if (first) gp(trace)[2] = wall_clock64();
+    if (first) trace[2] = wall_clock64();
     auto subtile = [&](int q0, uint4(&kr)[kU], uint4(&vr)[kU]) __attribute__((always_inline)) {
       const int ns = min(kGSub, p1 - q0);
       __syncthreads();  // the previous sub-tile is consumed
@@ -1593,7 +1609,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
         for (int i = 0; i < 4; ++i) S[(16 * rt + 4 * mq + i) * ss + 16 * pt + ml] = dd[i] * scale;
       }
       __syncthreads();
-      if (first && q0 == p0) gp(trace)[4] = wall_clock64();
+      if (first && q0 == p0) trace[4] = wall_clock64();
       // online softmax: one wave per row, lane = position; rows past nr and rows that see no
       // position yet get weight 0 and keep their sums (rescale 1)
       for (int r = wave; r < nrp; r += kWaves) {
@@ -1616,7 +1632,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
         }
       }
       __syncthreads();
-      if (first && q0 == p0) gp(trace)[5] = wall_clock64();
+      if (first && q0 == p0) trace[5] = wall_clock64();
       // value sums: A = weights [16 rows][32 positions] (high, low), B = value rows [32][16 columns]
 #pragma unroll
       for (int k = 0; k < kGqaTiles; ++k) {
@@ -1652,7 +1668,7 @@ __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* 
       }
     };
     for (int q0 = p0; q0 < p1; q0 += kGSub) subtile(q0, kra, vra);
-    if (first) gp(trace)[3] = wall_clock64();
+    if (first) trace[3] = wall_clock64();
     // the value sums to LDS (over the queries, no longer read), then the task's partial
     float* Acc = Qs;
 #pragma unroll
@@ -1784,7 +1800,7 @@ __device__ __forceinline__ void mla_prefetch_rows(const Params& p, const LayerDe
 }
 
 __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
-                                               const float* rope, uint64_t* trace) {
+                                               const float* rope, LdsU64* trace) {
   static_assert(kSub == 32, "score lanes map one position each in a half wave");
   // step values in scalar registers (read from the parameter block in LDS)
   const int kv_len = rfl(p.kv_len), Bmax = rfl(p.Bmax), B = rfl(p.B);
@@ -1928,7 +1944,7 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
         __syncthreads();
         fill_new(p0, nfirst);
         staged = true;
-        if (trace && tid == 0 && task == (int)blockIdx.x && t == 0) gp(trace)[2] = wall_clock64();
+        if (trace && tid == 0 && task == (int)blockIdx.x && t == 0) trace[2] = wall_clock64();
         for (int e = tid; e < nh * h2; e += kThreads) {
           const int h = e / h2, jj = e - h * h2;
           float* qr = Qt + h * lat + kvl;
@@ -1987,7 +2003,7 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
             for (int i = 0; i < 4; ++i) Sp[(kg * nh + 4 * mq + i) * kSub + 16 * pt + ml] = d[i];
           }
           __syncthreads();
-          if (mark) gp(trace)[4] = wall_clock64();
+          if (mark) trace[4] = wall_clock64();
           // running max and sum: half a wave per head
           for (int hp = wave; hp < (nh >> 1); hp += kWaves) {
             const int h = 2 * hp + (lane >> 5), pl = lane & 31;
@@ -2011,7 +2027,7 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
             }
           }
           __syncthreads();
-          if (mark) gp(trace)[5] = wall_clock64();
+          if (mark) trace[5] = wall_clock64();
           // values on the matrix cores: A = weights [16 heads][32 positions] (bf16 high and low
           // parts), B = cache rows [32 positions][16 columns]; wave -> column tiles 4 wave + ct
           {
@@ -2048,7 +2064,7 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
         }
       }
       __syncthreads();
-      if (trace && tid == 0 && task == (int)blockIdx.x && t == 0) gp(trace)[3] = wall_clock64();
+      if (trace && tid == 0 && task == (int)blockIdx.x && t == 0) trace[3] = wall_clock64();
       // values to LDS [nh][kvl] (the query's space), then to the partials in 16-byte rows
       float* Ut = Qt;
 #pragma unroll
@@ -2176,6 +2192,7 @@ struct Smem {
   unsigned long long hmax[MK_MAX_M];  // greedy steps: this workgroup's argmax keys of the LM head
   int amx[MK_MAX_M];
   int abort;
+  uint64_t stamps[2][kTraceStamps];  // trace stamps of the current and the previous record
 };
 
 enum PhaseType : int { PT_GEMV = 0, PT_ATTN_GQA, PT_ATTN_MLA, PT_MERGE, PT_KDA, PT_EXPERT };
@@ -2612,6 +2629,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       sm.rope[(t * kMaxRopePairs + j) * 2 + 1] = (float)sin(a);
     }
     fetch_layer(p, sm.lyd, 0);
+    if (tid_x() < 2 * kTraceStamps) (&sm.stamps[0][0])[tid_x()] = 0;
     if (tid_x() == 0) {  // no routed experts until a routing phase fills the queues (dense: never)
       sm.route.nu = 0;
       sm.route.ustart[0] = 0;
@@ -2638,25 +2656,25 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       // workgroup while it requests them after the poll). The routed-expert phase waits first
       // (routing needs every router logit). The weight rows are requested at one place so the
       // buffers are never copied.
-      barrier_arrive(p, gen);
-      uint64_t* trec = p.trace ? p.trace + ((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps : nullptr;
+      barrier_arrive(p, gen, (LdsU64*)sm.stamps);
+      LdsU64* trec = p.trace ? (LdsU64*)sm.stamps + ((gen - 1) & 1) * kTraceStamps : nullptr;
       const int type = rfl(describe<AF>(p, l, i, g, &sm.route, ly));
       if (l == p.L) {  // LM head: logits optional on greedy steps, per-workgroup argmax keys
         if (tid_x() < MK_MAX_M) sm.hmax[tid_x()] = 0ull;
         g.hmax = p.greedy ? sm.hmax : nullptr;
       }
       scalarize(g);
-      if (trec && tid_x() == 0) gp(trec)[10] = wall_clock64();
+      if (trec && tid_x() == 0) trec[10] = wall_clock64();
       const bool early = type == PT_GEMV;  // prepared while waiting
       if (!early) {
         if constexpr (AF != MK_ATTN_GQA)
           if (type == PT_ATTN_MLA) mla_prefetch_rows(p, ly, sm.buf);
-        if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort);
+        if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort, (LdsU64*)sm.stamps);
         MK_FINISH();
-        if (trec && tid_x() == 0) gp(trec)[7] = wall_clock64();
+        if (trec && tid_x() == 0) trec[7] = wall_clock64();
         if (type == PT_EXPERT) {
           compute_route(p, ws, l, &sm.route, sm.rsel, sm.rw, sm.cnt);
-          if (trec && tid_x() == 0) gp(trec)[6] = wall_clock64();
+          if (trec && tid_x() == 0) trec[6] = wall_clock64();
           g.rt = &sm.route;
           g.ntasks = rfl(sm.route.nu * p.F);
         }
@@ -2664,19 +2682,19 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       if (type == PT_GEMV || type == PT_EXPERT) {
         if constexpr (MF) {
           q = mmake_plan<MM>(g, sm.buf);
-          if (trec && tid_x() == 0) gp(trec)[11] = wall_clock64();
+          if (trec && tid_x() == 0) trec[11] = wall_clock64();
           mgemv_preload(g, q, b0, b1);
         } else {
           q = make_plan<MM>(g, sm.buf);
-          if (trec && tid_x() == 0) gp(trec)[11] = wall_clock64();
+          if (trec && tid_x() == 0) trec[11] = wall_clock64();
           gemv_preload(g, q, b0, b1);
         }
       }
       if (early) {
-        if (trec && tid_x() == 0) gp(trec)[9] = wall_clock64();
-        if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort);
+        if (trec && tid_x() == 0) trec[9] = wall_clock64();
+        if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort, (LdsU64*)sm.stamps);
         MK_FINISH();
-        if (trec && tid_x() == 0) gp(trec)[7] = wall_clock64();
+        if (trec && tid_x() == 0) trec[7] = wall_clock64();
       }
       switch (type) {
         case PT_GEMV:
@@ -2727,12 +2745,12 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
                                  __HIP_MEMORY_SCOPE_AGENT);
       }
       wait_vm();
-      if (trec && tid_x() == 0) gp(trec)[8] = wall_clock64();
+      if (trec && tid_x() == 0) trec[8] = wall_clock64();
     }
   }
   if (p.greedy || p.sample) {  // one more barrier: every row's logits (or argmax keys) are complete
-    barrier_arrive(p, gen);
-    if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort);
+    barrier_arrive(p, gen, (LdsU64*)sm.stamps);
+    if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort, (LdsU64*)sm.stamps);
     MK_FINISH();
   }
   if (p.sample) {
@@ -2757,13 +2775,14 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       }
     }
   }
-  if (p.trace) {
+  if (p.trace) {  // the last record, and one more holding the time the workgroup finished the step
     __syncthreads();
-    if (tid_x() == 0) {
-      uint64_t* tr = p.trace + ((size_t)gen * gridDim.x + blockIdx.x) * kTraceStamps;
-      const uint64_t now = wall_clock64();
-      for (int k = 0; k < kTraceStamps; ++k) gp(tr)[k] = now;
-    }
+    const int lane = tid_x();
+    if (lane < kTraceStamps)
+      gp(p.trace)[((size_t)(gen - 1) * gridDim.x + blockIdx.x) * kTraceStamps + lane] =
+          ((LdsU64*)sm.stamps)[((gen - 1) & 1) * kTraceStamps + lane];
+    const uint64_t now = wall_clock64();
+    if (lane < kTraceStamps) gp(p.trace)[((size_t)gen * gridDim.x + blockIdx.x) * kTraceStamps + lane] = now;
   }
 }
 

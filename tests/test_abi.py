@@ -355,3 +355,23 @@ def test_static_step_limits_on_host(mk):
     finally:
         mk.mk_destroy(ctx)
 
+
+def test_stream_probe_exports_and_arguments():
+    """libmkstream.so (the benchmark's read-bandwidth probe) exports what include/mk_stream.h declares,
+    and refuses bad arguments before launching anything."""
+    import ctypes
+
+    text = open(os.path.join(ROOT, "include", "mk_stream.h")).read()
+    declared = sorted(set(re.findall(r"^\s*int\s+(mk_\w+)\s*\(", text, re.M)))
+    path = os.path.join(ROOT, "decode_megakernel_cu_amd", "libmkstream.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True)
+    exported = sorted(l.split()[-1] for l in out.stdout.splitlines() if " T " in l and l.split()[-1].startswith("mk_"))
+    assert declared == exported == ["mk_stream_read"]
+    L = ctypes.CDLL(path)
+    L.mk_stream_read.restype = ctypes.c_int
+    L.mk_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    ok_ptr = 1 << 20  # 256-byte aligned; never dereferenced, every call below fails validation
+    for args in [(None, 16384, 0, ok_ptr), (ok_ptr, 16384, 0, None), (ok_ptr + 16, 16384, 0, ok_ptr),
+                 (ok_ptr, 0, 0, ok_ptr), (ok_ptr, 16385, 0, ok_ptr), (ok_ptr, 16384, 4, ok_ptr),
+                 (ok_ptr, 16384, -1, ok_ptr), (ok_ptr, (1 << 40) + 16384, 0, ok_ptr)]:
+        assert L.mk_stream_read(*args, None) == -1, args
