@@ -2,8 +2,7 @@
 //
 // One launch runs a whole decode step: embedding, every layer's attention block (GQA, MLA over
 // a compressed latent cache, or the gated delta rule) and MoE block, the final norm and the
-// LM head ("700 TPS on Kimi K3: A Case for TPU Megakernels", README and FAQ: the whole decode
-// step as one kernel). The grid is one workgroup per CU; dependent phases are separated by a
+// LM head (the whole decode step as one kernel: "tpu-megakernels README", FAQ). The grid is one workgroup per CU; dependent phases are separated by a
 // grid barrier built from one flag per workgroup (no same-address atomics), polled by one wave
 // with a clock-bounded watchdog so a lost workgroup can never hang the GPU.
 //
@@ -23,9 +22,10 @@
 //
 // Prefetch. The weights of a phase do not depend on activations, so as soon as the workgroup has
 // arrived at the barrier before a GEMV phase, every wave (the polling one included) issues the
-// loads of its first rows of that phase, and only then waits ("layer n+1 loads while layer n
-// computes", the news digests' account of the design); the barrier wait and the input staging
-// then overlap the HBM latency.
+// loads of its first rows of that phase, and only then waits (the next layer's weights already in
+// flight while the current one computes: video description "700 tok/s on a 2.8 Trillion Model: The
+// 92-Layer TPU Megakernel", timestamp "The Choreography: Layer n+1 Loads While Layer n Computes");
+// the barrier wait and the input staging then overlap the HBM latency.
 //
 // Nothing uses float atomics: every output element is owned by exactly one lane, so results are
 // bitwise reproducible from run to run.
@@ -910,7 +910,6 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
         dma_rows4<kCoherent>(ws.r, q.res, g.M, q.nloc, q.nloc,
                   [&](int m, int c) { return ws.off(g.out0 + (size_t)m * g.ldo0 + q.t0 + c); });
       wait_vm();
-      if (trace && sl == 0 && tid == 0) trace[12] = wall_clock64();
       __syncthreads();
       g.stage_finish<MM>(xin, gl, ks, ks, sl == 0, red);
     }
@@ -924,14 +923,12 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
       for (int e = 0; e < q.nelp; e += 2) {
         step_element<MM>(g, q, eg0 + e, cc, pc, k0, ks, xin, b0, a0, a1);
         step_element<MM>(g, q, eg0 + e + 1, cc, pc, k0, ks, xin, b1, a0, a1);
-        if (trace && sl == 0 && e == 0 && tid == 0) trace[13] = wall_clock64();
       }
     }
   }
   if (trace && tid == 0) trace[3] = wall_clock64();
   // epilogue: one thread per task (a task's rows may have been reduced by different lane groups)
   __syncthreads();
-  if (trace && tid == 0) trace[14] = wall_clock64();
   for (int i = tid; i < q.nloc; i += kThreads) {
     float* ac = q.acc + (size_t)i * 2 * MM;
     if (g.stage == S_NORM) {  // the RMS factor of each input row

@@ -255,10 +255,8 @@ int mk_poll(mk_ctx* ctx);
  * (GEMV) or values accumulated (attention), 4 first weight loads issued (GEMV), 5 epilogue written
  * (GEMV), 6 routing done (routed-expert phase), 7 phase entered (the first wave past the barrier),
  * 8 the phase's stores drained, 9 the phase prepared while waiting at its barrier (descriptor,
- * plan, first loads issued), 10 descriptor built, 11 plan built, 12 input copies landed (vector GEMV), 13 first two weight blocks
- * multiplied (vector GEMV, workgroup's first wave), 14 every wave's products reduced (vector GEMV), 15
- * reserved. One extra record per workgroup holds
- * the time it finished the step. */
+ * plan, first loads issued), 10 descriptor built, 11 plan built, 12-15 reserved (0). One extra
+ * record per workgroup holds the time it finished the step. */
 int mk_set_trace(mk_ctx* ctx, int enable);
 
 /* Where the GEMV phases (projections, router, experts, LM head) run. Steps with at least min_rows
