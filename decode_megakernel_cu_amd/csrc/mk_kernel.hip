@@ -498,19 +498,16 @@ struct Gemv {
   __device__ __forceinline__ void epilogue(int t, const float* a0, const float* a1, const float* res, int rs) const {
     switch (kind) {
       case G_STACK: {
-        float* o = out0;
-        int ld_o = ldo0;
-        if (t >= n0 + n1) {
-          o = out2;
-          ld_o = ldo2;
-          t -= n0 + n1;
-        } else if (t >= n0) {
-          o = out1;
-          ld_o = ldo1;
-          t -= n0;
+        // one store loop per output block: a pointer and stride selected per lane would be kept
+        // in a scratch array
+        if (t < n0) {
+          if (out0)
+            for (int k = 0; k < M; ++k) stc(out0 + (size_t)k * ldo0 + t, a0[k]);
+        } else if (t < n0 + n1) {
+          for (int k = 0; k < M; ++k) stc(out1 + (size_t)k * ldo1 + (t - n0), a0[k]);
+        } else {
+          for (int k = 0; k < M; ++k) stc(out2 + (size_t)k * ldo2 + (t - n0 - n1), a0[k]);
         }
-        if (o)
-          for (int k = 0; k < M; ++k) stc(o + (size_t)k * ld_o + t, a0[k]);
         if (hmax)
           for (int k = 0; k < M; ++k)
             __hip_atomic_fetch_max(hmax + k, argmax_key(a0[k], t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -2737,7 +2734,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       }
       if (l == p.L && p.greedy) {  // the workgroup's keys into the device-wide ones
         __syncthreads();
-        if (tid_x() < M && sm.hmax[tid_x()] != 0ull)
+        if (tid_x() < rfl(p.M) && sm.hmax[tid_x()] != 0ull)
           __hip_atomic_fetch_max((GLOBAL unsigned long long*)(p.amax + tid_x()), sm.hmax[tid_x()], __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -2750,13 +2747,16 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
     if (wave_id() == kPollWave) barrier_poll(p, gen, &sm.abort, (LdsU64*)sm.stamps);
     MK_FINISH();
   }
+  // (the step's row count read again from the parameter block: kept live from the start of the
+  // step to here, it would be spilled to scratch memory)
+  const int Mend = rfl(p.M);
   if (p.sample) {
-    for (int m = blockIdx.x; m < M; m += gridDim.x) sample_row(p, m, sm.buf);
+    for (int m = blockIdx.x; m < Mend; m += gridDim.x) sample_row(p, m, sm.buf);
   }
   if (p.greedy) {  // workgroup 0 turns the keys into tokens and accepts drafts
     if (blockIdx.x == 0) {
       const int tid = tid_x();
-      if (tid < M) {
+      if (tid < Mend) {
         const unsigned long long key =
             __hip_atomic_load((GLOBAL unsigned long long*)(p.amax + tid), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int tok = (int)(0xFFFFFFFFu - (uint32_t)key);
