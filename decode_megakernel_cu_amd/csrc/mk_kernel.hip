@@ -1810,14 +1810,18 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
   const int npos = kv_len + T, C = rfl(p.chunk), nsplit = rfl(p.nsplit), ntask = B * nsplit;
   const int tid = tid_x(), lane = lane_id(), wave = wave_id();
   uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);  // [kSub][cst] cache rows (bf16)
-  float* Qt = smem + kSub * cst / 2;                  // [nh][lat] query of one token (fp32), then
-  uint16_t* Qh = reinterpret_cast<uint16_t*>(Qt);     //   its bf16 high parts [nh][lat]
-  uint16_t* Ql = Qh + nh * lat;                       //   and low parts [nh][lat]; finally values [nh][kvl]
-  float* Nw = Qt + nh * lat;                          // [T][lat] new latent rows (values of their bf16)
-  float* Sp = Nw + T * lat;                           // [4][nh][kSub] partial scores of the K groups
-  float* S = Sp + 4 * nh * kSub;                      // [nh][kSub] weights
-  float* st = S + nh * kSub;                          // [nh][4] running max, running sum, rescale
-  float* nrm = st + nh * 4;                           // [8] RMS scale of the new rows
+  // The heads are the rows of 16-row matrix-core tiles: a share with fewer heads (an even number up
+  // to 16) pads them to 16. Padding rows are never filled; they only reach the tiles' padding rows,
+  // whose results are not used.
+  constexpr int nhp = 16;
+  float* Qt = smem + kSub * cst / 2;                  // [nhp][lat] query of one token (fp32), then
+  uint16_t* Qh = reinterpret_cast<uint16_t*>(Qt);     //   its bf16 high parts [nhp][lat]
+  uint16_t* Ql = Qh + nhp * lat;                      //   and low parts [nhp][lat]; finally values [nhp][kvl]
+  float* Nw = Qt + nhp * lat;                         // [T][lat] new latent rows (values of their bf16)
+  float* Sp = Nw + T * lat;                           // [4][nhp][kSub] partial scores of the K groups
+  float* S = Sp + 4 * nhp * kSub;                     // [nhp][kSub] weights
+  float* st = S + nhp * kSub;                         // [nhp][4] running max, running sum, rescale
+  float* nrm = st + nhp * 4;                          // [8] RMS scale of the new rows
   uint16_t* gk = reinterpret_cast<uint16_t*>(nrm + 8);  // [kvl] latent norm gain (bf16)
   uint16_t* Lc = kvc + (size_t)rfl(ly->ord) * Bmax * cap * lat;
   const float scale = 1.0f / sqrtf((float)qd);
@@ -1994,7 +1998,7 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
             }
             // D: column ml (position 16 pt + ml), rows 4 mq + i (heads 4 mq + i of this 16-head block)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Sp[(kg * nh + 4 * mq + i) * kSub + 16 * pt + ml] = d[i];
+            for (int i = 0; i < 4; ++i) Sp[(kg * nhp + 4 * mq + i) * kSub + 16 * pt + ml] = d[i];
           }
           __syncthreads();
           if (mark) trace[4] = wall_clock64();
@@ -2004,7 +2008,7 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
             float sv = -INFINITY;
             if (pl < n) {
               float a = 0.f;
-              for (int k = 0; k < 4; ++k) a += Sp[(k * nh + h) * kSub + pl];
+              for (int k = 0; k < 4; ++k) a += Sp[(k * nhp + h) * kSub + pl];
               sv = a * scale;
             }
             const float cm = wave_max(sv, 32);

@@ -121,6 +121,21 @@ def test_gqa_head_dim_limits(mk, head_dim):
         sizes(mk, replace(synth.TINY, head_dim=ok))
 
 
+@pytest.mark.parametrize("n_heads,ok", [(16, True), (8, True), (12, True), (2, True), (7, False), (18, False),
+                                         (32, False)])
+def test_mla_head_counts(mk, n_heads, ok):
+    # MLA attention puts the heads in the rows of one 16-row matrix-core tile: an even number of heads
+    # up to 16 (a share of the same model over more tensor-parallel ranks has fewer heads)
+    for base in (synth.K3, synth.K3_HYBRID):
+        cfg = replace(base, n_heads=n_heads)
+        if ok:
+            sizes(mk, cfg)
+        else:
+            with pytest.raises(mk.MkError) as e:
+                sizes(mk, cfg)
+            assert e.value.code == mk.MK_E_UNSUPPORTED
+
+
 def test_kv_capacity_limit(mk):
     # the split-KV merge keeps one task's statistics and values for every split (at least 16
     # positions each) in LDS: 921 splits fit, 922 do not

@@ -222,6 +222,17 @@ def test_k3_two_layers(B, T, kv_len):
     parity(K3_SMALL, synth.Spec(seed=2), B, T, kv_len)
 
 
+# a share of the same model over twice the tensor-parallel ranks: 8 heads, padded to the 16 rows of
+# the attention tiles (the absorbed query, the merge and W_uv keep 8)
+@pytest.mark.parametrize("B,T,kv_len", [(1, 1, 4096), (8, 1, 700), (1, 7, 2000)])
+def test_k3_two_layers_eight_heads(B, T, kv_len):
+    parity(replace(K3_SMALL, name="k3-2layer-8heads", n_heads=8), synth.Spec(seed=5), B, T, kv_len)
+
+
+def test_hybrid_four_layers_eight_heads():
+    parity(replace(HYB_SMALL, name="hybrid-4layer-8heads", n_heads=8), synth.Spec(seed=6), 2, 1, 300)
+
+
 def test_k3_two_layers_widest_rope():
     # rope_dim 128, the widest the host admits: 640-wide latent rows fill the register prefetch of
     # the next 32-position sub-tile exactly (2560 units of 16 bytes); batch 4 over 4097 positions
