@@ -617,7 +617,9 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   p.ql = g.q_lora; p.kvl = g.attn_kind == MK_ATTN_GQA ? 0 : g.kv_lora; p.rd = g.rope_dim; p.nd = g.nope_dim;
   p.vd = g.v_dim; p.dk = g.kda_dk; p.dv = g.kda_dv; p.E = g.n_experts; p.topk = g.top_k; p.F = g.ffn;
   p.SF = g.shared_ffn; p.norm_topk = g.norm_topk; p.cap = g.kv_capacity; p.Bmax = g.max_batch;
-  p.family = g.attn_kind;
+  // the MLA family's kernels are built for rope_dim 64; an MLA model with another runs on the
+  // hybrid family's kernels (the same MLA code with the rope dimension as a parameter)
+  p.family = g.attn_kind == MK_ATTN_MLA && g.rope_dim != 64 ? MK_ATTN_HYBRID : g.attn_kind;
   p.eps = g.rms_eps; p.rope_theta = g.rope_theta;
   p.B = B; p.T = T; p.M = M; p.kv_len = kv_len;
   p.chunk = chunk;
