@@ -1479,9 +1479,10 @@ __device__ __forceinline__ void rope_pair(const float* table, int t, int j, floa
 // are padded to 8 LDS banks apart and key, query and score rows to 4, which keeps every operand
 // read free of bank conflicts. The unnormalised value sums stay in registers: tile j of the
 // (row tile, 16-column tile) grid belongs to wave j % 8, rescaled as each row's maximum moves.
+template <int HD>
 __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
                                                const float* rope, LdsU64* trace) {
-  const int d = p.hd, nq = p.nh, nkv = p.nkv, T = p.T, cap = p.cap, d2 = d / 2, d4 = d / 4, d8 = d / 8;
+  const int d = HD ? HD : p.hd, nq = p.nh, nkv = p.nkv, T = p.T, cap = p.cap, d2 = d / 2, d4 = d / 4, d8 = d / 8;
   const int npos = p.kv_len + T, C = p.chunk, nsplit = p.nsplit, kvl = p.kv_len;
   const int qg = nq / nkv, nr = T * qg, nrt = (nr + 15) >> 4, nrp = 16 * nrt;
   const int nct = d >> 4, nvt = nrt * nct;  // value tiles: row tiles x column tiles
@@ -2717,7 +2718,8 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         case PT_ATTN_GQA:
           if constexpr (AF == MK_ATTN_GQA) {
             if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
-            gqa_attn_phase(p, ly, ws, sm.buf, sm.rope, trec);
+            if (p.hd == 128) gqa_attn_phase<128>(p, ly, ws, sm.buf, sm.rope, trec);
+            else gqa_attn_phase<0>(p, ly, ws, sm.buf, sm.rope, trec);
             resident = false;
           }
           break;
