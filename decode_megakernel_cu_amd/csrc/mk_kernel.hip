@@ -1479,14 +1479,14 @@ __device__ __forceinline__ void rope_pair(const float* table, int t, int j, floa
 // are padded to 8 LDS banks apart and key, query and score rows to 4, which keeps every operand
 // read free of bank conflicts. The unnormalised value sums stay in registers: tile j of the
 // (row tile, 16-column tile) grid belongs to wave j % 8, rescaled as each row's maximum moves.
-template <int HD>
+template <int HD, bool ONE>
 __device__ __forceinline__ void gqa_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
                                                const float* rope, LdsU64* trace) {
-  const int d = HD ? HD : p.hd, nq = p.nh, nkv = p.nkv, T = p.T, cap = p.cap, d2 = d / 2, d4 = d / 4, d8 = d / 8;
+  const int d = HD ? HD : p.hd, nq = p.nh, nkv = p.nkv, T = ONE ? 1 : p.T, cap = p.cap, d2 = d / 2, d4 = d / 4, d8 = d / 8;
   const int npos = p.kv_len + T, C = p.chunk, nsplit = p.nsplit, kvl = p.kv_len;
   const int qg = nq / nkv, nr = T * qg, nrt = (nr + 15) >> 4, nrp = 16 * nrt;
   const int nct = d >> 4, nvt = nrt * nct;  // value tiles: row tiles x column tiles
-  const int ntask = p.B * nkv * nsplit;
+  const int ntask = (ONE ? 1 : p.B) * nkv * nsplit;
   const int tid = tid_x(), lane = lane_id(), wave = wave_id(), ml = lane & 15, mq = lane >> 4;
   const int dk = d + 8;   // bf16 per staged key row and per query row (hi, lo)
   const int dv = d + 16;  // bf16 per staged value row
@@ -1797,13 +1797,13 @@ __device__ __forceinline__ void mla_prefetch_rows(const Params& p, const LayerDe
 // RD: the rope dimension when it is known at compile time (64 in the MLA family's instances, whose
 // models all have it), else 0 (read from the parameters: the hybrid family's instances, which also
 // run MLA models of other rope dimensions). Constant row strides and loop bounds take about 3% off
-// the K3-scale share's batch-1 step.
-template <int RD>
+// the K3-scale share's batch-1 step. ONE: the 1-row instance (one sequence, one new token).
+template <int RD, bool ONE>
 __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem,
                                                const float* rope, LdsU64* trace) {
   static_assert(kSub == 32, "score lanes map one position each in a half wave");
   // step values in scalar registers (read from the parameter block in LDS)
-  const int kv_len = rfl(p.kv_len), Bmax = rfl(p.Bmax), B = rfl(p.B);
+  const int kv_len = rfl(p.kv_len), Bmax = rfl(p.Bmax), B = ONE ? 1 : rfl(p.B);
   const float eps = rflf(p.eps);
   const float* a2 = rflp(p.a2);
   const float* a3 = rflp(p.a3);
@@ -1811,7 +1811,7 @@ __device__ __forceinline__ void mla_attn_phase(const Params& p, const LayerDev* 
   float* part = rflp(p.part);
   uint16_t* kvc = rflp(p.kv);
   constexpr int kvl = 512;  // the host admits kv_lora 512 only (a constant stride: 1% of the step)
-  const int nh = rfl(p.nh), rd = RD ? RD : rfl(p.rd), nd = rfl(p.nd), T = rfl(p.T), cap = rfl(p.cap);
+  const int nh = rfl(p.nh), rd = RD ? RD : rfl(p.rd), nd = rfl(p.nd), T = ONE ? 1 : rfl(p.T), cap = rfl(p.cap);
   const int lat = kvl + rd, qd = nd + rd, h2 = rd / 2, half = lat / 2;
   const int cst = lat + 8;  // bf16 per staged cache row: 16-byte aligned rows, banks staggered by 4
   const int npos = kv_len + T, C = rfl(p.chunk), nsplit = rfl(p.nsplit), ntask = B * nsplit;
@@ -2607,7 +2607,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   const char* wsb = rflp(p.wsb);
   const Ws ws{make_rsrc(wsb, (uint32_t)rfl((int)p.ws_bytes)), wsb};
   uint32_t gen = 0;
-  const int M = p.M, H = p.H;
+  const int M = MM == 1 ? 1 : p.M, H = p.H;
   const int rpairs = ((p.kvl > 0) ? p.rd : p.hd) / 2;
 
   // ---- embedding rows and the RoPE table of this step's positions ----
@@ -2669,6 +2669,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         g.hmax = p.greedy ? sm.hmax : nullptr;
       }
       scalarize(g);
+      if constexpr (MM == 1) g.M = 1;  // the 1-row instance runs one token row
       if (trec && tid_x() == 0) trec[10] = wall_clock64();
       const bool early = type == PT_GEMV;  // prepared while waiting
       if (!early) {
@@ -2718,15 +2719,15 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         case PT_ATTN_GQA:
           if constexpr (AF == MK_ATTN_GQA) {
             if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
-            if (p.hd == 128) gqa_attn_phase<128>(p, ly, ws, sm.buf, sm.rope, trec);
-            else gqa_attn_phase<0>(p, ly, ws, sm.buf, sm.rope, trec);
+            if (p.hd == 128) gqa_attn_phase<128, MM == 1 && !MF>(p, ly, ws, sm.buf, sm.rope, trec);
+            else gqa_attn_phase<0, MM == 1 && !MF>(p, ly, ws, sm.buf, sm.rope, trec);
             resident = false;
           }
           break;
         case PT_ATTN_MLA:
           if constexpr (AF != MK_ATTN_GQA) {
             if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
-            mla_attn_phase<AF == MK_ATTN_MLA ? 64 : 0>(p, ly, ws, sm.buf, sm.rope, trec);
+            mla_attn_phase<AF == MK_ATTN_MLA ? 64 : 0, MM == 1 && !MF>(p, ly, ws, sm.buf, sm.rope, trec);
             resident = false;
           }
           break;
