@@ -464,6 +464,8 @@ def main():
                     help="turn two rocprofv3 counter_collection CSVs (FETCH_SIZE, WRITE_SIZE) of a --calib run "
                          "into profiles/megakernel_{k3,dense}_pmc_traffic.json (by --workload) and exit")
     args = ap.parse_args()
+    if args.trace and not os.environ.get("MK_LIBRARY"):  # the build with the stamp code compiled in
+        os.environ["MK_LIBRARY"] = os.path.join(ROOT, "decode_megakernel_cu_amd", "libmk_trace.so")
     if args.ingest_pmc:
         ingest_pmc(*args.ingest_pmc, workload="dense" if args.workload == "dense" else "c3")
         return

@@ -18,6 +18,7 @@
 
 namespace mk {
 size_t kernel_lds_bytes();
+bool device_trace_built();
 hipError_t launch_decode(const Params& p, int nblocks, bool matrix_cores, hipStream_t stream);
 hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd, int kvl, hipStream_t stream);
 hipError_t occupancy(int* blocks_per_cu);
@@ -699,6 +700,9 @@ int mk_decode_step_static(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_
 
 int mk_set_trace(mk_ctx* c, int enable) {
   if (!c) return fail(MK_E_INVAL, "context is NULL");
+  if (enable && !device_trace_built())
+    return fail(MK_E_UNSUPPORTED, "this build has no device tracing: libmk_trace.so (the same sources built with "
+                "MK_DEVICE_TRACE) records it");
   c->trace = enable != 0;
   g_err.clear();
   return MK_OK;

@@ -38,6 +38,15 @@
 
 using namespace mk;
 
+// Device tracing (mk_set_trace): per-phase wall-clock stamps. Compiled in only with MK_DEVICE_TRACE
+// (the library libmk_trace.so): even when switched off at run time, the stamp code's checks and the
+// pointer they test cost about 2.4% of the K3-scale share's batch-1 step.
+#ifdef MK_DEVICE_TRACE
+constexpr bool kTrace = true;
+#else
+constexpr bool kTrace = false;
+#endif
+
 // Pointers into device memory are marked global so that loads and stores compile to global_*
 // instructions: flat ones would also count against the LDS counter, and the barrier's LDS wait
 // would then wait for prefetched weights.
@@ -280,7 +289,7 @@ __device__ __forceinline__ void barrier_arrive(const Params& p, uint32_t& gen, L
   wg_barrier();
   if (wave_id() == kPollWave) {
     const int lane = lane_id();
-    if (p.trace) {  // copy out the previous record and clear its row for the record after this one
+    if (kTrace && p.trace) {  // copy out the previous record and clear its row for the record after this one
       if (lane < kTraceStamps) {
         LdsU64* prev = stamps + (gen & 1) * kTraceStamps;
         if (gen >= 2) gp(p.trace)[((size_t)(gen - 2) * gridDim.x + blockIdx.x) * kTraceStamps + lane] = prev[lane];
@@ -296,7 +305,7 @@ __device__ __forceinline__ void barrier_arrive(const Params& p, uint32_t& gen, L
 __device__ __forceinline__ void barrier_poll(const Params& p, uint32_t gen, int* s_abort, LdsU64* stamps) {
   const uint32_t target = p.epoch + gen;
   const int lane = lane_id();
-  LdsU64* tr = p.trace ? stamps + ((gen - 1) & 1) * kTraceStamps : nullptr;
+  LdsU64* tr = kTrace && p.trace ? stamps + ((gen - 1) & 1) * kTraceStamps : nullptr;
   const uint64_t t0 = wall_clock64();
   int abort = 0;
   while (true) {
@@ -2662,7 +2671,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       // (routing needs every router logit). The weight rows are requested at one place so the
       // buffers are never copied.
       barrier_arrive(p, gen, (LdsU64*)sm.stamps);
-      LdsU64* trec = p.trace ? (LdsU64*)sm.stamps + ((gen - 1) & 1) * kTraceStamps : nullptr;
+      LdsU64* trec = kTrace && p.trace ? (LdsU64*)sm.stamps + ((gen - 1) & 1) * kTraceStamps : nullptr;
       const int type = rfl(describe<AF>(p, l, i, g, &sm.route, ly));
       if (l == p.L) {  // LM head: logits optional on greedy steps, per-workgroup argmax keys
         if (tid_x() < MK_MAX_M) sm.hmax[tid_x()] = 0ull;
@@ -2785,7 +2794,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
       }
     }
   }
-  if (p.trace) {  // the last record, and one more holding the time the workgroup finished the step
+  if (kTrace && p.trace) {  // the last record, and one more holding the time the workgroup finished the step
     __syncthreads();
     const int lane = tid_x();
     if (lane < kTraceStamps)
@@ -2847,6 +2856,8 @@ hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t stream) {
   hipLaunchKernelGGL(clear_words, dim3(1), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
+
+bool device_trace_built() { return kTrace; }
 
 size_t kernel_lds_bytes() { return sizeof(Smem) + sizeof(Params); }
 int max_grid() { return kMaxGrid; }

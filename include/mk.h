@@ -256,7 +256,9 @@ int mk_poll(mk_ctx* ctx);
  * (GEMV), 6 routing done (routed-expert phase), 7 phase entered (the first wave past the barrier),
  * 8 the phase's stores drained, 9 the phase prepared while waiting at its barrier (descriptor,
  * plan, first loads issued), 10 descriptor built, 11 plan built, 12-15 reserved (0). One extra
- * record per workgroup holds the time it finished the step. */
+ * record per workgroup holds the time it finished the step. Tracing is compiled into the library
+ * built with MK_DEVICE_TRACE (libmk_trace.so) only: the default build returns MK_E_UNSUPPORTED for
+ * enable != 0 (its kernels carry no stamp code, which is 2.4% faster). */
 int mk_set_trace(mk_ctx* ctx, int enable);
 
 /* Where the GEMV phases (projections, router, experts, LM head) run. Steps with at least min_rows

@@ -35,6 +35,27 @@ def test_every_declared_symbol_is_exported(mk):
         assert hasattr(mk.lib, n)
 
 
+def test_traced_build_exports_the_same_symbols(mk):
+    # libmk_trace.so: the same sources with the per-phase stamp code compiled in
+    path = os.path.join(ROOT, "decode_megakernel_cu_amd", "libmk_trace.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True)
+    exported = set(l.split()[-1] for l in out.stdout.splitlines() if " T " in l)
+    for n in declared_functions():
+        assert n in exported, n
+
+
+def test_default_build_refuses_tracing(mk, host_ctx):
+    # the default library carries no stamp code: enabling tracing is refused, disabling is fine
+    _, ctx = host_ctx
+    if os.path.basename(mk.LIB_PATH) != "libmk.so":
+        pytest.skip("another build of the library is loaded")
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_set_trace(ctx, True)
+    assert e.value.code == mk.MK_E_UNSUPPORTED
+    assert "MK_DEVICE_TRACE" in mk.mk_last_error()
+    mk.mk_set_trace(ctx, False)
+
+
 def test_library_is_gfx950():
     import decode_megakernel_cu_amd as mk
 
