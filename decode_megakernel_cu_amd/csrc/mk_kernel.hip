@@ -2616,7 +2616,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   const char* wsb = rflp(p.wsb);
   const Ws ws{make_rsrc(wsb, (uint32_t)rfl((int)p.ws_bytes)), wsb};
   uint32_t gen = 0;
-  const int M = MM == 1 ? 1 : p.M, H = p.H;
+  const int M = MM <= 2 ? MM : p.M, H = p.H;
   const int rpairs = ((p.kvl > 0) ? p.rd : p.hd) / 2;
 
   // ---- embedding rows and the RoPE table of this step's positions ----
@@ -2678,7 +2678,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         g.hmax = p.greedy ? sm.hmax : nullptr;
       }
       scalarize(g);
-      if constexpr (MM == 1) g.M = 1;  // the 1-row instance runs one token row
+      if constexpr (MM <= 2) g.M = MM;  // the 1- and 2-row instances run exactly that many token rows
       if (trec && tid_x() == 0) trec[10] = wall_clock64();
       const bool early = type == PT_GEMV;  // prepared while waiting
       if (!early) {
