@@ -241,6 +241,14 @@ def test_k3_two_layers_widest_rope():
     parity(cfg, synth.Spec(seed=9), 4, 1, 4096)
 
 
+@pytest.mark.parametrize("B,T,kv_len", [(1, 1, 4096), (1, 7, 600)])
+def test_k3_two_layers_rope128_on_hybrid_kernels(B, T, kv_len):
+    # an MLA model whose rope dimension is not 64 runs on the hybrid family's kernels: the 1-row
+    # instance and the matrix-core verify instance of that family
+    cfg = replace(K3_SMALL, name="k3-2layer-rope128", rope_dim=128)
+    parity(cfg, synth.Spec(seed=10), B, T, kv_len)
+
+
 def test_k3_two_layers_batch8_vector_units():
     parity(K3_SMALL, synth.Spec(seed=2), 8, 1, 33, mfma_min_rows=VECTOR_ONLY)
 
@@ -250,7 +258,9 @@ def test_k3_two_layers_peaked_mla():
     parity(K3_SMALL, spec, 2, 3, 300)
 
 
-@pytest.mark.parametrize("B,T", [(8, 1), (2, 3)])
+# (1, 1): the 1-row instance of the hybrid family (its MLA layer with the rope dimension read from
+# the parameters, one token row as a compile-time constant)
+@pytest.mark.parametrize("B,T", [(8, 1), (2, 3), (1, 1)])
 def test_hybrid_four_layers(B, T):
     parity(HYB_SMALL, synth.Spec(seed=4), B, T, 517)
 
