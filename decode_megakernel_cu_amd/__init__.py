@@ -17,6 +17,7 @@ LIB_PATH = os.environ.get("MK_LIBRARY") or os.path.join(_HERE, "libmk.so")
 MK_OK, MK_E_INVAL, MK_E_STATE, MK_E_KV_OVERFLOW, MK_E_NOMEM, MK_E_HIP, MK_E_DEVICE, MK_E_UNSUPPORTED = (
     0, -1, -2, -3, -4, -5, -6, -7)
 MK_MAX_M, MK_MAX_BATCH, MK_MAX_NEW_TOKENS, MK_DEVICE_NONE = 16, 8, 8, -1
+MK_MAX_KV_CAPACITY = 1 << 20
 
 # weight kinds, in the order of mk_weight_kind
 KINDS = ["embed", "final_norm", "lm_head", "attn_norm", "wq", "wk", "wv", "wo", "w_dq", "q_norm", "w_uq",

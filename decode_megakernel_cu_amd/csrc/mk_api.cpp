@@ -71,6 +71,12 @@ struct Layout {
   int nsplit_max = 0;
 };
 
+// Split-KV chunks per (sequence, kv head) that a step can have: a chunk holds at least kChunk
+// positions and at least the step's cache rows divided by the grid, so there is at most one
+// chunk per workgroup of the grid whatever the sequence length. The merge's LDS batches and the
+// workspace's partial results are sized for this many.
+int max_splits(int kv_capacity) { return std::min((kv_capacity + kChunk - 1) / kChunk, max_grid()); }
+
 int check_config(const mk_config* c) {
   if (!c) return fail(MK_E_INVAL, "config is NULL");
   if (c->preset < 0 || c->preset > 6) return fail(MK_E_INVAL, "preset %d is not 0 (custom) or a preset id 1..6", c->preset);
@@ -126,9 +132,12 @@ int check_config(const mk_config* c) {
         return fail(MK_E_UNSUPPORTED, "kda_dk must be 64 or 128 and kda_dv a multiple of 8");
     }
   }
+  // cache rows are addressed through 32-bit buffer ranges of one (layer, sequence) each
+  if (c->kv_capacity > MK_MAX_KV_CAPACITY)
+    return fail(MK_E_UNSUPPORTED, "kv_capacity %d above %d", c->kv_capacity, MK_MAX_KV_CAPACITY);
   // the split-KV merge holds in LDS, for one task, the statistics of every split of two (m, head)
   // units (4 floats each) and 32 values per split
-  if (40LL * ((c->kv_capacity + kChunk - 1) / kChunk) > kLdsFloats)
+  if (40LL * max_splits(c->kv_capacity) > kLdsFloats)
     return fail(MK_E_UNSUPPORTED, "kv_capacity %d too large for the split-KV merge", c->kv_capacity);
   return MK_OK;
 }
@@ -279,7 +288,7 @@ Layout make_layout(const mk_config& c) {
   Lt.state = (uint64_t)Lt.n_kda * Bm * c.n_heads * c.kda_dk * c.kda_dv * 4;
 
   // workspace: sized for the largest step of the model
-  Lt.nsplit_max = (c.kv_capacity + kChunk - 1) / kChunk;
+  Lt.nsplit_max = max_splits(c.kv_capacity);
   Lt.ws = ws_layout(c, (uint64_t)std::min(MK_MAX_M, c.max_batch * c.max_new_tokens), Lt.nsplit_max, true);
   return Lt;
 }
@@ -657,6 +666,7 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   const uint64_t dmax = g.attn_kind == MK_ATTN_GQA ? g.head_dim : std::max(g.kv_lora, g.kda_dv);
   if ((uint64_t)M * nh * p.nsplit * (dmax + kPartPad) > w.part_floats)
     return fail(MK_E_UNSUPPORTED, "attention partials exceed the workspace");
+  if (p.nsplit > c->lt.nsplit_max) return fail(MK_E_UNSUPPORTED, "%d split-KV chunks, at most %d", p.nsplit, c->lt.nsplit_max);
   hipError_t e = hipSetDevice(c->device);
   if (e == hipSuccess && use_static)  // barrier flags and status words start at zero
     e = launch_clear_words(p.flags, (int)((w.status + 64 * 4 - w.flags) / 4), static_cast<hipStream_t>(stream));

@@ -39,6 +39,7 @@ extern "C" {
 #define MK_MAX_M 16          /* batch * new tokens per step */
 #define MK_MAX_BATCH 8
 #define MK_MAX_NEW_TOKENS 8
+#define MK_MAX_KV_CAPACITY (1 << 20)  /* cache positions per sequence */
 #define MK_DEVICE_NONE (-1)  /* host-only context: validates and lays out, never launches */
 #define MK_TRACE_STAMPS 16   /* wall-clock stamps per trace record */
 
@@ -71,9 +72,10 @@ typedef enum { MK_ATTN_GQA = 0, MK_ATTN_MLA = 1, MK_ATTN_HYBRID = 2 } mk_attn_ki
  * README", FAQ: the dense BF16 decoder served beside the MoE model). Its layers have one grid
  * phase fewer (no routed-expert phase).
  * expert_pool_layers > 0: layer l uses the expert weights of pool slot l % expert_pool_layers.
- * kv_capacity is at most 14736 positions (921 split-KV chunks of 16): the merge of the chunks'
- * partial softmax results holds one task's statistics and values for every chunk in LDS;
- * larger capacities return MK_E_UNSUPPORTED. */
+ * kv_capacity is at most MK_MAX_KV_CAPACITY positions (larger returns MK_E_UNSUPPORTED). A step
+ * splits each sequence's positions into at most one split-KV chunk per workgroup of the grid
+ * (at most 256), whatever the length, so the merge of the chunks' partial softmax results and
+ * the workspace that holds them do not grow with kv_capacity. */
 typedef struct {
   int32_t preset;  /* informational: the mk_config_preset id this description came from, 0 for a custom model */
   int32_t n_layers, hidden, vocab, attn_kind;

@@ -158,14 +158,17 @@ def test_mla_head_counts(mk, n_heads, ok):
 
 
 def test_kv_capacity_limit(mk):
-    # the split-KV merge keeps one task's statistics and values for every split (at least 16
-    # positions each) in LDS: 921 splits fit, 922 do not
-    sizes(mk, replace(synth.TINY, kv_capacity=921 * 16))
-    sizes(mk, replace(synth.K3, kv_capacity=921 * 16))
-    for c in (synth.TINY, synth.K3):
+    # a step has at most one split-KV chunk per workgroup of the grid (256), so the merge's LDS and
+    # the workspace do not grow with the capacity: up to 2^20 positions are admitted, and the
+    # workspace of a 2^20-position context equals that of a 4104-position one
+    for c in (synth.TINY, synth.K3, synth.DENSE):
+        big = sizes(mk, replace(c, kv_capacity=mk.MK_MAX_KV_CAPACITY))
+        assert big.kv_bytes == sizes(mk, c).kv_bytes * mk.MK_MAX_KV_CAPACITY // c.kv_capacity
         with pytest.raises(mk.MkError) as e:
-            sizes(mk, replace(c, kv_capacity=921 * 16 + 1))
+            sizes(mk, replace(c, kv_capacity=mk.MK_MAX_KV_CAPACITY + 1))
         assert e.value.code == mk.MK_E_UNSUPPORTED
+    assert (sizes(mk, replace(synth.K3, kv_capacity=mk.MK_MAX_KV_CAPACITY)).workspace_bytes
+            == sizes(mk, replace(synth.K3, kv_capacity=4104)).workspace_bytes)
 
 
 def test_dense_layout_and_loading(mk):

@@ -249,6 +249,16 @@ def test_k3_two_layers_rope128_on_hybrid_kernels(B, T, kv_len):
     parity(cfg, synth.Spec(seed=10), B, T, kv_len)
 
 
+# contexts longer than 921 chunks of 16 positions: the chunks grow with the context (one per
+# workgroup at most), so the merge sees at most 256 splits. 20000 positions at batch 1: 209 splits
+# of 96 positions; 30000 at batch 2: 118 splits of 256; 131072 at batch 1: 241 splits of 544
+# (17 sub-tiles each); the 7-token verify over 50000 positions: 224 splits of 224
+@pytest.mark.parametrize("B,T,kv_len", [(1, 1, 20000), (2, 1, 30000), (1, 1, 131072), (1, 7, 50000)])
+def test_k3_two_layers_long_context(B, T, kv_len):
+    cfg = replace(K3_SMALL, name="k3-2layer-long", max_batch=2, kv_capacity=131080)
+    parity(cfg, synth.Spec(seed=31), B, T, kv_len)
+
+
 def test_k3_two_layers_batch8_vector_units():
     parity(K3_SMALL, synth.Spec(seed=2), 8, 1, 33, mfma_min_rows=VECTOR_ONLY)
 
@@ -356,6 +366,14 @@ def test_tiny_dense_ragged_rows():
 @pytest.mark.parametrize("B,T", [(1, 1), (8, 1), (1, 7)])
 def test_dense_two_layers(B, T):
     parity(DENSE_SMALL, synth.Spec(seed=20), B, T, 4096)
+
+
+# GQA over 40000 positions: 8 kv heads, 32 splits of 1264 positions per (sequence, kv head); and
+# batch 2 over 60000 (16 splits of 3760)
+@pytest.mark.parametrize("B,kv_len", [(1, 40000), (2, 60000)])
+def test_dense_two_layers_long_context(B, kv_len):
+    cfg = replace(DENSE_SMALL, name="dense-2layer-long", max_batch=2, kv_capacity=60008)
+    parity(cfg, synth.Spec(seed=32), B, 1, kv_len)
 
 
 # --------------------------------------------------------------------------------------------
