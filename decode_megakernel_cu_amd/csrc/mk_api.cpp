@@ -142,27 +142,30 @@ int check_config(const mk_config* c) {
   return MK_OK;
 }
 
+int instance_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+
 // Whether every GEMV phase of a step with M token rows fits the LDS carve-up of the kernel (mf: the
 // matrix-core executor): per workgroup share of nloc tasks, the task accumulators (3 x MM floats
-// per task) and one partial slot per accumulator tile plus one per wave (MM floats; a 16x16 tile
-// on the matrix cores, whose tiles are groups of 16 tasks) at the end of the buffer; before them
-// the staged input, at least one slab (8 columns; 32 on the matrix cores, rows padded by 4 floats)
-// of each staged row, or the whole window of per-head phases.
+// per task) and one partial slot per accumulator tile plus one per wave (MM floats; on the matrix
+// cores the S blocks of R x R floats of a 16x16 tile whose row and column segments match, the
+// tiles being groups of R = 16 / S tasks, S the instance's column segments) at the end of the buffer; before them the staged input, at least one slab (8 columns;
+// 32 S on the matrix cores, rows padded by 4 floats) of each staged row, or the whole window of
+// per-head phases.
 bool step_fits(const mk_config& c, int M, int nb, bool mf) {
   if (nb < 1) return true;
-  const long long MM = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
-  const long long pslot = mf ? 256 : MM, pad = mf ? 4 : 0, minw = mf ? 32 : 8;
+  const long long MM = instance_rows(M), S = mfma_segments((int)MM), R = 16 / S;
+  const long long pslot = mf ? 256 / S : MM, pad = mf ? 4 : 0, minw = mf ? 32 * S : 8;
   auto cap_of = [&](long long nloc, long long nat) {
     return (long long)kLdsFloats - nloc * 3 * MM - (nat + kWaves) * pslot - 8;
   };
-  auto groups = [&](long long nloc) { return mf ? (nloc + 15) / 16 : nloc; };
+  auto groups = [&](long long nloc) { return mf ? (nloc + R - 1) / R : nloc; };
   // pairs: weight-row kinds per task; down: the down projection (one accumulator tile per group)
   auto ok = [&](long long ntasks, long long rows, long long pairs, bool norm, bool down = false) {
     const long long nloc = (ntasks + nb - 1) / nb, ng = groups(nloc);
     return cap_of(nloc, down ? ng : ng * pairs) >= rows * (minw + pad) + (norm ? minw / 2 : 0);
   };
   auto ok_off = [&](long long ntasks, long long rph, long long seg) {
-    const long long nloc = mf ? 16 * ((ntasks / 16 + nb - 1) / nb) : (ntasks + nb - 1) / nb;
+    const long long nloc = mf ? R * ((ntasks / R + nb - 1) / nb) : (ntasks + nb - 1) / nb;
     const long long window = ((nloc + rph - 1) / rph + 1) * seg;
     return cap_of(nloc, groups(nloc)) >= M * (window + pad);
   };
@@ -181,17 +184,19 @@ bool step_fits(const mk_config& c, int M, int nb, bool mf) {
   return good;
 }
 
-// Whether the matrix-core GEMV executor can run every GEMV phase of this model: row lengths in
-// whole 32-column units, per-head rows in whole groups of 16 inside one head.
-bool mfma_shapes(const mk_config& c) {
+// Whether the matrix-core GEMV executor can run every GEMV phase of this model in the instance for
+// M token rows: row lengths in whole units of 32 S columns (S the instance's column segments),
+// per-head rows in whole groups of 16 inside one head.
+bool mfma_shapes(const mk_config& c, int M) {
   const long long H = c.hidden, F = c.ffn, SF = c.shared_ffn, nh = c.n_heads;
-  bool ok = H % 32 == 0 && F % 32 == 0 && SF % 32 == 0;
+  const long long u = 32LL * mfma_segments(instance_rows(M));
+  bool ok = H % u == 0 && F % u == 0 && SF % u == 0;
   if (c.attn_kind == MK_ATTN_GQA) {
-    ok = ok && (nh * c.head_dim) % 32 == 0;
+    ok = ok && (nh * c.head_dim) % u == 0;
   } else {
-    ok = ok && c.q_lora % 32 == 0 && c.nope_dim % 32 == 0 && c.kv_lora % 32 == 0 && (nh * c.v_dim) % 32 == 0 &&
+    ok = ok && c.q_lora % u == 0 && c.nope_dim % u == 0 && c.kv_lora % u == 0 && (nh * c.v_dim) % u == 0 &&
          c.kv_lora % 16 == 0 && c.v_dim % 16 == 0;
-    if (c.attn_kind == MK_ATTN_HYBRID) ok = ok && (nh * c.kda_dv) % 32 == 0;
+    if (c.attn_kind == MK_ATTN_HYBRID) ok = ok && (nh * c.kda_dv) % u == 0;
   }
   return ok;
 }
@@ -588,7 +593,7 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   if (!greedy && !d_logits) return fail(MK_E_INVAL, "logits must be non-NULL");
   if (g.attn_kind == MK_ATTN_HYBRID && !d_kda_state) return fail(MK_E_INVAL, "hybrid model needs the delta-rule state");
   const int M = B * T;
-  const bool mf = M >= c->mfma_min_rows && mfma_shapes(g) && step_fits(g, M, c->nblocks, true);
+  const bool mf = M >= c->mfma_min_rows && mfma_shapes(g, M) && step_fits(g, M, c->nblocks, true);
   if (!mf && !step_fits(g, M, c->nblocks, false))
     return fail(MK_E_UNSUPPORTED, "a phase of this step does not fit the workgroup's LDS");
   // split-KV: chunks (at least kChunk positions) sized so that the tasks of the step about fill the grid

@@ -20,6 +20,11 @@ constexpr int kMaxExperts = 256;
 constexpr int kTraceStamps = MK_TRACE_STAMPS;
 constexpr int kMaxRopePairs = 64;
 constexpr int kMaxQueue = MK_MAX_M * 8;  // token-expert pairs per step (top_k <= 8)
+// Column segments of a matrix-core tile in the instance for at most mm token rows: a 16x16x32
+// multiply takes 16 / S weight rows x S consecutive 32-column segments as its 16 A rows and
+// 16 / S token rows x the same S segments as its 16 B columns (only the products of matching
+// segments are used), so that one load instruction reads 16 / S rows x 64 S contiguous bytes.
+constexpr int mfma_segments(int mm) { return mm <= 4 ? 4 : mm <= 8 ? 2 : 1; }
 // The allocation-free step's workspace: a device array of the library, one per GPU, held until the
 // process ends (mk_decode_step_static). 64 MiB covers every step of the preset models.
 constexpr uint64_t kStaticScratchBytes = 64ull << 20;

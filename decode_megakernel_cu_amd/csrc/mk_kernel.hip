@@ -1074,25 +1074,35 @@ __device__ __forceinline__ void compute_route(const Params& p, const Ws& ws, int
 // Matrix-core GEMV executor (steps with several input rows)
 //
 // From a few input rows on, the vector executor above spends more issue slots on multiply-adds
-// and LDS reads than the weight stream allows; here the products run on the matrix cores. Weight rows are taken 16 at a time: for each 32-column unit a lane loads 16 bytes of one
-// row (lane l: row l % 16, columns 8 (l / 16) .. +8 of the unit) -- the A operand of a
-// 16x16x32 bf16 multiply as it comes from memory -- and the B operand holds the same 32 columns of
-// up to 16 input rows. The inputs are staged in LDS as fp32 and then rewritten in place, each run
-// of 8 columns as its bf16 high parts followed by the bf16 of the remainders (x = hi + lo to about
-// 16 significant bits), so two multiplies per unit give the products of the bf16 weights with the
-// fp32 inputs, accumulated in fp32.
+// and LDS reads than the weight stream allows; here the products run on the matrix cores.
 //
-// A tile is one group of 16 output rows and one of its weight-row kinds (SwiGLU gate or up; for
+// Column segments. An instance for at most MM input rows uses S = mfma_segments(MM) segments
+// (4 up to 4 rows, 2 up to 8, 1 above): a unit is 32 S columns, and the 16 A rows of a 16x16x32
+// bf16 multiply are R = 16 / S weight rows x S segments of 32 columns (A row s R + r: weight row r,
+// columns 32 s .. +32 of the unit), the 16 B columns are R input rows x the same S segments. Of the
+// 16x16 products only the S diagonal blocks where the A row's segment is the B column's are
+// used; their sum over segments is the dot over the unit. Lane l loads 16 bytes of weight row
+// (l % 16) % R, segment (l % 16) / R, columns 8 (l / 16) .. +8 of the segment: one load
+// instruction reads R rows x 64 S contiguous bytes (S = 1: 16 rows x 64 bytes, which streams
+// at about 5.1 TB/s here against 6.6 for 1 KB of one row; S = 4: 4 rows x 256 bytes). A
+// multiply still consumes 1 KB of weights, so S does not change the multiply count.
+//
+// The inputs are staged in LDS as fp32 and then rewritten in place, each run of 8 columns as its
+// bf16 high parts followed by the bf16 of the remainders (x = hi + lo to about 16 significant
+// bits), so two multiplies per unit give the products of the bf16 weights with the fp32 inputs,
+// accumulated in fp32.
+//
+// A tile is one group of R output rows and one of its weight-row kinds (SwiGLU gate or up; for
 // the down projection, each routed expert and the shared expert). The tiles' units form one
 // sequence, cut into eight contiguous ranges, one per wave; a wave streams its range in elements
 // of up to kNC units within one tile through the same two register buffers as the vector executor
 // (an element's loads are issued two elements ahead, the first two before the phase's barrier),
-// and writes its partial 16x16 result of each tile (each output group, for the down projection)
-// to its own LDS slot. After a slab the slots of each tile are summed in wave order -- a fixed
-// order, so results do not depend on timing -- into the same per-task accumulators the vector
-// executor fills, and the same epilogues write the outputs.
+// and writes the used blocks of its partial result of each tile (each output group, for the down
+// projection) to its own LDS slot. After a slab the slots of each tile are summed in wave order,
+// then segment order -- a fixed order, so results do not depend on timing -- into the same
+// per-task accumulators the vector executor fills, and the same epilogues write the outputs.
 //
-// Shapes: every row length and slab width is a multiple of 32 columns, and per-head rows (G_OFF)
+// Shapes: every row length and slab width is a multiple of 32 S columns, and per-head rows (G_OFF)
 // come in whole groups of 16 inside one head; the host launches this executor only then.
 // ----------------------------------------------------------------------------------------------
 struct MPlan {
@@ -1100,7 +1110,7 @@ struct MPlan {
   bool one_slab;
   float* acc;    // [nloc][2][MM] task accumulators
   float* res;    // [M][nloc] residual inputs
-  float* piece;  // [nat + kWaves][16 columns][16 rows] partial tiles, slot = acc tile + wave
+  float* piece;  // [nat + kWaves][S][R columns][R rows] partial tiles (the matching-segment blocks), slot = acc tile + wave
 };
 
 // A slab's unit counts: per tile (nuk), or for the down projection per routed-expert tile (ne) and
@@ -1109,20 +1119,23 @@ struct MGeo {
   int k0, ks, nuk, ne, ns, pg, U;
 };
 
+// (S: column segments per tile; a unit is 32 S columns)
+template <int S>
 __device__ __forceinline__ MGeo mgeo(const Gemv& g, const MPlan& q, int slab) {
+  constexpr int lu = S == 4 ? 7 : S == 2 ? 6 : 5;
   MGeo e;
   e.k0 = slab * q.KS;
   e.ks = imin(q.KS, q.Wst - e.k0);
   if (g.kind == G_DOWN) {
-    e.ne = imax(0, imin(g.F - e.k0, e.ks)) >> 5;
-    e.ns = g.SF > 0 ? imax(0, imin(g.SF - e.k0, e.ks)) >> 5 : 0;
+    e.ne = imax(0, imin(g.F - e.k0, e.ks)) >> lu;
+    e.ns = g.SF > 0 ? imax(0, imin(g.SF - e.k0, e.ks)) >> lu : 0;
     e.pg = rfl(g.rt->nu) * e.ne + e.ns;
     e.nuk = 0;
     e.U = q.ngrp * e.pg;
   } else {
     int len = e.ks;
     if (g.kind == G_OFF) len = g.seg;
-    e.nuk = len >> 5;
+    e.nuk = len >> lu;
     e.ne = e.ns = 0;
     e.pg = g.pairs * e.nuk;
     e.U = q.ngrp * e.pg;
@@ -1145,23 +1158,24 @@ __device__ __forceinline__ int wave_start(const MGeo& e, int w) { return (w * e.
 
 template <int MM>
 __device__ __forceinline__ MPlan mmake_plan(const Gemv& g, float* smem) {
+  constexpr int S = mfma_segments(MM), R = 16 / S;
   MPlan q;
   const unsigned gb = blockIdx.x, gn = gridDim.x;
   const bool offs = g.kind == G_OFF;
   int t1;
-  if (offs) {  // whole groups of 16 rows, so that a group never spans two heads
-    const unsigned ng = (unsigned)g.ntasks >> 4;
-    q.t0 = 16 * (int)(ng * gb / gn);
-    t1 = 16 * (int)(ng * (gb + 1) / gn);
+  if (offs) {  // whole groups of R rows, so that a group never spans two heads
+    const unsigned ng = (unsigned)g.ntasks / R;
+    q.t0 = R * (int)(ng * gb / gn);
+    t1 = R * (int)(ng * (gb + 1) / gn);
   } else {
     const unsigned nt = (unsigned)g.ntasks;
     q.t0 = (int)(nt * gb / gn);
     t1 = (int)(nt * (gb + 1) / gn);
   }
   q.nloc = t1 - q.t0;
-  q.ngrp = (q.nloc + 15) >> 4;
+  q.ngrp = (q.nloc + R - 1) / R;
   q.nat = g.kind == G_DOWN ? q.ngrp : q.ngrp * g.pairs;
-  const int in_cap = (kLdsFloats - q.nloc * 3 * MM - (q.nat + kWaves) * 256) & ~7;
+  const int in_cap = (kLdsFloats - q.nloc * 3 * MM - (q.nat + kWaves) * (256 / S)) & ~7;
   q.acc = smem + in_cap;
   q.res = q.acc + q.nloc * 2 * MM;
   q.piece = q.res + q.nloc * MM;
@@ -1177,10 +1191,10 @@ __device__ __forceinline__ MPlan mmake_plan(const Gemv& g, float* smem) {
     q.nslab = 1;
   } else {
     // staged rows at a stride of KS + 4 floats, then (S_NORM) the slab's gain in bf16
-    int cap = ((2 * (in_cap - 4 * rows)) / (2 * rows + (g.stage == S_NORM ? 1 : 0))) & ~31;
-    if (cap < 32) cap = 32;
+    int cap = ((2 * (in_cap - 4 * rows)) / (2 * rows + (g.stage == S_NORM ? 1 : 0))) & ~(32 * S - 1);
+    if (cap < 32 * S) cap = 32 * S;
     q.nslab = cdiv(q.Wst, cap);
-    q.KS = (cdiv(q.Wst, q.nslab) + 31) & ~31;  // balanced slabs
+    q.KS = (cdiv(q.Wst, q.nslab) + 32 * S - 1) & ~(32 * S - 1);  // balanced slabs
   }
   if (q.nloc == 0) q.nslab = 0;
   q.DS = q.KS + 4;
@@ -1198,11 +1212,12 @@ struct MCur {
 // (The cursor functions take and return cursors by value: stores to different fields of a
 // referenced cursor on different paths would be merged into one store through a selected address,
 // and the cursor would then live in scratch memory.)
+template <int S>
 __device__ __forceinline__ MCur mcur_slab(const Gemv& g, const MPlan& q, int slab) {
   const int w = wave_id();
   MCur c;
   for (; slab < q.nslab; ++slab) {
-    const MGeo e = mgeo(g, q, slab);
+    const MGeo e = mgeo<S>(g, q, slab);
     const int s = wave_start(e, w), t = wave_start(e, w + 1);
     if (t > s) {
       int j, us;
@@ -1229,13 +1244,14 @@ __device__ __forceinline__ MCur mcur_slab(const Gemv& g, const MPlan& q, int sla
   return c;
 }
 
+template <int S>
 __device__ __forceinline__ MCur madvance(const Gemv& g, const MPlan& q, const MCur& c0) {
   const int slab = c0.slab, n = c0.n;
   if (slab >= q.nslab) return c0;
-  if (n == 0) return mcur_slab(g, q, slab + 1);  // after the padding element
+  if (n == 0) return mcur_slab<S>(g, q, slab + 1);  // after the padding element
   const int rem = c0.rem - n, cnt = c0.cnt ^ 1;
   if (rem == 0) {
-    if (cnt == 0) return mcur_slab(g, q, slab + 1);
+    if (cnt == 0) return mcur_slab<S>(g, q, slab + 1);
     MCur c;  // the padding element keeps the slab's element count even
     c.slab = slab;
     c.j = c0.j;
@@ -1245,7 +1261,7 @@ __device__ __forceinline__ MCur madvance(const Gemv& g, const MPlan& q, const MC
     c.cnt = 0;
     return c;
   }
-  const MGeo e = mgeo(g, q, slab);
+  const MGeo e = mgeo<S>(g, q, slab);
   int j = c0.j, us = c0.us + n;
   if (us == tile_units(g, e, j)) {
     us = 0;
@@ -1262,44 +1278,51 @@ __device__ __forceinline__ MCur madvance(const Gemv& g, const MPlan& q, const MC
   return c;
 }
 
-// Issue the loads of element c into b: lane l reads row l % 16 of the tile's group at columns
-// 8 (l / 16) .. +8 of each unit (rows the workgroup does not own, and kinds a row lacks, read a
-// valid dummy address; their results are never used).
+// Issue the loads of element c into b: lane l reads row (l % 16) % R of the tile's group (R = 16 / S
+// rows), segment (l % 16) / R, columns 8 (l / 16) .. +8 of the segment, of each unit (rows the
+// workgroup does not own, and kinds a row lacks, read a valid dummy address; their results are
+// never used).
+template <int S>
 __device__ __forceinline__ void mload_element(const Gemv& g, const MPlan& q, const MCur& c, RowBuf& b) {
-  const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
+  constexpr int R = 16 / S;
+  const int lane = lane_id(), r = lane & (R - 1), sg = (lane & 15) / R, kq = lane >> 4;
   const uint16_t* w = g.safe;
   bool ok = false;
   if (c.slab < q.nslab && c.n > 0) {
-    const int gi = c.j / g.pairs, which = c.j - gi * g.pairs, i = gi * 16 + r;
+    const int gi = c.j / g.pairs, which = c.j - gi * g.pairs, i = gi * R + r;
     if (i < q.nloc) {
       const RowRef rr = g.row(q.t0 + i, which);
       if (rr.w) {
-        w = rr.w + c.slab * q.KS + 32 * c.us + 8 * kq;
+        w = rr.w + c.slab * q.KS + 32 * S * c.us + 32 * sg + 8 * kq;
         ok = true;
       }
     }
   }
 #pragma unroll
-  for (int u = 0; u < kNC; ++u) b.v[u] = ldw(ok && u < c.n ? w + 32 * u : g.safe);
+  for (int u = 0; u < kNC; ++u) b.v[u] = ldw(ok && u < c.n ? w + 32 * S * u : g.safe);
 }
 
+template <int S>
 __device__ __forceinline__ void mgemv_preload(const Gemv& g, const MPlan& q, RowBuf& b0, RowBuf& b1) {
-  MCur c = mcur_slab(g, q, 0);
-  mload_element(g, q, c, b0);
-  c = madvance(g, q, c);
-  mload_element(g, q, c, b1);
+  MCur c = mcur_slab<S>(g, q, 0);
+  mload_element<S>(g, q, c, b0);
+  c = madvance<S>(g, q, c);
+  mload_element<S>(g, q, c, b1);
 }
 
 // Consume the element at cc from b (its slab is staged in xs), then reuse b for the element at pc
-// (two ahead); a partial tile goes to its slot when the next element belongs to another.
+// (two ahead); a partial tile goes to its slot when the next element belongs to another. B column
+// n holds input row n % R at segment n / R of each unit.
+template <int S>
 __device__ __forceinline__ void mstep(const Gemv& g, const MPlan& q, MCur& cc, MCur& pc, const float* xs, RowBuf& b,
                                       f32x4& dt) {
-  const int lane = lane_id(), m = lane & 15, kq = lane >> 4;
+  constexpr int R = 16 / S;
+  const int lane = lane_id(), m = lane & 15, kq = lane >> 4, mt = m & (R - 1), sg = m / R;
   if (cc.n > 0) {
     const int gi = cc.j / g.pairs, which = cc.j - gi * g.pairs;
-    int brow = imin(m, g.M - 1);  // columns past the last input row repeat it; their results are unused
+    int brow = imin(mt, g.M - 1);  // columns past the last input row repeat it; their results are unused
     uint32_t keep = ~0u;
-    int col = 32 * cc.us + 8 * kq;
+    int col = 32 * S * cc.us + 32 * sg + 8 * kq;
     if (g.kind == G_DOWN) {
       const int nu = rfl(g.rt->nu);
       if (which < nu) {  // this expert's (token, weight) pair of the column's token, if any
@@ -1307,7 +1330,7 @@ __device__ __forceinline__ void mstep(const Gemv& g, const MPlan& q, MCur& cc, M
         bool has = false;
         int ps = 0;
         for (int s = s0; s < s1; ++s) {
-          if (g.rt->ptok[s] == m) {
+          if (g.rt->ptok[s] == mt) {
             ps = s;
             has = true;
           }
@@ -1318,28 +1341,32 @@ __device__ __forceinline__ void mstep(const Gemv& g, const MPlan& q, MCur& cc, M
         brow += g.np;
       }
     } else if (g.kind == G_OFF) {
-      col += ((q.t0 + 16 * gi) / g.rph) * g.seg - q.wbase;
+      col += ((q.t0 + R * gi) / g.rph) * g.seg - q.wbase;
     }
     const float* xp = xs + brow * q.DS + col;
 #pragma unroll
     for (int u = 0; u < kNC; ++u) {
       if (u < cc.n) {
-        const u32x4 h = *reinterpret_cast<const u32x4*>(xp + 32 * u) & keep;
-        const u32x4 l = *reinterpret_cast<const u32x4*>(xp + 32 * u + 4) & keep;
+        const u32x4 h = *reinterpret_cast<const u32x4*>(xp + 32 * S * u) & keep;
+        const u32x4 l = *reinterpret_cast<const u32x4*>(xp + 32 * S * u + 4) & keep;
         const bf16x8 a = as_bf16x8(u32x4{b.v[u].x, b.v[u].y, b.v[u].z, b.v[u].w});
         dt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(h), dt, 0, 0, 0);
         dt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(l), dt, 0, 0, 0);
       }
     }
   }
-  mload_element(g, q, pc, b);
+  mload_element<S>(g, q, pc, b);
   const MCur old = cc;
-  cc = madvance(g, q, cc);
-  pc = madvance(g, q, pc);
+  cc = madvance<S>(g, q, cc);
+  pc = madvance<S>(g, q, pc);
   if (old.n > 0 && (cc.slab != old.slab || cc.n == 0 || acc_tile(g, cc.j) != acc_tile(g, old.j))) {
-    // lane l holds column l % 16, rows 4 (l / 16) .. +4 of the tile
-    f32x4* slot = reinterpret_cast<f32x4*>(q.piece + (size_t)(acc_tile(g, old.j) + wave_id()) * 256 + m * 16 + 4 * kq);
-    *slot = dt;
+    // lane l holds column l % 16, rows 4 (l / 16) .. +4 of the tile; only the blocks where the row's
+    // segment is the column's are kept
+    if ((4 * kq) / R == sg) {
+      f32x4* slot = reinterpret_cast<f32x4*>(q.piece + (size_t)(acc_tile(g, old.j) + wave_id()) * (256 / S) +
+                                             (sg * R + mt) * R + ((4 * kq) & (R - 1)));
+      *slot = dt;
+    }
     dt = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
@@ -1388,6 +1415,7 @@ __device__ __forceinline__ void mconvert(const Gemv& g, float* xs, const uint16_
 template <int MM>
 __device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGeo& e, bool first, bool last,
                                         const float* red) {
+  constexpr int S = mfma_segments(MM), R = 16 / S;
   const int na = g.kind == G_DOWN ? 1 : g.pairs;
   const int n = na * MM * q.nloc;
   for (int x = tid_x(); x < n; x += kThreads) {
@@ -1400,7 +1428,7 @@ __device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGe
     } else if (k >= g.M) {
       continue;
     }
-    const int gi = i >> 4, r = i & 15;
+    const int gi = i / R, r = i & (R - 1);
     const int at = g.kind == G_DOWN ? gi : gi * g.pairs + a;
     int len = e.nuk;
     if (g.kind == G_DOWN) len = e.pg;
@@ -1408,7 +1436,10 @@ __device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGe
     float v = 0.f;
     for (int w = 0; w < kWaves; ++w) {  // the waves whose (non-empty) ranges meet the tile
       const int ws = wave_start(e, w), we = wave_start(e, w + 1);
-      if (we > ws && ws < u1 && we > u0) v += q.piece[(size_t)(at + w) * 256 + col * 16 + r];
+      if (we > ws && ws < u1 && we > u0) {  // the products of matching segments (A row, B column sg R + .)
+#pragma unroll
+        for (int sg = 0; sg < S; ++sg) v += q.piece[(size_t)(at + w) * (256 / S) + (sg * R + col) * R + r];
+      }
     }
     float* ac = q.acc + (size_t)i * 2 * MM + a * MM + k;
     if (!first) v += *ac;
@@ -1427,12 +1458,13 @@ __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const
   const bool keep = keep_in && q.one_slab;
   const bool resid = g.kind == G_RESID || g.kind == G_DOWN;
   const int rows = g.stage == S_DOWN ? g.np + g.M : g.M;
-  MCur cc = mcur_slab(g, q, 0);
-  MCur pc = madvance(g, q, madvance(g, q, cc));
+  constexpr int S = mfma_segments(MM);
+  MCur cc = mcur_slab<S>(g, q, 0);
+  MCur pc = madvance<S>(g, q, madvance<S>(g, q, cc));
   f32x4 dt = {0.f, 0.f, 0.f, 0.f};
   if (trace && tid == 0) trace[4] = trace[2] = wall_clock64();
   for (int sl = 0; sl < q.nslab; ++sl) {
-    const MGeo e = mgeo(g, q, sl);
+    const MGeo e = mgeo<S>(g, q, sl);
     __syncthreads();
     uint16_t* gl = reinterpret_cast<uint16_t*>(xs + rows * q.DS);
     if (!keep) {
@@ -1447,8 +1479,8 @@ __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const
     __syncthreads();
     if (trace && sl == 0 && tid == 0) trace[2] = wall_clock64();
     while (cc.slab == sl) {
-      mstep(g, q, cc, pc, xs, b0, dt);
-      mstep(g, q, cc, pc, xs, b1, dt);
+      mstep<S>(g, q, cc, pc, xs, b0, dt);
+      mstep<S>(g, q, cc, pc, xs, b1, dt);
     }
     __syncthreads();
     mreduce<MM>(g, q, e, sl == 0, sl == q.nslab - 1, red);
@@ -2698,7 +2730,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         if constexpr (MF) {
           q = mmake_plan<MM>(g, sm.buf);
           if (trec && tid_x() == 0) trec[11] = wall_clock64();
-          mgemv_preload(g, q, b0, b1);
+          mgemv_preload<mfma_segments(MM)>(g, q, b0, b1);
         } else {
           q = make_plan<MM>(g, sm.buf);
           if (trec && tid_x() == 0) trec[11] = wall_clock64();
