@@ -250,15 +250,18 @@ PHASES = {
     "kda": ["qkv", "delta_rule", "w_o"],
 }
 MOE_PHASES = ["router+shared_up", "experts_up", "experts_down"]
+# 1- and 2-row steps fold the router onto the attention output projection: two MoE phases
+MOE_PHASES_FUSED = ["shared+experts_up", "experts_down"]
 DENSE_PHASES = ["gate+up", "down"]  # n_experts = 0: the SwiGLU block alone
 
 
-def phase_names(cfg) -> list[str]:
+def phase_names(cfg, fused: bool = False) -> list[str]:
     names = ["embed"]
     for l in range(cfg.n_layers):
         kind = cfg.layer_kind(l)
         if cfg.n_experts:
-            names += [f"{kind}:{p}" for p in PHASES[kind]] + [f"moe:{p}" for p in MOE_PHASES]
+            moe = MOE_PHASES_FUSED if fused else MOE_PHASES
+            names += [f"{kind}:{p}" for p in PHASES[kind]] + [f"moe:{p}" for p in moe]
         else:
             names += [f"{kind}:{p}" for p in PHASES[kind]] + [f"ffn:{p}" for p in DENSE_PHASES]
     return names + ["lm_head"]
@@ -271,6 +274,8 @@ def trace_summary(cfg, tr: np.ndarray, tick_ns: float = 10.0) -> dict:
     workgroups of the differences between its stamps (a stamp of 0 means the phase has no such
     mark)."""
     names = phase_names(cfg)
+    if tr.shape[0] < len(names) and cfg.n_experts:  # a step with the router folded: one MoE phase fewer per layer
+        names = phase_names(cfg, fused=True)
     t = tr.astype(np.int64)
     arr, dep = t[:, :, 0], t[:, :, 1]
     t0 = arr[0].min()

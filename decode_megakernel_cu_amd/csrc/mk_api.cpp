@@ -21,6 +21,8 @@ size_t kernel_lds_bytes();
 bool device_trace_built();
 hipError_t launch_decode(const Params& p, int nblocks, bool matrix_cores, hipStream_t stream);
 hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd, int kvl, hipStream_t stream);
+hipError_t launch_fold_router(const uint16_t* router, const uint16_t* gain, const uint16_t* wo, float* out, int E, int H,
+                              int K, hipStream_t stream);
 hipError_t occupancy(int* blocks_per_cu);
 int max_grid();
 hipError_t static_scratch(int device, void** out);
@@ -65,6 +67,7 @@ struct Layout {
   std::map<Key, Slot> tensors;
   std::vector<LayerDev> layers;  // offsets (as pointers relative to 0) until rebased
   uint64_t arena = 0;
+  uint64_t derived = 0;  // bytes of the arena holding tensors derived at load time (rwx)
   WsLayout ws{};
   uint64_t kv = 0, state = 0;
   int n_mla = 0, n_kda = 0, n_gqa = 0;
@@ -203,6 +206,29 @@ bool mfma_shapes(const mk_config& c, int M) {
 
 WsLayout ws_layout(const mk_config& c, uint64_t M, uint64_t nsplit, bool trace);
 
+// input width of layer l's attention output projection
+uint64_t wo_width(const mk_config& c, int l) {
+  const int k = layer_kind(c, l);
+  return (uint64_t)c.n_heads * (k == kGqa ? c.head_dim : k == kMla ? c.v_dim : c.kda_dv);
+}
+
+// Whether a step of M token rows on the vector executor folds the router onto the attention output
+// projection (see Params::rfuse): a MoE model, at most two rows, and the output projection's LDS
+// carve-up (per workgroup: its task accumulators, the staged input, the layer input's M rows and
+// its router rows) fits every layer.
+bool router_fusion(const mk_config& c, int M, int nb) {
+  if (c.n_experts <= 0 || M > 2 || nb < 1) return false;
+  const long long E = c.n_experts, MM = instance_rows(M), H = c.hidden;
+  const long long P = std::max(1LL, std::min(8LL, nb / E)), nr = P > 1 ? 1 : (E + nb - 1) / nb;
+  const long long nloc = (H + nb - 1) / nb;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const long long K = (long long)wo_width(c, l), span = 4 * (((H + K) / 4 + P - 1) / P);
+    const long long cap = ((long long)kLdsFloats - nloc * 3 * MM) & ~7LL;
+    if (M * K + M * span + nr * span > cap) return false;
+  }
+  return true;
+}
+
 Layout make_layout(const mk_config& c) {
   Layout Lt;
   const uint64_t H = c.hidden, V = c.vocab, E = c.n_experts, F = c.ffn, SF = c.shared_ffn;
@@ -258,7 +284,14 @@ Layout make_layout(const mk_config& c) {
       d.wo = rel(put(MK_W_WO, l, -1, H * nh * dv * 2));
     }
     d.moe_norm = rel(put(MK_W_MOE_NORM, l, -1, H * 2));
-    if (E) d.router = rel(put(MK_W_ROUTER, l, -1, E * H * 2));
+    if (E) {
+      d.router = rel(put(MK_W_ROUTER, l, -1, E * H * 2));
+      // derived, not loaded (no slot of the tensor map): the router folded onto W_o
+      const uint64_t rb = E * (H + wo_width(c, l)) * 4;
+      d.rwx = reinterpret_cast<const float*>(off);
+      off = align_up(off + rb);
+      Lt.derived += align_up(rb);
+    }
     if (SF) {
       d.sh_gate = rel(put(MK_W_SH_GATE, l, -1, SF * H * 2));
       d.sh_up = rel(put(MK_W_SH_UP, l, -1, SF * H * 2));
@@ -335,6 +368,8 @@ WsLayout ws_layout(const mk_config& c, uint64_t M, uint64_t nsplit, bool trace) 
   w.trace = take(w.trace_slots * kTraceStamps * 8);
   w.rope = take((uint64_t)MK_MAX_NEW_TOKENS * kMaxRopePairs * 2 * 4);
   w.x = take(M * H * 4);
+  w.x2 = take(M * H * 4);
+  w.ssq = take(M * kMaxBlocks * 4);
   w.a1 = take(M * w1 * 4);
   w.a2 = take(M * w2 * 4);
   w.a3 = take(M * w3 * 4);
@@ -343,7 +378,8 @@ WsLayout ws_layout(const mk_config& c, uint64_t M, uint64_t nsplit, bool trace) 
   w.o2 = take(M * std::max<uint64_t>(wo2, 1) * 4);
   w.part = take(part * 4);
   w.part_floats = part;
-  w.rlog = take(M * E * 4);
+  // router logits; with router fusion up to 8 partial logits per (row, expert), E * 8 <= 8 * grid
+  w.rlog = take(M * std::max<uint64_t>(E * 8, kMaxBlocks) * 4);
   w.sact = take(M * std::max<uint64_t>(SF, 1) * 4);
   w.eact = take(M * c.top_k * F * 4);
   w.amax = take(M * 8);
@@ -500,6 +536,7 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
       for (auto p : ps)
         if (*p) *p = reinterpret_cast<const uint16_t*>(base + reinterpret_cast<uintptr_t>(*p));
       if (d.alpha) d.alpha = reinterpret_cast<const float*>(base + reinterpret_cast<uintptr_t>(d.alpha));
+      if (d.rwx) d.rwx = reinterpret_cast<const float*>(base + reinterpret_cast<uintptr_t>(d.rwx));
       if (d.beta) d.beta = reinterpret_cast<const float*>(base + reinterpret_cast<uintptr_t>(d.beta));
     }
     e = hipMemcpy(c->arena, tab.data(), sizeof(LayerDev) * tab.size(), hipMemcpyHostToDevice);
@@ -554,6 +591,22 @@ int mk_load_weights(mk_ctx* c, const mk_tensor_desc* d, int n, void* stream) {
     if (!c->loaded[idx]) {
       c->loaded[idx] = 1;
       c->n_loaded++;
+    }
+    // a MoE layer's folded router, once its three factors are in the arena (again whenever one of
+    // them is replaced)
+    if ((t.kind == MK_W_ROUTER || t.kind == MK_W_MOE_NORM || t.kind == MK_W_WO) && c->cfg.n_experts > 0 &&
+        c->device != MK_DEVICE_NONE) {
+      const int l = t.layer;
+      const Key kr(MK_W_ROUTER, l, -1), kg(MK_W_MOE_NORM, l, -1), ko(MK_W_WO, l, -1);
+      if (c->loaded[c->index[kr]] && c->loaded[c->index[kg]] && c->loaded[c->index[ko]]) {
+        const LayerDev& d = c->lt.layers[l];
+        auto at = [&](const void* rel) { return c->arena + reinterpret_cast<uintptr_t>(rel); };
+        const hipError_t e = launch_fold_router(
+            reinterpret_cast<const uint16_t*>(at(d.router)), reinterpret_cast<const uint16_t*>(at(d.moe_norm)),
+            reinterpret_cast<const uint16_t*>(at(d.wo)), reinterpret_cast<float*>(at(d.rwx)), c->cfg.n_experts,
+            c->cfg.hidden, (int)wo_width(c->cfg, l), st);
+        if (e != hipSuccess) return fail(MK_E_HIP, "folded router of layer %d failed: %s", l, hipGetErrorString(e));
+      }
     }
   }
   g_err.clear();
@@ -652,6 +705,8 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   auto f = [&](uint64_t o) { return reinterpret_cast<float*>(ws + o); };
   p.rope = f(w.rope); p.x = f(w.x); p.a1 = f(w.a1); p.a2 = f(w.a2); p.a3 = f(w.a3); p.a4 = f(w.a4);
   p.att = f(w.att); p.o2 = f(w.o2); p.part = f(w.part); p.rlog = f(w.rlog); p.sact = f(w.sact); p.eact = f(w.eact);
+  p.x2 = f(w.x2); p.ssq = f(w.ssq);
+  p.rfuse = !mf && router_fusion(g, M, c->nblocks) && !std::getenv("MK_NO_ROUTER_FUSION") ? 1 : 0;
   p.wsb = reinterpret_cast<const char*>(ws);
   p.ws_bytes = (uint32_t)w.total;
   p.watchdog_ticks = c->watchdog_ticks;
@@ -680,9 +735,9 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   if (!use_static) c->launches++;
   c->last_status = ws + w.status;
   int nb = (greedy || smp) ? 2 : 1;  // the LM head's barrier, and the one before greedy or sampled tokens
-  for (int l = 0; l < g.n_layers; ++l) {  // attention phases, then 3 MoE phases (dense: 2)
+  for (int l = 0; l < g.n_layers; ++l) {  // attention phases, then 3 MoE phases (router fusion, dense: 2)
     const int k = layer_kind(g, l);
-    nb += (k == kGqa ? 4 : k == kMla ? 7 : 3) + (g.n_experts ? 3 : 2);
+    nb += (k == kGqa ? 4 : k == kMla ? 7 : 3) + (g.n_experts && !p.rfuse ? 3 : 2);
   }
   c->last_barriers = use_static ? 0 : nb;  // a static step records no trace
   g_err.clear();

@@ -41,13 +41,17 @@ struct alignas(16) LayerDev {
   const uint16_t *kwq, *kwk, *kwv;                                  // KDA
   const float *alpha, *beta;
   const uint16_t *exp_gate, *exp_up, *exp_down;                     // pool slot base, [E][F][H] / [E][H][F]
-  const void* pad2;                                                 // size a multiple of 16 (copied in 16-byte units)
+  // MoE layers: the router folded onto the attention block's output projection, derived from router,
+  // moe_norm and wo when all three are loaded. Row e: [W_r[e][t] g[t] for t < H | sum over t of
+  // W_r[e][t] g[t] W_o[t][j] for j < K] (fp32; K the output projection's input width), so that the
+  // router logit of x + W_o o before the norm's 1/rms factor is row e . [x | o].
+  const float* rwx;
 };
 static_assert(sizeof(LayerDev) % 16 == 0, "layer table rows are copied in 16-byte units");
 
 // Workspace carve-up (byte offsets from the workspace base).
 struct WsLayout {
-  uint64_t flags, status, trace, rope, x, a1, a2, a3, a4, att, o2, part, rlog, sact, eact, amax, scratch, total;
+  uint64_t flags, status, trace, rope, x, x2, ssq, a1, a2, a3, a4, att, o2, part, rlog, sact, eact, amax, scratch, total;
   uint64_t part_floats;  // capacity of the partials buffer in floats
   uint64_t trace_slots;  // barriers x blocks the trace region holds
 };
@@ -74,6 +78,13 @@ struct Params {
   uint32_t* flags;
   uint32_t* status;  // [0] error code, [1] abort flag, [2] detail
   float *rope, *x, *a1, *a2, *a3, *a4, *att, *o2, *part, *rlog, *sact, *eact;
+  // router fusion (1- and 2-row vector instances of MoE models): the output projection also computes
+  // the router logits from the layer's input and its own input (rows rwx of the layer table), and the
+  // shared expert's gate/up rows run in the routed-expert phase, one phase fewer per layer. The
+  // hidden state then alternates between x (input of even layers) and x2 (input of odd layers).
+  int32_t rfuse;
+  float* x2;
+  float* ssq;  // [grid][M] per-workgroup sums of squares of the MoE input (router fusion)
   const char* wsb;    // workspace base: activations are addressed by byte offsets from here
   uint32_t ws_bytes;  // workspace size (< 2^31)
   uint64_t watchdog_ticks;  // wall-clock ticks a barrier may wait

@@ -480,6 +480,10 @@ struct Gemv {
         else r.w = (which ? Wu : Wg) + (size_t)(t - E) * K;
         break;
       case G_EXP: {
+        if (t >= n0) {  // router fusion: the shared expert's gate/up pair (every token row)
+          r.w = (which ? W1 : W0) + (size_t)(t - n0) * K;
+          break;
+        }
         const int u = t / F, j = t - u * F;
         r.w = (which ? Wu : Wg) + ((size_t)rt->uexp[u] * F + j) * K;
         const int s0 = rt->ustart[u];
@@ -537,6 +541,10 @@ struct Gemv {
         }
         break;
       default: {  // G_EXP
+        if (t >= n0) {
+          for (int k = 0; k < M; ++k) stc(sact + (size_t)k * SF + (t - n0), silu(a0[k]) * a1[k]);
+          break;
+        }
         const int u = t / F, j = t - u * F;
         const int s0 = rt->ustart[u], n = rt->ustart[u + 1] - s0;
         for (int k = 0; k < n; ++k) stc(eact + (size_t)(s0 + k) * F + j, silu(a0[k]) * a1[k]);
@@ -598,12 +606,12 @@ struct Gemv {
   // the token whose input row slot k of task t dotted (G_EXP: its expert's pairs in order), and the
   // number of slots
   __device__ __forceinline__ int token_of(int t, int k) const {
-    if (kind != G_EXP) return k;
+    if (kind != G_EXP || t >= n0) return k;
     const int s0 = rt->ustart[t / F];
     return rt->ptok[s0 + k];
   }
   __device__ __forceinline__ int slots_of(int t) const {
-    if (kind != G_EXP) return M;
+    if (kind != G_EXP || t >= n0) return M;
     const int u = t / F;
     return rt->ustart[u + 1] - rt->ustart[u];
   }
@@ -892,6 +900,98 @@ __device__ __forceinline__ void step_element(const Gemv& g, const Plan& q, int e
   if (task_end) reduce_task<MM>(g, q, v, first, a0, a1);
 }
 
+// The hidden state entering layer l (l == L: the final norm's input). With router fusion the
+// attention block's output projection writes the next layer's input into the other buffer (its
+// router rows read the whole input of the layer while other workgroups write their outputs).
+__device__ __forceinline__ float* xcur(const Params& p, int l) { return p.rfuse && (l & 1) ? p.x2 : p.x; }
+
+// Router fusion: the folded router rows (E rows of width RW = H + K) are split over the workgroups
+// of the output projection. With at least twice as many workgroups as rows, row e is cut into
+// P = min(8, grid / E) column parts, part q on workgroup e P + q (partial logits summed by the
+// router in order of q); otherwise each workgroup takes whole rows [e0, e0 + nr) (P = 1).
+struct RPart {
+  int e0, nr, q, c0, c1;  // rows, part, columns [c0, c1) (multiples of 4)
+};
+__device__ __forceinline__ int router_parts(int E) { return imax(1, imin(8, (int)gridDim.x / E)); }
+__device__ __forceinline__ RPart router_part(int E, int RW) {
+  RPart r{0, 0, 0, 0, RW};
+  const int P = router_parts(E), b = blockIdx.x;
+  if (P > 1) {
+    if (b < E * P) {
+      const int U = RW >> 2;
+      r.e0 = b / P;
+      r.q = b - r.e0 * P;
+      r.nr = 1;
+      r.c0 = 4 * (U * r.q / P);
+      r.c1 = 4 * (U * (r.q + 1) / P);
+    }
+  } else {
+    r.e0 = (int)((unsigned)E * b / gridDim.x);
+    r.nr = (int)((unsigned)E * (b + 1) / gridDim.x) - r.e0;
+  }
+  return r;
+}
+
+// Router fusion, the output projection's side work (1- and 2-row vector instances). Before the
+// phase's barrier (the folded rows are weights, and the layer's input was complete several barriers
+// ago): copy this workgroup's part of the folded router rows and the matching columns of the
+// layer's input rows into LDS after the staged input (xs: the staged input, KS its row stride):
+// xo [M][span], then wr [nr][span]. The phase's staging wait covers these copies too.
+template <int MM>
+__device__ __forceinline__ void router_side_issue(const Params& p, const LayerDev* ly, int l, const Ws& ws, float* xs,
+                                                  int KS, int K) {
+  const int E = p.E, H = p.H, RW = H + K;
+  const RPart rp = router_part(E, RW);
+  if (rp.nr == 0) return;
+  const int span = rp.c1 - rp.c0, hx = imax(0, imin(rp.c1, H) - rp.c0);
+  float* xo = xs + MM * KS;
+  float* wr = xo + MM * span;
+  const float* xl = xcur(p, l);
+  dma_rows<kCoherent>(ws.r, xo, MM, hx >> 2, span,
+                      [&](int r, int c) { return ws.off(xl + (size_t)r * H + rp.c0 + 4 * c); });
+  const Rsrc rr = make_rsrc(rflp(ly->rwx) + (size_t)rp.e0 * RW, (uint32_t)(rp.nr * RW * 4));
+  dma_rows<0>(rr, wr, rp.nr, span >> 2, span, [&](int r, int c) { return (uint32_t)((r * RW + rp.c0 + 4 * c) * 4); });
+}
+
+// After the phase (its staged data untouched, its outputs written): the partial logits of the
+// part, rlog[q][m][e] = columns [c0, c1) of wr[e] . [layer input | o] (the router logit before the
+// norm's factor), one wave per (row, token); and the sums of squares of this workgroup's outputs
+// (x + W_o o, the MoE input) per token, ssq[workgroup][m].
+template <int MM>
+__device__ __forceinline__ void router_side_finish(const Params& p, const float* xs, int KS, int K, int nloc,
+                                                   const float* acc, const float* res) {
+  const int E = p.E, H = p.H, RW = H + K, lane = lane_id();
+  const RPart rp = router_part(E, RW);
+  const int span = rp.c1 - rp.c0, hx = imax(0, imin(rp.c1, H) - rp.c0);
+  const float* xo = xs + MM * KS;
+  const float* wr = xo + MM * span;
+  float* rlog = rflp(p.rlog);
+  for (int j = wave_id(); j < rp.nr * MM; j += kWaves) {
+    const int r = j / MM, m = j - r * MM;
+    const float* w = wr + (size_t)r * span;
+    float a = 0.f;
+    for (int c = 4 * lane; c < span; c += 256) {
+      const float* xv = c < hx ? xo + (size_t)m * span + c : xs + (size_t)m * KS + (rp.c0 + c - H);
+      a += dot4(*reinterpret_cast<const f32x4*>(w + c), *reinterpret_cast<const f32x4*>(xv));
+    }
+    a = wave_sum(a, 64);
+    if (lane == 0) stc(rlog + ((size_t)rp.q * MM + m) * E + rp.e0 + r, a);
+  }
+  if (wave_id() == 0) {
+    float* ssq = rflp(p.ssq);
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      float ss = 0.f;
+      for (int i = lane; i < nloc; i += 64) {
+        const float v = res[m * nloc + i] + acc[(size_t)i * 2 * MM + m];
+        ss += v * v;
+      }
+      ss = wave_sum(ss, 64);
+      if (lane == 0) stc(ssq + (size_t)blockIdx.x * MM + m, ss);
+    }
+  }
+}
+
 // Returns true when the LDS input buffer ends the phase holding the whole normalised input.
 // The first two elements of the stream were requested by gemv_preload.
 template <int MM>
@@ -912,9 +1012,11 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
     uint16_t* gl = reinterpret_cast<uint16_t*>(xin + (g.stage == S_DOWN ? g.np + g.M : g.M) * ks);
     if (!keep) {
       g.stage_issue(ws, xin, gl, q.wbase + k0, ks, ks);
-      if (resid && sl == 0)  // this workgroup's residual inputs, [token][task]
+      if (resid && sl == 0) {  // this workgroup's residual inputs, [token][task]
+        const float* rs = g.kind == G_RESID ? g.src2 : g.out0;
         dma_rows4<kCoherent>(ws.r, q.res, g.M, q.nloc, q.nloc,
-                  [&](int m, int c) { return ws.off(g.out0 + (size_t)m * g.ldo0 + q.t0 + c); });
+                  [&](int m, int c) { return ws.off(rs + (size_t)m * g.ldo0 + q.t0 + c); });
+      }
       wait_vm();
       __syncthreads();
       g.stage_finish<MM>(xin, gl, ks, ks, sl == 0, red);
@@ -958,18 +1060,43 @@ __device__ __forceinline__ bool gemv_phase(const Gemv& g, const Plan& q, const W
 // the model asks; then the unique experts in ascending order, each with its (token, weight)
 // pairs in token order
 // ----------------------------------------------------------------------------------------------
+// fused: router fusion. rlog then holds P partial logits per (token, expert), [P][M][E], without the
+// norm's factor 1/rms, and ssq the output projection's per-workgroup sums of squares of the MoE
+// input [grid][M]; both are summed here in a fixed order. Otherwise rlog holds finished logits.
 __device__ __forceinline__ void compute_route(const Params& p, const Ws& ws, int layer, Route* rt, int* sel,
-                                              float* wsel, int* cnt) {
+                                              float* wsel, int* cnt, bool fused) {
   const int M = p.M, E = p.E, K = p.topk, lane = lane_id(), tid = tid_x();
   constexpr int R = kMaxExperts / 64;
   for (int m = wave_id(); m < M; m += kWaves) {
     float r[R];
+    if (!fused) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const int e = lane + 64 * k;
-      const float v = ws.ld1(p.rlog + (size_t)m * E + min(e, E - 1));
-      r[k] = e < E ? v : -INFINITY;
+      for (int k = 0; k < R; ++k) r[k] = ws.ld1(p.rlog + (size_t)m * E + min(lane + 64 * k, E - 1));
+    } else {
+      const int P = router_parts(E), G = gridDim.x;
+      float v[8][R], s[kMaxGrid / 64];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+          v[q][k] = ws.ld1(p.rlog + ((size_t)min(q, P - 1) * M + m) * E + min(lane + 64 * k, E - 1));
+#pragma unroll
+      for (int k = 0; k < kMaxGrid / 64; ++k) s[k] = ws.ld1(p.ssq + (size_t)min(lane + 64 * k, G - 1) * M + m);
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < kMaxGrid / 64; ++k) ss += lane + 64 * k < G ? s[k] : 0.f;
+      ss = wave_sum(ss, 64);
+      const float inv = 1.0f / sqrtf(ss / (float)p.H + p.eps);
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        float t = v[0][k];
+#pragma unroll
+        for (int q = 1; q < 8; ++q) t += q < P ? v[q][k] : 0.f;
+        r[k] = t * inv;
+      }
     }
+#pragma unroll
+    for (int k = 0; k < R; ++k) r[k] = lane + 64 * k < E ? r[k] : -INFINITY;
     float mx = r[0];
 #pragma unroll
     for (int k = 1; k < R; ++k) mx = fmaxf(mx, r[k]);
@@ -1469,9 +1596,11 @@ __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const
     uint16_t* gl = reinterpret_cast<uint16_t*>(xs + rows * q.DS);
     if (!keep) {
       g.stage_issue(ws, xs, gl, q.wbase + e.k0, e.ks, q.DS);
-      if (resid && sl == 0)
+      if (resid && sl == 0) {
+        const float* rs = g.kind == G_RESID ? g.src2 : g.out0;
         dma_rows4<kCoherent>(ws.r, q.res, g.M, q.nloc, q.nloc,
-                             [&](int m, int c) { return ws.off(g.out0 + (size_t)m * g.ldo0 + q.t0 + c); });
+                             [&](int m, int c) { return ws.off(rs + (size_t)m * g.ldo0 + q.t0 + c); });
+      }
       wait_vm();
       __syncthreads();
       mconvert<MM>(g, xs, gl, e.ks, q.DS, sl == 0, red);
@@ -2260,13 +2389,16 @@ __device__ __forceinline__ void plain_input(Gemv& g, const float* src, int ld, i
   g.K = K;
   g.Wst = K;
 }
-__device__ __forceinline__ void resid_out(Gemv& g, const Params& p, const uint16_t* w, int K) {
+
+// the attention block's output projection of layer l: residual from the layer's input, output
+// into the MoE block's input
+__device__ __forceinline__ void resid_out(Gemv& g, const Params& p, const LayerDev* ly, int l) {
   g.kind = G_RESID;
-  g.W0 = g.safe = w;
-  g.out0 = p.x;
+  g.W0 = g.safe = ly->wo;
+  g.src2 = xcur(p, l);
+  g.out0 = xcur(p, l + 1);
   g.ldo0 = p.H;
   g.ntasks = p.H;
-  (void)K;
 }
 
 // Phase i of layer l (l == L: the final norm and LM head; ly: the layer's table row, in LDS). Fills
@@ -2280,7 +2412,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
   g.pairs = 1;
   g.n1 = 0;
   if (l == p.L) {
-    norm_input(g, p.x, p.H, p.H, p.final_norm);
+    norm_input(g, xcur(p, l), p.H, p.H, p.final_norm);
     g.kind = G_STACK;
     g.W0 = g.safe = p.lm_head;
     g.n0 = p.V;
@@ -2291,9 +2423,12 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
   }
   const int kind = ly->kind;
   const int na = attn_phases(kind);
+  float* xl = xcur(p, l);
   if (i >= na) {
-    if (i == na) {
-      norm_input(g, p.x, p.H, p.H, ly->moe_norm);
+    float* xm = xcur(p, l + 1);  // the MoE block's input (and output: its residual is added in place)
+    const bool rf = p.rfuse;
+    if (i == na && !rf) {
+      norm_input(g, xm, p.H, p.H, ly->moe_norm);
       g.kind = G_RS;
       g.E = p.E;
       g.SF = p.SF;
@@ -2307,8 +2442,8 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
       g.pairs = p.SF > 0 ? 2 : 1;
       return PT_GEMV;
     }
-    if (i == na + 1 && p.E > 0) {  // a dense model has no routed-expert phase
-      norm_input(g, p.x, p.H, p.H, ly->moe_norm);
+    if (i == na + (rf ? 0 : 1) && p.E > 0) {  // a dense model has no routed-expert phase
+      norm_input(g, xm, p.H, p.H, ly->moe_norm);
       g.kind = G_EXP;
       g.F = p.F;
       g.Wg = g.safe = ly->exp_gate;
@@ -2316,6 +2451,12 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
       g.eact = p.eact;
       g.pairs = 2;
       g.ntasks = 0;  // known after routing
+      if (rf) {  // router fusion: the shared expert's gate/up pairs follow the routed ones
+        g.W0 = ly->sh_gate;
+        g.W1 = ly->sh_up;
+        g.SF = p.SF;
+        g.sact = p.sact;
+      }
       return PT_EXPERT;
     }
     // routed down projections (pool rows [E][H][F]) and the shared down projection
@@ -2332,7 +2473,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
     g.Wg = ly->exp_down;
     g.safe = p.E ? ly->exp_down : ly->sh_down;  // dense: the (empty) expert pool has no rows
     g.Wu = ly->sh_down;
-    g.out0 = p.x;
+    g.out0 = xm;
     g.ldo0 = p.H;
     g.ntasks = p.H;
     g.pairs = rt->nu + (p.SF > 0 ? 1 : 0);
@@ -2341,7 +2482,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
   if constexpr (Fam == MK_ATTN_GQA) {
     const int dq = p.nh * p.hd, dkv = p.nkv * p.hd;
     if (i == 0) {
-      norm_input(g, p.x, p.H, p.H, ly->attn_norm);
+      norm_input(g, xl, p.H, p.H, ly->attn_norm);
       g.kind = G_STACK;
       g.W0 = g.safe = ly->wq; g.W1 = ly->wk; g.W2 = ly->wv;
       g.n0 = dq; g.n1 = dkv;
@@ -2353,14 +2494,14 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
     if (i == 1) return PT_ATTN_GQA;
     if (i == 2) return PT_MERGE;
     plain_input(g, p.att, dq, dq);
-    resid_out(g, p, ly->wo, dq);
+    resid_out(g, p, ly, l);
     return PT_GEMV;
   } else {
   if (kind == kMla) {
     const int lat = p.kvl + p.rd, qd = p.nd + p.rd;
     switch (i) {
       case 0:
-        norm_input(g, p.x, p.H, p.H, ly->attn_norm);
+        norm_input(g, xl, p.H, p.H, ly->attn_norm);
         g.kind = G_STACK;
         g.W0 = g.safe = ly->w_dq; g.W1 = ly->w_dkv;
         g.n0 = p.ql; g.n1 = lat;
@@ -2408,7 +2549,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
         return PT_GEMV;
       default:
         plain_input(g, p.o2, p.nh * p.vd, p.nh * p.vd);
-        resid_out(g, p, ly->wo, p.nh * p.vd);
+        resid_out(g, p, ly, l);
         return PT_GEMV;
     }
   }
@@ -2416,7 +2557,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
   if constexpr (Fam != MK_ATTN_HYBRID) return PT_GEMV;  // (no such layer)
   const int dq = p.nh * p.dk, dvv = p.nh * p.dv;
   if (i == 0) {
-    norm_input(g, p.x, p.H, p.H, ly->attn_norm);
+    norm_input(g, xl, p.H, p.H, ly->attn_norm);
     g.kind = G_STACK;
     g.W0 = g.safe = ly->kwq; g.W1 = ly->kwk; g.W2 = ly->kwv;
     g.n0 = dq; g.n1 = dq;
@@ -2427,7 +2568,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
   }
   if (i == 1) return PT_KDA;
   plain_input(g, p.att, dvv, dvv);
-  resid_out(g, p, ly->wo, dvv);
+  resid_out(g, p, ly, l);
   return PT_GEMV;
   }
 }
@@ -2691,7 +2832,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   bool resident = false;  // the LDS input buffer holds this layer's normalised MoE input
   for (int l = 0; l <= p.L; ++l) {
     const LayerDev* ly = &sm.lyd[l & 1];
-    const int nph = (l == p.L) ? 1 : attn_phases(ly->kind) + (p.E ? 3 : 2);
+    const int nph = (l == p.L) ? 1 : attn_phases(ly->kind) + (p.E && !p.rfuse ? 3 : 2);
     for (int i = 0; i < nph; ++i) {
       Gemv g{};
       typename PlanOf<MF>::type q{};
@@ -2720,10 +2861,11 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         MK_FINISH();
         if (trec && tid_x() == 0) trec[7] = wall_clock64();
         if (type == PT_EXPERT) {
-          compute_route(p, ws, l, &sm.route, sm.rsel, sm.rw, sm.cnt);
+          compute_route(p, ws, l, &sm.route, sm.rsel, sm.rw, sm.cnt, p.rfuse != 0);
           if (trec && tid_x() == 0) trec[6] = wall_clock64();
           g.rt = &sm.route;
-          g.ntasks = rfl(sm.route.nu * p.F);
+          g.n0 = rfl(sm.route.nu * p.F);  // routed pairs; router fusion: the shared pairs after them
+          g.ntasks = rfl(sm.route.nu * p.F + (p.rfuse ? p.SF : 0));
         }
       }
       if (type == PT_GEMV || type == PT_EXPERT) {
@@ -2735,6 +2877,8 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
           q = make_plan<MM>(g, sm.buf);
           if (trec && tid_x() == 0) trec[11] = wall_clock64();
           gemv_preload(g, q, b0, b1);
+          if constexpr (MM <= 2)
+            if (g.kind == G_RESID && p.rfuse) router_side_issue<MM>(p, ly, l, ws, sm.buf, q.KS, g.Wst);
         }
       }
       if (early) {
@@ -2751,6 +2895,8 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
             resident = mgemv_phase<MM>(g, q, ws, sm.buf, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
           else
             resident = gemv_phase<MM>(g, q, ws, sm.buf, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
+          if constexpr (!MF && MM <= 2)
+            if (g.kind == G_RESID && p.rfuse) router_side_finish<MM>(p, sm.buf, q.KS, g.Wst, q.nloc, q.acc, q.res);
           break;
         }
         // The next layer's table row is requested during the layer's attention phase, which waits
@@ -2852,6 +2998,30 @@ __global__ void transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd,
   }
 }
 
+// The router of one MoE layer folded onto its attention output projection. The router logit of the
+// MoE input x' = x + W_o o before the norm's factor is sum over t of W_r[e][t] g[t] x'[t]
+// = sum_t (W_r[e][t] g[t]) x[t] + sum_j (sum_t W_r[e][t] g[t] W_o[t][j]) o[j]. Row e of out holds
+// the two coefficient vectors, [H] then [K]: the products of two bf16 values (exact in fp32), and the
+// sums over t accumulated in fp64 and rounded once to fp32. One thread per output element.
+__global__ void fold_router(const uint16_t* wr, const uint16_t* gain, const uint16_t* wo, float* out, int E, int H,
+                            int K) {
+  const int W = H + K;
+  const size_t n = (size_t)E * W;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + tid_x(); e < n; e += (size_t)gridDim.x * blockDim.x) {
+    const size_t i = e / W, c = e - i * W;
+    const uint16_t* w = wr + i * H;
+    if (c < (size_t)H) {
+      gp(out)[e] = bf2f(gp(w)[c]) * bf2f(gp(gain)[c]);
+    } else {
+      const size_t j = c - H;
+      double acc = 0.0;
+      for (int t = 0; t < H; ++t)
+        acc += (double)(bf2f(gp(w)[t]) * bf2f(gp(gain)[t])) * (double)bf2f(gp(wo)[(size_t)t * K + j]);
+      gp(out)[e] = (float)acc;
+    }
+  }
+}
+
 }  // namespace
 
 // The workspace of mk_decode_step_static: one copy of this array on every GPU the library runs on.
@@ -2934,6 +3104,12 @@ hipError_t launch_decode(const Params& p, int nblocks, bool matrix_cores, hipStr
 
 hipError_t launch_transpose_uk(const uint16_t* src, uint16_t* dst, int nh, int nd, int kvl, hipStream_t stream) {
   hipLaunchKernelGGL(transpose_uk, dim3(256), dim3(256), 0, stream, src, dst, nh, nd, kvl);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_router(const uint16_t* router, const uint16_t* gain, const uint16_t* wo, float* out, int E, int H,
+                              int K, hipStream_t stream) {
+  hipLaunchKernelGGL(fold_router, dim3(1024), dim3(256), 0, stream, router, gain, wo, out, E, H, K);
   return hipGetLastError();
 }
 

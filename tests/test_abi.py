@@ -80,9 +80,12 @@ def test_query_sizes_match_documented_layouts(mk):
     c = synth.K3
     assert s.kv_bytes == c.n_layers * c.max_batch * c.kv_capacity * c.latent_dim * 2
     assert s.kda_state_bytes == 0
-    # every weight tensor is in the arena once (plus the layer table and 256-byte padding)
+    # every weight tensor is in the arena once, plus each MoE layer's router folded onto its
+    # attention output projection (fp32 [n_experts][hidden + n_heads * v_dim], derived at load
+    # time), the layer table and 256-byte padding
     total = sum(synth.numel(t.shape) * (4 if t.dist == "sigmoid" else 2) for t in synth.tensor_list(c))
-    assert total <= s.arena_bytes <= total + 256 * (len(synth.tensor_list(c)) + 1) + c.n_layers * 256
+    total += c.n_layers * c.n_experts * (c.hidden + c.n_heads * c.v_dim) * 4
+    assert total <= s.arena_bytes <= total + 256 * (len(synth.tensor_list(c)) + 1) + 2 * c.n_layers * 256
     assert s.arena_bytes < 288e9  # fits one MI355X
     h = sizes(mk, synth.K3_HYBRID)
     nk = len(synth.K3_HYBRID.kda_layers())
