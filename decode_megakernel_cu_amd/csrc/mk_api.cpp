@@ -212,19 +212,24 @@ uint64_t wo_width(const mk_config& c, int l) {
   return (uint64_t)c.n_heads * (k == kGqa ? c.head_dim : k == kMla ? c.v_dim : c.kda_dv);
 }
 
-// Whether a step of M token rows on the vector executor folds the router onto the attention output
-// projection (see Params::rfuse): a MoE model, at most two rows, and the output projection's LDS
-// carve-up (per workgroup: its task accumulators, the staged input, the layer input's M rows and
-// its router rows) fits every layer.
-bool router_fusion(const mk_config& c, int M, int nb) {
-  if (c.n_experts <= 0 || M > 2 || nb < 1) return false;
-  const long long E = c.n_experts, MM = instance_rows(M), H = c.hidden;
+// Whether a step of M token rows folds the router onto the attention output projection (see
+// Params::rfuse): a MoE model, at most two rows on the vector executor or five to eight on the
+// matrix cores (at four rows the separate router phase measured 0.5% faster), and the output
+// projection's LDS carve-up fits every layer. Per workgroup: its task accumulators
+// (and on the matrix cores the partial-tile slots) at the end; before them the staged input (one
+// slab; rows padded by 4 floats on the matrix cores), the layer input's M rows and the router rows
+// of its part.
+bool router_fusion(const mk_config& c, int M, int nb, bool mf) {
+  if (c.n_experts <= 0 || nb < 1 || M > (mf ? 8 : 2) || (mf && M <= 4)) return false;
+  const long long E = c.n_experts, MM = instance_rows(M), H = c.hidden, S = mfma_segments((int)MM), R = 16 / S;
   const long long P = std::max(1LL, std::min(8LL, nb / E)), nr = P > 1 ? 1 : (E + nb - 1) / nb;
-  const long long nloc = (H + nb - 1) / nb;
+  const long long nloc = (H + nb - 1) / nb, ngrp = (nloc + R - 1) / R;
   for (int l = 0; l < c.n_layers; ++l) {
     const long long K = (long long)wo_width(c, l), span = 4 * (((H + K) / 4 + P - 1) / P);
-    const long long cap = ((long long)kLdsFloats - nloc * 3 * MM) & ~7LL;
-    if (M * K + M * span + nr * span > cap) return false;
+    long long cap = (long long)kLdsFloats - nloc * 3 * MM;
+    if (mf) cap -= (ngrp + kWaves) * (256 / S);
+    cap &= ~7LL;
+    if (M * (K + (mf ? 4 : 0)) + M * span + nr * span > cap) return false;
   }
   return true;
 }
@@ -706,7 +711,7 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   p.rope = f(w.rope); p.x = f(w.x); p.a1 = f(w.a1); p.a2 = f(w.a2); p.a3 = f(w.a3); p.a4 = f(w.a4);
   p.att = f(w.att); p.o2 = f(w.o2); p.part = f(w.part); p.rlog = f(w.rlog); p.sact = f(w.sact); p.eact = f(w.eact);
   p.x2 = f(w.x2); p.ssq = f(w.ssq);
-  p.rfuse = !mf && router_fusion(g, M, c->nblocks) && !std::getenv("MK_NO_ROUTER_FUSION") ? 1 : 0;
+  p.rfuse = router_fusion(g, M, c->nblocks, mf) && !std::getenv("MK_NO_ROUTER_FUSION") ? 1 : 0;
   p.wsb = reinterpret_cast<const char*>(ws);
   p.ws_bytes = (uint32_t)w.total;
   p.watchdog_ticks = c->watchdog_ticks;

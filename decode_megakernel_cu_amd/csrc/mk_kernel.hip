@@ -932,63 +932,64 @@ __device__ __forceinline__ RPart router_part(int E, int RW) {
   return r;
 }
 
-// Router fusion, the output projection's side work (1- and 2-row vector instances). Before the
-// phase's barrier (the folded rows are weights, and the layer's input was complete several barriers
-// ago): copy this workgroup's part of the folded router rows and the matching columns of the
-// layer's input rows into LDS after the staged input (xs: the staged input, KS its row stride):
-// xo [M][span], then wr [nr][span]. The phase's staging wait covers these copies too.
-template <int MM>
-__device__ __forceinline__ void router_side_issue(const Params& p, const LayerDev* ly, int l, const Ws& ws, float* xs,
-                                                  int KS, int K) {
+// Router fusion, the output projection's side work. Before the phase's barrier (the folded rows are
+// weights, and the layer's input was complete several barriers ago): copy this workgroup's part of
+// the folded router rows and the matching columns of the layer's M input rows into LDS, at xo
+// (after the staged input): xo [M][span], then wr [nr][span]. The phase's staging wait covers these
+// copies too.
+__device__ __forceinline__ void router_side_issue(const Params& p, const LayerDev* ly, int l, const Ws& ws, float* xo,
+                                                  int M, int K) {
   const int E = p.E, H = p.H, RW = H + K;
   const RPart rp = router_part(E, RW);
   if (rp.nr == 0) return;
   const int span = rp.c1 - rp.c0, hx = imax(0, imin(rp.c1, H) - rp.c0);
-  float* xo = xs + MM * KS;
-  float* wr = xo + MM * span;
+  float* wr = xo + M * span;
   const float* xl = xcur(p, l);
-  dma_rows<kCoherent>(ws.r, xo, MM, hx >> 2, span,
+  dma_rows<kCoherent>(ws.r, xo, M, hx >> 2, span,
                       [&](int r, int c) { return ws.off(xl + (size_t)r * H + rp.c0 + 4 * c); });
   const Rsrc rr = make_rsrc(rflp(ly->rwx) + (size_t)rp.e0 * RW, (uint32_t)(rp.nr * RW * 4));
   dma_rows<0>(rr, wr, rp.nr, span >> 2, span, [&](int r, int c) { return (uint32_t)((r * RW + rp.c0 + 4 * c) * 4); });
 }
 
-// After the phase (its staged data untouched, its outputs written): the partial logits of the
-// part, rlog[q][m][e] = columns [c0, c1) of wr[e] . [layer input | o] (the router logit before the
-// norm's factor), one wave per (row, token); and the sums of squares of this workgroup's outputs
-// (x + W_o o, the MoE input) per token, ssq[workgroup][m].
-template <int MM>
-__device__ __forceinline__ void router_side_finish(const Params& p, const float* xs, int KS, int K, int nloc,
-                                                   const float* acc, const float* res) {
-  const int E = p.E, H = p.H, RW = H + K, lane = lane_id();
-  const RPart rp = router_part(E, RW);
-  const int span = rp.c1 - rp.c0, hx = imax(0, imin(rp.c1, H) - rp.c0);
-  const float* xo = xs + MM * KS;
-  const float* wr = xo + MM * span;
-  float* rlog = rflp(p.rlog);
-  for (int j = wave_id(); j < rp.nr * MM; j += kWaves) {
-    const int r = j / MM, m = j - r * MM;
+// Once the copies and the phase's input o (fp32 rows at stride DS in xs) have landed: the partial
+// logits of the part, rlog[q][m][e] = columns [c0, c1) of wr[e] . [layer input | o] (the router
+// logit before the norm's factor), one wave per (row, token).
+struct RSide {
+  float* rlog;  // nullptr: no side work
+  int E, H, M;
+};
+__device__ __forceinline__ void router_side_logits(const RSide& rs, const float* xs, int DS, int K, const float* xo) {
+  const int RW = rs.H + K, lane = lane_id();
+  const RPart rp = router_part(rs.E, RW);
+  const int span = rp.c1 - rp.c0, hx = imax(0, imin(rp.c1, rs.H) - rp.c0);
+  const float* wr = xo + rs.M * span;
+  for (int j = wave_id(); j < rp.nr * rs.M; j += kWaves) {
+    const int r = j / rs.M, m = j - r * rs.M;
     const float* w = wr + (size_t)r * span;
     float a = 0.f;
     for (int c = 4 * lane; c < span; c += 256) {
-      const float* xv = c < hx ? xo + (size_t)m * span + c : xs + (size_t)m * KS + (rp.c0 + c - H);
+      const float* xv = c < hx ? xo + (size_t)m * span + c : xs + (size_t)m * DS + (rp.c0 + c - rs.H);
       a += dot4(*reinterpret_cast<const f32x4*>(w + c), *reinterpret_cast<const f32x4*>(xv));
     }
     a = wave_sum(a, 64);
-    if (lane == 0) stc(rlog + ((size_t)rp.q * MM + m) * E + rp.e0 + r, a);
+    if (lane == 0) stc(rs.rlog + ((size_t)rp.q * rs.M + m) * rs.E + rp.e0 + r, a);
   }
-  if (wave_id() == 0) {
-    float* ssq = rflp(p.ssq);
-#pragma unroll
-    for (int m = 0; m < MM; ++m) {
-      float ss = 0.f;
-      for (int i = lane; i < nloc; i += 64) {
-        const float v = res[m * nloc + i] + acc[(size_t)i * 2 * MM + m];
-        ss += v * v;
-      }
-      ss = wave_sum(ss, 64);
-      if (lane == 0) stc(ssq + (size_t)blockIdx.x * MM + m, ss);
+}
+
+// After the phase: the sums of squares of this workgroup's outputs (x + W_o o, the MoE input) per
+// token, ssq[workgroup][m] (acc: task accumulators [nloc][2][MM], res: residuals [M][nloc]).
+template <int MM>
+__device__ __forceinline__ void router_side_ssq(float* ssq, int M, int nloc, const float* acc, const float* res) {
+  if (wave_id() != 0) return;
+  const int lane = lane_id();
+  for (int m = 0; m < M; ++m) {
+    float ss = 0.f;
+    for (int i = lane; i < nloc; i += 64) {
+      const float v = res[m * nloc + i] + acc[(size_t)i * 2 * MM + m];
+      ss += v * v;
     }
+    ss = wave_sum(ss, 64);
+    if (lane == 0) stc(ssq + (size_t)blockIdx.x * M + m, ss);
   }
 }
 
@@ -1548,7 +1549,7 @@ __device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGe
   for (int x = tid_x(); x < n; x += kThreads) {
     const int ak = x / q.nloc, i = x - ak * q.nloc, a = ak / MM, k = ak - a * MM;
     int col = k;
-    if (g.kind == G_EXP) {
+    if (g.kind == G_EXP && q.t0 + i < g.n0) {
       const int u = (q.t0 + i) / g.F, s0 = g.rt->ustart[u];
       if (k >= g.rt->ustart[u + 1] - s0) continue;
       col = g.rt->ptok[s0 + k];
@@ -1579,7 +1580,7 @@ __device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGe
 // the split bf16 form this executor reads).
 template <int MM>
 __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const Ws& ws, float* smem, float* red,
-                                            RowBuf& b0, RowBuf& b1, bool keep_in, LdsU64* trace) {
+                                            RowBuf& b0, RowBuf& b1, bool keep_in, LdsU64* trace, const RSide& rs) {
   float* xs = smem;
   const int tid = tid_x();
   const bool keep = keep_in && q.one_slab;
@@ -1603,6 +1604,11 @@ __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const
       }
       wait_vm();
       __syncthreads();
+      // router fusion: the side logits read the fp32 input before it is converted in place
+      if (rs.rlog && sl == 0) {
+        router_side_logits(rs, xs, q.DS, g.Wst, xs + g.M * q.DS);
+        __syncthreads();  // every wave has read the fp32 rows before any converts them
+      }
       mconvert<MM>(g, xs, gl, e.ks, q.DS, sl == 0, red);
     }
     __syncthreads();
@@ -2873,12 +2879,13 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
           q = mmake_plan<MM>(g, sm.buf);
           if (trec && tid_x() == 0) trec[11] = wall_clock64();
           mgemv_preload<mfma_segments(MM)>(g, q, b0, b1);
+          if (g.kind == G_RESID && p.rfuse) router_side_issue(p, ly, l, ws, sm.buf + g.M * q.DS, g.M, g.Wst);
         } else {
           q = make_plan<MM>(g, sm.buf);
           if (trec && tid_x() == 0) trec[11] = wall_clock64();
           gemv_preload(g, q, b0, b1);
           if constexpr (MM <= 2)
-            if (g.kind == G_RESID && p.rfuse) router_side_issue<MM>(p, ly, l, ws, sm.buf, q.KS, g.Wst);
+            if (g.kind == G_RESID && p.rfuse) router_side_issue(p, ly, l, ws, sm.buf + MM * q.KS, MM, g.Wst);
         }
       }
       if (early) {
@@ -2891,12 +2898,16 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
         case PT_GEMV:
         case PT_EXPERT: {
           const bool keep = type == PT_EXPERT && resident;
-          if constexpr (MF)
-            resident = mgemv_phase<MM>(g, q, ws, sm.buf, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
-          else
+          const bool side = g.kind == G_RESID && p.rfuse;
+          if constexpr (MF) {
+            const RSide rs{side ? rflp(p.rlog) : nullptr, p.E, p.H, g.M};
+            resident = mgemv_phase<MM>(g, q, ws, sm.buf, sm.red, b0, b1, keep, trec, rs) && g.kind == G_RS;
+          } else {
             resident = gemv_phase<MM>(g, q, ws, sm.buf, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
-          if constexpr (!MF && MM <= 2)
-            if (g.kind == G_RESID && p.rfuse) router_side_finish<MM>(p, sm.buf, q.KS, g.Wst, q.nloc, q.acc, q.res);
+            if constexpr (MM <= 2)
+              if (side) router_side_logits(RSide{rflp(p.rlog), p.E, p.H, MM}, sm.buf, q.KS, g.Wst, sm.buf + MM * q.KS);
+          }
+          if (side) router_side_ssq<MM>(rflp(p.ssq), g.M, q.nloc, q.acc, q.res);
           break;
         }
         // The next layer's table row is requested during the layer's attention phase, which waits
