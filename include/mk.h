@@ -89,7 +89,7 @@ typedef struct {
 } mk_config;
 
 typedef struct {
-  uint64_t arena_bytes;      /* weights (device, caller-allocated, 256-byte aligned) */
+  uint64_t arena_bytes;      /* weights and the folded router rows derived from them (device, caller-allocated, 256-byte aligned) */
   uint64_t workspace_bytes;  /* activations, attention partials, barrier flags, status (device) */
   uint64_t kv_bytes;         /* KV cache (device), layout below */
   uint64_t kda_state_bytes;  /* recurrent state of delta-rule layers (device, fp32), 0 if none */
@@ -162,6 +162,8 @@ int mk_query_sizes(const mk_config* cfg, mk_sizes* out);
 
 /* Create a context on HIP device `device` (or MK_DEVICE_NONE) over caller buffers of at least the
  * queried sizes. The workspace is cleared here (once); the arena is filled by mk_load_weights.
+ * A barrier that waits longer than MK_WATCHDOG_MS milliseconds (environment, default 2000) ends
+ * the step with MK_E_DEVICE instead of hanging.
  * (The pages' program likewise runs over buffers laid out ahead of time, with static shapes:
  * video description "700 tok/s on a 2.8 Trillion Model", timestamp "What It Costs: Static Shapes,
  * Cold Compiles, and Tradeoffs".) arena and workspace must be 256-byte aligned device pointers;
@@ -171,6 +173,13 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
 
 /* Copy (and, where the kernel wants another layout, repack) n tensors into the arena, in stream
  * order on hip_stream. Every tensor of the model must have been loaded once before the first step.
+ * Once a MoE layer's ROUTER, MOE_NORM and WO are all in the arena (and again whenever one of them is
+ * loaded anew), a kernel on hip_stream derives that layer's folded router rows, which the arena also
+ * holds (fp32 [n_experts][hidden + W_o's input width]: ROUTER times MOE_NORM's gain, then that
+ * product times WO, summed in fp64): the router logit of x + W_o o is linear in [x | o] before the
+ * norm's 1/rms factor, so steps of 1-2 token rows (5-8 on the matrix cores) compute it in the
+ * attention output projection's phase and route right after it. Setting the environment variable
+ * MK_NO_ROUTER_FUSION makes every step use the separate router phase instead (for comparisons).
  * (The pages' demos likewise prepare their kernel layouts from the checkpoints before serving:
  * tpu-megakernels README, section "Setup".) The source of each descriptor must stay valid until the
  * stream reaches the copy. MK_E_INVAL for an unknown tensor, a wrong byte count or a NULL source. */

@@ -222,6 +222,28 @@ def test_k3_two_layers(B, T, kv_len):
     parity(K3_SMALL, synth.Spec(seed=2), B, T, kv_len)
 
 
+# The router folded onto the attention output projection (1-2 rows on the vector executor, 5-8 on
+# the matrix cores) against the separate router phase (MK_NO_ROUTER_FUSION): both match the oracle,
+# select the same experts, and their logits agree to fp32 summation-order differences.
+@pytest.mark.parametrize("B,T,kv_len,rows", [(1, 1, 4096, 3), (2, 1, 500, 3), (8, 1, 33, 3), (1, 7, 300, 3),
+                                              (2, 1, 77, 2)])
+def test_router_fusion_against_router_phase(B, T, kv_len, rows, monkeypatch):
+    runs = {}
+    for fused in (True, False):
+        if fused:
+            monkeypatch.delenv("MK_NO_ROUTER_FUSION", raising=False)
+        else:
+            monkeypatch.setenv("MK_NO_ROUTER_FUSION", "1")
+        dm, got, route, ref, caches, init = run_pair(K3_SMALL, synth.Spec(seed=4), B, T, kv_len, mfma_min_rows=rows)
+        check_logits(got, ref)
+        check_route(route, ref)
+        check_cache(K3_SMALL, dm, caches, init, B, T, kv_len)
+        runs[fused] = (got, route)
+    assert np.array_equal(runs[True][1], runs[False][1])
+    diff = np.abs(runs[True][0] - runs[False][0]).max() / np.abs(runs[False][0]).max()
+    assert diff < 1e-4, f"fused and separate router phases differ by {diff:.3e} of the logit scale"
+
+
 # a share of the same model over twice the tensor-parallel ranks: 8 heads, padded to the 16 rows of
 # the attention tiles (the absorbed query, the merge and W_uv keep 8)
 @pytest.mark.parametrize("B,T,kv_len", [(1, 1, 4096), (8, 1, 700), (1, 7, 2000)])
