@@ -951,17 +951,32 @@ __device__ __forceinline__ void router_side_issue(const Params& p, const LayerDe
   dma_rows<0>(rr, wr, rp.nr, span >> 2, span, [&](int r, int c) { return (uint32_t)((r * RW + rp.c0 + 4 * c) * 4); });
 }
 
-// Once the copies and the phase's input o (fp32 rows at stride DS in xs) have landed: the partial
-// logits of the part, rlog[q][m][e] = columns [c0, c1) of wr[e] . [layer input | o] (the router
-// logit before the norm's factor), one wave per (row, token).
+// After the phase's barrier, for the matrix-core executor (which converts its staged input in place
+// to bf16 parts): copy the part's columns of the phase's input o (rows of stride ld at src) into
+// xo beside the layer input's, so that xo[m] holds the part's columns of [layer input | o].
+__device__ __forceinline__ void router_side_issue_o(const Params& p, const Ws& ws, float* xo, int M, int K,
+                                                    const float* src, int ld) {
+  const int H = p.H;
+  const RPart rp = router_part(p.E, H + K);
+  if (rp.nr == 0) return;
+  const int span = rp.c1 - rp.c0, hx = imax(0, imin(rp.c1, H) - rp.c0), o0 = imax(rp.c0, H) - H;
+  dma_rows<kCoherent>(ws.r, xo + hx, M, (span - hx) >> 2, span,
+                      [&](int r, int c) { return ws.off(src + (size_t)r * ld + o0 + 4 * c); });
+}
+
+// Once the copies and the phase's input have landed: the partial logits of the part, rlog[q][m][e]
+// = columns [c0, c1) of wr[e] . [layer input | o] (the router logit before the norm's factor), one
+// wave per (row, token). The o columns come from xs (fp32 rows at stride DS), or from xo when
+// o_in_xo (router_side_issue_o).
 struct RSide {
-  float* rlog;  // nullptr: no side work
+  float* rlog;
   int E, H, M;
 };
-__device__ __forceinline__ void router_side_logits(const RSide& rs, const float* xs, int DS, int K, const float* xo) {
+__device__ __forceinline__ void router_side_logits(const RSide& rs, const float* xs, int DS, int K, const float* xo,
+                                                   bool o_in_xo) {
   const int RW = rs.H + K, lane = lane_id();
   const RPart rp = router_part(rs.E, RW);
-  const int span = rp.c1 - rp.c0, hx = imax(0, imin(rp.c1, rs.H) - rp.c0);
+  const int span = rp.c1 - rp.c0, hx = o_in_xo ? span : imax(0, imin(rp.c1, rs.H) - rp.c0);
   const float* wr = xo + rs.M * span;
   for (int j = wave_id(); j < rp.nr * rs.M; j += kWaves) {
     const int r = j / rs.M, m = j - r * rs.M;
@@ -1580,7 +1595,7 @@ __device__ __forceinline__ void mreduce(const Gemv& g, const MPlan& q, const MGe
 // the split bf16 form this executor reads).
 template <int MM>
 __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const Ws& ws, float* smem, float* red,
-                                            RowBuf& b0, RowBuf& b1, bool keep_in, LdsU64* trace, const RSide& rs) {
+                                            RowBuf& b0, RowBuf& b1, bool keep_in, LdsU64* trace) {
   float* xs = smem;
   const int tid = tid_x();
   const bool keep = keep_in && q.one_slab;
@@ -1604,11 +1619,6 @@ __device__ __forceinline__ bool mgemv_phase(const Gemv& g, const MPlan& q, const
       }
       wait_vm();
       __syncthreads();
-      // router fusion: the side logits read the fp32 input before it is converted in place
-      if (rs.rlog && sl == 0) {
-        router_side_logits(rs, xs, q.DS, g.Wst, xs + g.M * q.DS);
-        __syncthreads();  // every wave has read the fp32 rows before any converts them
-      }
       mconvert<MM>(g, xs, gl, e.ks, q.DS, sl == 0, red);
     }
     __syncthreads();
@@ -2900,12 +2910,13 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
           const bool keep = type == PT_EXPERT && resident;
           const bool side = g.kind == G_RESID && p.rfuse;
           if constexpr (MF) {
-            const RSide rs{side ? rflp(p.rlog) : nullptr, p.E, p.H, g.M};
-            resident = mgemv_phase<MM>(g, q, ws, sm.buf, sm.red, b0, b1, keep, trec, rs) && g.kind == G_RS;
+            if (side) router_side_issue_o(p, ws, sm.buf + g.M * q.DS, g.M, g.Wst, g.src, g.ld);
+            resident = mgemv_phase<MM>(g, q, ws, sm.buf, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
+            if (side) router_side_logits(RSide{rflp(p.rlog), p.E, p.H, g.M}, sm.buf, q.DS, g.Wst, sm.buf + g.M * q.DS, true);
           } else {
             resident = gemv_phase<MM>(g, q, ws, sm.buf, sm.red, b0, b1, keep, trec) && g.kind == G_RS;
             if constexpr (MM <= 2)
-              if (side) router_side_logits(RSide{rflp(p.rlog), p.E, p.H, MM}, sm.buf, q.KS, g.Wst, sm.buf + MM * q.KS);
+              if (side) router_side_logits(RSide{rflp(p.rlog), p.E, p.H, MM}, sm.buf, q.KS, g.Wst, sm.buf + MM * q.KS, false);
           }
           if (side) router_side_ssq<MM>(rflp(p.ssq), g.M, q.nloc, q.acc, q.res);
           break;
