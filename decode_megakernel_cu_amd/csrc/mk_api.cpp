@@ -213,14 +213,13 @@ uint64_t wo_width(const mk_config& c, int l) {
 }
 
 // Whether a step of M token rows folds the router onto the attention output projection (see
-// Params::rfuse): a MoE model, at most two rows on the vector executor or five to eight on the
-// matrix cores (at four rows the separate router phase measured 0.5% faster), and the output
-// projection's LDS carve-up fits every layer. Per workgroup: its task accumulators
+// Params::rfuse): a MoE model, at most two rows on the vector executor or eight on the matrix
+// cores, and the output projection's LDS carve-up fits every layer. Per workgroup: its task accumulators
 // (and on the matrix cores the partial-tile slots) at the end; before them the staged input (one
 // slab; rows padded by 4 floats on the matrix cores), the layer input's M rows and the router rows
 // of its part.
 bool router_fusion(const mk_config& c, int M, int nb, bool mf) {
-  if (c.n_experts <= 0 || nb < 1 || M > (mf ? 8 : 2) || (mf && M <= 4)) return false;
+  if (c.n_experts <= 0 || nb < 1 || M > (mf ? 8 : 2)) return false;
   const long long E = c.n_experts, MM = instance_rows(M), H = c.hidden, S = mfma_segments((int)MM), R = 16 / S;
   const long long P = std::max(1LL, std::min(8LL, nb / E)), nr = P > 1 ? 1 : (E + nb - 1) / nb;
   const long long nloc = (H + nb - 1) / nb, ngrp = (nloc + R - 1) / R;

@@ -177,7 +177,7 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
  * loaded anew), a kernel on hip_stream derives that layer's folded router rows, which the arena also
  * holds (fp32 [n_experts][hidden + W_o's input width]: ROUTER times MOE_NORM's gain, then that
  * product times WO, summed in fp64): the router logit of x + W_o o is linear in [x | o] before the
- * norm's 1/rms factor, so steps of 1-2 token rows (5-8 on the matrix cores) compute it in the
+ * norm's 1/rms factor, so steps of 1-2 token rows (up to 8 on the matrix cores) compute it in the
  * attention output projection's phase and route right after it. Setting the environment variable
  * MK_NO_ROUTER_FUSION makes every step use the separate router phase instead (for comparisons).
  * (The pages' demos likewise prepare their kernel layouts from the checkpoints before serving:
