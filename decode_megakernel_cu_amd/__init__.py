@@ -175,6 +175,7 @@ def mk_set_trace(ctx, enable: bool) -> None:
 
 
 MK_MFMA_MIN_ROWS = 3  # MK_MFMA_MIN_ROWS
+MK_MFMA_MIN_ROWS_DENSE = 2  # MK_MFMA_MIN_ROWS_DENSE
 MK_MAX_M = 16
 
 

@@ -504,7 +504,7 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
   c->launches = 0;
   c->poisoned = false;
   c->trace = false;
-  c->mfma_min_rows = kMfmaMinRows;
+  c->mfma_min_rows = cfg->n_experts > 0 ? kMfmaMinRows : MK_MFMA_MIN_ROWS_DENSE;
   c->last_barriers = 0;
   c->last_status = nullptr;
   c->n_loaded = 0;

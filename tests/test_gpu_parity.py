@@ -390,6 +390,11 @@ def test_dense_two_layers(B, T):
     parity(DENSE_SMALL, synth.Spec(seed=20), B, T, 4096)
 
 
+# two token rows of the dense model on the matrix cores (its default from two rows)
+def test_dense_two_layers_two_rows_matrix_cores():
+    parity(DENSE_SMALL, synth.Spec(seed=21), 2, 1, 4096, mfma_min_rows=2)
+
+
 # GQA over 40000 positions: 8 kv heads, 32 splits of 1264 positions per (sequence, kv head); and
 # batch 2 over 60000 (16 splits of 3760)
 @pytest.mark.parametrize("B,kv_len", [(1, 40000), (2, 60000)])
