@@ -244,6 +244,13 @@ def test_router_fusion_against_router_phase(B, T, kv_len, rows, monkeypatch):
     assert diff < 1e-4, f"fused and separate router phases differ by {diff:.3e} of the logit scale"
 
 
+# more experts than half the grid: each workgroup takes whole folded router rows (no column parts)
+@pytest.mark.parametrize("B,T", [(1, 1), (4, 1), (1, 5)])
+def test_router_fusion_whole_rows(B, T):
+    cfg = replace(synth.TINY, name="tiny-200experts", n_experts=200, top_k=2)
+    parity(cfg, synth.Spec(seed=6), B, T, 40)
+
+
 # a share of the same model over twice the tensor-parallel ranks: 8 heads, padded to the 16 rows of
 # the attention tiles (the absorbed query, the merge and W_uv keep 8)
 @pytest.mark.parametrize("B,T,kv_len", [(1, 1, 4096), (8, 1, 700), (1, 7, 2000)])
