@@ -244,6 +244,14 @@ def test_router_fusion_against_router_phase(B, T, kv_len, rows, monkeypatch):
     assert diff < 1e-4, f"fused and separate router phases differ by {diff:.3e} of the logit scale"
 
 
+# renormalised router weights (norm_topk) with a shared expert: the folded router at 1 row (vector
+# units) and 4 rows (matrix cores), and the separate router phase at 16 rows
+@pytest.mark.parametrize("B,T,kv_len", [(1, 1, 40), (4, 1, 40), (2, 8, 30)])
+def test_tiny_norm_topk_shared(B, T, kv_len):
+    cfg = replace(synth.TINY, name="tiny-normtopk", norm_topk=1, shared_ffn=256)
+    parity(cfg, synth.Spec(seed=8), B, T, kv_len)
+
+
 # more experts than half the grid: each workgroup takes whole folded router rows (no column parts)
 @pytest.mark.parametrize("B,T", [(1, 1), (4, 1), (1, 5)])
 def test_router_fusion_whole_rows(B, T):
