@@ -247,6 +247,8 @@ def cpu_baseline(sample_layers: int = 8, budget_s: float = 12.0) -> dict:
 PHASES = {
     "gqa": ["qkv", "attention", "merge", "w_o"],
     "mla": ["q_a+kv_a", "q_b", "absorb", "attention", "merge", "w_uv", "w_o"],
+    # 2-row steps merge the split-KV partials and apply W_uv in one phase
+    "mla_mfused": ["q_a+kv_a", "q_b", "absorb", "attention", "merge+w_uv", "w_o"],
     "kda": ["qkv", "delta_rule", "w_o"],
 }
 MOE_PHASES = ["router+shared_up", "experts_up", "experts_down"]
@@ -255,15 +257,16 @@ MOE_PHASES_FUSED = ["shared+experts_up", "experts_down"]
 DENSE_PHASES = ["gate+up", "down"]  # n_experts = 0: the SwiGLU block alone
 
 
-def phase_names(cfg, fused: bool = False) -> list[str]:
+def phase_names(cfg, fused: bool = False, mfused: bool = False) -> list[str]:
     names = ["embed"]
     for l in range(cfg.n_layers):
         kind = cfg.layer_kind(l)
+        attn = PHASES["mla_mfused" if kind == "mla" and mfused else kind]
         if cfg.n_experts:
             moe = MOE_PHASES_FUSED if fused else MOE_PHASES
-            names += [f"{kind}:{p}" for p in PHASES[kind]] + [f"moe:{p}" for p in moe]
+            names += [f"{kind}:{p}" for p in attn] + [f"moe:{p}" for p in moe]
         else:
-            names += [f"{kind}:{p}" for p in PHASES[kind]] + [f"ffn:{p}" for p in DENSE_PHASES]
+            names += [f"{kind}:{p}" for p in attn] + [f"ffn:{p}" for p in DENSE_PHASES]
     return names + ["lm_head"]
 
 
@@ -273,9 +276,12 @@ def trace_summary(cfg, tr: np.ndarray, tick_ns: float = 10.0) -> dict:
     itself from the last arrival to the last departure. Segments inside a phase are medians over
     workgroups of the differences between its stamps (a stamp of 0 means the phase has no such
     mark)."""
-    names = phase_names(cfg)
-    if tr.shape[0] < len(names) and cfg.n_experts:  # a step with the router folded: one MoE phase fewer per layer
-        names = phase_names(cfg, fused=True)
+    # steps with the router folded (one MoE phase fewer per layer) or the merge and W_uv fused (one
+    # MLA phase fewer): the longest phase list the trace holds (greedy and sampling steps add a barrier)
+    for fused, mfused in ((False, False), (True, False), (True, True), (False, True)):
+        names = phase_names(cfg, fused, mfused)
+        if len(names) <= tr.shape[0]:
+            break
     t = tr.astype(np.int64)
     arr, dep = t[:, :, 0], t[:, :, 1]
     t0 = arr[0].min()

@@ -655,6 +655,13 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
     return fail(MK_E_UNSUPPORTED, "a phase of this step does not fit the workgroup's LDS");
   // split-KV: chunks (at least kChunk positions) sized so that the tasks of the step about fill the grid
   const int npos = kv_len + T;
+  // merge and W_uv in one phase: MLA layers, 2 rows on the vector executor, v_dim 128 (four 32-row
+  // blocks per head), a workgroup per (row, head, block). Each such workgroup reads all of its
+  // head's split-KV partials (266 KB at batch 1 over 4096 positions): at 1 row that read costs what
+  // the phase saves (9.56 ms against 9.51), at 2 rows, with twice the workgroups, it gains 2%
+  // (12.65 against 12.90); longer splits make the attention slower than the read gets faster.
+  const bool mfuse = g.attn_kind != MK_ATTN_GQA && !mf && M == 2 && g.v_dim == 128 && g.kv_lora == 512 &&
+                     M * g.n_heads * 4 <= c->nblocks && !std::getenv("MK_NO_MERGE_FUSION");
   int chunk = kChunk;
   if (g.attn_kind != MK_ATTN_GQA && c->nblocks > 0) {  // whole kSub-position tiles per task
     const int even = (int)(((long long)B * npos + c->nblocks - 1) / c->nblocks);
@@ -711,6 +718,7 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   p.att = f(w.att); p.o2 = f(w.o2); p.part = f(w.part); p.rlog = f(w.rlog); p.sact = f(w.sact); p.eact = f(w.eact);
   p.x2 = f(w.x2); p.ssq = f(w.ssq);
   p.rfuse = router_fusion(g, M, c->nblocks, mf) && !std::getenv("MK_NO_ROUTER_FUSION") ? 1 : 0;
+  p.mfuse = mfuse ? 1 : 0;
   p.wsb = reinterpret_cast<const char*>(ws);
   p.ws_bytes = (uint32_t)w.total;
   p.watchdog_ticks = c->watchdog_ticks;
@@ -741,7 +749,7 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   int nb = (greedy || smp) ? 2 : 1;  // the LM head's barrier, and the one before greedy or sampled tokens
   for (int l = 0; l < g.n_layers; ++l) {  // attention phases, then 3 MoE phases (router fusion, dense: 2)
     const int k = layer_kind(g, l);
-    nb += (k == kGqa ? 4 : k == kMla ? 7 : 3) + (g.n_experts && !p.rfuse ? 3 : 2);
+    nb += (k == kGqa ? 4 : k == kMla ? 7 - p.mfuse : 3) + (g.n_experts && !p.rfuse ? 3 : 2);
   }
   c->last_barriers = use_static ? 0 : nb;  // a static step records no trace
   g_err.clear();

@@ -83,6 +83,8 @@ struct Params {
   // shared expert's gate/up rows run in the routed-expert phase, one phase fewer per layer. The
   // hidden state then alternates between x (input of even layers) and x2 (input of odd layers).
   int32_t rfuse;
+  // split-KV merge and W_uv in one phase (the 2-row vector instances of MLA layers)
+  int32_t mfuse;
   float* x2;
   float* ssq;  // [grid][M] per-workgroup sums of squares of the MoE input (router fusion)
   const char* wsb;    // workspace base: activations are addressed by byte offsets from here

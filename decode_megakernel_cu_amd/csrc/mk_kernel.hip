@@ -2386,9 +2386,105 @@ struct Smem {
   uint64_t stamps[2][kTraceStamps];  // trace stamps of the current and the previous record
 };
 
-enum PhaseType : int { PT_GEMV = 0, PT_ATTN_GQA, PT_ATTN_MLA, PT_MERGE, PT_KDA, PT_EXPERT };
+enum PhaseType : int { PT_GEMV = 0, PT_ATTN_GQA, PT_ATTN_MLA, PT_MERGE, PT_KDA, PT_EXPERT, PT_MUV };
 
-__device__ __forceinline__ int attn_phases(int kind) { return kind == kGqa ? 4 : kind == kMla ? 7 : 3; }
+__device__ __forceinline__ int attn_phases(int kind, int mfuse) {
+  return kind == kGqa ? 4 : kind == kMla ? 7 - mfuse : 3;
+}
+
+// ----------------------------------------------------------------------------------------------
+// Split-KV merge and W_uv in one phase (mfuse; the host uses it for 2-row steps of MLA layers). Task
+// (token m, head h, block rb of 32 of the head's v_dim = 128 output rows) runs on workgroup
+// m*nh*4 + h*4 + rb: it merges the head's split-KV partials itself (every block of the head reads
+// the same partials) and multiplies the merged 512 values by its 32 rows of W_uv, so W_uv waits on
+// no grid barrier of its own. Merge arithmetic as merge_phase: weights exp(max_s - max), values
+// summed and divided by the weighted sums.
+// ----------------------------------------------------------------------------------------------
+constexpr int kMuvRB = 4;     // output row blocks per head
+constexpr int kMuvNB = 8;     // splits per thread per batch of loads
+template <int MM>
+__device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem) {
+  constexpr int kvl = 512, vd = 128, rows = vd / kMuvRB;  // the host admits kv_lora 512, v_dim 128
+  static_assert(rows * 16 == kThreads, "one thread per (row, 32-column quarter) of the block");
+  const int nh = rfl(p.nh), nsplit = rfl(p.nsplit), stride = kvl + kPartPad;
+  const int b = blockIdx.x;
+  if (b >= MM * nh * kMuvRB) return;
+  const int m = b / (nh * kMuvRB), h = (b / kMuvRB) % nh, rb = b % kMuvRB;
+  const int tid = tid_x(), lane = lane_id(), w = wave_id();
+  const float* part = rflp(p.part) + (size_t)(m * nh + h) * nsplit * stride;
+  float* hdr = smem;                // [nsplit][4] max, sum
+  f32x4* grp = reinterpret_cast<f32x4*>(hdr + 4 * kMaxGrid);  // [4][128] split-group sums
+  float* vb = hdr + 4 * kMaxGrid + 4 * 4 * 128;               // [512] merged values
+  float* ls = vb + kvl;                                       // the weighted sum
+  // this thread's W_uv row (rb*rows + tid/16) and its 32 columns [32 (tid%16), +32), 4 chunks
+  const uint16_t* wr = rflp(ly->w_uv) + ((size_t)h * vd + rb * rows + (tid >> 4)) * kvl + 32 * (tid & 15);
+  uint4 wv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) wv[u] = ldw(wr + 8 * u);
+  dma_rows<kCoherent>(ws.r, hdr, 1, nsplit, 0, [&](int, int c) { return ws.off(part + (size_t)c * stride); });
+  // values: thread (quad cq of the 128, split group sg of 4) sums splits sg + 4k
+  const int cq = tid & 127, sg = tid >> 7, per = (nsplit + 3 - sg) >> 2, nb = (per + kMuvNB - 1) / kMuvNB;
+  auto load = [&](f32x4 (&v)[kMuvNB], int k) {
+#pragma unroll
+    for (int u = 0; u < kMuvNB; ++u) {
+      const int s = min(sg + 4 * (k * kMuvNB + u), nsplit - 1);
+      v[u] = ws.ld4(part + (size_t)s * stride + kPartPad + 4 * cq);
+    }
+  };
+  f32x4 va[kMuvNB], vbb[kMuvNB];
+  load(va, 0);
+  wait_vm();
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int s = lane; s < nsplit; s += 64) mx = fmaxf(mx, hdr[4 * s]);
+  mx = wave_max(mx, 64);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto add = [&](const f32x4 (&v)[kMuvNB], int k) {
+#pragma unroll
+    for (int u = 0; u < kMuvNB; ++u) {
+      const int j = k * kMuvNB + u, s = sg + 4 * j;
+      if (j < per) {
+        const float ms = hdr[4 * s];
+        acc += (ms == -INFINITY ? 0.f : __expf(ms - mx)) * v[u];
+      }
+    }
+  };
+  for (int k = 0; k < nb; k += 2) {
+    if (k + 1 < nb) load(vbb, k + 1);
+    add(va, k);
+    if (k + 2 < nb) load(va, k + 2);
+    if (k + 1 < nb) add(vbb, k + 1);
+  }
+  grp[sg * 128 + cq] = acc;
+  if (w == 0) {  // the weighted sum of the splits' sums
+    float l = 0.f;
+    for (int s = lane; s < nsplit; s += 64) {
+      const float ms = hdr[4 * s];
+      l += (ms == -INFINITY ? 0.f : __expf(ms - mx)) * hdr[4 * s + 1];
+    }
+    l = wave_sum(l, 64);
+    if (lane == 0) ls[0] = l;
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const f32x4 v = grp[tid] + grp[128 + tid] + grp[256 + tid] + grp[384 + tid];
+    *reinterpret_cast<f32x4*>(vb + 4 * tid) = v * (1.0f / ls[0]);
+  }
+  __syncthreads();
+  // this workgroup's W_uv rows: 16 threads per row, 32 columns each
+  float a = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float f[8];
+    unpack8(wv[u], f);
+    const float* x = vb + 32 * (tid & 15) + 8 * u;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(x), x1 = *reinterpret_cast<const f32x4*>(x + 4);
+    a += f[0] * x0.x + f[1] * x0.y + f[2] * x0.z + f[3] * x0.w + f[4] * x1.x + f[5] * x1.y + f[6] * x1.z + f[7] * x1.w;
+  }
+  a = wave_sum(a, 16);
+  if ((tid & 15) == 0) stc(rflp(p.o2) + ((size_t)m * nh + h) * vd + rb * rows + (tid >> 4), a);
+}
+
 
 __device__ __forceinline__ void norm_input(Gemv& g, const float* src, int ld, int K, const uint16_t* gain) {
   g.stage = S_NORM;
@@ -2438,7 +2534,7 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
     return PT_GEMV;
   }
   const int kind = ly->kind;
-  const int na = attn_phases(kind);
+  const int na = attn_phases(kind, p.mfuse);
   float* xl = xcur(p, l);
   if (i >= na) {
     float* xm = xcur(p, l + 1);  // the MoE block's input (and output: its residual is added in place)
@@ -2515,7 +2611,8 @@ __device__ __forceinline__ int describe(const Params& p, int l, int i, Gemv& g, 
   } else {
   if (kind == kMla) {
     const int lat = p.kvl + p.rd, qd = p.nd + p.rd;
-    switch (i) {
+    if (p.mfuse && i == 4) return PT_MUV;
+    switch (p.mfuse && i >= 5 ? i + 1 : i) {
       case 0:
         norm_input(g, xl, p.H, p.H, ly->attn_norm);
         g.kind = G_STACK;
@@ -2848,7 +2945,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
   bool resident = false;  // the LDS input buffer holds this layer's normalised MoE input
   for (int l = 0; l <= p.L; ++l) {
     const LayerDev* ly = &sm.lyd[l & 1];
-    const int nph = (l == p.L) ? 1 : attn_phases(ly->kind) + (p.E && !p.rfuse ? 3 : 2);
+    const int nph = (l == p.L) ? 1 : attn_phases(ly->kind, p.mfuse) + (p.E && !p.rfuse ? 3 : 2);
     for (int i = 0; i < nph; ++i) {
       Gemv g{};
       typename PlanOf<MF>::type q{};
@@ -2937,6 +3034,12 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
           if constexpr (AF != MK_ATTN_GQA) {
             if (l + 1 < p.L) fetch_layer(p, sm.lyd, l + 1);
             mla_attn_phase<AF == MK_ATTN_MLA ? 64 : 0, MM == 1 && !MF>(p, ly, ws, sm.buf, sm.rope, trec);
+            resident = false;
+          }
+          break;
+        case PT_MUV:  // (the 2-row instances only: in the 1-row ones its code alone cost 1%)
+          if constexpr (AF != MK_ATTN_GQA && MM == 2 && !MF) {
+            muv_phase<MM>(p, ly, ws, sm.buf);
             resident = false;
           }
           break;

@@ -244,6 +244,27 @@ def test_router_fusion_against_router_phase(B, T, kv_len, rows, monkeypatch):
     assert diff < 1e-4, f"fused and separate router phases differ by {diff:.3e} of the logit scale"
 
 
+# The split-KV merge and W_uv in one phase (2 token rows of MLA layers on the vector executor)
+# against the separate merge phase (MK_NO_MERGE_FUSION): both match the oracle, select the same
+# experts, and their logits agree to fp32 summation-order differences.
+@pytest.mark.parametrize("B,T,kv_len", [(2, 1, 4096), (1, 2, 300)])
+def test_merge_fusion_against_merge_phase(B, T, kv_len, monkeypatch):
+    runs = {}
+    for fused in (True, False):
+        if fused:
+            monkeypatch.delenv("MK_NO_MERGE_FUSION", raising=False)
+        else:
+            monkeypatch.setenv("MK_NO_MERGE_FUSION", "1")
+        dm, got, route, ref, caches, init = run_pair(K3_SMALL, synth.Spec(seed=9), B, T, kv_len)
+        check_logits(got, ref)
+        check_route(route, ref)
+        check_cache(K3_SMALL, dm, caches, init, B, T, kv_len)
+        runs[fused] = (got, route)
+    assert np.array_equal(runs[True][1], runs[False][1])
+    diff = np.abs(runs[True][0] - runs[False][0]).max() / np.abs(runs[False][0]).max()
+    assert diff < 1e-4, f"fused and separate merge phases differ by {diff:.3e} of the logit scale"
+
+
 # renormalised router weights (norm_topk) with a shared expert: the folded router at 1 row (vector
 # units) and 4 rows (matrix cores), and the separate router phase at 16 rows
 @pytest.mark.parametrize("B,T,kv_len", [(1, 1, 40), (4, 1, 40), (2, 8, 30)])
@@ -261,7 +282,7 @@ def test_router_fusion_whole_rows(B, T):
 
 # a share of the same model over twice the tensor-parallel ranks: 8 heads, padded to the 16 rows of
 # the attention tiles (the absorbed query, the merge and W_uv keep 8)
-@pytest.mark.parametrize("B,T,kv_len", [(1, 1, 4096), (8, 1, 700), (1, 7, 2000)])
+@pytest.mark.parametrize("B,T,kv_len", [(1, 1, 4096), (8, 1, 700), (1, 7, 2000), (2, 1, 700)])
 def test_k3_two_layers_eight_heads(B, T, kv_len):
     parity(replace(K3_SMALL, name="k3-2layer-8heads", n_heads=8), synth.Spec(seed=5), B, T, kv_len)
 
