@@ -367,7 +367,7 @@ WsLayout ws_layout(const mk_config& c, uint64_t M, uint64_t nsplit, bool trace) 
     return at;
   };
   w.flags = take(kMaxBlocks * 4);
-  w.status = take(64 * 4);
+  w.status = take(kStatusWords * 4);
   w.trace_slots = trace ? (uint64_t)(3 + 10 * c.n_layers) * kMaxBlocks : 0;
   w.trace = take(w.trace_slots * kTraceStamps * 8);
   w.rope = take((uint64_t)MK_MAX_NEW_TOKENS * kMaxRopePairs * 2 * 4);
@@ -655,13 +655,15 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
     return fail(MK_E_UNSUPPORTED, "a phase of this step does not fit the workgroup's LDS");
   // split-KV: chunks (at least kChunk positions) sized so that the tasks of the step about fill the grid
   const int npos = kv_len + T;
-  // merge and W_uv in one phase: MLA layers, 2 rows on the vector executor, v_dim 128 (four 32-row
-  // blocks per head), a workgroup per (row, head, block). Each such workgroup reads all of its
-  // head's split-KV partials (266 KB at batch 1 over 4096 positions): at 1 row that read costs what
-  // the phase saves (9.56 ms against 9.51), at 2 rows, with twice the workgroups, it gains 2%
-  // (12.65 against 12.90); longer splits make the attention slower than the read gets faster.
-  const bool mfuse = g.attn_kind != MK_ATTN_GQA && !mf && M == 2 && g.v_dim == 128 && g.kv_lora == 512 &&
-                     M * g.n_heads * 4 <= c->nblocks && !std::getenv("MK_NO_MERGE_FUSION");
+  // merge and W_uv in one phase: MLA layers, 1 or 2 rows on the vector executor, v_dim 128 (four
+  // 32-row blocks per head). At 2 rows a workgroup per (row, head, block) reads all of its head's
+  // split-KV partials (134 KB over 4096 positions): 2% faster than the separate phases. At 1 row
+  // that read is 266 KB, which costs what the phase saves, so each head's 512 latent values are
+  // split over 4 more workgroups (a quarter of the partials each; 16 workgroups per head, with a
+  // counter per head and row block in the last 64 flag words).
+  const bool mfuse = g.attn_kind != MK_ATTN_GQA && !mf && M <= 2 && g.v_dim == 128 && g.kv_lora == 512 &&
+                     g.n_heads <= 16 && g.n_heads * 4 * (M == 1 ? 4 : M) <= c->nblocks &&
+                     !std::getenv("MK_NO_MERGE_FUSION");
   int chunk = kChunk;
   if (g.attn_kind != MK_ATTN_GQA && c->nblocks > 0) {  // whole kSub-position tiles per task
     const int even = (int)(((long long)B * npos + c->nblocks - 1) / c->nblocks);
@@ -741,7 +743,8 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   if (p.nsplit > c->lt.nsplit_max) return fail(MK_E_UNSUPPORTED, "%d split-KV chunks, at most %d", p.nsplit, c->lt.nsplit_max);
   hipError_t e = hipSetDevice(c->device);
   if (e == hipSuccess && use_static)  // barrier flags and status words start at zero
-    e = launch_clear_words(p.flags, (int)((w.status + 64 * 4 - w.flags) / 4), static_cast<hipStream_t>(stream));
+    e = launch_clear_words(p.flags, (int)((w.status + kStatusWords * 4 - w.flags) / 4),
+                           static_cast<hipStream_t>(stream));
   if (e == hipSuccess) e = launch_decode(p, c->nblocks, mf, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MK_E_HIP, "launch failed: %s", hipGetErrorString(e));
   if (!use_static) c->launches++;

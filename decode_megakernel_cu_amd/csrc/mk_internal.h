@@ -12,6 +12,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBlocks = 1024;         // barrier flag slots
 constexpr int kLdsFloats = 36 * 1024;    // 144 KiB of LDS per workgroup
 constexpr int kChunk = 16;               // minimum cache positions per split-KV task
+constexpr int kStatusWords = 64;        // status words: [0] error code, [1] abort flag, [2] detail, [3] token
 constexpr int kSub = 32;                 // cache positions an MLA task stages at once
 constexpr int kGSub = 64;                // cache positions a GQA task stages at once (one per lane)
 constexpr int kGqaTiles = 3;             // GQA value-sum tiles (16 rows x 16 columns) per wave
@@ -75,15 +76,15 @@ struct Params {
   uint16_t* kv;  // GQA: K block then V block; MLA: latent
   float* kda_state;
   // workspace
-  uint32_t* flags;
-  uint32_t* status;  // [0] error code, [1] abort flag, [2] detail
+  uint32_t* flags;   // [kMaxBlocks]: barrier flags, then (the last 64) the 1-row merge counters
+  uint32_t* status;  // [0] error code, [1] abort flag, [2] detail, [3] token
   float *rope, *x, *a1, *a2, *a3, *a4, *att, *o2, *part, *rlog, *sact, *eact;
   // router fusion (1- and 2-row vector instances of MoE models): the output projection also computes
   // the router logits from the layer's input and its own input (rows rwx of the layer table), and the
   // shared expert's gate/up rows run in the routed-expert phase, one phase fewer per layer. The
   // hidden state then alternates between x (input of even layers) and x2 (input of odd layers).
   int32_t rfuse;
-  // split-KV merge and W_uv in one phase (the 2-row vector instances of MLA layers)
+  // split-KV merge and W_uv in one phase (the 1- and 2-row vector instances of MLA layers)
   int32_t mfuse;
   float* x2;
   float* ssq;  // [grid][M] per-workgroup sums of squares of the MoE input (router fusion)

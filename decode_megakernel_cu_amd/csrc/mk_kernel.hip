@@ -2393,42 +2393,60 @@ __device__ __forceinline__ int attn_phases(int kind, int mfuse) {
 }
 
 // ----------------------------------------------------------------------------------------------
-// Split-KV merge and W_uv in one phase (mfuse; the host uses it for 2-row steps of MLA layers). Task
-// (token m, head h, block rb of 32 of the head's v_dim = 128 output rows) runs on workgroup
-// m*nh*4 + h*4 + rb: it merges the head's split-KV partials itself (every block of the head reads
-// the same partials) and multiplies the merged 512 values by its 32 rows of W_uv, so W_uv waits on
-// no grid barrier of its own. Merge arithmetic as merge_phase: weights exp(max_s - max), values
-// summed and divided by the weighted sums.
+// Split-KV merge and W_uv in one phase (mfuse; the host uses it for 1- and 2-row steps of MLA
+// layers), so W_uv waits on no grid barrier of its own. Merge arithmetic as merge_phase: weights
+// exp(max_s - max), values summed and divided by the weighted sums.
+// 2 rows: task (token m, head h, block rb of 32 of the head's v_dim = 128 output rows) runs on
+// workgroup m*nh*4 + h*4 + rb; it merges all 512 of the head's latent values (every block of the
+// head reads the same partials) and multiplies them by its 32 rows of W_uv.
+// 1 row: the head's latent values are also split into 4 blocks jb of 128, so 16 workgroups share a
+// head and each reads a quarter of its partials. Task (h, jb, rb) runs on workgroup
+// rb*nh*4 + h*4 + jb (the four row blocks that read the same values sit on one XCD) and writes the
+// 32 partial sums of its latent block. The fourth of a (h, rb)'s four blocks to finish (an integer
+// counter per (h, rb) that grows by 4 per phase, so old mod 4 == 3 marks it) adds the four partials
+// in block order, so the result does not depend on which block finished last.
 // ----------------------------------------------------------------------------------------------
 constexpr int kMuvRB = 4;     // output row blocks per head
 constexpr int kMuvNB = 8;     // splits per thread per batch of loads
+// the 1-row step's counters, one per (head, row block): the last 64 of the barrier's flag words,
+// which no grid polls
+constexpr int kMuvCtr = kMaxBlocks - 64;
+static_assert(kMaxGrid <= kMuvCtr, "the merge counters sit beyond the barrier's flags");
 template <int MM>
 __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem) {
   constexpr int kvl = 512, vd = 128, rows = vd / kMuvRB;  // the host admits kv_lora 512, v_dim 128
-  static_assert(rows * 16 == kThreads, "one thread per (row, 32-column quarter) of the block");
+  constexpr int JB = MM == 1 ? 4 : 1;                     // latent blocks per head
+  constexpr int cols = kvl / JB, nq = cols / 4, ng = kThreads / nq, nu = 4 / JB;
+  static_assert(rows * 16 == kThreads, "one thread per (row, 1/16 of the block's columns)");
   const int nh = rfl(p.nh), nsplit = rfl(p.nsplit), stride = kvl + kPartPad;
   const int b = blockIdx.x;
-  if (b >= MM * nh * kMuvRB) return;
-  const int m = b / (nh * kMuvRB), h = (b / kMuvRB) % nh, rb = b % kMuvRB;
+  if (b >= MM * nh * kMuvRB * JB) return;
+  int m, h, rb, jb;
+  if constexpr (JB == 1) {
+    m = b / (nh * kMuvRB); h = (b / kMuvRB) % nh; rb = b % kMuvRB; jb = 0;
+  } else {
+    m = 0; rb = b / (nh * JB); h = (b % (nh * JB)) / JB; jb = b % JB;
+  }
   const int tid = tid_x(), lane = lane_id(), w = wave_id();
   const float* part = rflp(p.part) + (size_t)(m * nh + h) * nsplit * stride;
   float* hdr = smem;                // [nsplit][4] max, sum
-  f32x4* grp = reinterpret_cast<f32x4*>(hdr + 4 * kMaxGrid);  // [4][128] split-group sums
-  float* vb = hdr + 4 * kMaxGrid + 4 * 4 * 128;               // [512] merged values
-  float* ls = vb + kvl;                                       // the weighted sum
-  // this thread's W_uv row (rb*rows + tid/16) and its 32 columns [32 (tid%16), +32), 4 chunks
-  const uint16_t* wr = rflp(ly->w_uv) + ((size_t)h * vd + rb * rows + (tid >> 4)) * kvl + 32 * (tid & 15);
-  uint4 wv[4];
+  f32x4* grp = reinterpret_cast<f32x4*>(hdr + 4 * kMaxGrid);  // [ng][nq] split-group sums
+  float* vb = hdr + 4 * kMaxGrid + 4 * kThreads;              // [cols] merged values
+  float* ls = vb + kvl;                                       // the weighted sum; the counter's verdict
+  // this thread's W_uv row (rb*rows + tid/16) and its 8*nu columns of the block, nu chunks
+  const uint16_t* wr =
+      rflp(ly->w_uv) + ((size_t)h * vd + rb * rows + (tid >> 4)) * kvl + jb * cols + 8 * nu * (tid & 15);
+  uint4 wv[nu];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) wv[u] = ldw(wr + 8 * u);
+  for (int u = 0; u < nu; ++u) wv[u] = ldw(wr + 8 * u);
   dma_rows<kCoherent>(ws.r, hdr, 1, nsplit, 0, [&](int, int c) { return ws.off(part + (size_t)c * stride); });
-  // values: thread (quad cq of the 128, split group sg of 4) sums splits sg + 4k
-  const int cq = tid & 127, sg = tid >> 7, per = (nsplit + 3 - sg) >> 2, nb = (per + kMuvNB - 1) / kMuvNB;
+  // values: thread (quad cq of the block, split group sg of ng) sums splits sg + ng*k
+  const int cq = tid % nq, sg = tid / nq, per = (nsplit + ng - 1 - sg) / ng, nb = (per + kMuvNB - 1) / kMuvNB;
   auto load = [&](f32x4 (&v)[kMuvNB], int k) {
 #pragma unroll
     for (int u = 0; u < kMuvNB; ++u) {
-      const int s = min(sg + 4 * (k * kMuvNB + u), nsplit - 1);
-      v[u] = ws.ld4(part + (size_t)s * stride + kPartPad + 4 * cq);
+      const int s = min(sg + ng * (k * kMuvNB + u), nsplit - 1);
+      v[u] = ws.ld4(part + (size_t)s * stride + kPartPad + jb * cols + 4 * cq);
     }
   };
   f32x4 va[kMuvNB], vbb[kMuvNB];
@@ -2442,7 +2460,7 @@ __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, c
   auto add = [&](const f32x4 (&v)[kMuvNB], int k) {
 #pragma unroll
     for (int u = 0; u < kMuvNB; ++u) {
-      const int j = k * kMuvNB + u, s = sg + 4 * j;
+      const int j = k * kMuvNB + u, s = sg + ng * j;
       if (j < per) {
         const float ms = hdr[4 * s];
         acc += (ms == -INFINITY ? 0.f : __expf(ms - mx)) * v[u];
@@ -2455,7 +2473,7 @@ __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, c
     if (k + 2 < nb) load(va, k + 2);
     if (k + 1 < nb) add(vbb, k + 1);
   }
-  grp[sg * 128 + cq] = acc;
+  grp[sg * nq + cq] = acc;
   if (w == 0) {  // the weighted sum of the splits' sums
     float l = 0.f;
     for (int s = lane; s < nsplit; s += 64) {
@@ -2466,23 +2484,49 @@ __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, c
     if (lane == 0) ls[0] = l;
   }
   __syncthreads();
-  if (tid < 128) {
-    const f32x4 v = grp[tid] + grp[128 + tid] + grp[256 + tid] + grp[384 + tid];
+  if (tid < nq) {
+    f32x4 v = grp[tid];
+#pragma unroll
+    for (int g = 1; g < ng; ++g) v += grp[g * nq + tid];
     *reinterpret_cast<f32x4*>(vb + 4 * tid) = v * (1.0f / ls[0]);
   }
   __syncthreads();
-  // this workgroup's W_uv rows: 16 threads per row, 32 columns each
+  // this workgroup's W_uv rows over its block: 16 threads per row, 8*nu columns each
   float a = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < nu; ++u) {
     float f[8];
     unpack8(wv[u], f);
-    const float* x = vb + 32 * (tid & 15) + 8 * u;
+    const float* x = vb + 8 * nu * (tid & 15) + 8 * u;
     const f32x4 x0 = *reinterpret_cast<const f32x4*>(x), x1 = *reinterpret_cast<const f32x4*>(x + 4);
     a += f[0] * x0.x + f[1] * x0.y + f[2] * x0.z + f[3] * x0.w + f[4] * x1.x + f[5] * x1.y + f[6] * x1.z + f[7] * x1.w;
   }
   a = wave_sum(a, 16);
-  if ((tid & 15) == 0) stc(rflp(p.o2) + ((size_t)m * nh + h) * vd + rb * rows + (tid >> 4), a);
+  float* o2 = rflp(p.o2) + ((size_t)m * nh + h) * vd + rb * rows;
+  if constexpr (JB == 1) {
+    if ((tid & 15) == 0) stc(o2 + (tid >> 4), a);
+  } else {
+    // partials [h][rb][jb][rows] in the merge's output buffer (unused when the merge is fused)
+    float* op = rflp(p.att) + (size_t)(h * kMuvRB + rb) * JB * rows;
+    if ((tid & 15) == 0) stc(op + jb * rows + (tid >> 4), a);
+    wait_vm();  // this workgroup's partials complete before its count
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add((GLOBAL uint32_t*)(p.flags + kMuvCtr + h * kMuvRB + rb), 1u,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      reinterpret_cast<uint32_t*>(ls)[1] = old % JB;
+    }
+    __syncthreads();
+    if (reinterpret_cast<const uint32_t*>(ls)[1] == JB - 1 && tid < rows) {
+      float q[JB];
+#pragma unroll
+      for (int j = 0; j < JB; ++j) q[j] = ws.ld1(op + j * rows + tid);
+      float sum = q[0];
+#pragma unroll
+      for (int j = 1; j < JB; ++j) sum += q[j];
+      stc(o2 + tid, sum);
+    }
+  }
 }
 
 
@@ -3037,8 +3081,8 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
             resident = false;
           }
           break;
-        case PT_MUV:  // (the 2-row instances only: in the 1-row ones its code alone cost 1%)
-          if constexpr (AF != MK_ATTN_GQA && MM == 2 && !MF) {
+        case PT_MUV:
+          if constexpr (AF != MK_ATTN_GQA && MM <= 2 && !MF) {
             muv_phase<MM>(p, ly, ws, sm.buf);
             resident = false;
           }
