@@ -76,7 +76,7 @@ struct Params {
   uint16_t* kv;  // GQA: K block then V block; MLA: latent
   float* kda_state;
   // workspace
-  uint32_t* flags;   // [kMaxBlocks]: barrier flags, then (the last 64) the 1-row merge counters
+  uint32_t* flags;   // [kMaxBlocks]: barrier flags, then (the last 128) the merge counters
   uint32_t* status;  // [0] error code, [1] abort flag, [2] detail, [3] token
   float *rope, *x, *a1, *a2, *a3, *a4, *att, *o2, *part, *rlog, *sact, *eact;
   // router fusion (1- and 2-row vector instances of MoE models): the output projection also computes

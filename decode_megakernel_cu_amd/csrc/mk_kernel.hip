@@ -2396,37 +2396,30 @@ __device__ __forceinline__ int attn_phases(int kind, int mfuse) {
 // Split-KV merge and W_uv in one phase (mfuse; the host uses it for 1- and 2-row steps of MLA
 // layers), so W_uv waits on no grid barrier of its own. Merge arithmetic as merge_phase: weights
 // exp(max_s - max), values summed and divided by the weighted sums.
-// 2 rows: task (token m, head h, block rb of 32 of the head's v_dim = 128 output rows) runs on
-// workgroup m*nh*4 + h*4 + rb; it merges all 512 of the head's latent values (every block of the
-// head reads the same partials) and multiplies them by its 32 rows of W_uv.
-// 1 row: the head's latent values are also split into 4 blocks jb of 128, so 16 workgroups share a
-// head and each reads a quarter of its partials. Task (h, jb, rb) runs on workgroup
-// rb*nh*4 + h*4 + jb (the four row blocks that read the same values sit on one XCD) and writes the
-// 32 partial sums of its latent block. The fourth of a (h, rb)'s four blocks to finish (an integer
-// counter per (h, rb) that grows by 4 per phase, so old mod 4 == 3 marks it) adds the four partials
-// in block order, so the result does not depend on which block finished last.
+// The head's 512 latent values are split into JB blocks (4 at 1 row, 2 at 2 rows: 256 tasks at 16
+// heads), and its 128 W_uv output rows into 4 blocks rb of 32. Task (m, h, jb, rb) runs on workgroup
+// rb*M*nh*JB + (m*nh + h)*JB + jb (the four row blocks that read the same values sit on one XCD): it
+// merges its latent block (1/JB of the head's partials) and writes the 32 partial sums of its
+// W_uv block over it. The last of a (m, h, rb)'s JB tasks to finish (an integer counter per
+// (m, h, rb) that grows by JB per phase, so old mod JB == JB - 1 marks it) adds the JB partials in
+// block order, so the result does not depend on which task finished last.
 // ----------------------------------------------------------------------------------------------
 constexpr int kMuvRB = 4;     // output row blocks per head
 constexpr int kMuvNB = 8;     // splits per thread per batch of loads
-// the 1-row step's counters, one per (head, row block): the last 64 of the barrier's flag words,
-// which no grid polls
-constexpr int kMuvCtr = kMaxBlocks - 64;
+// the counters, one per (row, head, row block): the last 128 of the barrier's flag words, which no
+// grid polls
+constexpr int kMuvCtr = kMaxBlocks - 128;
 static_assert(kMaxGrid <= kMuvCtr, "the merge counters sit beyond the barrier's flags");
 template <int MM>
 __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem) {
   constexpr int kvl = 512, vd = 128, rows = vd / kMuvRB;  // the host admits kv_lora 512, v_dim 128
-  constexpr int JB = MM == 1 ? 4 : 1;                     // latent blocks per head
+  constexpr int JB = MM == 1 ? 4 : 2;                     // latent blocks per head
   constexpr int cols = kvl / JB, nq = cols / 4, ng = kThreads / nq, nu = 4 / JB;
   static_assert(rows * 16 == kThreads, "one thread per (row, 1/16 of the block's columns)");
   const int nh = rfl(p.nh), nsplit = rfl(p.nsplit), stride = kvl + kPartPad;
   const int b = blockIdx.x;
   if (b >= MM * nh * kMuvRB * JB) return;
-  int m, h, rb, jb;
-  if constexpr (JB == 1) {
-    m = b / (nh * kMuvRB); h = (b / kMuvRB) % nh; rb = b % kMuvRB; jb = 0;
-  } else {
-    m = 0; rb = b / (nh * JB); h = (b % (nh * JB)) / JB; jb = b % JB;
-  }
+  const int g = b % (MM * nh * JB), rb = b / (MM * nh * JB), m = g / (nh * JB), h = (g / JB) % nh, jb = g % JB;
   const int tid = tid_x(), lane = lane_id(), w = wave_id();
   const float* part = rflp(p.part) + (size_t)(m * nh + h) * nsplit * stride;
   float* hdr = smem;                // [nsplit][4] max, sum
@@ -2502,30 +2495,25 @@ __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, c
     a += f[0] * x0.x + f[1] * x0.y + f[2] * x0.z + f[3] * x0.w + f[4] * x1.x + f[5] * x1.y + f[6] * x1.z + f[7] * x1.w;
   }
   a = wave_sum(a, 16);
-  float* o2 = rflp(p.o2) + ((size_t)m * nh + h) * vd + rb * rows;
-  if constexpr (JB == 1) {
-    if ((tid & 15) == 0) stc(o2 + (tid >> 4), a);
-  } else {
-    // partials [h][rb][jb][rows] in the merge's output buffer (unused when the merge is fused)
-    float* op = rflp(p.att) + (size_t)(h * kMuvRB + rb) * JB * rows;
-    if ((tid & 15) == 0) stc(op + jb * rows + (tid >> 4), a);
-    wait_vm();  // this workgroup's partials complete before its count
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t old = __hip_atomic_fetch_add((GLOBAL uint32_t*)(p.flags + kMuvCtr + h * kMuvRB + rb), 1u,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      reinterpret_cast<uint32_t*>(ls)[1] = old % JB;
-    }
-    __syncthreads();
-    if (reinterpret_cast<const uint32_t*>(ls)[1] == JB - 1 && tid < rows) {
-      float q[JB];
+  // partials [m][h][rb][jb][rows] in the merge's output buffer (unused when the merge is fused)
+  float* op = rflp(p.att) + (size_t)((m * nh + h) * kMuvRB + rb) * JB * rows;
+  if ((tid & 15) == 0) stc(op + jb * rows + (tid >> 4), a);
+  wait_vm();  // this workgroup's partials complete before its count
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t* ctr = p.flags + kMuvCtr + (m * nh + h) * kMuvRB + rb;
+    const uint32_t old = __hip_atomic_fetch_add((GLOBAL uint32_t*)ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    reinterpret_cast<uint32_t*>(ls)[1] = old % JB;
+  }
+  __syncthreads();
+  if (reinterpret_cast<const uint32_t*>(ls)[1] == JB - 1 && tid < rows) {
+    float q[JB];
 #pragma unroll
-      for (int j = 0; j < JB; ++j) q[j] = ws.ld1(op + j * rows + tid);
-      float sum = q[0];
+    for (int j = 0; j < JB; ++j) q[j] = ws.ld1(op + j * rows + tid);
+    float sum = q[0];
 #pragma unroll
-      for (int j = 1; j < JB; ++j) sum += q[j];
-      stc(o2 + tid, sum);
-    }
+    for (int j = 1; j < JB; ++j) sum += q[j];
+    stc(rflp(p.o2) + ((size_t)m * nh + h) * vd + rb * rows + tid, sum);
   }
 }
 
