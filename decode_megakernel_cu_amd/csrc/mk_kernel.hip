@@ -2401,8 +2401,10 @@ __device__ __forceinline__ int attn_phases(int kind, int mfuse) {
 // rb*M*nh*JB + (m*nh + h)*JB + jb (the four row blocks that read the same values sit on one XCD): it
 // merges its latent block (1/JB of the head's partials) and writes the 32 partial sums of its
 // W_uv block over it. The last of a (m, h, rb)'s JB tasks to finish (an integer counter per
-// (m, h, rb) that grows by JB per phase, so old mod JB == JB - 1 marks it) adds the JB partials in
-// block order, so the result does not depend on which task finished last.
+// (m, h, rb); old == JB - 1 marks it) adds the JB partials in block order, so the result does not
+// depend on which task finished last, and sets the counter back to zero: every phase, whatever
+// its JB, starts from zero (the workspace starts zeroed; the static scratch's flags are cleared
+// before each launch), and the store completes before that workgroup's next barrier arrival.
 // ----------------------------------------------------------------------------------------------
 constexpr int kMuvRB = 4;     // output row blocks per head
 constexpr int kMuvNB = 8;     // splits per thread per batch of loads
@@ -2500,13 +2502,14 @@ __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, c
   if ((tid & 15) == 0) stc(op + jb * rows + (tid >> 4), a);
   wait_vm();  // this workgroup's partials complete before its count
   __syncthreads();
+  uint32_t* ctr = p.flags + kMuvCtr + (m * nh + h) * kMuvRB + rb;
   if (tid == 0) {
-    uint32_t* ctr = p.flags + kMuvCtr + (m * nh + h) * kMuvRB + rb;
     const uint32_t old = __hip_atomic_fetch_add((GLOBAL uint32_t*)ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    reinterpret_cast<uint32_t*>(ls)[1] = old % JB;
+    reinterpret_cast<uint32_t*>(ls)[1] = old;
   }
   __syncthreads();
   if (reinterpret_cast<const uint32_t*>(ls)[1] == JB - 1 && tid < rows) {
+    if (tid == 0) stc_u32(ctr, 0u);  // every arrival is in: the next phase starts from zero
     float q[JB];
 #pragma unroll
     for (int j = 0; j < JB; ++j) q[j] = ws.ld1(op + j * rows + tid);

@@ -267,6 +267,14 @@ def test_merge_fusion_against_merge_phase(B, T, kv_len, monkeypatch):
     assert diff < 1e-4, f"fused and separate merge phases differ by {diff:.3e} of the logit scale"
 
 
+# 2-row and 1-row steps in turn on one context (the model's single MLA layer fuses the merge with
+# 2 latent blocks at 2 rows and 4 at 1 row): each step's counters start at zero whatever the
+# previous step's row count
+def test_merge_fusion_row_counts_alternate():
+    for B in (2, 1, 2, 1):
+        parity(HYB_SMALL, synth.Spec(seed=3), B, 1, 300)
+
+
 # renormalised router weights (norm_topk) with a shared expert: the folded router at 1 row (vector
 # units) and 4 rows (matrix cores), and the separate router phase at 16 rows
 @pytest.mark.parametrize("B,T,kv_len", [(1, 1, 40), (4, 1, 40), (2, 8, 30)])
