@@ -2396,8 +2396,8 @@ __device__ __forceinline__ int attn_phases(int kind, int mfuse) {
 // Split-KV merge and W_uv in one phase (mfuse; the host uses it for 1- and 2-row steps of MLA
 // layers), so W_uv waits on no grid barrier of its own. Merge arithmetic as merge_phase: weights
 // exp(max_s - max), values summed and divided by the weighted sums.
-// The head's 512 latent values are split into JB blocks (4 at 1 row, 2 at 2 rows: 256 tasks at 16
-// heads), and its 128 W_uv output rows into 4 blocks rb of 32. Task (m, h, jb, rb) runs on workgroup
+// The head's 512 latent values are split into JB blocks (4 at 1 row, 2 at 2 rows, 1 at 4 rows on the
+// matrix-core instance: 256 tasks at 16 heads), and its 128 W_uv output rows into 4 blocks rb of 32. Task (m, h, jb, rb) runs on workgroup
 // rb*M*nh*JB + (m*nh + h)*JB + jb (the four row blocks that read the same values sit on one XCD): it
 // merges its latent block (1/JB of the head's partials) and writes the 32 partial sums of its
 // W_uv block over it. The last of a (m, h, rb)'s JB tasks to finish (an integer counter per
@@ -2415,7 +2415,7 @@ static_assert(kMaxGrid <= kMuvCtr, "the merge counters sit beyond the barrier's 
 template <int MM>
 __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem) {
   constexpr int kvl = 512, vd = 128, rows = vd / kMuvRB;  // the host admits kv_lora 512, v_dim 128
-  constexpr int JB = MM == 1 ? 4 : 2;                     // latent blocks per head
+  constexpr int JB = MM == 1 ? 4 : MM == 2 ? 2 : 1;       // latent blocks per head
   constexpr int cols = kvl / JB, nq = cols / 4, ng = kThreads / nq, nu = 4 / JB;
   static_assert(rows * 16 == kThreads, "one thread per (row, 1/16 of the block's columns)");
   const int nh = rfl(p.nh), nsplit = rfl(p.nsplit), stride = kvl + kPartPad;
@@ -2497,6 +2497,10 @@ __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, c
     a += f[0] * x0.x + f[1] * x0.y + f[2] * x0.z + f[3] * x0.w + f[4] * x1.x + f[5] * x1.y + f[6] * x1.z + f[7] * x1.w;
   }
   a = wave_sum(a, 16);
+  if constexpr (JB == 1) {  // whole heads: the sum is complete
+    if ((tid & 15) == 0) stc(rflp(p.o2) + ((size_t)m * nh + h) * vd + rb * rows + (tid >> 4), a);
+    return;
+  }
   // partials [m][h][rb][jb][rows] in the merge's output buffer (unused when the merge is fused)
   float* op = rflp(p.att) + (size_t)((m * nh + h) * kMuvRB + rb) * JB * rows;
   if ((tid & 15) == 0) stc(op + jb * rows + (tid >> 4), a);
@@ -3073,7 +3077,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
           }
           break;
         case PT_MUV:
-          if constexpr (AF != MK_ATTN_GQA && MM <= 2 && !MF) {
+          if constexpr (AF != MK_ATTN_GQA && ((MM <= 2 && !MF) || (MM == 4 && MF))) {
             muv_phase<MM>(p, ly, ws, sm.buf);
             resident = false;
           }
