@@ -2396,8 +2396,9 @@ __device__ __forceinline__ int attn_phases(int kind, int mfuse) {
 // Split-KV merge and W_uv in one phase (mfuse; the host uses it for 1- and 2-row steps of MLA
 // layers), so W_uv waits on no grid barrier of its own. Merge arithmetic as merge_phase: weights
 // exp(max_s - max), values summed and divided by the weighted sums.
-// The head's 512 latent values are split into JB blocks (4 at 1 row, 2 at 2 rows, 1 at 4 rows on the
-// matrix-core instance: 256 tasks at 16 heads), and its 128 W_uv output rows into 4 blocks rb of 32. Task (m, h, jb, rb) runs on workgroup
+// The head's 512 latent values are split into JB blocks (4 at 1 row, 2 at 2 rows, 1 at 4 and 8 rows
+// on the matrix-core instances) and its 128 W_uv output rows into RB blocks rb (4 of 32 rows; 2 of 64
+// at 8 rows), 256 tasks at 16 heads. Task (m, h, jb, rb) runs on workgroup
 // rb*M*nh*JB + (m*nh + h)*JB + jb (the four row blocks that read the same values sit on one XCD): it
 // merges its latent block (1/JB of the head's partials) and writes the 32 partial sums of its
 // W_uv block over it. The last of a (m, h, rb)'s JB tasks to finish (an integer counter per
@@ -2406,7 +2407,7 @@ __device__ __forceinline__ int attn_phases(int kind, int mfuse) {
 // its JB, starts from zero (the workspace starts zeroed; the static scratch's flags are cleared
 // before each launch), and the store completes before that workgroup's next barrier arrival.
 // ----------------------------------------------------------------------------------------------
-constexpr int kMuvRB = 4;     // output row blocks per head
+constexpr int kMuvRB = 4;     // output row blocks per head (up to 4 rows)
 constexpr int kMuvNB = 8;     // splits per thread per batch of loads
 // the counters, one per (row, head, row block): the last 128 of the barrier's flag words, which no
 // grid polls
@@ -2414,13 +2415,15 @@ constexpr int kMuvCtr = kMaxBlocks - 128;
 static_assert(kMaxGrid <= kMuvCtr, "the merge counters sit beyond the barrier's flags");
 template <int MM>
 __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, const Ws& ws, float* smem) {
-  constexpr int kvl = 512, vd = 128, rows = vd / kMuvRB;  // the host admits kv_lora 512, v_dim 128
-  constexpr int JB = MM == 1 ? 4 : MM == 2 ? 2 : 1;       // latent blocks per head
-  constexpr int cols = kvl / JB, nq = cols / 4, ng = kThreads / nq, nu = 4 / JB;
-  static_assert(rows * 16 == kThreads, "one thread per (row, 1/16 of the block's columns)");
+  constexpr int kvl = 512, vd = 128;                 // the host admits kv_lora 512, v_dim 128
+  constexpr int JB = MM == 1 ? 4 : MM == 2 ? 2 : 1;  // latent blocks per head
+  constexpr int RB = MM == 8 ? 2 : kMuvRB;           // output row blocks per head
+  constexpr int rows = vd / RB, tpr = kThreads / rows;  // threads per output row
+  constexpr int cols = kvl / JB, nq = cols / 4, ng = kThreads / nq, nu = cols / (8 * tpr);
+  static_assert(nu >= 1 && nu * 8 * tpr == cols, "tpr threads per row, 8*nu of the block's columns each");
   const int nh = rfl(p.nh), nsplit = rfl(p.nsplit), stride = kvl + kPartPad;
   const int b = blockIdx.x;
-  if (b >= MM * nh * kMuvRB * JB) return;
+  if (b >= MM * nh * RB * JB) return;
   const int g = b % (MM * nh * JB), rb = b / (MM * nh * JB), m = g / (nh * JB), h = (g / JB) % nh, jb = g % JB;
   const int tid = tid_x(), lane = lane_id(), w = wave_id();
   const float* part = rflp(p.part) + (size_t)(m * nh + h) * nsplit * stride;
@@ -2428,9 +2431,9 @@ __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, c
   f32x4* grp = reinterpret_cast<f32x4*>(hdr + 4 * kMaxGrid);  // [ng][nq] split-group sums
   float* vb = hdr + 4 * kMaxGrid + 4 * kThreads;              // [cols] merged values
   float* ls = vb + kvl;                                       // the weighted sum; the counter's verdict
-  // this thread's W_uv row (rb*rows + tid/16) and its 8*nu columns of the block, nu chunks
+  // this thread's W_uv row (rb*rows + tid/tpr) and its 8*nu columns of the block, nu chunks
   const uint16_t* wr =
-      rflp(ly->w_uv) + ((size_t)h * vd + rb * rows + (tid >> 4)) * kvl + jb * cols + 8 * nu * (tid & 15);
+      rflp(ly->w_uv) + ((size_t)h * vd + rb * rows + tid / tpr) * kvl + jb * cols + 8 * nu * (tid % tpr);
   uint4 wv[nu];
 #pragma unroll
   for (int u = 0; u < nu; ++u) wv[u] = ldw(wr + 8 * u);
@@ -2486,27 +2489,27 @@ __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, c
     *reinterpret_cast<f32x4*>(vb + 4 * tid) = v * (1.0f / ls[0]);
   }
   __syncthreads();
-  // this workgroup's W_uv rows over its block: 16 threads per row, 8*nu columns each
+  // this workgroup's W_uv rows over its block: tpr threads per row, 8*nu columns each
   float a = 0.f;
 #pragma unroll
   for (int u = 0; u < nu; ++u) {
     float f[8];
     unpack8(wv[u], f);
-    const float* x = vb + 8 * nu * (tid & 15) + 8 * u;
+    const float* x = vb + 8 * nu * (tid % tpr) + 8 * u;
     const f32x4 x0 = *reinterpret_cast<const f32x4*>(x), x1 = *reinterpret_cast<const f32x4*>(x + 4);
     a += f[0] * x0.x + f[1] * x0.y + f[2] * x0.z + f[3] * x0.w + f[4] * x1.x + f[5] * x1.y + f[6] * x1.z + f[7] * x1.w;
   }
-  a = wave_sum(a, 16);
+  a = wave_sum(a, tpr);
   if constexpr (JB == 1) {  // whole heads: the sum is complete
-    if ((tid & 15) == 0) stc(rflp(p.o2) + ((size_t)m * nh + h) * vd + rb * rows + (tid >> 4), a);
+    if (tid % tpr == 0) stc(rflp(p.o2) + ((size_t)m * nh + h) * vd + rb * rows + tid / tpr, a);
     return;
   }
   // partials [m][h][rb][jb][rows] in the merge's output buffer (unused when the merge is fused)
-  float* op = rflp(p.att) + (size_t)((m * nh + h) * kMuvRB + rb) * JB * rows;
+  float* op = rflp(p.att) + (size_t)((m * nh + h) * RB + rb) * JB * rows;
   if ((tid & 15) == 0) stc(op + jb * rows + (tid >> 4), a);
   wait_vm();  // this workgroup's partials complete before its count
   __syncthreads();
-  uint32_t* ctr = p.flags + kMuvCtr + (m * nh + h) * kMuvRB + rb;
+  uint32_t* ctr = p.flags + kMuvCtr + (m * nh + h) * RB + rb;
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add((GLOBAL uint32_t*)ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     reinterpret_cast<uint32_t*>(ls)[1] = old;
@@ -3077,7 +3080,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(Params pk) {
           }
           break;
         case PT_MUV:
-          if constexpr (AF != MK_ATTN_GQA && ((MM <= 2 && !MF) || (MM == 4 && MF))) {
+          if constexpr (AF != MK_ATTN_GQA && ((MM <= 2 && !MF) || ((MM == 4 || MM == 8) && MF))) {
             muv_phase<MM>(p, ly, ws, sm.buf);
             resident = false;
           }
