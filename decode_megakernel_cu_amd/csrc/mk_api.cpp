@@ -656,14 +656,14 @@ static int decode_step(mk_ctx* c, int B, int T, int kv_len, const int32_t* d_tok
   // split-KV: chunks (at least kChunk positions) sized so that the tasks of the step about fill the grid
   const int npos = kv_len + T;
   // merge and W_uv in one phase: MLA layers with v_dim 128 and kv_lora 512, 1 or 2 rows on the
-  // vector executor or exactly 4 or 8 on the matrix cores. A workgroup per (row, head, latent block,
-  // block of W_uv rows): 4 latent blocks at 1 row, 2 at 2 rows, 1 at 4 and 8 rows (64-row blocks at
-  // 8), so 16 workgroups per head, with a counter per (row, head, row block) in the last 128 flag
-  // words where a head's latent values are split. With whole heads
+  // vector executor or 3 to 8 on the matrix cores. A workgroup per (row, head, latent block, block
+  // of W_uv rows): 4 latent blocks at 1 row, 2 at 2 rows, 1 at 3-8 rows (64-row blocks in the 8-row
+  // instance), at most 256 workgroups at 16 heads, with a counter per (row, head, row block) in the
+  // last 128 flag words where a head's latent values are split. With whole heads
   // per workgroup at 1 row, each one's read of the head's split-KV partials (266 KB over 4096
   // positions) cost what the phase saved.
-  const bool mfuse = g.attn_kind != MK_ATTN_GQA && (mf ? M == 4 || M == 8 : M <= 2) && g.v_dim == 128 &&
-                     g.kv_lora == 512 && g.n_heads <= 16 && g.n_heads * 16 <= c->nblocks &&
+  const bool mfuse = g.attn_kind != MK_ATTN_GQA && (mf ? M >= 3 && M <= 8 : M <= 2) && g.v_dim == 128 &&
+                     g.kv_lora == 512 && g.n_heads <= 16 && g.n_heads * (M <= 2 ? 16 : M <= 4 ? 4 * M : 2 * M) <= c->nblocks &&
                      !std::getenv("MK_NO_MERGE_FUSION");
   int chunk = kChunk;
   if (g.attn_kind != MK_ATTN_GQA && c->nblocks > 0) {  // whole kSub-position tiles per task

@@ -2396,9 +2396,9 @@ __device__ __forceinline__ int attn_phases(int kind, int mfuse) {
 // Split-KV merge and W_uv in one phase (mfuse; the host uses it for 1- and 2-row steps of MLA
 // layers), so W_uv waits on no grid barrier of its own. Merge arithmetic as merge_phase: weights
 // exp(max_s - max), values summed and divided by the weighted sums.
-// The head's 512 latent values are split into JB blocks (4 at 1 row, 2 at 2 rows, 1 at 4 and 8 rows
-// on the matrix-core instances) and its 128 W_uv output rows into RB blocks rb (4 of 32 rows; 2 of 64
-// at 8 rows), 256 tasks at 16 heads. Task (m, h, jb, rb) runs on workgroup
+// The head's 512 latent values are split into JB blocks (4 at 1 row, 2 at 2 rows, 1 at 3-8 rows on
+// the matrix-core instances) and its 128 W_uv output rows into RB blocks rb (4 of 32 rows; 2 of 64
+// in the 8-row instance), at most 256 tasks at 16 heads. Task (m, h, jb, rb) runs on workgroup
 // rb*M*nh*JB + (m*nh + h)*JB + jb (the four row blocks that read the same values sit on one XCD): it
 // merges its latent block (1/JB of the head's partials) and writes the 32 partial sums of its
 // W_uv block over it. The last of a (m, h, rb)'s JB tasks to finish (an integer counter per
@@ -2422,9 +2422,10 @@ __device__ __forceinline__ void muv_phase(const Params& p, const LayerDev* ly, c
   constexpr int cols = kvl / JB, nq = cols / 4, ng = kThreads / nq, nu = cols / (8 * tpr);
   static_assert(nu >= 1 && nu * 8 * tpr == cols, "tpr threads per row, 8*nu of the block's columns each");
   const int nh = rfl(p.nh), nsplit = rfl(p.nsplit), stride = kvl + kPartPad;
+  const int M = MM <= 2 ? MM : rfl(p.M);  // the matrix-core instances take 3..MM rows
   const int b = blockIdx.x;
-  if (b >= MM * nh * RB * JB) return;
-  const int g = b % (MM * nh * JB), rb = b / (MM * nh * JB), m = g / (nh * JB), h = (g / JB) % nh, jb = g % JB;
+  if (b >= M * nh * RB * JB) return;
+  const int g = b % (M * nh * JB), rb = b / (M * nh * JB), m = g / (nh * JB), h = (g / JB) % nh, jb = g % JB;
   const int tid = tid_x(), lane = lane_id(), w = wave_id();
   const float* part = rflp(p.part) + (size_t)(m * nh + h) * nsplit * stride;
   float* hdr = smem;                // [nsplit][4] max, sum

@@ -180,7 +180,7 @@ int mk_create(const mk_config* cfg, int device, void* d_arena, uint64_t arena_by
  * norm's 1/rms factor, so steps of 1-2 token rows (up to 8 on the matrix cores) compute it in the
  * attention output projection's phase and route right after it. Setting the environment variable
  * MK_NO_ROUTER_FUSION makes every step use the separate router phase instead (for comparisons);
- * MK_NO_MERGE_FUSION likewise keeps the split-KV merge and W_uv in separate phases at 1, 2, 4 and 8 token rows.
+ * MK_NO_MERGE_FUSION likewise keeps the split-KV merge and W_uv in separate phases at 1 to 8 token rows.
  * (The pages' demos likewise prepare their kernel layouts from the checkpoints before serving:
  * tpu-megakernels README, section "Setup".) The source of each descriptor must stay valid until the
  * stream reaches the copy. MK_E_INVAL for an unknown tensor, a wrong byte count or a NULL source. */

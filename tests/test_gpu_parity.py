@@ -245,13 +245,13 @@ def test_router_fusion_against_router_phase(B, T, kv_len, rows, monkeypatch):
 
 
 # The split-KV merge and W_uv in one phase (1 and 2 token rows of MLA layers on the vector executor,
-# where 4 or 2 workgroups split each head's latent values and the last adds their partials, and 4
-# and 8 rows on the matrix cores, whole heads per workgroup)
+# where 4 or 2 workgroups split each head's latent values and the last adds their partials, and 3
+# to 8 rows on the matrix cores, whole heads per workgroup)
 # against the separate merge phase (MK_NO_MERGE_FUSION): both match the oracle, select the same
 # experts, and their logits agree to fp32 summation-order differences. 1 row over 5 positions has a
 # single split.
 @pytest.mark.parametrize("B,T,kv_len", [(2, 1, 4096), (1, 2, 300), (1, 1, 4096), (1, 1, 5), (4, 1, 4096),
-                                         (1, 4, 300), (8, 1, 4096), (2, 4, 300)])
+                                         (1, 4, 300), (8, 1, 4096), (2, 4, 300), (1, 7, 4096), (3, 1, 500)])
 def test_merge_fusion_against_merge_phase(B, T, kv_len, monkeypatch):
     runs = {}
     for fused in (True, False):
